@@ -1,0 +1,477 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each check cites the passage or identity it follows.  The `check_*`
+helpers raise AssertionError; the tests call them on the oracle as it is,
+and the planted-mistake tests at the end call them on an oracle with one
+plausible mistake patched in, to show that the pins would catch it.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+from conftest import golden
+from oracle import moe as O
+import datagen
+
+
+def _route_one(x, W_r, k, b_r=None):
+    x64 = np.asarray(x, dtype=np.float64)
+    z = O.router_logits(x64, W_r, b_r)
+    p = O.softmax(z)
+    idx = O.top_k(z, k)
+    g = O.gates(z, p, idx)
+    return z, p, idx, g
+
+
+# ---------------------------------------------------------------------------
+# softmax: the typical-logit table and a library routine
+# ---------------------------------------------------------------------------
+
+def check_softmax_table():
+    g = golden("softmax_typical_logits.json")
+    for case in g["cases"]:
+        p = O.softmax(np.array([case["logits"]]))[0]
+        assert np.allclose(np.round(p, g["digits"]), case["probs"], atol=0, rtol=0), p
+        assert abs(p.sum() - 1.0) < 1e-15
+
+
+def test_softmax_table():
+    check_softmax_table()
+
+
+def test_softmax_matches_scipy_and_is_shift_invariant():
+    rng = np.random.default_rng(1)
+    z = rng.normal(size=(50, 17)) * 30
+    assert np.allclose(O.softmax(z), scipy.special.softmax(z, axis=1), rtol=1e-13, atol=1e-300)
+    assert np.allclose(O.softmax(z + 1000.0), O.softmax(z), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the worked top-2 example
+# ---------------------------------------------------------------------------
+
+def _worked_router():
+    g = golden("worked_top2.json")
+    x = np.array(g["x"])
+    l = np.array(g["router_logits"])
+    # W_r such that W_r x = l: W_r = l x^T / |x|^2 (the page's x . W_g, transposed)
+    W_r = (np.outer(l, x) / np.dot(x, x)).astype(np.float32)
+    return g, x, l, W_r
+
+
+def check_worked_top2():
+    g, x, l, W_r = _worked_router()
+    z, p, idx, gate = _route_one(x[None, :], W_r, g["k"])
+    assert np.allclose(z[0], l, atol=1e-6)
+    assert sorted(idx[0].tolist()) == g["kept_experts"]
+    assert idx[0].tolist() == [1, 0]          # best first: 1.6 > 1.05
+    G = np.zeros(len(l))
+    G[idx[0]] = gate[0]
+    assert np.round(G, g["digits"]).tolist() == g["G"], G
+    # renormalising the full-softmax probabilities of the kept pair gives the same gates
+    pk = p[0, idx[0]]
+    assert np.allclose(pk / pk.sum(), gate[0], rtol=1e-6)
+
+
+def test_worked_top2():
+    check_worked_top2()
+
+
+def test_worked_top2_output_is_gate_weighted_sum():
+    """y = 0.366 E_0(x) + 0.634 E_1(x) for the worked example, with random experts."""
+    g, x, l, W_r = _worked_router()
+    rng = np.random.default_rng(3)
+    E, d, f = 4, 3, 5
+    W1 = rng.normal(size=(E, f, d)).astype(np.float32)
+    W2 = rng.normal(size=(E, d, f)).astype(np.float32)
+    r = O.forward(x[None, :].astype(np.float32), W_r, W1, W2, k=2, cf=4.0, alpha=0.01,
+                  act="relu", dtype="f32")
+    e0 = O.expert_ffn(x[None, :], W1[0].astype(np.float64), W2[0].astype(np.float64), "relu")
+    e1 = O.expert_ffn(x[None, :], W1[1].astype(np.float64), W2[1].astype(np.float64), "relu")
+    G0 = float(r["gate"][0, 1])
+    G1 = float(r["gate"][0, 0])
+    assert round(G0, 3) == 0.366 and round(G1, 3) == 0.634
+    assert np.allclose(r["y"][0], G0 * e0[0] + G1 * e1[0], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# ties: the all-zero router
+# ---------------------------------------------------------------------------
+
+def check_tie_break():
+    g = golden("tie_break.json")
+    E, k = g["E"], g["k"]
+    rng = np.random.default_rng(5)
+    T, d = 200, 12
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    W_r = np.zeros((E, d), dtype=np.float32)
+    r = O.forward(x, W_r, np.zeros((E, 4, d), np.float32), np.zeros((E, d, 4), np.float32),
+                  k=k, cf=float(E), alpha=0.01, act="relu", dtype="f32")
+    assert (r["expert_idx"] == np.array(g["chosen"])[None, :]).all()
+    rc = r["route_count"]
+    assert all(rc[e] == 0 for e in g["empty_experts"])
+    assert rc[0] == T and rc[1] == T
+    # k = 1 with capacity: a closed form -- tokens 0..C-1 keep slot t, the rest drop
+    r1 = O.forward(x, W_r, np.zeros((E, 4, d), np.float32), np.zeros((E, d, 4), np.float32),
+                   k=1, cf=1.0, alpha=0.01, act="relu", dtype="f32")
+    C = r1["C"]
+    assert C == 25
+    assert (r1["slot"][:C, 0] == np.arange(C)).all()
+    assert (r1["slot"][C:, 0] == -1).all() and (r1["drop_mask"][C:, 0] == 1).all()
+    assert (r1["drop_mask"][:C, 0] == 0).all()
+    assert r1["expert_count"].tolist() == [C] + [0] * (E - 1)
+
+
+def test_tie_break():
+    check_tie_break()
+
+
+# ---------------------------------------------------------------------------
+# fp32 router: the bf16 collapse
+# ---------------------------------------------------------------------------
+
+def check_fp32_router():
+    g = golden("bf16_collapse.json")
+    # the page's scores, with the experts swapped so that a bf16 router
+    # (which would tie, and tie-break to expert 0) picks a different expert
+    scores = list(reversed(g["logits"]))         # [4.00, 4.01]
+    bits = datagen.f32_to_bf16_bits(np.array(scores, np.float32))
+    assert (datagen.bf16_bits_to_f32(bits) == g["bf16_value"]).all()   # both collapse to 4.0
+    W_r = np.array(scores, dtype=np.float32)[:, None]
+    z, p, idx, gate = _route_one(np.ones((1, 1)), W_r, 1)
+    assert idx[0, 0] == 1 - g["fp32_argmax"]
+    assert z[0, 1] - z[0, 0] > 0.005
+
+
+def test_fp32_router():
+    check_fp32_router()
+
+
+def test_bf16_spacing():
+    g = golden("bf16_collapse.json")
+    four = datagen.f32_to_bf16_bits(np.array([4.0], np.float32)).astype(np.uint32)
+    nxt = datagen.bf16_bits_to_f32((four + 1).astype(np.uint16))[0]
+    assert nxt - 4.0 == g["bf16_spacing_4_to_8"]
+
+
+def test_router_logits_are_correctly_rounded_fp32():
+    """The fp32 logit is the fp64 dot product rounded once (checked with exact fractions)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=(6, 7)).astype(np.float32)
+    W = rng.normal(size=(3, 7)).astype(np.float32)
+    z = O.router_logits(x.astype(np.float64), W)
+    for t in range(6):
+        for i in range(3):
+            exact = sum(Fraction(float(W[i, j])) * Fraction(float(x[t, j])) for j in range(7))
+            below = np.float32(float(exact))
+            # the fp32 neighbours of the exact value bracket the result within one ulp
+            assert abs(Fraction(float(z[t, i])) - exact) <= abs(
+                Fraction(float(np.spacing(np.float32(abs(below)))))) / 2 + Fraction(1, 10**30)
+
+
+# ---------------------------------------------------------------------------
+# auxiliary loss: uniform value 1, Cauchy-Schwarz
+# ---------------------------------------------------------------------------
+
+def check_aux_uniform():
+    rng = np.random.default_rng(11)
+    for k in (1, 2):
+        E, T, d = 8, 64, 5
+        x = rng.normal(size=(T, d))
+        z, p, idx, g = _route_one(x, np.zeros((E, d), np.float32), k)
+        # all-zero router: P_i = 1/E exactly, so N sum f_i P_i = sum f_i = 1
+        assert abs(O.aux_loss(p, idx, E, 0.01) - 0.01) < 1e-15
+    # balanced choices: f_i = 1/E, so N sum f_i P_i = sum P_i = 1 whatever P is
+    E = 6
+    T = E * 7
+    x = np.zeros((T, E))
+    x[np.arange(T), np.arange(T) % E] = 1.0
+    x += rng.normal(size=x.shape) * 0.01
+    W_r = (np.eye(E) * 3.0).astype(np.float32)
+    z, p, idx, g = _route_one(x, W_r, 1)
+    assert (np.bincount(idx[:, 0], minlength=E) == T // E).all()
+    assert abs(O.aux_loss(p, idx, E, 1.0) - 1.0) < 1e-12
+
+
+def test_aux_uniform():
+    check_aux_uniform()
+
+
+def test_aux_cauchy_schwarz():
+    """When P equals f (near one-hot probabilities), N sum f_i^2 >= 1, equality iff uniform."""
+    E, T = 5, 100
+    x = np.zeros((T, E))
+    hot = np.array([0] * 40 + [1] * 30 + [2] * 20 + [3] * 10)
+    x[np.arange(T), hot] = 1.0
+    W_r = (np.eye(E) * 60.0).astype(np.float32)
+    z, p, idx, g = _route_one(x, W_r, 1)
+    f = np.bincount(idx[:, 0], minlength=E) / T
+    aux = O.aux_loss(p, idx, E, 1.0)
+    assert abs(aux - E * np.sum(f * f)) < 1e-12
+    assert aux > 1.0
+
+
+def test_aux_k2_counts_both_ranks():
+    """k = 2: f counts both choices over k T, so a balanced pair split gives exactly 1.
+
+    First choices alone are unbalanced here (experts 0 and 3 only), so a loss
+    that counted only rank 0 would not give 1.
+    """
+    E = 4
+    pref = [(0, 1), (0, 2), (3, 1), (3, 2)]
+    x = np.zeros((len(pref), E))
+    for t, (a, b) in enumerate(pref):
+        x[t, a] = 2.0
+        x[t, b] = 1.0
+    W_r = np.eye(E, dtype=np.float32)
+    z, p, idx, g = _route_one(x, W_r, 2)
+    assert idx.tolist() == [list(q) for q in pref]
+    assert (np.bincount(idx.reshape(-1), minlength=E) == 2).all()
+    assert abs(O.aux_loss(p, idx, E, 1.0) - 1.0) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# capacity and slots
+# ---------------------------------------------------------------------------
+
+def check_capacity_exercise():
+    g = golden("capacity_exercise.json")
+    E, k, T, cf = g["E"], g["k"], g["T"], g["cf"]
+    C = O.capacity(T, E, k, cf)
+    assert C == g["C"]
+    t = np.arange(T)
+    uni = np.stack([(2 * t) % E, (2 * t + 1) % E], axis=1)
+    assert (np.bincount(uni.reshape(-1), minlength=E) == g["uniform_per_expert"]).all()
+    slot, drop, cnt = O.assign_slots(uni, E, C)
+    assert int(drop.sum()) == g["uniform_dropped"]
+    hot = np.where(t[:, None] < 512,
+                   np.stack([np.zeros(T, int), 1 + t % 7], axis=1),
+                   np.stack([1 + t % 7, 1 + (t + 1) % 7], axis=1))
+    n_hot = int((hot == 0).sum())
+    assert n_hot == g["hot_expert_assignments"] == round(g["hot_expert_share"] * k * T)
+    slot, drop, cnt = O.assign_slots(hot, E, C)
+    assert int(drop.sum()) == g["hot_expert_dropped"]
+    assert round(100.0 * drop.sum() / (k * T), 1) == g["dropped_fraction_percent"]
+    # the dropped ones are the hot expert's latest tokens (token order)
+    assert (drop[:C, 0] == 0).all() and (drop[C:512, 0] == 1).all()
+    assert cnt[0] == C
+
+
+def test_capacity_exercise():
+    check_capacity_exercise()
+
+
+def check_rank_major():
+    """GShard rule: every first choice is placed before any second choice."""
+    idx = np.array([[0, 1], [1, 2]])
+    slot, drop, cnt = O.assign_slots(idx, 3, 1)
+    # token 1's first choice (expert 1) takes the only slot; token 0's second choice drops
+    assert slot[1, 0] == 0 and drop[1, 0] == 0
+    assert drop[0, 1] == 1 and slot[0, 1] == -1
+    assert cnt.tolist() == [1, 1, 1]
+
+
+def test_rank_major():
+    check_rank_major()
+
+
+def test_capacity_rounding_covers_even_split():
+    """cf = 1: slots cover the ideal even split, so a perfectly even routing never drops."""
+    for T, E in [(10, 3), (1000, 7), (16384, 64), (513, 8)]:
+        C = O.capacity(T, E, 1, 1.0)
+        assert C >= T / E and C - 1 < T / E
+        idx = (np.arange(T) % E)[:, None]
+        slot, drop, cnt = O.assign_slots(idx, E, C)
+        assert drop.sum() == 0
+    assert O.capacity(1000, 10, 1, 1.1) == 110
+    assert O.capacity(16, 2, 2, 8.0) == 16        # never above T
+
+
+def test_idle_capacity():
+    """No drops and exact C: idle fraction of the slots is 1 - 1/cf ([CMU-L16] section 6.1)."""
+    T, E = 1024, 8
+    idx = (np.arange(T) % E)[:, None]
+    for cf in (2.0, 1.25, 1.0):
+        C = O.capacity(T, E, 1, cf)
+        slot, drop, cnt = O.assign_slots(idx, E, C)
+        assert drop.sum() == 0
+        idle = 1.0 - cnt.sum() / (E * C)
+        assert abs(idle - (1.0 - 1.0 / cf)) < 1e-12
+
+
+def test_slot_invariants_random():
+    rng = np.random.default_rng(21)
+    for k in (1, 2, 3):
+        T, E = 300, 7
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        C = O.capacity(T, E, k, 0.8)
+        slot, drop, cnt = O.assign_slots(idx, E, C)
+        assert cnt.sum() + drop.sum() == k * T
+        assert ((slot >= 0) == (drop == 0)).all()
+        for e in range(E):
+            s = []
+            for j in range(k):
+                for t in range(T):
+                    if idx[t, j] == e and drop[t, j] == 0:
+                        s.append(slot[t, j])
+            assert s == list(range(len(s))) and len(s) == cnt[e] <= C
+
+
+# ---------------------------------------------------------------------------
+# experts: the split identity
+# ---------------------------------------------------------------------------
+
+def _split_identity(act):
+    g = golden("split_identity.json")
+    n = g["n_experts"]
+    rng = np.random.default_rng(7)
+    d, f, T = 6, 4, 5
+    W = [rng.normal(size=(f, d)) for _ in range(n)]
+    V = [rng.normal(size=(f, d)) for _ in range(n)]
+    b = [rng.normal(size=f) for _ in range(n)]
+    U = [rng.normal(size=(d, f)) for _ in range(n)]
+    c = rng.normal(size=d)
+    x = rng.normal(size=(T, d))
+    Wd, Vd, bd, Ud = np.vstack(W), np.vstack(V), np.concatenate(b), np.hstack(U)
+    if act == "relu":
+        dense = (Ud @ np.maximum(Wd @ x.T + bd[:, None], 0.0)).T + c
+    else:
+        a = Wd @ x.T
+        dense = (Ud @ (a * scipy.special.expit(a) * (Vd @ x.T))).T + c
+    def expert(i, ci):
+        if act == "relu":
+            return O.expert_ffn(x, W[i], U[i], "relu", b1=b[i], b2=ci)
+        return O.expert_ffn(x, W[i], U[i], "swiglu", b2=ci, W3=V[i])
+    split = sum(expert(i, c if i == 0 else np.zeros(d)) for i in range(n))
+    assert np.max(np.abs(split - dense)) < 1e-12
+    full = sum(expert(i, c) for i in range(n))
+    assert np.allclose(full - dense, (n - 1) * c[None, :], atol=1e-12)
+    assert np.max(np.abs(full - dense)) > 0.1
+
+
+def check_split_identity():
+    _split_identity("relu")
+    _split_identity("swiglu")
+
+
+def test_split_identity():
+    check_split_identity()
+
+
+def test_silu_values():
+    a = np.array([0.0, 1.0, -1.0, 30.0, -30.0])
+    assert np.allclose(O.silu(a), a * scipy.special.expit(a), rtol=1e-15, atol=1e-300)
+    assert O.silu(np.array([1.0]))[0] == pytest.approx(0.7310585786300049, rel=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# sizes the pages print for the Mixtral-shaped workload
+# ---------------------------------------------------------------------------
+
+def test_mixtral_sizes():
+    g = golden("sizes.json")
+    c = datagen.CONFIGS["mixtral"]
+    per_expert = 3 * c["d"] * c["f"]
+    assert round(per_expert / 1e6, 1) == g["mixtral_expert_params_millions"]
+    disp = c["T"] * c["k"] * c["d"] * 2
+    assert round(disp / 1e6) == g["mixtral_dispatch_MB"]
+    c5 = datagen.CONFIGS["many_expert"]
+    assert 2 * c5["E"] * c5["d"] * c5["f"] == 2 ** 31      # ~2.1e9 expert parameters
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+# ---------------------------------------------------------------------------
+
+def _top_k_bf16(z, k):
+    bits = datagen.f32_to_bf16_bits(np.asarray(z, np.float32))
+    return np.argsort(-datagen.bf16_bits_to_f32(bits), axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def _top_k_high_tie(z, k):
+    zz = np.asarray(z, np.float32)[:, ::-1]
+    o = np.argsort(-zz, axis=1, kind="stable")[:, :k]
+    return (zz.shape[1] - 1 - o).astype(np.int32)
+
+
+def _gates_raw(z, p, idx):
+    return p[np.arange(idx.shape[0])[:, None], idx].astype(np.float32)
+
+
+def _assign_token_major(idx, E, C):
+    T, k = idx.shape
+    fill = [0] * E
+    slot = np.full((T, k), -1, np.int32)
+    drop = np.zeros((T, k), np.uint8)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if fill[e] < C:
+                slot[t, j] = fill[e]
+                fill[e] += 1
+            else:
+                drop[t, j] = 1
+    return slot, drop, np.array(fill)
+
+
+def _capacity_floor(T, E, k, cf):
+    return int(min(T, math.floor(k * T * cf / E)))
+
+
+def _softmax_wrong_axis(z):
+    e = np.exp(np.asarray(z, np.float64))
+    return e / e.sum(axis=0, keepdims=True)   # normalises over tokens, not experts
+
+
+@pytest.mark.parametrize("name,repl,check", [
+    ("top_k", _top_k_bf16, check_fp32_router),
+    ("top_k", _top_k_high_tie, check_tie_break),
+    ("gates", _gates_raw, check_worked_top2),
+    ("assign_slots", _assign_token_major, check_rank_major),
+    ("softmax", _softmax_wrong_axis, check_softmax_table),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, repl, check):
+    monkeypatch.setattr(O, name, repl)
+    with pytest.raises(Exception):
+        check()
+
+
+def test_planted_capacity_floor_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "capacity", _capacity_floor)
+    with pytest.raises(AssertionError):
+        test_capacity_rounding_covers_even_split()
+
+
+def test_planted_bias_on_every_expert_is_caught(monkeypatch):
+    """An expert FFN that adds its output bias twice breaks the split identity."""
+    orig = O.expert_ffn
+
+    def twice(u, W1, W2, act, b1=None, b2=None, W3=None):
+        o = orig(u, W1, W2, act, b1, b2, W3)
+        return o if b2 is None else o + np.asarray(b2)[None, :]
+    monkeypatch.setattr(O, "expert_ffn", twice)
+    with pytest.raises(AssertionError):
+        check_split_identity()
+
+
+def test_planted_transposed_weight_is_caught(monkeypatch):
+    """Using W1 as [d, f] (x W1 instead of W1 x) breaks the split identity."""
+    orig = O.expert_ffn
+
+    def transposed(u, W1, W2, act, b1=None, b2=None, W3=None):
+        W1 = np.asarray(W1)
+        W1t = W1.T.reshape(W1.shape) if W1.shape[0] != W1.shape[1] else W1.T
+        return orig(u, W1t, W2, act, b1, b2, W3)
+    monkeypatch.setattr(O, "expert_ffn", transposed)
+    with pytest.raises(Exception):
+        check_split_identity()
+
+
+def test_planted_first_rank_only_aux_is_caught(monkeypatch):
+    orig = O.aux_loss
+    monkeypatch.setattr(O, "aux_loss", lambda p, idx, E, a: orig(p, idx[:, :1], E, a))
+    with pytest.raises(AssertionError):
+        test_aux_k2_counts_both_ranks()
