@@ -1,0 +1,215 @@
+/*
+ * moe.h -- C ABI of the Switch-Transformer MoE layer forward on MI355X (gfx950).
+ *
+ * Pages cited (title, then section):
+ *   [CS25-L5]  "Lecture05", notes on Stanford CS25 lecture 5 "Scaling
+ *              Transformers through Sparsity"
+ *   [SW-RES]   "Training Stability, Results & Limitations" (Switch results)
+ *   [SW-GLaM]  "从 Switch Transformer 到 GLaM"
+ *   [CMU-L16]  "第 16 讲 · 混合专家（MoE）", notes on CMU 10-423 lecture 16
+ *
+ * Conventions shared by every entry point
+ *   - Sizes: T tokens, d model width, dff expert hidden width, E experts,
+ *     k experts per token, C capacity (slots per expert).
+ *   - Every pointer argument is a DEVICE pointer (hipMalloc'd or a torch
+ *     CUDA tensor) unless stated otherwise.  All arrays are dense, row-major,
+ *     16-byte aligned.  The library never allocates, frees or synchronises;
+ *     every buffer is owned by the caller.  It keeps no global mutable state
+ *     and is safe to call from several threads on distinct streams.
+ *   - dtype: MOE_F32 or MOE_BF16 names the storage type of x, W1, W3, W2,
+ *     b1, b2, the dispatch buffer, the expert outputs and y.  The router
+ *     weight W_r, its bias and the gates are always fp32 ([CS25-L5]
+ *     "稳定训练" and [SW-RES] section 2.1: the router runs in float32 while
+ *     the experts keep bfloat16).  bf16 expert arithmetic accumulates in fp32.
+ *   - Weight orientation follows [SW-GLaM] "Dense Scaling 与 MoE 的核心差异":
+ *     h = W_r x and FFN(x) = W_2 sigma(W_1 x), so W_r is [E, d],
+ *     W1 and W3 are [E, dff, d], W2 is [E, d, dff] (out-features x
+ *     in-features, the layout of torch.nn.Linear weights).
+ *   - Errors: arguments are checked before anything is enqueued; a failed
+ *     check returns MOE_ERR_* and writes nothing.  After each launch the
+ *     HIP launch status is checked (MOE_ERR_HIP).  Faults inside kernels
+ *     surface at the caller's next synchronisation.  After an error the
+ *     contents of the outputs are unspecified.
+ *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 8), d and dff multiples of 8,
+ *     T * k < 2^31, capacity_factor finite and > 0.  T = 0 is accepted:
+ *     nothing is routed, per-expert counts and sums are zero and the
+ *     auxiliary loss is 0.
+ *   - All work is enqueued on `stream` (NULL = the null stream) and the
+ *     call returns without waiting.  Results are deterministic: two calls on
+ *     the same inputs give bitwise identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned buffer */
+    MOE_ERR_UNSUPPORTED = 2,        /* unknown dtype / activation, or a size past a limit */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4                 /* a HIP launch reported an error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(int status);
+
+/*
+ * Expert capacity C = ceil(capacity_factor * k * T / E - 1e-9), clamped to
+ * [0, T].  Host function, no GPU work.
+ * [SW-GLaM] "Expert Capacity 与 Token Dropping": C = (T/N) x capacity factor;
+ * [CMU-L16] exercise 3 scales it by k (1.25 x 2 x 1024 / 8 = 320).  Rounding
+ * up keeps a factor of 1 covering the even split ([CS25-L5] "Capacity
+ * Factor").  Returns -1 for invalid arguments (T < 0, E < 1, k < 1,
+ * capacity_factor not finite or <= 0).
+ */
+int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor);
+
+/* Workspace bytes needed by moe_router / moe_dispatch / moe_expert_ffn /
+ * moe_forward for the given sizes (host functions).  0 means "none";
+ * SIZE_MAX means the sizes are invalid. */
+size_t moe_router_workspace_bytes(int64_t T, int32_t E, int32_t k);
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
+size_t moe_expert_ffn_workspace_bytes(int32_t E, int64_t C, int32_t dff, moe_dtype dt);
+size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
+                           int64_t C, moe_dtype dt, moe_act act);
+
+/*
+ * Where moe_forward keeps its intermediates inside `ws` (byte offsets), so
+ * a caller can read them after the call: slot [T,k] int32, expert_count [E]
+ * int32, route_count [E] int32, prob_sum [E] fp32, the dispatch buffer
+ * xbuf [E,C,d] and the expert outputs ybuf [E,C,d] (storage dtype).
+ * Returns MOE_OK or MOE_ERR_INVALID_ARGUMENT.  Host function.
+ */
+typedef struct {
+    size_t slot, expert_count, route_count, prob_sum, xbuf, ybuf, total;
+} moe_ws_layout;
+moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32_t E,
+                                        int32_t k, int64_t C, moe_dtype dt, moe_act act,
+                                        moe_ws_layout *out /* host pointer */);
+
+/*
+ * Router: logits, softmax, top-k selection and gates for every token.
+ * [SW-GLaM] "Dense Scaling 与 MoE 的核心差异" (h(x) = W_r x, softmax) and
+ * "Switch Transformer：把 MoE 做简单" (i* = argmax p, gate p_{i*});
+ * [CMU-L16] section 2.3 (top-k keeps k logits, softmax over them).
+ *   x           [T, d]  storage dtype
+ *   W_r         [E, d]  fp32;  b_r [E] fp32 added to the logits, or NULL
+ *   expert_idx  [T, k]  int32 out, best first; ties go to the lower index
+ *                       ([CMU-L16] section 2.3: an all-zero router picks
+ *                       the lowest-indexed experts)
+ *   gate        [T, k]  fp32 out; k = 1: full-softmax probability of the
+ *                       chosen expert; k >= 2: softmax over the k kept logits
+ *   prob_sum    [E]     fp32 out, sum over tokens of the softmax p_i(x)
+ *   route_count [E]     int32 out, number of (token, rank) choices per expert
+ *                       (before capacity)
+ * Logits are fp32 ([SW-RES] section 2.1); non-finite inputs do not fault
+ * and still give indices in [0, E).
+ */
+moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                      int64_t T, int32_t d, int32_t E, int32_t k,
+                      int32_t *expert_idx, float *gate, float *prob_sum, int32_t *route_count,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch: capacity slots in token order and the expert-major permutation.
+ * [CS25-L5] "Capacity Factor 与 Token Dropping" (capacity-aware dispatch:
+ * tokens in order fill their expert's C slots, overflow skips the expert);
+ * [CMU-L16] section 6.1 (first choices of all tokens are placed before any
+ * second choice); [SW-GLaM] "All-to-All" (data-sharded -> expert-sharded
+ * layout, here a permutation inside one GPU's memory).
+ *   expert_idx   [T, k]     int32 in, values in [0, E)
+ *   C            capacity (0 <= C <= T), e.g. from moe_capacity
+ *   slot         [T, k]     int32 out, slot within the expert or -1 if dropped
+ *   drop_mask    [T, k]     uint8 out, 1 = this choice was dropped
+ *   expert_count [E]        int32 out, kept choices per expert (<= C)
+ *   xbuf         [E, C, d]  storage dtype out; row s of expert e holds x of the
+ *                           token in slot s; rows >= expert_count[e] are
+ *                           left untouched
+ */
+moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx,
+                        int64_t T, int32_t d, int32_t E, int32_t k, int64_t C,
+                        int32_t *slot, uint8_t *drop_mask, int32_t *expert_count, void *xbuf,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Experts: every expert's FFN on its kept rows, as grouped GEMMs.
+ * ReLU expert y = W_2 relu(W_1 x + b_1) + b_2 ([SW-GLaM] FFN equation;
+ * [CMU-L16] section 2.1); SwiGLU expert y = W_2 (silu(W_1 x) * (W_3 x))
+ * ([CMU-L16] section 2.3, Swish with beta = 1; b1 and b2 must be NULL).
+ *   xbuf  [E, C, d] in, rows < expert_count[e] are read
+ *   W1, W3 [E, dff, d]; W2 [E, d, dff]; b1 [E, dff] or NULL; b2 [E, d] or NULL
+ *   ybuf  [E, C, d] out, rows < expert_count[e] written, others untouched
+ * The hidden activations go through `ws` in the storage dtype.
+ */
+moe_status moe_expert_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count,
+                          int32_t E, int64_t C, int32_t d, int32_t dff,
+                          const void *W1, const void *b1, const void *W3, const void *W2,
+                          const void *b2, moe_act act,
+                          void *ybuf, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Combine and auxiliary loss.
+ * y_t = sum over kept choices j of gate[t,j] * ybuf[expert_idx[t,j], slot[t,j]]
+ * ([CS25-L5] "Switch Layer": gate times expert output; [CMU-L16] section
+ * 2.3), summed in fp32 in rank order and rounded once to the storage dtype.
+ * A dropped choice contributes 0 and gates are not renormalised; a token
+ * with every choice dropped gets y = 0 (it continues on the residual path,
+ * which the caller adds: [CS25-L5] "Capacity Factor", [CMU-L16] section 6.1).
+ * aux_loss[0] = alpha * E * sum_i f_i P_i with f_i = route_count_i / (k T)
+ * and P_i = prob_sum_i / T ([SW-GLaM] "负载均衡"), fp32, computed on the
+ * device in fp64.
+ */
+moe_status moe_combine(const void *ybuf, moe_dtype dt, const int32_t *expert_idx,
+                       const int32_t *slot, const float *gate, const float *prob_sum,
+                       const int32_t *route_count, int64_t T, int32_t d, int32_t E, int32_t k,
+                       int64_t C, float alpha, void *y, float *aux_loss, hipStream_t stream);
+
+/*
+ * The whole layer: router, dispatch, experts, combine and loss, enqueued
+ * back to back with C = moe_capacity(T, E, k, capacity_factor).  Outputs
+ * y [T,d] (storage dtype, MoE branch only), aux_loss [1] fp32,
+ * expert_idx [T,k] int32, gate [T,k] fp32, drop_mask [T,k] uint8; every
+ * other intermediate stays in `ws` (see moe_forward_workspace_layout).
+ */
+moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                       const void *W1, const void *b1, const void *W3, const void *W2,
+                       const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
+                       int32_t E, int32_t k, double capacity_factor, float alpha,
+                       void *y, float *aux_loss, int32_t *expert_idx, float *gate,
+                       uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_forward with stage timing: identical work and results, plus HIP events
+ * recorded on `stream` at the stage boundaries, for callers that time the
+ * stages of the layer ([CS25-L5] "Capacity Factor" asks that dispatch
+ * traffic and step time be logged alongside the routing statistics).
+ * stage_events [MOE_STAGE_EVENTS] host array of caller-created events:
+ *   [0] start  [1] after router  [2] after dispatch (slots, permutation,
+ *   GEMM tile map)  [3] after expert GEMM 1 (+activation)  [4] after expert
+ *   GEMM 2  [5] after combine and loss.
+ * NULL array or NULL entries -> MOE_ERR_INVALID_ARGUMENT, nothing enqueued.
+ */
+#define MOE_STAGE_EVENTS 6
+moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                              const void *W1, const void *b1, const void *W3, const void *W2,
+                              const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
+                              int32_t E, int32_t k, double capacity_factor, float alpha,
+                              void *y, float *aux_loss, int32_t *expert_idx, float *gate,
+                              uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t *stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -236,12 +236,14 @@ def expert_ffn(u: np.ndarray, W1: np.ndarray, W2: np.ndarray, act: str,
 
 
 def experts_by_slot(x64, idx, slot, E, C, W1, W2, act, b1=None, b2=None, W3=None,
-                    dtype="f32", experts=None):
+                    dtype="f32", experts=None, tokens=None):
     """Expert outputs of every kept (token, rank), one batch per expert.
 
     Returns ybuf [E, C, d] float64 (rows at or beyond an expert's count are
     zero) and out [T, k, d] float64 (zero for dropped choices).
-    `experts` limits the work to a subset of experts (others stay zero).
+    `experts` limits the work to a subset of experts and `tokens` to a
+    subset of tokens (everything else stays zero): the same definitions,
+    evaluated on a sample of a workload too large to run whole.
     [CS25-L5] "Capacity Factor": run_batched_experts over the slot lists.
     """
     T, k = idx.shape
@@ -249,8 +251,12 @@ def experts_by_slot(x64, idx, slot, E, C, W1, W2, act, b1=None, b2=None, W3=None
     ybuf = np.zeros((E, C, d), dtype=np.float64)
     out = np.zeros((T, k, d), dtype=np.float64)
     todo = range(E) if experts is None else experts
+    want = np.ones((T, 1), dtype=bool)
+    if tokens is not None:
+        want = np.zeros((T, 1), dtype=bool)
+        want[np.asarray(tokens), 0] = True
     for e in todo:
-        tt, jj = np.nonzero((idx == e) & (slot >= 0))
+        tt, jj = np.nonzero((idx == e) & (slot >= 0) & want)
         if tt.size == 0:
             continue
         order = np.argsort(slot[tt, jj], kind="stable")
@@ -299,12 +305,14 @@ def route(x, W_r, b_r, k, dtype):
 
 
 def forward(x, W_r, W1, W2, *, k, cf, alpha, act, dtype, W3=None, b1=None, b2=None,
-            b_r=None, experts=None):
+            b_r=None, experts=None, tokens=None):
     """The full layer forward; returns a dict of every intermediate.
 
     Keys: z (fp32 logits), p (float64 probabilities), expert_idx, gate,
     prob_sum (sum_t p), route_count, C, slot, drop_mask, expert_count,
     ybuf [E, C, d], y [T, d] (float64, MoE branch only), aux_loss.
+    With `tokens` (or `experts`) given, expert outputs, ybuf and y are only
+    evaluated for those tokens (experts); the routing is always complete.
     """
     T = x.shape[0]
     E = W_r.shape[0]
@@ -312,7 +320,7 @@ def forward(x, W_r, W1, W2, *, k, cf, alpha, act, dtype, W3=None, b1=None, b2=No
     C = capacity(T, E, k, cf)
     slot, drop, count = assign_slots(idx, E, C)
     ybuf, out = experts_by_slot(x64, idx, slot, E, C, W1, W2, act, b1, b2, W3,
-                                dtype, experts)
+                                dtype, experts, tokens)
     y = combine(g, drop, out)
     return dict(z=z, p=p, expert_idx=idx, gate=g, prob_sum=p.sum(axis=0),
                 route_count=route_count(idx, E), C=C, slot=slot, drop_mask=drop,
@@ -320,11 +328,11 @@ def forward(x, W_r, W1, W2, *, k, cf, alpha, act, dtype, W3=None, b1=None, b2=No
                 aux_loss=aux_loss(p, idx, E, alpha))
 
 
-def forward_cfg(cfg: dict, experts=None) -> dict:
+def forward_cfg(cfg: dict, experts=None, tokens=None) -> dict:
     """forward() on a dict produced by datagen.make / datagen.random_case."""
     return forward(cfg["x"], cfg["W_r"], cfg["W1"], cfg["W2"], k=cfg["k"], cf=cfg["cf"],
                    alpha=cfg["alpha"], act=cfg["act"], dtype=cfg["dtype"], W3=cfg["W3"],
-                   b1=cfg["b1"], b2=cfg["b2"], b_r=cfg["b_r"], experts=experts)
+                   b1=cfg["b1"], b2=cfg["b2"], b_r=cfg["b_r"], experts=experts, tokens=tokens)
 
 
 def near_tie_tokens(z: np.ndarray, k: int, gap: float = 1e-5) -> np.ndarray:

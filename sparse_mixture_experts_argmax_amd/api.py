@@ -1,0 +1,208 @@
+"""Python face of the C ABI: torch tensors in, torch tensors out.
+
+Argument marshalling only -- shapes, dtypes, device pointers and the current
+HIP stream are passed to libmoe.so, and every step of the layer runs in its
+kernels.  Tensors must live on a ROCm device; bf16 layers take torch.bfloat16
+x / expert weights, fp32 layers torch.float32; the router weight, its bias
+and the gates are always float32.
+
+Layouts (see include/moe.h): x [T, d]; W_r [E, d]; W1, W3 [E, dff, d];
+W2 [E, d, dff]; b1 [E, dff]; b2 [E, d]; b_r [E].
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+_ACT = {"relu": L.MOE_ACT_RELU, "swiglu": L.MOE_ACT_SWIGLU}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.MOE_BF16
+    if t.dtype == torch.float32:
+        return L.MOE_F32
+    raise TypeError(f"unsupported storage dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _same(dtype, *ts):
+    for t in ts:
+        if t is not None and t.dtype != dtype:
+            raise TypeError(f"expected {dtype}, got {t.dtype}")
+
+
+def capacity(T: int, E: int, k: int, capacity_factor: float) -> int:
+    """C = ceil(capacity_factor * k * T / E), at most T (host arithmetic in the library)."""
+    c = L.LIB.moe_capacity(T, E, k, capacity_factor)
+    if c < 0:
+        raise ValueError("invalid capacity arguments")
+    return int(c)
+
+
+def workspace_bytes(T, d, dff, E, k, C, dtype, act="relu") -> int:
+    code = L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32
+    n = L.LIB.moe_workspace_bytes(T, d, dff, E, k, C, code, _ACT[act])
+    if n == L.SIZE_MAX:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def _workspace(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def router(x, W_r, k: int = 1, b_r=None, workspace=None):
+    """Router: returns (expert_idx [T,k] int32, gate [T,k] fp32, prob_sum [E] fp32, route_count [E] int32)."""
+    T, d = x.shape
+    E = W_r.shape[0]
+    dev = x.device
+    _same(torch.float32, W_r, b_r)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
+    route_count = torch.empty(E, dtype=torch.int32, device=dev)
+    need = L.LIB.moe_router_workspace_bytes(T, E, k)
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid router sizes")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    L.check("moe_router", L.LIB.moe_router(
+        _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
+        _ptr(prob_sum), _ptr(route_count), _ptr(ws), ws.numel(), _stream(dev)))
+    return idx, gate, prob_sum, route_count
+
+
+def dispatch(x, expert_idx, E: int, C: int, workspace=None):
+    """Dispatch: returns (slot [T,k] int32, drop_mask [T,k] uint8, expert_count [E] int32, xbuf [E,C,d])."""
+    T, d = x.shape
+    k = expert_idx.shape[1]
+    dev = x.device
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+    drop = torch.empty((T, k), dtype=torch.uint8, device=dev)
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    xbuf = torch.empty((E, C, d), dtype=x.dtype, device=dev)
+    need = L.LIB.moe_dispatch_workspace_bytes(T, E, k)
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid dispatch sizes")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    L.check("moe_dispatch", L.LIB.moe_dispatch(
+        _ptr(x), _dtype_code(x), _ptr(expert_idx), T, d, E, k, C, _ptr(slot), _ptr(drop),
+        _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
+    return slot, drop, count, xbuf
+
+
+def expert_ffn(xbuf, expert_count, W1, W2, *, W3=None, b1=None, b2=None, act="relu",
+               workspace=None, ybuf=None):
+    """Grouped expert FFN: returns ybuf [E, C, d] (rows >= expert_count[e] untouched)."""
+    E, C, d = xbuf.shape
+    dff = W1.shape[1]
+    dev = xbuf.device
+    _same(xbuf.dtype, W1, W2, W3, b1, b2)
+    if ybuf is None:
+        ybuf = torch.empty_like(xbuf)
+    need = L.LIB.moe_expert_ffn_workspace_bytes(E, C, dff, _dtype_code(xbuf))
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid expert sizes")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    L.check("moe_expert_ffn", L.LIB.moe_expert_ffn(
+        _ptr(xbuf), _dtype_code(xbuf), _ptr(expert_count), E, C, d, dff, _ptr(W1), _ptr(b1),
+        _ptr(W3), _ptr(W2), _ptr(b2), _ACT[act], _ptr(ybuf), _ptr(ws), ws.numel(), _stream(dev)))
+    return ybuf
+
+
+def combine(ybuf, expert_idx, slot, gate, prob_sum, route_count, T: int, alpha: float = 1e-2):
+    """Combine and aux loss: returns (y [T, d], aux_loss [1] fp32)."""
+    E, C, d = ybuf.shape
+    k = expert_idx.shape[1]
+    dev = ybuf.device
+    y = torch.empty((T, d), dtype=ybuf.dtype, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    L.check("moe_combine", L.LIB.moe_combine(
+        _ptr(ybuf), _dtype_code(ybuf), _ptr(expert_idx), _ptr(slot), _ptr(gate), _ptr(prob_sum),
+        _ptr(route_count), T, d, E, k, C, alpha, _ptr(y), _ptr(aux), _stream(dev)))
+    return y, aux
+
+
+class ForwardPlan:
+    """The fused layer for fixed sizes, with its outputs and workspace allocated once.
+
+    plan = ForwardPlan(T, d, dff, E, k, dtype, act=..., capacity_factor=..., alpha=...)
+    y, aux, idx, gate, drop = plan(x, W_r, W1, W2, W3=..., b1=..., b2=..., b_r=...)
+    Each call overwrites the same output tensors.
+    """
+
+    def __init__(self, T, d, dff, E, k, dtype, *, act="relu", capacity_factor=1.25, alpha=1e-2,
+                 device="cuda"):
+        self.T, self.d, self.dff, self.E, self.k = T, d, dff, E, k
+        self.dtype, self.act = dtype, act
+        self.capacity_factor, self.alpha = float(capacity_factor), float(alpha)
+        self.C = capacity(T, E, k, capacity_factor)
+        dev = torch.device(device)
+        self.device = dev
+        self.y = torch.empty((T, d), dtype=dtype, device=dev)
+        self.aux = torch.empty(1, dtype=torch.float32, device=dev)
+        self.expert_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.drop_mask = torch.empty((T, k), dtype=torch.uint8, device=dev)
+        self.ws = _workspace(workspace_bytes(T, d, dff, E, k, self.C, dtype, act), dev)
+        lay = L.WsLayout()
+        L.check("moe_forward_workspace_layout", L.LIB.moe_forward_workspace_layout(
+            T, d, dff, E, k, self.C, L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32,
+            _ACT[act], lay))
+        self.layout = lay
+
+    def __call__(self, x, W_r, W1, W2, *, W3=None, b1=None, b2=None, b_r=None, stream=None):
+        if tuple(x.shape) != (self.T, self.d) or x.dtype != self.dtype:
+            raise ValueError("x does not match the plan")
+        _same(self.dtype, W1, W2, W3, b1, b2)
+        _same(torch.float32, W_r, b_r)
+        s = stream.cuda_stream if stream is not None else _stream(self.device)
+        L.check("moe_forward", L.LIB.moe_forward(
+            _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
+            _ptr(b2), _ACT[self.act], self.T, self.d, self.dff, self.E, self.k,
+            self.capacity_factor, self.alpha, _ptr(self.y), _ptr(self.aux), _ptr(self.expert_idx),
+            _ptr(self.gate), _ptr(self.drop_mask), _ptr(self.ws), self.ws.numel(), s))
+        return self.y, self.aux, self.expert_idx, self.gate, self.drop_mask
+
+    def intermediate(self, name: str) -> torch.Tensor:
+        """A view of an intermediate inside the workspace (valid after a call)."""
+        lay, T, k, E, C, d = self.layout, self.T, self.k, self.E, self.C, self.d
+        es = 2 if self.dtype == torch.bfloat16 else 4
+        spec = {
+            "slot": (lay.slot, (T, k), torch.int32, 4),
+            "expert_count": (lay.expert_count, (E,), torch.int32, 4),
+            "route_count": (lay.route_count, (E,), torch.int32, 4),
+            "prob_sum": (lay.prob_sum, (E,), torch.float32, 4),
+            "xbuf": (lay.xbuf, (E, C, d), self.dtype, es),
+            "ybuf": (lay.ybuf, (E, C, d), self.dtype, es),
+        }[name]
+        off, shape, dt, sz = spec
+        n = 1
+        for s in shape:
+            n *= s
+        return self.ws[off:off + n * sz].view(dt).view(shape)
+
+
+def forward(x, W_r, W1, W2, *, W3=None, b1=None, b2=None, b_r=None, k=1, capacity_factor=1.25,
+            alpha=1e-2, act="relu"):
+    """The whole layer: returns (y, aux_loss, expert_idx, gate, drop_mask)."""
+    T, d = x.shape
+    E = W_r.shape[0]
+    dff = W1.shape[1]
+    plan = ForwardPlan(T, d, dff, E, k, x.dtype, act=act, capacity_factor=capacity_factor,
+                       alpha=alpha, device=x.device)
+    return plan(x, W_r, W1, W2, W3=W3, b1=b1, b2=b2, b_r=b_r)

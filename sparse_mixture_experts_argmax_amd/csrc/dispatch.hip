@@ -1,0 +1,159 @@
+// Dispatch: capacity slots in token order, drops, and the expert-major permutation.
+//
+// [CS25-L5] "Capacity Factor 与 Token Dropping": tokens, in order, take the
+// next free slot of their expert while fewer than C are taken; the rest skip
+// the expert.  [CMU-L16] section 6.1: every first choice is placed before
+// any second choice.  The slot of choice (t, j) is therefore the number of
+// choices of the same expert that come before it in the order
+// (rank 0, token 0..T-1), (rank 1, token 0..T-1), ...
+//
+// That count is computed without atomics, so it is deterministic:
+//   slot_rank  -- per block of 256 tokens and rank j: the position of each
+//                 choice among same-expert choices of the block (wave ballots
+//                 over the bits of the expert index, then the counts of the
+//                 earlier waves) and the block's per-expert histogram.
+//   slot_scan  -- per expert, an exclusive scan of the histograms in
+//                 (rank, block) order: the slots taken before each block.
+//   permute    -- slot = scan + in-block position; slots >= C drop; kept
+//                 rows are copied x[t] -> xbuf[e, slot] with 16-byte moves.
+// [SW-GLaM] "All-to-All": the data-sharded -> expert-sharded relayout, done
+// here as a permutation inside one GPU's memory.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(DISPATCH_TOK_BLOCK) void slot_rank_kernel(
+    const int32_t *__restrict__ expert_idx, int64_t T, int E, int k, int nbits,
+    int32_t *__restrict__ rank, int32_t *__restrict__ hist) {
+    extern __shared__ int sc[];                     // [4 waves][E]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = blockIdx.y;
+    const int nblk = gridDim.x;
+    const int64_t t = (int64_t)blockIdx.x * DISPATCH_TOK_BLOCK + tid;
+
+    for (int q = tid; q < 4 * E; q += DISPATCH_TOK_BLOCK) sc[q] = 0;
+    int e = (t < T) ? expert_idx[t * k + j] : -1;
+    const bool ok = e >= 0 && e < E;               // out-of-range indices are treated as dropped
+    if (!ok) e = 0;
+
+    // lanes of this wave that chose the same expert
+    uint64_t same = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(ok && bit);
+        same &= bit ? m : ~m;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rw = __popcll(same & below);
+    __syncthreads();
+    if (ok && rw == 0) sc[wave * E + e] = __popcll(same);
+    __syncthreads();
+    if (ok) {
+        int r = rw;
+        for (int w = 0; w < wave; ++w) r += sc[w * E + e];
+        rank[(int64_t)j * T + t] = r;
+    }
+    // histogram, laid out [E][k * nblk] so that the scan reads it contiguously
+    for (int n = tid; n < E; n += DISPATCH_TOK_BLOCK)
+        hist[(int64_t)n * k * nblk + (int64_t)j * nblk + blockIdx.x] =
+            ((sc[n] + sc[E + n]) + sc[2 * E + n]) + sc[3 * E + n];
+}
+
+// One wave per expert: exclusive scan over (rank, block), in place.
+__global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hist, int L, int E,
+                                                        int64_t C, int32_t *__restrict__ expert_count) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    int32_t *h = hist + (int64_t)e * L;
+    int run = 0;
+    for (int b0 = 0; b0 < L; b0 += 64) {
+        const int b = b0 + lane;
+        const int v = (b < L) ? h[b] : 0;
+        int inc = v;
+        for (int m = 1; m < 64; m <<= 1) {
+            const int u = __shfl_up(inc, m);
+            if (lane >= m) inc += u;
+        }
+        if (b < L) h[b] = run + inc - v;
+        run += __shfl(inc, 63);
+    }
+    if (lane == 0) expert_count[e] = (int32_t)((int64_t)run < C ? (int64_t)run : C);
+}
+
+// One wave per (token, rank) choice; lanes move 16-byte pieces of the row.
+__global__ __launch_bounds__(256) void permute_kernel(
+    const uint8_t *__restrict__ x, int row_bytes, const int32_t *__restrict__ expert_idx,
+    const int32_t *__restrict__ rank, const int32_t *__restrict__ base, int64_t T, int E, int k,
+    int nblk, int64_t C, int32_t *__restrict__ slot, uint8_t *__restrict__ drop,
+    uint8_t *__restrict__ xbuf) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int pieces = row_bytes >> 4;
+    for (int64_t a = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); a < T * k; a += nwaves) {
+        const int64_t t = a / k;
+        const int j = (int)(a - t * k);
+        const int e = expert_idx[a];
+        int64_t s = -1;
+        if (e >= 0 && e < E) {
+            const int blk = (int)(t / DISPATCH_TOK_BLOCK);
+            s = (int64_t)base[(int64_t)e * k * nblk + (int64_t)j * nblk + blk] + rank[(int64_t)j * T + t];
+            if (s >= C) s = -1;
+        }
+        if (lane == 0) {
+            slot[a] = (int32_t)s;
+            drop[a] = (s < 0) ? 1 : 0;
+        }
+        if (s >= 0) {
+            const uint8_t *src = x + t * row_bytes;
+            uint8_t *dst = xbuf + ((int64_t)e * C + s) * row_bytes;
+            for (int p = lane; p < pieces; p += 64) st16(dst + p * 16, ld16(src + p * 16));
+        }
+    }
+}
+
+int bits_for(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+}  // namespace
+
+hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, int32_t *rank,
+                            int32_t *hist, hipStream_t s) {
+    const int nblk = dispatch_blocks(T);
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL(slot_rank_kernel, dim3(nblk, k), dim3(DISPATCH_TOK_BLOCK),
+                       (size_t)4 * E * sizeof(int), s, expert_idx, T, E, k, bits_for(E), rank, hist);
+    return hipGetLastError();
+}
+
+hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
+                            int32_t *expert_count, hipStream_t s) {
+    hipLaunchKernelGGL(slot_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, s, hist, nblk * k, E, C,
+                       expert_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
+                          const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
+                          int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,
+                          hipStream_t s) {
+    const int64_t n = T * k;
+    if (n == 0) return hipSuccess;
+    int64_t blocks = (n + 3) / 4;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(permute_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint8_t *>(x), d * elem_bytes, expert_idx, rank, base,
+                       T, E, k, dispatch_blocks(T), C, slot, drop_mask,
+                       reinterpret_cast<uint8_t *>(xbuf));
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Internal launchers of the MoE kernels (called only by the C ABI layer).
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router -----------------------------------------------------------
+// Number of per-block partial rows the router writes for T tokens.
+int router_blocks(int64_t T, int dtype_bf16, int E);
+hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
+                         int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
+                         float *part_prob, int32_t *part_cnt, hipStream_t s);
+hipError_t launch_router_reduce(const float *part_prob, const int32_t *part_cnt, int nblk,
+                                int E, float *prob_sum, int32_t *route_count, hipStream_t s);
+
+// ---- dispatch ---------------------------------------------------------
+constexpr int DISPATCH_TOK_BLOCK = 256;
+inline int dispatch_blocks(int64_t T) { return (int)((T + DISPATCH_TOK_BLOCK - 1) / DISPATCH_TOK_BLOCK); }
+hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, int32_t *rank,
+                            int32_t *hist, hipStream_t s);
+hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
+                            int32_t *expert_count, hipStream_t s);
+hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
+                          const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
+                          int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,
+                          hipStream_t s);
+
+// ---- experts ----------------------------------------------------------
+// Row-tile height of the grouped GEMM; tile_map holds E+1 prefix sums of
+// ceil(expert_count / GEMM_BM).
+int gemm_bm(int dtype_bf16);
+hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
+                           hipStream_t s);
+// out[e, m, :] = act(A[e, m, :] . B[e]^T (+ bias[e]))  for m < count[e]
+// act: 0 none, 1 relu, 2 swiglu (silu(A.B^T) * (A.B3^T)).
+// rows_bound: an upper bound of sum_e count[e] (sizes the grid).
+hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, const void *bias,
+                               int dtype_bf16, int act, const int32_t *expert_count,
+                               const int32_t *tile_map, int E, int64_t C, int N, int K,
+                               int64_t rows_bound, void *out, hipStream_t s);
+
+// ---- combine ----------------------------------------------------------
+hipError_t launch_combine(const void *ybuf, int dtype_bf16, const int32_t *expert_idx,
+                          const int32_t *slot, const float *gate, const float *prob_sum,
+                          const int32_t *route_count, int64_t T, int d, int E, int k, int64_t C,
+                          float alpha, void *y, float *aux_loss, hipStream_t s);
+
+}  // namespace moe

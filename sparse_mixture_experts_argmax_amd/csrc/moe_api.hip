@@ -1,0 +1,405 @@
+// C ABI of the MoE layer forward: argument checks, workspace carving and the
+// launch sequence of every entry point.  See include/moe.h for the contract.
+#include "moe.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_E = 1024;
+constexpr int MAX_K = 8;
+constexpr int64_t MAX_DIM = 1 << 20;
+
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool act_ok(int a) { return a == MOE_ACT_RELU || a == MOE_ACT_SWIGLU; }
+
+// Router partial rows are sized for the smaller token tile of the two router kernels.
+constexpr int64_t ROUTER_MIN_TOK = 8;
+
+struct RouterWs {
+    size_t part_prob, part_cnt, total;
+};
+RouterWs router_ws(int64_t T, int E) {
+    RouterWs w;
+    const int64_t nblk = (T + ROUTER_MIN_TOK - 1) / ROUTER_MIN_TOK;
+    w.part_prob = 0;
+    w.part_cnt = up((size_t)nblk * E * 4);
+    w.total = w.part_cnt + up((size_t)nblk * E * 4);
+    return w;
+}
+
+struct DispatchWs {
+    size_t rank, hist, total;
+};
+DispatchWs dispatch_ws(int64_t T, int E, int k) {
+    DispatchWs w;
+    w.rank = 0;
+    w.hist = up((size_t)T * k * 4);
+    w.total = w.hist + up((size_t)E * k * moe::dispatch_blocks(T) * 4);
+    return w;
+}
+
+struct FfnWs {
+    size_t tile_map, h, total;
+};
+FfnWs ffn_ws(int E, int64_t C, int dff, moe_dtype dt) {
+    FfnWs w;
+    w.tile_map = 0;
+    w.h = up((size_t)(E + 1) * 4);
+    w.total = w.h + up((size_t)E * C * dff * esize(dt));
+    return w;
+}
+
+struct ForwardWs {
+    RouterWs r;
+    DispatchWs dsp;
+    FfnWs f;
+    size_t router, prob_sum, route_count, dispatch, expert_count, slot, xbuf, ffn, ybuf, total;
+};
+ForwardWs forward_ws(int64_t T, int d, int dff, int E, int k, int64_t C, moe_dtype dt) {
+    ForwardWs w;
+    w.r = router_ws(T, E);
+    w.dsp = dispatch_ws(T, E, k);
+    w.f = ffn_ws(E, C, dff, dt);
+    size_t o = 0;
+    w.router = o;        o += w.r.total;
+    w.prob_sum = o;      o += up((size_t)E * 4);
+    w.route_count = o;   o += up((size_t)E * 4);
+    w.dispatch = o;      o += w.dsp.total;
+    w.expert_count = o;  o += up((size_t)E * 4);
+    w.slot = o;          o += up((size_t)T * k * 4);
+    w.xbuf = o;          o += up((size_t)E * C * d * esize(dt));
+    w.ffn = o;           o += w.f.total;
+    w.ybuf = o;          o += up((size_t)E * C * d * esize(dt));
+    w.total = o;
+    return w;
+}
+
+// Size limits shared by the entry points.
+moe_status check_sizes(int64_t T, int32_t E, int32_t k) {
+    if (T < 0 || E < 1 || k < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (E > MAX_E || k > MAX_K || k > E) return MOE_ERR_UNSUPPORTED;
+    if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+moe_status check_width(int64_t w) {
+    if (w < 8 || (w % 8) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (w > MAX_DIM) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+// A pointer that must be present (or may be NULL when its array is empty).
+bool ptr_ok(const void *p, bool empty_ok) { return (p == nullptr) ? empty_ok : aligned16(p); }
+bool opt_ok(const void *p) { return p == nullptr || aligned16(p); }
+// Scalars/small arrays only need natural alignment.
+bool ptr4_ok(const void *p, bool empty_ok) {
+    return (p == nullptr) ? empty_ok : (((uintptr_t)p & 3u) == 0);
+}
+
+#define MOE_CHECK(expr)                          \
+    do {                                         \
+        const moe_status st_ = (expr);           \
+        if (st_ != MOE_OK) return st_;           \
+    } while (0)
+#define MOE_HIP(expr)                            \
+    do {                                         \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+moe_status check_ffn_args(moe_dtype dt, moe_act act, const void *W1, const void *b1,
+                          const void *W3, const void *W2, const void *b2) {
+    if (!dtype_ok(dt) || !act_ok(act)) return MOE_ERR_UNSUPPORTED;
+    if (!ptr_ok(W1, false) || !ptr_ok(W2, false)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!opt_ok(b1) || !opt_ok(b2) || !opt_ok(W3)) return MOE_ERR_INVALID_ARGUMENT;
+    if (act == MOE_ACT_SWIGLU) {
+        if (W3 == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+        if (b1 != nullptr || b2 != nullptr) return MOE_ERR_UNSUPPORTED;
+    } else if (W3 != nullptr) {
+        return MOE_ERR_INVALID_ARGUMENT;
+    }
+    return MOE_OK;
+}
+
+moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                      int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
+                      float *gate, float *prob_sum, int32_t *route_count, char *ws,
+                      hipStream_t stream) {
+    const RouterWs w = router_ws(T, E);
+    float *part_prob = reinterpret_cast<float *>(ws + w.part_prob);
+    int32_t *part_cnt = reinterpret_cast<int32_t *>(ws + w.part_cnt);
+    const int bf16 = dt == MOE_BF16;
+    MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
+                               part_cnt, stream));
+    MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
+                                      prob_sum, route_count, stream));
+    return MOE_OK;
+}
+
+moe_status run_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, int64_t T,
+                        int32_t d, int32_t E, int32_t k, int64_t C, int32_t *slot,
+                        uint8_t *drop_mask, int32_t *expert_count, void *xbuf, char *ws,
+                        hipStream_t stream) {
+    const DispatchWs w = dispatch_ws(T, E, k);
+    int32_t *rank = reinterpret_cast<int32_t *>(ws + w.rank);
+    int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
+    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, stream));
+    MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, C, expert_count, stream));
+    MOE_HIP(moe::launch_permute(x, (int)esize(dt), expert_idx, rank, hist, T, d, E, k, C, slot,
+                                drop_mask, xbuf, stream));
+    return MOE_OK;
+}
+
+moe_status run_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count, int32_t E,
+                   int64_t C, int32_t d, int32_t dff, const void *W1, const void *b1,
+                   const void *W3, const void *W2, const void *b2, moe_act act, void *ybuf,
+                   int64_t rows_bound, char *ws, hipStream_t stream) {
+    if (C == 0) return MOE_OK;
+    const FfnWs w = ffn_ws(E, C, dff, dt);
+    int32_t *tile_map = reinterpret_cast<int32_t *>(ws + w.tile_map);
+    void *H = ws + w.h;
+    const int bf16 = dt == MOE_BF16;
+    MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16), tile_map, stream));
+    const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
+    MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, E, C,
+                                     dff, d, rows_bound, H, stream));
+    MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, E, C,
+                                     d, dff, rows_bound, ybuf, stream));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor) {
+    if (T < 0 || E < 1 || k < 1 || !isfinite(capacity_factor) || capacity_factor <= 0.0)
+        return -1;
+    const double c = ceil((double)k * (double)T * capacity_factor / (double)E - 1e-9);
+    if (c <= 0.0) return 0;
+    if (c >= (double)T) return T;
+    return (int64_t)c;
+}
+
+size_t moe_router_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+    if (check_sizes(T, E, k) != MOE_OK) return SIZE_MAX;
+    return router_ws(T, E).total;
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+    if (check_sizes(T, E, k) != MOE_OK) return SIZE_MAX;
+    return dispatch_ws(T, E, k).total;
+}
+
+size_t moe_expert_ffn_workspace_bytes(int32_t E, int64_t C, int32_t dff, moe_dtype dt) {
+    if (E < 1 || E > MAX_E || C < 0 || check_width(dff) != MOE_OK || !dtype_ok(dt)) return SIZE_MAX;
+    return ffn_ws(E, C, dff, dt).total;
+}
+
+size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k, int64_t C,
+                           moe_dtype dt, moe_act act) {
+    if (check_sizes(T, E, k) != MOE_OK || check_width(d) != MOE_OK ||
+        check_width(dff) != MOE_OK || !dtype_ok(dt) || !act_ok(act) || C < 0 || C > T)
+        return SIZE_MAX;
+    return forward_ws(T, d, dff, E, k, C, dt).total;
+}
+
+moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
+                                        int64_t C, moe_dtype dt, moe_act act, moe_ws_layout *out) {
+    if (out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (moe_workspace_bytes(T, d, dff, E, k, C, dt, act) == SIZE_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    const ForwardWs w = forward_ws(T, d, dff, E, k, C, dt);
+    out->slot = w.slot;
+    out->expert_count = w.expert_count;
+    out->route_count = w.route_count;
+    out->prob_sum = w.prob_sum;
+    out->xbuf = w.xbuf;
+    out->ybuf = w.ybuf;
+    out->total = w.total;
+    return MOE_OK;
+}
+
+moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                      int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
+                      float *gate, float *prob_sum, int32_t *route_count, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr4_ok(expert_idx, empty) ||
+        !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = router_ws(T, E).total;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
+                      static_cast<char *>(ws), stream);
+}
+
+moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, int64_t T,
+                        int32_t d, int32_t E, int32_t k, int64_t C, int32_t *slot,
+                        uint8_t *drop_mask, int32_t *expert_count, void *xbuf, void *ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    if (C < 0 || C > T) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(slot, empty) ||
+        (drop_mask == nullptr && !empty) || !ptr4_ok(expert_count, false) || !ptr_ok(xbuf, C == 0))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = dispatch_ws(T, E, k).total;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    return run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
+                        static_cast<char *>(ws), stream);
+}
+
+moe_status moe_expert_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count, int32_t E,
+                          int64_t C, int32_t d, int32_t dff, const void *W1, const void *b1,
+                          const void *W3, const void *W2, const void *b2, moe_act act,
+                          void *ybuf, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (E < 1 || C < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (E > MAX_E) return MOE_ERR_UNSUPPORTED;
+    MOE_CHECK(check_width(d));
+    MOE_CHECK(check_width(dff));
+    MOE_CHECK(check_ffn_args(dt, act, W1, b1, W3, W2, b2));
+    if (!ptr_ok(xbuf, C == 0) || !ptr4_ok(expert_count, false) || !ptr_ok(ybuf, C == 0))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = ffn_ws(E, C, dff, dt).total;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    return run_ffn(xbuf, dt, expert_count, E, C, d, dff, W1, b1, W3, W2, b2, act, ybuf,
+                   (int64_t)E * C, static_cast<char *>(ws), stream);
+}
+
+moe_status moe_combine(const void *ybuf, moe_dtype dt, const int32_t *expert_idx,
+                       const int32_t *slot, const float *gate, const float *prob_sum,
+                       const int32_t *route_count, int64_t T, int32_t d, int32_t E, int32_t k,
+                       int64_t C, float alpha, void *y, float *aux_loss, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    if (C < 0 || C > T || !isfinite(alpha)) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(ybuf, empty || C == 0) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(slot, empty) ||
+        !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false) ||
+        !ptr_ok(y, empty) || !ptr4_ok(aux_loss, false))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_HIP(moe::launch_combine(ybuf, dt == MOE_BF16, expert_idx, slot, gate, prob_sum,
+                                route_count, T, d, E, k, C, alpha, y, aux_loss, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                        const void *W1, const void *b1, const void *W3, const void *W2,
+                        const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff, int32_t E,
+                        int32_t k, double capacity_factor, float alpha, void *y, float *aux_loss,
+                        int32_t *expert_idx, float *gate, uint8_t *drop_mask, void *ws,
+                        size_t ws_bytes, hipStream_t stream, hipEvent_t *ev) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    MOE_CHECK(check_width(dff));
+    MOE_CHECK(check_ffn_args(dt, act, W1, b1, W3, W2, b2));
+    if (!isfinite(alpha)) return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t C = moe_capacity(T, E, k, capacity_factor);
+    if (C < 0) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr_ok(y, empty) ||
+        !ptr4_ok(aux_loss, false) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(gate, empty) ||
+        (drop_mask == nullptr && !empty))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (ev != nullptr) {
+        for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
+            if (ev[i] == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    }
+    const ForwardWs w = forward_ws(T, d, dff, E, k, C, dt);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    char *base = static_cast<char *>(ws);
+    float *prob_sum = reinterpret_cast<float *>(base + w.prob_sum);
+    int32_t *route_count = reinterpret_cast<int32_t *>(base + w.route_count);
+    int32_t *expert_count = reinterpret_cast<int32_t *>(base + w.expert_count);
+    int32_t *slot = reinterpret_cast<int32_t *>(base + w.slot);
+    void *xbuf = base + w.xbuf;
+    void *ybuf = base + w.ybuf;
+    const int bf16 = dt == MOE_BF16;
+    int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.ffn + w.f.tile_map);
+    void *H = base + w.ffn + w.f.h;
+    const int64_t rows = T * (int64_t)k;
+    auto mark = [&](int i) -> bool { return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess; };
+
+    if (!mark(0)) return MOE_ERR_HIP;
+    MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
+                         base + w.router, stream));
+    if (!mark(1)) return MOE_ERR_HIP;
+    MOE_CHECK(run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
+                           base + w.dispatch, stream));
+    if (C > 0) MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16), tile_map, stream));
+    if (!mark(2)) return MOE_ERR_HIP;
+    if (C > 0) {
+        const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
+        MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, E, C,
+                                         dff, d, rows, H, stream));
+    }
+    if (!mark(3)) return MOE_ERR_HIP;
+    if (C > 0)
+        MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, E, C, d,
+                                         dff, rows, ybuf, stream));
+    if (!mark(4)) return MOE_ERR_HIP;
+    MOE_HIP(moe::launch_combine(ybuf, bf16, expert_idx, slot, gate, prob_sum, route_count, T, d, E,
+                                k, C, alpha, y, aux_loss, stream));
+    if (!mark(5)) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                       const void *W1, const void *b1, const void *W3, const void *W2,
+                       const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
+                       int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
+                       float *aux_loss, int32_t *expert_idx, float *gate, uint8_t *drop_mask,
+                       void *ws, size_t ws_bytes, hipStream_t stream) {
+    return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k,
+                        capacity_factor, alpha, y, aux_loss, expert_idx, gate, drop_mask, ws,
+                        ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                              const void *W1, const void *b1, const void *W3, const void *W2,
+                              const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
+                              int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
+                              float *aux_loss, int32_t *expert_idx, float *gate,
+                              uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t *stage_events) {
+    if (stage_events == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k,
+                        capacity_factor, alpha, y, aux_loss, expert_idx, gate, drop_mask, ws,
+                        ws_bytes, stream, stage_events);
+}
+
+}  // extern "C"

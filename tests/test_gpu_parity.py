@@ -1,0 +1,214 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Workloads: the five seeded configurations at full size, plus small ragged
+cases (token counts that are not multiples of any tile, expert counts that
+are not multiples of 16, widths that leave K and N tails in the GEMMs,
+k = 2 and 3, forced drops, the router bias, more than 256 experts).
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import sparse_mixture_experts_argmax_amd as moe
+from oracle import moe as O
+from gpu_util import (AUX_RTOL, check_routing, check_y, device_inputs, host_bits, host_f64)
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny", "switch_base", "zipf_skew", "mixtral", "many_expert"]
+
+SMALL = {
+    # name: T, d, f, E, k, cf, dtype, act, ffn_bias, router_bias, logit_scale
+    "ragged_f32": (333, 24, 40, 5, 1, 1.1, "f32", "relu", True, False, 3.0),
+    "ragged_bf16": (1000, 40, 72, 12, 1, 0.9, "bf16", "relu", True, True, 4.0),
+    "top2_swiglu": (777, 64, 136, 10, 2, 1.0, "bf16", "swiglu", False, False, 6.0),
+    "top3_relu": (517, 32, 96, 7, 3, 0.8, "bf16", "relu", False, False, 5.0),
+    "e300_generic": (400, 32, 64, 300, 2, 2.0, "bf16", "relu", False, False, 2.0),
+    "f32_swiglu": (150, 16, 24, 6, 2, 1.5, "f32", "swiglu", False, True, 4.0),
+    "tiles": (4096, 256, 384, 16, 1, 1.25, "bf16", "relu", True, False, 1.0),
+}
+
+
+def _small(name, seed=0):
+    T, d, f, E, k, cf, dt, act, fb, rb, sc = SMALL[name]
+    return datagen.random_case(seed=seed + 11, T=T, d=d, f=f, E=E, k=k, cf=cf, dtype=dt, act=act,
+                               ffn_bias=fb, router_bias=rb, logit_scale=sc)
+
+
+_CACHE = {}
+
+
+def _full(name, with_experts=True):
+    key = (name, with_experts)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = datagen.make(name, seed=0, with_experts=with_experts)
+    return _CACHE[key]
+
+
+def _run_router(cfg):
+    t = device_inputs(cfg)
+    idx, gate, prob_sum, route_count = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    torch.cuda.synchronize()
+    return t, idx, gate, prob_sum, route_count
+
+
+def _router_checks(cfg, idx, gate, prob_sum, route_count):
+    x64 = O.widen(cfg["x"], cfg["dtype"])
+    z = O.router_logits(x64, cfg["W_r"], cfg["b_r"])
+    p = O.softmax(z)
+    ref_idx = O.top_k(z, cfg["k"])
+    ref = dict(z=z, expert_idx=ref_idx, gate=O.gates(z, p, ref_idx))
+    gi = idx.cpu().numpy()
+    agree = check_routing(gi, gate.cpu().numpy(), ref, cfg["k"])
+    E = cfg["E"]
+    assert (route_count.cpu().numpy() == O.route_count(gi, E)).all()
+    np.testing.assert_allclose(prob_sum.cpu().numpy(), p.sum(axis=0), rtol=2e-6, atol=1e-6)
+    return z, p, gi, agree
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_router_full(name):
+    cfg = _full(name, with_experts=False)
+    print(f"router parity: {name} T={cfg['T']} E={cfg['E']} k={cfg['k']}", flush=True)
+    t, idx, gate, ps, rc = _run_router(cfg)
+    _router_checks(cfg, idx, gate, ps, rc)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_router_small(name):
+    cfg = _small(name)
+    t, idx, gate, ps, rc = _run_router(cfg)
+    _router_checks(cfg, idx, gate, ps, rc)
+
+
+def _dispatch_checks(cfg, t, gi, C):
+    idx_t = torch.from_numpy(gi).to(t["x"].device)
+    slot, drop, count, xbuf = moe.dispatch(t["x"], idx_t, cfg["E"], C)
+    torch.cuda.synchronize()
+    rs, rd, rc = O.assign_slots(gi, cfg["E"], C)
+    s = slot.cpu().numpy()
+    assert (s == rs).all()
+    assert (drop.cpu().numpy() == rd).all()
+    assert (count.cpu().numpy() == rc).all()
+    xb = host_bits(xbuf)
+    xh = host_bits(t["x"])
+    tt, jj = np.nonzero(s >= 0)
+    ee = gi[tt, jj]
+    assert (xb[ee, s[tt, jj]] == xh[tt]).all()
+    return slot, drop, count, xbuf
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_dispatch_full(name):
+    cfg = _full(name, with_experts=False)
+    print(f"dispatch parity: {name}", flush=True)
+    t, idx, gate, ps, rc = _run_router(cfg)
+    z, p, gi, agree = _router_checks(cfg, idx, gate, ps, rc)
+    C = O.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
+    assert moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"]) == C
+    _dispatch_checks(cfg, t, gi, C)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dispatch_small(name):
+    cfg = _small(name)
+    t, idx, gate, ps, rc = _run_router(cfg)
+    z, p, gi, agree = _router_checks(cfg, idx, gate, ps, rc)
+    C = O.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
+    _dispatch_checks(cfg, t, gi, C)
+
+
+def _forward_checks(cfg, tokens=None):
+    t = device_inputs(cfg)
+    plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"], t["x"].dtype,
+                           act=cfg["act"], capacity_factor=cfg["cf"], alpha=cfg["alpha"],
+                           device=t["x"].device)
+    y, aux, idx, gate, drop = plan(t["x"], t["W_r"], t["W1"], t["W2"], W3=t["W3"], b1=t["b1"],
+                                   b2=t["b2"], b_r=t["b_r"])
+    torch.cuda.synchronize()
+    ref = O.forward_cfg(cfg, tokens=tokens)
+    gi = idx.cpu().numpy()
+    agree = check_routing(gi, gate.cpu().numpy(), ref, cfg["k"])
+    # capacity assignment: exact against the oracle's rule on the GPU's own choices
+    rs, rd, rc = O.assign_slots(gi, cfg["E"], ref["C"])
+    assert (plan.intermediate("slot").cpu().numpy() == rs).all()
+    assert (drop.cpu().numpy() == rd).all()
+    assert (plan.intermediate("expert_count").cpu().numpy() == rc).all()
+    if agree.all():
+        assert (rs == ref["slot"]).all() and (rd == ref["drop_mask"]).all()
+    # outputs on tokens whose routing and slots agree with the oracle
+    same_slots = np.all(rs == ref["slot"], axis=1) & agree
+    rows = np.nonzero(same_slots)[0] if tokens is None else np.intersect1d(np.nonzero(same_slots)[0], tokens)
+    yg = host_f64(y)
+    err = check_y(yg, ref["y"], rows, cfg["dtype"])
+    # the loss: the oracle's definition on the GPU's choices
+    aux_ref = O.aux_loss(ref["p"], gi, cfg["E"], cfg["alpha"])
+    assert abs(float(aux.cpu()[0]) - aux_ref) <= AUX_RTOL * abs(aux_ref)
+    # dropped everywhere -> y == 0
+    all_dropped = np.all(rd == 1, axis=1)
+    if all_dropped.any():
+        assert (yg[all_dropped] == 0).all()
+    return err, plan
+
+
+@pytest.mark.parametrize("name", ["tiny", "switch_base", "zipf_skew"])
+def test_forward_full(name):
+    cfg = _full(name)
+    print(f"forward parity: {name} (all tokens)", flush=True)
+    err, _ = _forward_checks(cfg)
+    print(f"  y max-abs {err[0]:.3e}  mean relative {err[1]:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "many_expert"])
+def test_forward_full_sampled(name):
+    """Full-size workloads, y checked on a seeded sample of tokens the oracle evaluates one by one."""
+    cfg = _full(name)
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(cfg["T"], size=192, replace=False))
+    tokens = np.unique(np.concatenate([tokens, [0, cfg["T"] - 1]]))
+    print(f"forward parity: {name} ({tokens.size} sampled tokens)", flush=True)
+    err, _ = _forward_checks(cfg, tokens=tokens)
+    print(f"  y max-abs {err[0]:.3e}  mean relative {err[1]:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    _forward_checks(_small(name))
+
+
+def test_split_api_equals_forward():
+    """router -> dispatch -> expert_ffn -> combine gives the fused call's outputs bitwise."""
+    cfg = _small("top2_swiglu", seed=3)
+    t = device_inputs(cfg)
+    C = moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
+    idx, gate, ps, rc = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    slot, drop, count, xbuf = moe.dispatch(t["x"], idx, cfg["E"], C)
+    ybuf = moe.expert_ffn(xbuf, count, t["W1"], t["W2"], W3=t["W3"], act=cfg["act"])
+    y, aux = moe.combine(ybuf, idx, slot, gate, ps, rc, cfg["T"], alpha=cfg["alpha"])
+    y2, aux2, idx2, gate2, drop2 = moe.forward(t["x"], t["W_r"], t["W1"], t["W2"], W3=t["W3"],
+                                               b_r=t["b_r"], k=cfg["k"], capacity_factor=cfg["cf"],
+                                               alpha=cfg["alpha"], act=cfg["act"])
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(drop, drop2)
+    assert torch.equal(gate.view(torch.int32), gate2.view(torch.int32))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(aux.view(torch.int32), aux2.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["switch_base", "top2_swiglu"])
+def test_deterministic(name):
+    cfg = _full(name) if name in FULL else _small(name)
+    t = device_inputs(cfg)
+    plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"], t["x"].dtype,
+                           act=cfg["act"], capacity_factor=cfg["cf"], alpha=cfg["alpha"])
+    outs = []
+    for _ in range(2):
+        y, aux, idx, gate, drop = plan(t["x"], t["W_r"], t["W1"], t["W2"], W3=t["W3"], b1=t["b1"],
+                                       b2=t["b2"], b_r=t["b_r"])
+        torch.cuda.synchronize()
+        outs.append([host_bits(v).copy() for v in (y, aux, idx, gate, drop)] +
+                    [plan.intermediate("slot").cpu().numpy().copy()])
+    for a, b in zip(*outs):
+        assert (a == b).all()
