@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the Switch MoE layer forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload switch_base]
+
+A step is one whole layer forward (router, dispatch, expert FFN, combine
+and loss) over one batch of seeded synthetic inputs already resident in
+HBM.  W untimed steps, then K timed steps bracketed by device
+synchronisation; value = tokens per second over the K steps.
+
+Each timed step records HIP events at the stage boundaries on the stream the
+kernels run on (moe_forward_staged), giving each stage's average duration
+over the timed region; the roofline object reports the stage that takes the
+longest, with its algorithmic bytes / flops per launch (see `stage_work`).
+The CPU baseline times the CPU oracle on the same workload, on this host.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+METRIC = "MoE-layer fwd tokens/s (1 GPU) + grouped-GEMM MFMA % of peak + permute GB/s"
+
+
+def stage_work(cfg: dict, A: int) -> dict:
+    """Algorithmic bytes and flops of each stage for one forward.
+
+    A = kept (token, rank) choices.  Only real rows count: weights once, the
+    activations each stage must read or write, no padding, no re-reads.
+      router   x [T,d] + W_r [E,d] fp32 read, expert_idx + gate [T,k] written;
+               flops 2 T d E (fp32)
+      dispatch 2 A d s (x rows read, xbuf rows written) + T k (4 + 4 + 1)
+               (indices read, slots and drop flags written)
+      gemm1    W1 (+W3) [E,f,d] + A d s read + A f s written;
+               flops 2 A d f (x2 for SwiGLU)
+      gemm2    W2 [E,d,f] + A f s read + A d s written; flops 2 A f d
+      combine  A d s read + T d s written + T k 12 (indices, slots, gates)
+    """
+    T, d, f, E, k = cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"]
+    s = 2 if cfg["dtype"] == "bf16" else 4
+    m = 2 if cfg["act"] == "swiglu" else 1
+    return {
+        "router": dict(bytes=T * d * s + E * d * 4 + T * k * 8, flops=2 * T * d * E, dtype="f32"),
+        "dispatch": dict(bytes=2 * A * d * s + T * k * 9, flops=0, dtype=cfg["dtype"]),
+        "expert_gemm1": dict(bytes=m * E * f * d * s + A * d * s + A * f * s, flops=2 * m * A * d * f,
+                             dtype=cfg["dtype"]),
+        "expert_gemm2": dict(bytes=E * d * f * s + A * f * s + A * d * s, flops=2 * A * f * d,
+                             dtype=cfg["dtype"]),
+        "combine": dict(bytes=A * d * s + T * d * s + T * k * 12, flops=0, dtype=cfg["dtype"]),
+    }
+
+
+def roofline_of(work: dict, seconds: float) -> dict:
+    """Which roofline bounds a stage, and the achieved rate against that peak."""
+    peak_f = PEAK_TFLOPS[work["dtype"]]
+    t_mem = work["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_flop = work["flops"] / (peak_f * 1e12) if work["flops"] else 0.0
+    if t_flop > t_mem:
+        ach = work["flops"] / seconds / 1e12
+        return dict(bound="mfma" if work["dtype"] == "bf16" else "alu", achieved=round(ach, 2),
+                    peak=peak_f, unit="TFLOP/s", frac=round(ach / peak_f, 4))
+    ach = work["bytes"] / seconds / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(ach / PEAK_HBM_GBS, 4))
+
+
+class HipEvents:
+    """HIP events through the runtime torch already loaded (same process, same runtime)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def cpu_baseline(cfg: dict, min_seconds: float) -> dict:
+    """The CPU oracle on the whole workload, repeated until min_seconds have passed."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe as O
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.forward_cfg(cfg)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 20:
+            break
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return dict(value=round(cfg["T"] * reps / el, 1), unit="tokens/s",
+                cores=int(max(blas) if blas else 1), kind="oracle",
+                sample=f"whole {cfg['name']} workload ({cfg['T']} tokens) x {reps} runs, "
+                       f"{el:.1f} s; NumPy oracle, fp64 experts")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="switch_base", choices=datagen.CONFIG_ORDER)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
+                         "reference kernel that scales the HBM byte counters), then exit")
+    args = ap.parse_args(argv)
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer's multi-GPU "
+              "expert-parallel path is not built", file=sys.stderr)
+        return 2
+
+    import torch
+    import sparse_mixture_experts_argmax_amd as moe
+    from sparse_mixture_experts_argmax_amd import _lib as L
+    from sparse_mixture_experts_argmax_amd.api import _dtype_code, _ptr, _ACT
+
+    cfg = datagen.make(args.workload, seed=0)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+
+    def todev(a, bf=False):
+        if a is None:
+            return None
+        t = torch.from_numpy(a.view("int16") if bf else a)
+        return (t.view(torch.bfloat16) if bf else t).to(dev)
+
+    bf = cfg["dtype"] == "bf16"
+    x = todev(cfg["x"], bf)
+    W_r = todev(cfg["W_r"])
+    b_r = todev(cfg["b_r"])
+    W1, W3, W2 = todev(cfg["W1"], bf), todev(cfg["W3"], bf), todev(cfg["W2"], bf)
+    b1, b2 = todev(cfg["b1"], bf), todev(cfg["b2"], bf)
+    plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"], dt, act=cfg["act"],
+                           capacity_factor=cfg["cf"], alpha=cfg["alpha"], device=dev)
+    stream = torch.cuda.current_stream(dev)
+    hip = HipEvents()
+    nev = L.MOE_STAGE_EVENTS
+    events = hip.create(nev * args.steps)
+
+    def step(i=None):
+        if i is None:
+            return plan(x, W_r, W1, W2, W3=W3, b1=b1, b2=b2, b_r=b_r)
+        arr = (ctypes.c_void_p * nev)(*events[i * nev:(i + 1) * nev])
+        L.check("moe_forward_staged", L.LIB.moe_forward_staged(
+            _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
+            _ptr(b2), _ACT[cfg["act"]], cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"],
+            plan.capacity_factor, plan.alpha, _ptr(plan.y), _ptr(plan.aux), _ptr(plan.expert_idx),
+            _ptr(plan.gate), _ptr(plan.drop_mask), _ptr(plan.ws), plan.ws.numel(),
+            stream.cuda_stream, arr))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {name: 0.0 for name in L.STAGES}
+    for i in range(args.steps):
+        ev = events[i * nev:(i + 1) * nev]
+        for j, name in enumerate(L.STAGES):
+            stage_ms[name] += hip.elapsed_ms(ev[j], ev[j + 1]) / args.steps
+    hip.destroy(events)
+
+    A = int(plan.intermediate("expert_count").sum().item())
+    drops = int(plan.drop_mask.sum().item())
+    work = stage_work(cfg, A)
+    stages = {}
+    for name in L.STAGES:
+        r = roofline_of(work[name], stage_ms[name] / 1e3)
+        stages[name] = dict(us=round(stage_ms[name] * 1e3, 2), bytes=work[name]["bytes"],
+                            flops=work[name]["flops"], **r)
+    dominant = max(L.STAGES, key=lambda n: stage_ms[n])
+    dom = dict(stages[dominant])
+    roofline = dict(bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"], unit=dom["unit"],
+                    frac=dom["frac"], traffic=None, kernel=dominant,
+                    algorithmic_bytes=work[dominant]["bytes"], algorithmic_flops=work[dominant]["flops"],
+                    avg_us=dom["us"])
+    ffn_s = (stage_ms["expert_gemm1"] + stage_ms["expert_gemm2"]) / 1e3
+    ffn_flops = work["expert_gemm1"]["flops"] + work["expert_gemm2"]["flops"]
+    peak = PEAK_TFLOPS[cfg["dtype"]]
+    ms_per_step = elapsed / args.steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(cfg["T"] * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (seeded, LayerNorm(N(0,1)) tokens, truncated-normal sigma=sqrt(0.1/fan_in) weights)",
+        "config": {"workload": cfg["name"], "T": cfg["T"], "d_model": cfg["d"], "d_ff": cfg["f"],
+                   "experts": cfg["E"], "k": cfg["k"], "capacity_factor": cfg["cf"],
+                   "capacity": plan.C, "act": cfg["act"], "router": "fp32",
+                   "kept_assignments": A, "dropped": drops},
+        "grouped_gemm_mfma_pct": round(100.0 * ffn_flops / ffn_s / 1e12 / peak, 2),
+        "permute_GBps": round(work["dispatch"]["bytes"] / (stage_ms["dispatch"] / 1e3) / 1e9, 1),
+        "stages": stages,
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -47,12 +47,27 @@ __device__ __forceinline__ void split3(float w, uint16_t &h, uint16_t &m, uint16
     l = f2bf(r2);
 }
 
+// Register stage of one K chunk: this thread's share of the W_r chunk (fp32)
+// and its x fragment.  Loads are never conditional (indices are clamped and
+// out-of-range values zeroed when used) so that the compiler only waits for a
+// stage when it is consumed, DEPTH chunks after its loads were issued.
+template <int WPER>
+struct RStage {
+    float4 w[WPER];
+    u32x4 x;
+    bool xin;
+};
+
+template <int NB>
+constexpr int router_depth() { return NB <= 4 ? 4 : (NB <= 8 ? 3 : 2); }
+
 template <int NB>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
     float *__restrict__ part_prob, int32_t *__restrict__ part_cnt) {
     constexpr int EP = NB * 16;
+    constexpr int DEPTH = router_depth<NB>();
     __shared__ __attribute__((aligned(16))) uint16_t sW[3][EP * RM_STRIDE];
     __shared__ float sProb[RM_WAVES][EP];
     __shared__ int sCnt[EP];
@@ -68,28 +83,42 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 
     constexpr int WPIECES = EP * (RM_KC / 4);           // float4 pieces per chunk
     constexpr int WPER = (WPIECES + 255) / 256;
-    float4 wpre[WPER];
+    // this thread's W pieces: row p/8 (clamped to E-1), column (p%8)*4
+    const float *wrow[WPER];
+    bool wok[WPER];
+#pragma unroll
+    for (int q = 0; q < WPER; ++q) {
+        const int p = tid + q * 256;
+        int row = p >> 3;
+        wok[q] = p < WPIECES && row < E;
+        row = row < E ? row : E - 1;
+        wrow[q] = Wr + (int64_t)row * d + (p & 7) * 4;
+    }
+    const int64_t txr = (tw + col < T) ? tw + col : T - 1;
+    const uint16_t *xrow = x + txr * d + 8 * kg;
+    const bool tok_in = tw + col < T;
 
-    auto load_w = [&](int k0) {
+    auto load = [&](RStage<WPER> &st, int c) {
+        const int k0 = c * RM_KC;
 #pragma unroll
         for (int q = 0; q < WPER; ++q) {
-            const int p = tid + q * 256;
-            const int row = p >> 3;
-            const int c4 = (p & 7) * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p < WPIECES && row < E && k0 + c4 < d)
-                v = *reinterpret_cast<const float4 *>(Wr + (int64_t)row * d + k0 + c4);
-            wpre[q] = v;
+            const int kc = k0 + ((tid + q * 256) & 7) * 4;
+            st.w[q] = *reinterpret_cast<const float4 *>(wrow[q] + (kc < d ? k0 : 0));
         }
+        st.xin = tok_in && (k0 + 8 * kg < d);
+        st.x = ld16(xrow + (k0 + 8 * kg < d ? k0 : 0));
     };
-    auto store_w = [&]() {
+    auto store_w = [&](const RStage<WPER> &st, int c) {
+        const int k0 = c * RM_KC;
 #pragma unroll
         for (int q = 0; q < WPER; ++q) {
             const int p = tid + q * 256;
             if (p < WPIECES) {
                 const int row = p >> 3;
                 const int c4 = (p & 7) * 4;
-                const float w[4] = {wpre[q].x, wpre[q].y, wpre[q].z, wpre[q].w};
+                const bool ok = wok[q] && (k0 + c4 < d);
+                const float w[4] = {ok ? st.w[q].x : 0.f, ok ? st.w[q].y : 0.f,
+                                    ok ? st.w[q].z : 0.f, ok ? st.w[q].w : 0.f};
                 uint16_t h[4], m[4], l[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) split3(w[j], h[j], m[j], l[j]);
@@ -104,31 +133,14 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             }
         }
     };
-    auto load_x = [&](int k0) -> u32x4 {
-        const int64_t t = tw + col;
-        const int kk = k0 + 8 * kg;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t < T && kk < d) v = ld16(x + t * d + kk);
-        return v;
-    };
 
     f32x4 acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nchunk = (d + RM_KC - 1) / RM_KC;
-    load_w(0);
-    u32x4 xpre = load_x(0);
     const int boff = col * RM_STRIDE + 8 * kg;
-    for (int c = 0; c < nchunk; ++c) {
-        __syncthreads();
-        store_w();
-        const bf16x8 a = as_bf16x8(xpre);
-        __syncthreads();
-        if (c + 1 < nchunk) {
-            load_w((c + 1) * RM_KC);
-            xpre = load_x((c + 1) * RM_KC);
-        }
+    auto compute = [&](const RStage<WPER> &st) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bf16x8 a = as_bf16x8(st.xin ? st.x : z);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int o = nb * 16 * RM_STRIDE + boff;
@@ -139,7 +151,29 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, acc[nb], 0, 0, 0);
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[nb], 0, 0, 0);
         }
+    };
+
+    // ring of DEPTH register stages; chunk c lives in stage c % DEPTH
+    const int nchunk = (d + RM_KC - 1) / RM_KC;
+    RStage<WPER> st[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load(st[s], s < nchunk ? s : nchunk - 1);
+    auto step = [&](RStage<WPER> &cur, int c) {
+        __syncthreads();                     // the previous chunk's MFMAs are done with sW
+        store_w(cur, c);
+        __syncthreads();
+        compute(cur);
+        const int cn = c + DEPTH;
+        load(cur, cn < nchunk ? cn : nchunk - 1);
+    };
+    int c0 = 0;
+    for (; c0 + DEPTH <= nchunk; c0 += DEPTH) {      // whole rounds: no exits inside
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) step(st[s], c0 + s);
     }
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s)              // the last nchunk % DEPTH chunks
+        if (c0 + s < nchunk) step(st[s], c0 + s);
 
     // ---- epilogue: lane holds logits of tokens tw + 4*kg + i, experts nb*16 + col
     float bias[NB];
