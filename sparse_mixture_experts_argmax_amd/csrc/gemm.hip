@@ -65,280 +65,275 @@ __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ tile_map, i
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
-#define MOE_LDS_AS __attribute__((address_space(3)))
-#define MOE_GLB_AS __attribute__((address_space(1)))
-
-// s_waitcnt with vmcnt = V and lgkmcnt = 0 (expcnt left alone), gfx9 encoding.
-template <int V>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(V >= 0 && V < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// Tile shape: block BM x BN, K step 64, STAGES-deep LDS ring; 4 waves in a
-// 2 x 2 grid, each wave (BM/2) x (BN/2) = FM x FN MFMA 16x16 fragments.
-// LDS rows are 64 bf16 = 128 bytes = 8 pieces of 16 bytes; piece c of row r
-// is stored at position c ^ (r % 8), so the 16 rows of a fragment read and
-// the 8 rows of a DMA write each touch every bank group once.
-template <int BM_, int BN_, int STAGES_>
+// Tile shape: block BM x BN, K step 64; 4 waves in a 2 x 2 grid, each wave
+// (BM/2) x (BN/2) = FM x FN 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16:
+// on gfx950 one wave per SIMD keeps it issuing at nearly the full rate,
+// which the 16x16x32 form does not reach).  LDS rows are 64 bf16 =
+// 128 bytes = 8 pieces of 16 bytes; piece c of row r is stored at position
+// c ^ (r % 8), so the 16 rows of a fragment read and the 8 rows of a staging
+// write each touch every bank group once, with no padding.
+template <int BM_, int BN_, int MINB_ = 1>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = 64, STAGES = STAGES_;
-    static constexpr int FM = BM / 32, FN = BN / 32;    // 16x16 fragments per wave
-    static constexpr int AI = BM / 32, BI = BN / 32;    // DMA instructions per wave per stage
+    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int MINB = MINB_;                  // blocks per CU the registers are sized for
+    static constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 fragments per wave
+    static constexpr int LA = BM * 8 / 256;             // 16-byte A pieces per thread per K tile
+    static constexpr int LB = BN * 8 / 256;             // 16-byte B pieces per thread per K tile
     static constexpr int OUT_STRIDE = BN + 8;           // staged output row (bf16 elements)
-    static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+    // element offset of logical piece c of row r
+    static __device__ __forceinline__ int off(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
 };
 
-// Persistent grouped GEMM.  Each block walks a list of output tiles; the
-// K tiles of all its output tiles form one stream that flows through a
-// three-stage LDS ring filled by 16-byte DMA (global_load_lds), so the loads
-// of the next output tile overlap the MFMAs of the current one.
-template <class TL, int ACT, bool BIAS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(
+// Register stage of one K tile: this thread's 16-byte pieces of A, B (and B3).
+template <int LA, int LB, bool DUAL>
+struct Stage {
+    u32x4 a[LA];
+    u32x4 b[LB];
+    u32x4 b3[DUAL ? LB : 1];
+    bool in;          // false: these columns lie past K and are stored as zeros
+};
+
+template <class TL, int ACT, bool BIAS, bool KTAIL>
+__global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ B3,
     const uint16_t *__restrict__ bias, const int32_t *__restrict__ count,
     const int32_t *__restrict__ tile_map, int E, int64_t C, int N, int K, int tiles_n,
     uint16_t *__restrict__ out) {
-    constexpr int BM = TL::BM, BN = TL::BN, S = TL::STAGES;
-    constexpr int FM = TL::FM, FN = TL::FN, AI = TL::AI, BI = TL::BI;
+    constexpr int BM = TL::BM, BN = TL::BN;
+    constexpr int LA = TL::LA, LB = TL::LB, FM = TL::FM, FN = TL::FN;
     constexpr bool DUAL = (ACT == 2);
     constexpr int NBT = DUAL ? 2 : 1;                    // weight tiles per stage
-    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-    constexpr int STAGE_BYTES = A_BYTES + NBT * B_BYTES;
-    constexpr int PER = AI + NBT * BI;                   // DMA instructions per wave per stage
-    static_assert(S == 3, "the ring below is written out for three stages");
-    // one LDS array per stage: the compiler then sees that reads of one stage
-    // cannot alias the DMA in flight into another and adds no wait of its own
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE_BYTES];
+    constexpr int STAGE_ELEMS = (BM + NBT * BN) * 64;
+    constexpr int OUT_ELEMS = BM * TL::OUT_STRIDE;
+    constexpr int SMEM_ELEMS = 2 * STAGE_ELEMS > OUT_ELEMS ? 2 * STAGE_ELEMS : OUT_ELEMS;
+    // two LDS stages of [A | B | B3] tiles; reused for the output tile at the end
+    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
     __shared__ int s_map[MAX_E_LDS + 1];
-    __shared__ int s_cnt[MAX_E_LDS];
 
-    for (int i = threadIdx.x; i <= E; i += blockDim.x) {
-        s_map[i] = tile_map[i];
-        if (i < E) s_cnt[i] = count[i];
-    }
-    __syncthreads();
-
-    // this block's output tiles: its XCD (blocks are dealt to the 8 XCDs
-    // round-robin) owns one contiguous share of the tile order, and the
-    // XCD's blocks take that share's tiles in turn
-    const int total = s_map[E] * tiles_n;
-    const int per_xcd_blocks = gridDim.x >> 3;
-    const int share = (total + 7) >> 3;
-    const int lo = (blockIdx.x & 7) * share + (blockIdx.x >> 3);
-    const int hi = min(total, ((blockIdx.x & 7) + 1) * share);
-    if (lo >= hi) return;
-    const int my_tiles = (hi - lo + per_xcd_blocks - 1) / per_xcd_blocks;
+    int e, mt, nt;
+    if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt)) return;
+    const int cnt = count[e];
+    const int m0 = mt * BM;
+    const int n0 = nt * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS DMA base)
+    const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
+
+    const uint16_t *Ae = A + (int64_t)e * C * K;
+    const uint16_t *Be = B + (int64_t)e * N * K;
     const int64_t b3off = DUAL ? (int64_t)(B3 - B) : 0;
 
-    // tile index -> (expert, first row, first column)
-    auto locate = [&](int lt, int &e, int &m0, int &n0) {
-        const int L = lo + lt * per_xcd_blocks;
-        int a = 0, b = E - 1;                           // largest e with s_map[e] * tiles_n <= L
-        while (a < b) {
-            const int mid = (a + b + 1) >> 1;
-            if (s_map[mid] * tiles_n <= L) a = mid; else b = mid - 1;
-        }
-        e = a;
-        const int r = L - s_map[e] * tiles_n;
-        const int mtiles = s_map[e + 1] - s_map[e];
-        const int nt = r / mtiles;
-        m0 = (r - nt * mtiles) * BM;
-        n0 = nt * BN;
-    };
+    // staging: piece q = tid + i*256 -> row q / 8, logical piece q % 8 (rows past
+    // the count / past N read a valid row whose result is discarded)
+    const int pc = tid & 7;
+    const uint16_t *pa[LA];
+    const uint16_t *pb[LB];
+    int soa[LA], sob[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int r = (tid >> 3) + i * 32;
+        int am = m0 + r;
+        am = am < cnt ? am : cnt - 1;
+        pa[i] = Ae + (int64_t)am * K + pc * 8;
+        soa[i] = TL::off(r, pc);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int r = (tid >> 3) + i * 32;
+        int bn = n0 + r;
+        bn = bn < N ? bn : N - 1;
+        pb[i] = Be + (int64_t)bn * K + pc * 8;
+        sob[i] = TL::off(r, pc);
+    }
 
-    // DMA sources of the tile being loaded: wave instruction i fills LDS rows
-    // [8 (wave*AI + i), +8); lane l lands at position l of that 1 KB block =
-    // row l/8, piece l%8, which holds logical piece (l%8) ^ (l/8) of the row
-    // (rows past the count / past N read a valid row whose result is dropped)
-    const int lr = lane >> 3;
-    const int lc = (lane & 7) ^ lr;
-    const uint16_t *asrc[AI];
-    const uint16_t *bsrc[BI];
-    auto point = [&](int lt) {
-        int e, m0, n0;
-        locate(lt, e, m0, n0);
-        const int cnt = s_cnt[e];
-        const uint16_t *Ae = A + (int64_t)e * C * K;
-        const uint16_t *Be = B + (int64_t)e * N * K;
-#pragma unroll
-        for (int i = 0; i < AI; ++i) {
-            int am = m0 + (wave * AI + i) * 8 + lr;
-            am = am < cnt ? am : cnt - 1;
-            asrc[i] = Ae + (int64_t)am * K + lc * 8;
+    using St = Stage<LA, LB, DUAL>;
+    // loads of K tile kt.  With KTAIL (K not a multiple of 64) pieces past K
+    // are read from column 0 and zeroed when stored (a select at load time
+    // would make the wave wait for the load right away).
+    auto gload = [&](St &st, int kt) {
+        int kk = kt * 64;
+        if (KTAIL) {
+            st.in = kk + pc * 8 < K;
+            kk = st.in ? kk : -pc * 8;
         }
 #pragma unroll
-        for (int j = 0; j < BI; ++j) {
-            int bn = n0 + (wave * BI + j) * 8 + lr;
-            bn = bn < N ? bn : N - 1;
-            bsrc[j] = Be + (int64_t)bn * K + lc * 8;
+        for (int i = 0; i < LA; ++i) st.a[i] = ld16(pa[i] + kk);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            st.b[i] = ld16(pb[i] + kk);
+            if (DUAL) st.b3[i] = ld16(pb[i] + b3off + kk);
         }
+        __builtin_amdgcn_sched_barrier(0);     // issue the loads here, ahead of the MFMAs
     };
-
-    const int nk = (K + 63) >> 6;                       // K tiles per output tile
-    const int steps = my_tiles * nk;
-    // the last K tile of a tile with K % 64 != 0: pieces past K are cleared
-    // in LDS after their DMA has landed (they were loaded from column 0)
-    const bool ktail = (K & 63) != 0;
-    const bool tail_piece = ktail && ((nk - 1) * 64 + lc * 8 >= K);
-
-    // loads of step g (steps are issued in order; a tile's first K tile sets
-    // up that tile's sources)
-    auto issue = [&](uint8_t *base, int g) {
-        g = g < steps ? g : steps - 1;                  // past the end: reload the last step
-        const int lt = g / nk;
-        const int kt = g - lt * nk;
-        if (kt == 0) point(lt);
-        const int k0 = (ktail && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * 64;
-#pragma unroll
-        for (int i = 0; i < AI; ++i)
-            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(asrc[i] + k0),
-                                             (MOE_LDS_AS void *)(base + (wave * AI + i) * 1024), 16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < BI; ++j)
-            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(bsrc[j] + k0),
-                                             (MOE_LDS_AS void *)(base + A_BYTES + (wave * BI + j) * 1024), 16, 0, 0);
-        if (DUAL) {
-#pragma unroll
-            for (int j = 0; j < BI; ++j)
-                __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(bsrc[j] + b3off + k0),
-                                                 (MOE_LDS_AS void *)(base + A_BYTES + B_BYTES + (wave * BI + j) * 1024),
-                                                 16, 0, 0);
-        }
-    };
-    auto clear_tail = [&](uint8_t *base) {
+    auto sstore = [&](const St &st, int buf) {
+        uint16_t *sa = smem + buf * STAGE_ELEMS;
+        uint16_t *sb = sa + BM * 64;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        if (tail_piece) {
+        const bool in = KTAIL ? st.in : true;
 #pragma unroll
-            for (int i = 0; i < AI; ++i) *reinterpret_cast<u32x4 *>(base + (wave * AI + i) * 1024 + lane * 16) = z;
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4 *>(sa + soa[i]) = in ? st.a[i] : z;
 #pragma unroll
-            for (int j = 0; j < NBT * BI; ++j)
-                *reinterpret_cast<u32x4 *>(base + A_BYTES + (wave * BI + (j % BI)) * 1024 + (j / BI) * B_BYTES + lane * 16) = z;
+        for (int i = 0; i < LB; ++i) {
+            *reinterpret_cast<u32x4 *>(sb + sob[i]) = in ? st.b[i] : z;
+            if (DUAL) *reinterpret_cast<u32x4 *>(sb + BN * 64 + sob[i]) = in ? st.b3[i] : z;
         }
     };
 
-    // accumulators hold C^T fragments: acc[i][j] = W rows (n) x X rows (m), so
-    // each lane ends with 4 consecutive output columns of one output row
-    f32x4 acc[FM][FN];
-    f32x4 acc3[DUAL ? FM : 1][DUAL ? FN : 1];
-    auto zero_acc = [&]() {
+    // accumulators hold C^T fragments: acc[i][j] = W rows (n) x X rows (m); lane
+    // l holds output row m = l % 32 of the fragment and, for g = 0..3, the four
+    // consecutive columns n = 8g + 4 (l / 32) + 0..3 in elements 4g .. 4g+3
+    f32x16 acc[FM][FN];
+    f32x16 acc3[DUAL ? FM : 1][DUAL ? FN : 1];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int i = 0; i < (DUAL ? FM : 1); ++i)
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 #pragma unroll
-            for (int j = 0; j < (DUAL ? FN : 1); ++j) acc3[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    };
+    for (int i = 0; i < (DUAL ? FM : 1); ++i)
+#pragma unroll
+        for (int j = 0; j < (DUAL ? FN : 1); ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc3[i][j][q] = 0.f;
 
-    // fragment reads: row (base + lane%16), logical piece ks*4 + lane/16, stored at
-    // piece ^ (row % 8) = piece ^ (lane % 8) (fragment bases are multiples of 16)
-    const int arow = (wm * (BM / 2) + (lane & 15)) * 128;
-    const int brow = (wn * (BN / 2) + (lane & 15)) * 128;
-    auto compute = [&](const uint8_t *sa) {
-        const uint8_t *sb = sa + A_BYTES;
+    // fragment reads (32x16 operands): row (base + lane%32), logical piece
+    // 2 ks + lane/32; the fragment bases are multiples of 32, so the stored
+    // piece is piece ^ (lane % 8)
+    const int arow = (wm * (BM / 2) + (lane & 31)) * 64;
+    const int brow = (wn * (BN / 2) + (lane & 31)) * 64;
+    auto compute = [&](int buf) {
+        const uint16_t *sa = smem + buf * STAGE_ELEMS;
+        const uint16_t *sb = sa + BM * 64;
+        // every fragment of the K tile is read first, into its own registers, so
+        // the reads of later 16-wide k steps overlap the MFMAs of earlier ones
+        bf16x8 af[4][FM], bfr[4][FN], bf3[DUAL ? 4 : 1][DUAL ? FN : 1];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int pofs = (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16);
-            bf16x8 af[FM], bfr[FN];
+        for (int ks = 0; ks < 4; ++ks) {
+            const int pofs = ((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 3;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                af[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 16 * 128 + pofs));
+                af[ks][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 32 * 64 + pofs));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * 128 + pofs));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+                bfr[ks][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 32 * 64 + pofs));
             if (DUAL) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + B_BYTES + brow + j * 16 * 128 + pofs));
+                    bf3[DUAL ? ks : 0][DUAL ? j : 0] =
+                        as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + BN * 64 + brow + j * 32 * 64 + pofs));
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
+            if (DUAL) {
 #pragma unroll
                 for (int i = 0; i < (DUAL ? FM : 1); ++i)
 #pragma unroll
                     for (int j = 0; j < (DUAL ? FN : 1); ++j)
-                        acc3[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc3[i][j], 0, 0, 0);
+                        acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf3[DUAL ? ks : 0][j], af[ks][i],
+                                                                             acc3[i][j], 0, 0, 0);
             }
         }
     };
 
-    // epilogue of local tile lt: bias, activation, bf16, 8-byte stores of the
-    // 4 consecutive columns each lane holds (no LDS: the ring stays in flight)
-    auto epilogue = [&](int lt) {
-        int e, m0, n0;
-        locate(lt, e, m0, n0);
-        const int cnt = s_cnt[e];
-        uint16_t *oe = out + (int64_t)e * C * N;
+    // ---- pipeline: K tile kt is loaded into registers three steps ahead, stored
+    // into LDS buffer kt % 2 one step ahead and consumed at step kt.  Register
+    // stage r holds tiles r, r+3, ...; the steady-state loop (six steps, no
+    // conditional memory operations) only waits for a load when its stage is
+    // stored to LDS, two compute steps after the loads were issued.
+    const int nk = (K + 63) >> 6;
+    St r0, r1, r2;
+    gload(r0, 0);
+    if (nk > 1) gload(r1, 1);
+    if (nk > 2) gload(r2, 2);
+    sstore(r0, 0);
+    __syncthreads();
+#define MOE_STEP(KT, RFREE, RNEXT, CUR, NXT, LOAD)              \
+    do {                                                       \
+        if (LOAD) gload(RFREE, (KT) + 3);                      \
+        compute(CUR);                                          \
+        if ((KT) + 1 < nk) sstore(RNEXT, NXT);                 \
+        __syncthreads();                                       \
+    } while (0)
+    int kt = 0;
+    for (; kt + 9 <= nk; kt += 6) {
+        MOE_STEP(kt + 0, r0, r1, 0, 1, true);
+        MOE_STEP(kt + 1, r1, r2, 1, 0, true);
+        MOE_STEP(kt + 2, r2, r0, 0, 1, true);
+        MOE_STEP(kt + 3, r0, r1, 1, 0, true);
+        MOE_STEP(kt + 4, r1, r2, 0, 1, true);
+        MOE_STEP(kt + 5, r2, r0, 1, 0, true);
+    }
+    // tail: at most 8 steps, loads only while tiles remain
+#define MOE_TAIL(S, RF, RN, CB, NB)                                       \
+    if (kt + (S) < nk) MOE_STEP(kt + (S), RF, RN, CB, NB, kt + (S) + 3 < nk);
+    MOE_TAIL(0, r0, r1, 0, 1)
+    MOE_TAIL(1, r1, r2, 1, 0)
+    MOE_TAIL(2, r2, r0, 0, 1)
+    MOE_TAIL(3, r0, r1, 1, 0)
+    MOE_TAIL(4, r1, r2, 0, 1)
+    MOE_TAIL(5, r2, r0, 1, 0)
+    MOE_TAIL(6, r0, r1, 0, 1)
+    MOE_TAIL(7, r1, r2, 1, 0)
+#undef MOE_TAIL
+#undef MOE_STEP
+
+    // ---- epilogue: bias, activation, bf16, staged through LDS
+    constexpr int OS = TL::OUT_STRIDE;
+    uint16_t *so = smem;    // [BM][OUT_STRIDE]; every wave is past its last LDS read
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int nl = wn * (BN / 2) + j * 32 + 8 * g + 4 * (lane >> 5);   // 4 consecutive columns
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (BIAS && n < N) {
-                const uint2 bb = *reinterpret_cast<const uint2 *>(bias + (int64_t)e * N + n);
-                bv[0] = bf2f((uint16_t)(bb.x & 0xFFFFu)); bv[1] = bf2f((uint16_t)(bb.x >> 16));
-                bv[2] = bf2f((uint16_t)(bb.y & 0xFFFFu)); bv[3] = bf2f((uint16_t)(bb.y >> 16));
+            if (BIAS) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = n0 + nl + r;
+                    bv[r] = (n < N) ? bf2f(bias[(int64_t)e * N + n]) : 0.f;
+                }
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+                const int ml = wm * (BM / 2) + i * 32 + (lane & 31);
                 float v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float t = acc[i][j][r] + bv[r];
+                    float t = acc[i][j][4 * g + r] + bv[r];
                     if (ACT == 1) t = fmaxf(t, 0.f);
-                    if (ACT == 2) t = silu(t) * acc3[DUAL ? i : 0][DUAL ? j : 0][r];
+                    if (ACT == 2) t = silu(t) * acc3[DUAL ? i : 0][DUAL ? j : 0][4 * g + r];
                     v[r] = t;
                 }
-                if (m < cnt && n < N) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(v[0], v[1]);
-                    pk.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2 *>(oe + (int64_t)m * N + n) = pk;
-                }
+                uint2 pk;
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2 *>(so + ml * OS + nl) = pk;
             }
         }
-    };
-
-    // ---- the stream: step g consumes K tile g % nk of local tile g / nk from
-    // stage g % 3 after waiting for it (the newer stage stays in flight), and
-    // refills the stage consumed at step g-1 with step g+2
-    auto step = [&](uint8_t *cur, uint8_t *refill, int g) {
-        const int ct = g / nk;                      // local output tile of this step
-        const int ck = g - ct * nk;                 // its K tile
-        wait_vm_lgkm0<(S - 2) * PER>();
-        if (ktail && ck == nk - 1) {
-            clear_tail(cur);
-            wait_vm_lgkm0<(S - 2) * PER>();
-        }
-        __builtin_amdgcn_s_barrier();
-        issue(refill, g + 2);
-        if (ck == 0) zero_acc();
-        compute(cur);
-        if (ck == nk - 1) epilogue(ct);
-    };
-    issue(st0, 0);
-    issue(st1, 1);
-    int g = 0;
-    for (; g + 3 <= steps; g += 3) {
-        step(st0, st2, g);
-        step(st1, st0, g + 1);
-        step(st2, st1, g + 2);
     }
-    if (g < steps) step(st0, st2, g);
-    if (g + 1 < steps) step(st1, st0, g + 1);
-    wait_vm_lgkm0<0>();          // no DMA may outlive the block
+    __syncthreads();
+    uint16_t *oe = out + (int64_t)e * C * N;
+    constexpr int PIECES = BM * BN / 8;
+#pragma unroll
+    for (int q = tid; q < PIECES; q += 256) {
+        const int r = q / (BN / 8);
+        const int c = (q % (BN / 8)) * 8;
+        const int m = m0 + r;
+        const int n = n0 + c;
+        if (m < cnt && n < N)
+            st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(so + r * OS + c));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -443,23 +438,12 @@ int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_bound) {
 
 }  // namespace
 
-// The tile shape of the bf16 path (one shape for both expert GEMMs, so they
-// share one tile map).
-using TileBF16 = Tile<128, 128, 3>;
-
-// Compute units of the current device (8 XCDs x 32 on MI355X), times 1 block each.
-int persistent_blocks() {
-    static thread_local int cached = 0;
-    if (cached == 0) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-            cached = ((cus + 7) / 8) * 8;
-        else
-            cached = 256;
-    }
-    return cached;
-}
+// The tile shapes of the bf16 path: one BM for both expert GEMMs, so they share
+// one tile map. The gated (two-matrix) variant holds twice the accumulators and
+// runs one block per CU; the others fit two.
+using TileBF16 = Tile<128, 128, 2>;
+using TileBF16Gated = Tile<128, 128, 1>;
+static_assert(TileBF16::BM == TileBF16Gated::BM && TileBF16::BN == TileBF16Gated::BN, "one tile map");
 
 int gemm_bm(int dtype_bf16) { return dtype_bf16 ? TileBF16::BM : FBM; }
 
@@ -476,20 +460,22 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
     if (C == 0 || rows_bound == 0) return hipSuccess;
     if (dtype_bf16) {
         const int tiles_n = (N + TileBF16::BN - 1) / TileBF16::BN;
-        // persistent: one block per CU (the LDS ring takes most of a CU), at most
-        // as many blocks as tiles, a multiple of the 8 XCDs
-        int64_t g = grid_for(C, E, TileBF16::BM, tiles_n, rows_bound);
-        if (g > persistent_blocks()) g = persistent_blocks();
-        const dim3 grid((unsigned)g);
+        const dim3 grid((unsigned)grid_for(C, E, TileBF16::BM, tiles_n, rows_bound));
         const uint16_t *a = (const uint16_t *)A, *b = (const uint16_t *)B, *b3 = (const uint16_t *)B3,
                        *bi = (const uint16_t *)bias;
         uint16_t *o = (uint16_t *)out;
-#define MOE_GEMM(ACTV, BIASV)                                                                  \
-    hipLaunchKernelGGL((gemm_bf16_kernel<TileBF16, ACTV, BIASV>), grid, dim3(256), 0, s, a, b, b3, bi, \
-                       expert_count, tile_map, E, C, N, K, tiles_n, o)
-        if (act == 0) { if (bias) MOE_GEMM(0, true); else MOE_GEMM(0, false); }
-        else if (act == 1) { if (bias) MOE_GEMM(1, true); else MOE_GEMM(1, false); }
-        else MOE_GEMM(2, false);
+#define MOE_GEMM(TL, ACTV, BIASV)                                                              \
+    do {                                                                                       \
+        if (K % 64 == 0)                                                                       \
+            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, false>), grid, dim3(256), 0, s, \
+                               a, b, b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);   \
+        else                                                                                   \
+            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, true>), grid, dim3(256), 0, s, \
+                               a, b, b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);   \
+    } while (0)
+        if (act == 0) { if (bias) MOE_GEMM(TileBF16, 0, true); else MOE_GEMM(TileBF16, 0, false); }
+        else if (act == 1) { if (bias) MOE_GEMM(TileBF16, 1, true); else MOE_GEMM(TileBF16, 1, false); }
+        else MOE_GEMM(TileBF16Gated, 2, false);
 #undef MOE_GEMM
     } else {
         const int tiles_n = (N + FBN - 1) / FBN;
