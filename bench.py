@@ -19,9 +19,13 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -78,6 +82,145 @@ def roofline_of(work: dict, seconds: float) -> dict:
     ach = work["bytes"] / seconds / 1e9
     return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                 frac=round(ach / PEAK_HBM_GBS, 4))
+
+
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_argmax_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_TAG = "traffic-json: "
+COPY_PROBE_BYTES = 1 << 30
+
+# The rocprofv3 runs that the traffic summary is built from; {w} is the
+# workload, {o} the output directory.  Counters are collected in runs of
+# their own, one counter group per pass.
+PROFILE_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d {o}/ktrace -o k -- "
+    "python3 $REPO/bench.py --workload {w} --steps 10 --warmup 3 --cpu-seconds 0",
+    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/fetch -o f -- "
+    "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0",
+    "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/write -o w -- "
+    "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0",
+    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/copy_fetch -o c -- "
+    "python3 $REPO/bench.py --copy-probe %d" % COPY_PROBE_BYTES,
+    "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/copy_write -o c -- "
+    "python3 $REPO/bench.py --copy-probe %d" % COPY_PROBE_BYTES,
+    "python3 $REPO/bench.py --summarize {o} --workload {w} > $REPO/profiles/kernels_{w}.md",
+]
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if path.endswith((".hip", ".h")):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+_GEMM_ACT = re.compile(r"gemm_(?:bf16|f32)_kernel<(?:[^<>]*<[^<>]*>, )?(\d+),")
+
+
+def kernel_stage(name: str) -> str:
+    """The forward stage a kernel belongs to, from its (demangled) name."""
+    if "router" in name:
+        return "router"
+    if any(t in name for t in ("slot_rank", "slot_scan", "permute_kernel", "tile_map")):
+        return "dispatch"
+    m = _GEMM_ACT.search(name)
+    if m:
+        return "expert_gemm2" if m.group(1) == "0" else "expert_gemm1"
+    if "combine" in name:
+        return "combine"
+    return "other"
+
+
+def _counter_rows(d: str):
+    files = glob.glob(os.path.join(d, "*counter_collection.csv"))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _per_stage_kib(d: str, counter: str) -> dict:
+    """Mean counter value (KiB) per launch of each stage's kernels."""
+    acc = {}
+    for r in _counter_rows(d):
+        if r["Counter_Name"] != counter:
+            continue
+        st = kernel_stage(r["Kernel_Name"])
+        acc.setdefault(st, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _copy_kib(d: str, counter: str) -> float:
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(d)
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no copy kernel under {d}")
+    return sum(vals) / len(vals)
+
+
+def summarize(prof_dir: str, workload: str) -> str:
+    """Markdown summary of one profile set: kernel times and HBM traffic per launch."""
+    stats = glob.glob(os.path.join(prof_dir, "ktrace", "*kernel_stats.csv"))
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {prof_dir}/ktrace")
+    with open(stats[0]) as fh:
+        krows = list(csv.DictReader(fh))
+    fetch = _per_stage_kib(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
+    write = _per_stage_kib(os.path.join(prof_dir, "write"), "WRITE_SIZE")
+    kib = COPY_PROBE_BYTES / 1024
+    f_scale = kib / _copy_kib(os.path.join(prof_dir, "copy_fetch"), "FETCH_SIZE")
+    w_scale = kib / _copy_kib(os.path.join(prof_dir, "copy_write"), "WRITE_SIZE")
+    lines = [f"# Kernel times and HBM traffic, workload {workload}", "",
+             "Made by (REPO = the repository root, on an MI355X):", "", "```"]
+    lines += [c.format(w=workload, o="$REPO/gpurun_out/prof_" + workload) for c in PROFILE_COMMANDS]
+    lines += ["```", "", "## rocprofv3 --kernel-trace --stats", "",
+              "| kernel | stage | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in krows:
+        nm = r["Name"]
+        short = re.sub(r"\(.*$", "", nm.replace("moe::(anonymous namespace)::", ""))
+        short = short.replace("void ", "")
+        lines.append(f"| `{short}` | {kernel_stage(nm)} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} "
+                     f"| {float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.1f} |")
+    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc, scaled by the copy probe)", "",
+              f"Copy probe: {COPY_PROBE_BYTES} bytes copied device to device; FETCH_SIZE scale "
+              f"{f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f} (bytes moved / counter KiB*1024).", "",
+              "| stage | FETCH KiB (raw) | WRITE KiB (raw) | fetch bytes | write bytes | traffic bytes |",
+              "|---|---|---|---|---|---|"]
+    traffic = {}
+    for st in sorted(set(fetch) | set(write)):
+        fb = fetch.get(st, 0.0) * 1024 * f_scale
+        wb = write.get(st, 0.0) * 1024 * w_scale
+        traffic[st] = dict(fetch_bytes=round(fb), write_bytes=round(wb), traffic_bytes=round(fb + wb))
+        lines.append(f"| {st} | {fetch.get(st, 0):.1f} | {write.get(st, 0):.1f} | {fb:.0f} | {wb:.0f} "
+                     f"| {fb + wb:.0f} |")
+    lines += ["", "Per launch means the mean over that stage's kernel launches in the profiled steps; "
+              "the dispatch stage is several kernels, each counted as one launch.", "",
+              TRAFFIC_TAG + json.dumps(dict(workload=workload, source_digest=source_digest(),
+                                             fetch_scale=round(f_scale, 5), write_scale=round(w_scale, 5),
+                                             stages=traffic)), ""]
+    return "\n".join(lines)
+
+
+def committed_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed profile summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None, "no profile summary"
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith(TRAFFIC_TAG):
+                rec = json.loads(line[len(TRAFFIC_TAG):])
+                if rec.get("source_digest") != source_digest():
+                    return None, "kernel sources changed since the counters were taken"
+                st = rec["stages"].get(stage)
+                return (st["traffic_bytes"] if st else None), path
+    return None, "no traffic record"
 
 
 class HipEvents:
@@ -140,7 +283,13 @@ def main(argv=None):
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel that scales the HBM byte counters), then exit")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="only print the markdown summary of the rocprofv3 output under DIR "
+                         "(ktrace/, fetch/, write/, copy_fetch/, copy_write/), then exit")
     args = ap.parse_args(argv)
+    if args.summarize:
+        print(summarize(args.summarize, args.workload))
+        return 0
     if args.copy_probe:
         import torch
         n = args.copy_probe // 4
@@ -221,8 +370,10 @@ def main(argv=None):
                             flops=work[name]["flops"], **r)
     dominant = max(L.STAGES, key=lambda n: stage_ms[n])
     dom = dict(stages[dominant])
+    traffic, traffic_src = committed_traffic(cfg["name"], dominant)
     roofline = dict(bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"], unit=dom["unit"],
-                    frac=dom["frac"], traffic=None, kernel=dominant,
+                    frac=dom["frac"], traffic=traffic, traffic_unit="bytes/launch",
+                    traffic_source=traffic_src, kernel=dominant,
                     algorithmic_bytes=work[dominant]["bytes"], algorithmic_flops=work[dominant]["flops"],
                     avg_us=dom["us"])
     ffn_s = (stage_ms["expert_gemm1"] + stage_ms["expert_gemm2"]) / 1e3

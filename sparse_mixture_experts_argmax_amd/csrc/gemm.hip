@@ -25,6 +25,9 @@
 //   * The epilogue adds the bias, applies the activation, rounds to bf16 and
 //     stages the tile in LDS so that rows go out as coalesced 16-byte stores.
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 x 16 tiles).
+#ifndef MOE_RD_PATTERN
+#define MOE_RD_PATTERN 0
+#endif
 #include "common.h"
 #include "launch.h"
 
@@ -65,50 +68,67 @@ __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ tile_map, i
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
-// Tile shape: block BM x BN, K step 64; 4 waves in a 2 x 2 grid, each wave
-// (BM/2) x (BN/2) = FM x FN 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16:
-// on gfx950 one wave per SIMD keeps it issuing at nearly the full rate,
-// which the 16x16x32 form does not reach).  LDS rows are 64 bf16 =
-// 128 bytes = 8 pieces of 16 bytes; piece c of row r is stored at position
-// c ^ (r % 8), so the 16 rows of a fragment read and the 8 rows of a staging
-// write each touch every bank group once, with no padding.
-template <int BM_, int BN_, int MINB_ = 1>
-struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = 64;
-    static constexpr int MINB = MINB_;                  // blocks per CU the registers are sized for
-    static constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 fragments per wave
-    static constexpr int LA = BM * 8 / 256;             // 16-byte A pieces per thread per K tile
-    static constexpr int LB = BN * 8 / 256;             // 16-byte B pieces per thread per K tile
-    static constexpr int OUT_STRIDE = BN + 8;           // staged output row (bf16 elements)
-    static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-    // element offset of logical piece c of row r
-    static __device__ __forceinline__ int off(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
-};
+#define MOE_LDS_AS __attribute__((address_space(3)))
+#define MOE_GLB_AS __attribute__((address_space(1)))
 
-// Register stage of one K tile: this thread's 16-byte pieces of A, B (and B3).
-template <int LA, int LB, bool DUAL>
-struct Stage {
-    u32x4 a[LA];
-    u32x4 b[LB];
-    u32x4 b3[DUAL ? LB : 1];
-    bool in;          // false: these columns lie past K and are stored as zeros
+// s_waitcnt vmcnt(V) lgkmcnt(0) (expcnt left alone), gfx9 encoding.  The
+// 16-byte LDS DMA below is counted by vmcnt; a waitcnt of our own lets a
+// stage be waited for while the newer stages stay in flight.
+template <int V>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses only (lgkmcnt), so DMA loads of
+// later stages stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Tile shape: block BM x BN (BN = output columns; the gated form also stages
+// the matching BN rows of the second weight), K step 64, an S-deep ring of
+// LDS stages filled by 16-byte DMA (global_load_lds).  4 waves in a 2 x 2
+// grid; each wave owns (BM/2) x (BN/2) outputs = FM x FN fragments of
+// v_mfma_f32_32x32x16_bf16 (on gfx950 one wave per SIMD keeps this form
+// issuing at nearly the full rate).  Large wave tiles keep the LDS bytes read
+// per MFMA low: a 128 x 128 wave tile reads 16 KB of fragments per 64 MFMAs.
+// LDS rows are 64 bf16 = 128 bytes = 8 pieces of 16 bytes; piece c of row r
+// is stored at position c ^ (r % 8), so the 8 rows of a fragment read phase
+// and of a DMA instruction each touch every bank group once.
+template <int BM_, int BN_, int S_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, S = S_;
+    static constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 fragments per wave
+    static constexpr int AI = BM / 32, BI = BN / 32;    // 1 KB DMA instructions per wave per stage
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && S >= 2 && S <= 4, "tile");
 };
 
 template <class TL, int ACT, bool BIAS, bool KTAIL>
-__global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ B3,
     const uint16_t *__restrict__ bias, const int32_t *__restrict__ count,
     const int32_t *__restrict__ tile_map, int E, int64_t C, int N, int K, int tiles_n,
     uint16_t *__restrict__ out) {
-    constexpr int BM = TL::BM, BN = TL::BN;
-    constexpr int LA = TL::LA, LB = TL::LB, FM = TL::FM, FN = TL::FN;
+    constexpr int BM = TL::BM, BN = TL::BN, S = TL::S;
+    constexpr int FM = TL::FM, FN = TL::FN, AI = TL::AI, BI = TL::BI;
     constexpr bool DUAL = (ACT == 2);
     constexpr int NBT = DUAL ? 2 : 1;                    // weight tiles per stage
-    constexpr int STAGE_ELEMS = (BM + NBT * BN) * 64;
-    constexpr int OUT_ELEMS = BM * TL::OUT_STRIDE;
-    constexpr int SMEM_ELEMS = 2 * STAGE_ELEMS > OUT_ELEMS ? 2 * STAGE_ELEMS : OUT_ELEMS;
-    // two LDS stages of [A | B | B3] tiles; reused for the output tile at the end
-    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    constexpr int STAGE = A_BYTES + NBT * B_BYTES;
+    constexpr int PER = AI + NBT * BI;                   // DMA instructions per wave per stage
+    // DMA instructions a wave issues after a stage's own before that stage is
+    // waited for: those of the S - 2 newer stages
+    constexpr int NEWER = (S - 2) * PER;
+    static_assert(BM * BN <= STAGE, "an output half-tile must fit one stage buffer");
+    // one LDS array per stage: the compiler then sees that the fragment reads of
+    // one stage cannot alias the DMA in flight into another and adds no wait
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
     __shared__ int s_map[MAX_E_LDS + 1];
 
     int e, mt, nt;
@@ -119,73 +139,78 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (DMA base)
     const int wm = wave >> 1;
     const int wn = wave & 1;
-
-    const uint16_t *Ae = A + (int64_t)e * C * K;
-    const uint16_t *Be = B + (int64_t)e * N * K;
     const int64_t b3off = DUAL ? (int64_t)(B3 - B) : 0;
 
-    // staging: piece q = tid + i*256 -> row q / 8, logical piece q % 8 (rows past
-    // the count / past N read a valid row whose result is discarded)
-    const int pc = tid & 7;
-    const uint16_t *pa[LA];
-    const uint16_t *pb[LB];
-    int soa[LA], sob[LB];
+    // DMA sources: wave instruction i fills LDS rows [8 (wave * AI + i), +8);
+    // lane l lands at byte 16 l of that 1 KB block = row l / 8, position l % 8,
+    // which holds logical piece (l % 8) ^ (l / 8) of its row.  Rows past the
+    // count / past N read a valid row; their results are never stored.
+    const int lr = lane >> 3;
+    const int lc = (lane & 7) ^ lr;
+    const uint16_t *asrc[AI];
+    const uint16_t *bsrc[BI];
+    {
+        const uint16_t *Ae = A + (int64_t)e * C * K;
+        const uint16_t *Be = B + (int64_t)e * N * K;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int r = (tid >> 3) + i * 32;
-        int am = m0 + r;
-        am = am < cnt ? am : cnt - 1;
-        pa[i] = Ae + (int64_t)am * K + pc * 8;
-        soa[i] = TL::off(r, pc);
+        for (int i = 0; i < AI; ++i) {
+            int am = m0 + (wave * AI + i) * 8 + lr;
+            am = am < cnt ? am : cnt - 1;
+            asrc[i] = Ae + (int64_t)am * K + lc * 8;
+        }
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            int bn = n0 + (wave * BI + j) * 8 + lr;
+            bn = bn < N ? bn : N - 1;
+            bsrc[j] = Be + (int64_t)bn * K + lc * 8;
+        }
     }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int r = (tid >> 3) + i * 32;
-        int bn = n0 + r;
-        bn = bn < N ? bn : N - 1;
-        pb[i] = Be + (int64_t)bn * K + pc * 8;
-        sob[i] = TL::off(r, pc);
-    }
+    const int nk = (K + 63) >> 6;
+    // with K % 64 != 0 the pieces of the last K tile that lie past K are read
+    // from column 0 and cleared in LDS once they have landed
+    const bool tail_piece = KTAIL && ((nk - 1) * 64 + lc * 8 >= K);
 
-    using St = Stage<LA, LB, DUAL>;
-    // loads of K tile kt.  With KTAIL (K not a multiple of 64) pieces past K
-    // are read from column 0 and zeroed when stored (a select at load time
-    // would make the wave wait for the load right away).
-    auto gload = [&](St &st, int kt) {
-        int kk = kt * 64;
-        if (KTAIL) {
-            st.in = kk + pc * 8 < K;
-            kk = st.in ? kk : -pc * 8;
-        }
+    auto issue = [&](uint8_t *base, int kt) {
+        const int k0 = (KTAIL && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * 64;
 #pragma unroll
-        for (int i = 0; i < LA; ++i) st.a[i] = ld16(pa[i] + kk);
+        for (int i = 0; i < AI; ++i)
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(asrc[i] + k0),
+                                             (MOE_LDS_AS void *)(base + (wave * AI + i) * 1024), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            st.b[i] = ld16(pb[i] + kk);
-            if (DUAL) st.b3[i] = ld16(pb[i] + b3off + kk);
+        for (int j = 0; j < BI; ++j)
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(bsrc[j] + k0),
+                                             (MOE_LDS_AS void *)(base + A_BYTES + (wave * BI + j) * 1024),
+                                             16, 0, 0);
+        if (DUAL) {
+#pragma unroll
+            for (int j = 0; j < BI; ++j)
+                __builtin_amdgcn_global_load_lds(
+                    (const MOE_GLB_AS void *)(bsrc[j] + b3off + k0),
+                    (MOE_LDS_AS void *)(base + A_BYTES + B_BYTES + (wave * BI + j) * 1024), 16, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);     // issue the loads here, ahead of the MFMAs
+        // keep every DMA of the stage ahead of the MFMAs that follow (left to
+        // itself the scheduler sinks them to the end of the step, which leaves
+        // almost no time for them to land)
+        __builtin_amdgcn_sched_barrier(0);
     };
-    auto sstore = [&](const St &st, int buf) {
-        uint16_t *sa = smem + buf * STAGE_ELEMS;
-        uint16_t *sb = sa + BM * 64;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const bool in = KTAIL ? st.in : true;
+    auto clear_tail = [&](uint8_t *base) {
+        if (tail_piece) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4 *>(sa + soa[i]) = in ? st.a[i] : z;
+            for (int i = 0; i < AI; ++i) *reinterpret_cast<u32x4 *>(base + (wave * AI + i) * 1024 + lane * 16) = z;
 #pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            *reinterpret_cast<u32x4 *>(sb + sob[i]) = in ? st.b[i] : z;
-            if (DUAL) *reinterpret_cast<u32x4 *>(sb + BN * 64 + sob[i]) = in ? st.b3[i] : z;
+            for (int j = 0; j < NBT * BI; ++j)
+                *reinterpret_cast<u32x4 *>(base + A_BYTES + (j / BI) * B_BYTES + (wave * BI + (j % BI)) * 1024 +
+                                           lane * 16) = z;
         }
     };
 
-    // accumulators hold C^T fragments: acc[i][j] = W rows (n) x X rows (m); lane
-    // l holds output row m = l % 32 of the fragment and, for g = 0..3, the four
-    // consecutive columns n = 8g + 4 (l / 32) + 0..3 in elements 4g .. 4g+3
+    // accumulators hold C^T fragments: acc[i][j] = weight rows (n) x x rows (m);
+    // lane l holds output row m = l % 32 of the fragment and, for g = 0..3, the
+    // four consecutive columns n = 8 g + 4 (l / 32) + 0..3 in elements 4g..4g+3
     f32x16 acc[FM][FN];
     f32x16 acc3[DUAL ? FM : 1][DUAL ? FN : 1];
 #pragma unroll
@@ -201,96 +226,150 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc3[i][j][q] = 0.f;
 
-    // fragment reads (32x16 operands): row (base + lane%32), logical piece
-    // 2 ks + lane/32; the fragment bases are multiples of 32, so the stored
-    // piece is piece ^ (lane % 8)
-    const int arow = (wm * (BM / 2) + (lane & 31)) * 64;
-    const int brow = (wn * (BN / 2) + (lane & 31)) * 64;
-    auto compute = [&](int buf) {
-        const uint16_t *sa = smem + buf * STAGE_ELEMS;
-        const uint16_t *sb = sa + BM * 64;
-        // every fragment of the K tile is read first, into its own registers, so
-        // the reads of later 16-wide k steps overlap the MFMAs of earlier ones
-        bf16x8 af[4][FM], bfr[4][FN], bf3[DUAL ? 4 : 1][DUAL ? FN : 1];
+    // fragment reads (32 x 16 operands): row (base + lane % 32), logical piece
+    // 2 ks + lane / 32; fragment bases are multiples of 32, so the stored
+    // position is piece ^ (lane % 8)
+    const int arow = (wm * (BM / 2) + (lane & 31)) * 128;
+    const int brow = (wn * (BN / 2) + (lane & 31)) * 128;
+    // fragments of two k steps: the reads of k step ks + 1 are issued between
+    // the MFMAs of k step ks
+    bf16x8 af[2][FM], bfr[2][FN], bf3[DUAL ? 2 : 1][DUAL ? FN : 1];
+    auto rd = [&](const uint8_t *sa, int ks, int sl) {
+        const uint8_t *sb = sa + A_BYTES;
+        const int pofs = ((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 4;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int pofs = ((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 3;
+        for (int i = 0; i < FM; ++i)
+            af[sl][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 32 * 128 + pofs));
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[ks][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 32 * 64 + pofs));
+        for (int j = 0; j < FN; ++j)
+            bfr[sl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 32 * 128 + pofs));
+        if (DUAL) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[ks][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 32 * 64 + pofs));
-            if (DUAL) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bf3[DUAL ? ks : 0][DUAL ? j : 0] =
-                        as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + BN * 64 + brow + j * 32 * 64 + pofs));
-            }
+                bf3[DUAL ? sl : 0][DUAL ? j : 0] =
+                    as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + B_BYTES + brow + j * 32 * 128 + pofs));
         }
+    };
+    // per k step: R fragment reads (of the next k step) and M MFMAs; one read
+    // goes after each of the first R MFMAs
+    constexpr int R = FM + (DUAL ? 2 : 1) * FN;
+    constexpr int M = FM * FN * (DUAL ? 2 : 1);
+    static_assert(M >= R, "read/MFMA interleave");
+    // the MFMAs of one K tile; the fragments of its k step 0 are already read
+    auto compute = [&](const uint8_t *sa) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            const int sl = ks & 1;
+            if (ks < 3) rd(sa, ks + 1, sl ^ 1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[sl][j], af[sl][i], acc[i][j], 0, 0, 0);
             if (DUAL) {
 #pragma unroll
                 for (int i = 0; i < (DUAL ? FM : 1); ++i)
 #pragma unroll
                     for (int j = 0; j < (DUAL ? FN : 1); ++j)
-                        acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf3[DUAL ? ks : 0][j], af[ks][i],
+                        acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf3[DUAL ? sl : 0][j], af[sl][i],
                                                                              acc3[i][j], 0, 0, 0);
             }
+            if (ks < 3) {
+#if MOE_RD_PATTERN == 1
+                __builtin_amdgcn_sched_group_barrier(0x100, R, 0);       // the reads first
+                __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+#elif MOE_RD_PATTERN == 2
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
+#else
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
+#endif
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // ---- pipeline: K tile kt is loaded into registers three steps ahead, stored
-    // into LDS buffer kt % 2 one step ahead and consumed at step kt.  Register
-    // stage r holds tiles r, r+3, ...; the steady-state loop (six steps, no
-    // conditional memory operations) only waits for a load when its stage is
-    // stored to LDS, two compute steps after the loads were issued.
-    const int nk = (K + 63) >> 6;
-    St r0, r1, r2;
-    gload(r0, 0);
-    if (nk > 1) gload(r1, 1);
-    if (nk > 2) gload(r2, 2);
-    sstore(r0, 0);
-    __syncthreads();
-#define MOE_STEP(KT, RFREE, RNEXT, CUR, NXT, LOAD)              \
-    do {                                                       \
-        if (LOAD) gload(RFREE, (KT) + 3);                      \
-        compute(CUR);                                          \
-        if ((KT) + 1 < nk) sstore(RNEXT, NXT);                 \
-        __syncthreads();                                       \
-    } while (0)
+    // ---- the ring: K tile kt lives in stage kt % S.  Step kt waits for its
+    // own DMA (the S - 2 newer stages stay in flight), passes one barrier (all
+    // waves have landed their part of kt and finished reading kt - 1), refills
+    // the stage of kt - 1 with kt + S - 1, then runs the MFMAs of kt.
+    issue(st0, 0);
+    if (S > 2 && nk > 1) issue(st1, 1);
+    if (S > 3 && nk > 2) issue(st2, 2);
     int kt = 0;
-    for (; kt + 9 <= nk; kt += 6) {
-        MOE_STEP(kt + 0, r0, r1, 0, 1, true);
-        MOE_STEP(kt + 1, r1, r2, 1, 0, true);
-        MOE_STEP(kt + 2, r2, r0, 0, 1, true);
-        MOE_STEP(kt + 3, r0, r1, 1, 0, true);
-        MOE_STEP(kt + 4, r1, r2, 0, 1, true);
-        MOE_STEP(kt + 5, r2, r0, 1, 0, true);
+    // steady state: every step refills a stage, so the wait count is fixed
+    // and the loop body has no branch
+#define MOE_STEP(CUR, NXT)                                                      \
+    {                                                                           \
+        wait_vm_lgkm0<NEWER>();                                                 \
+        lds_barrier();                                                          \
+        rd(CUR, 0, 0);                                                          \
+        issue(NXT, kt + S - 1);                                                 \
+        compute(CUR);                                                           \
+        ++kt;                                                                   \
     }
-    // tail: at most 8 steps, loads only while tiles remain
-#define MOE_TAIL(S, RF, RN, CB, NB)                                       \
-    if (kt + (S) < nk) MOE_STEP(kt + (S), RF, RN, CB, NB, kt + (S) + 3 < nk);
-    MOE_TAIL(0, r0, r1, 0, 1)
-    MOE_TAIL(1, r1, r2, 1, 0)
-    MOE_TAIL(2, r2, r0, 0, 1)
-    MOE_TAIL(3, r0, r1, 1, 0)
-    MOE_TAIL(4, r1, r2, 0, 1)
-    MOE_TAIL(5, r2, r0, 1, 0)
-    MOE_TAIL(6, r0, r1, 0, 1)
-    MOE_TAIL(7, r1, r2, 1, 0)
-#undef MOE_TAIL
+    for (; kt + 2 * S - 1 <= nk;) {
+        if constexpr (S == 2) {
+            MOE_STEP(st0, st1)
+            MOE_STEP(st1, st0)
+        } else if constexpr (S == 3) {
+            MOE_STEP(st0, st2)
+            MOE_STEP(st1, st0)
+            MOE_STEP(st2, st1)
+        } else {
+            MOE_STEP(st0, st3)
+            MOE_STEP(st1, st0)
+            MOE_STEP(st2, st1)
+            MOE_STEP(st3, st2)
+        }
+    }
 #undef MOE_STEP
+    // drain: at most 2 S - 2 steps, refilling while K tiles remain; kt % S == 0 here
+#define MOE_TAIL(CUR, NXT)                                                      \
+    if (kt < nk) {                                                              \
+        if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
+        else wait_vm_lgkm0<0>();                                                \
+        if (KTAIL && kt == nk - 1) clear_tail(CUR);                             \
+        lds_barrier();                                                          \
+        rd(CUR, 0, 0);                                                          \
+        if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
+        __builtin_amdgcn_sched_barrier(0);                                      \
+        compute(CUR);                                                           \
+        ++kt;                                                                   \
+    }
+    if constexpr (S == 2) {
+        MOE_TAIL(st0, st1)
+        MOE_TAIL(st1, st0)
+    } else if constexpr (S == 3) {
+        MOE_TAIL(st0, st2)
+        MOE_TAIL(st1, st0)
+        MOE_TAIL(st2, st1)
+        MOE_TAIL(st0, st2)
+    } else {
+        MOE_TAIL(st0, st3)
+        MOE_TAIL(st1, st0)
+        MOE_TAIL(st2, st1)
+        MOE_TAIL(st3, st2)
+        MOE_TAIL(st0, st3)
+        MOE_TAIL(st1, st0)
+    }
+#undef MOE_TAIL
 
-    // ---- epilogue: bias, activation, bf16, staged through LDS
-    constexpr int OS = TL::OUT_STRIDE;
-    uint16_t *so = smem;    // [BM][OUT_STRIDE]; every wave is past its last LDS read
+    // ---- epilogue: bias, activation, bf16; the tile is staged in LDS (row
+    // half wm in stage buffer wm, pieces of 16 bytes swizzled by row) so that
+    // rows go out as coalesced 16-byte stores
+    constexpr int P = BN / 8;                            // 16-byte pieces per output row
+    lds_barrier();                                       // every wave is past its last fragment read
+    uint8_t *so = wm ? st1 : st0;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -298,41 +377,47 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
             const int nl = wn * (BN / 2) + j * 32 + 8 * g + 4 * (lane >> 5);   // 4 consecutive columns
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if (BIAS) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = n0 + nl + r;
-                    bv[r] = (n < N) ? bf2f(bias[(int64_t)e * N + n]) : 0.f;
+                const int n = n0 + nl;
+                if (n < N) {
+                    const uint2 bb = *reinterpret_cast<const uint2 *>(bias + (int64_t)e * N + n);
+                    bv[0] = bf2f((uint16_t)(bb.x & 0xFFFFu));
+                    bv[1] = bf2f((uint16_t)(bb.x >> 16));
+                    bv[2] = bf2f((uint16_t)(bb.y & 0xFFFFu));
+                    bv[3] = bf2f((uint16_t)(bb.y >> 16));
                 }
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int ml = wm * (BM / 2) + i * 32 + (lane & 31);
+                const int r = i * 32 + (lane & 31);      // row within the half
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float t = acc[i][j][4 * g + r] + bv[r];
+                for (int q = 0; q < 4; ++q) {
+                    float t = acc[i][j][4 * g + q] + bv[q];
                     if (ACT == 1) t = fmaxf(t, 0.f);
-                    if (ACT == 2) t = silu(t) * acc3[DUAL ? i : 0][DUAL ? j : 0][4 * g + r];
-                    v[r] = t;
+                    if (ACT == 2) t = silu(t) * acc3[DUAL ? i : 0][DUAL ? j : 0][4 * g + q];
+                    v[q] = t;
                 }
                 uint2 pk;
                 pk.x = pack_bf16x2(v[0], v[1]);
                 pk.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2 *>(so + ml * OS + nl) = pk;
+                const int pc = (nl >> 3) ^ (r & (P - 1));
+                *reinterpret_cast<uint2 *>(so + r * (BN * 2) + (pc << 4) + ((nl & 4) << 1)) = pk;
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     uint16_t *oe = out + (int64_t)e * C * N;
-    constexpr int PIECES = BM * BN / 8;
+    static_assert((BM * P) % 256 == 0, "whole store rounds");
 #pragma unroll
-    for (int q = tid; q < PIECES; q += 256) {
-        const int r = q / (BN / 8);
-        const int c = (q % (BN / 8)) * 8;
-        const int m = m0 + r;
-        const int n = n0 + c;
-        if (m < cnt && n < N)
-            st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(so + r * OS + c));
+    for (int it = 0; it < BM * P / 256; ++it) {
+        const int q = tid + it * 256;
+        const int R = q / P;                             // tile row
+        const int p = q % P;
+        const int r = R % (BM / 2);
+        const uint8_t *src = (R < BM / 2 ? st0 : st1) + r * (BN * 2) + ((p ^ (r & (P - 1))) << 4);
+        const int m = m0 + R;
+        const int n = n0 + p * 8;
+        if (m < cnt && n < N) st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(src));
     }
 }
 
@@ -438,14 +523,20 @@ int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_bound) {
 
 }  // namespace
 
-// The tile shapes of the bf16 path: one BM for both expert GEMMs, so they share
-// one tile map. The gated (two-matrix) variant holds twice the accumulators and
-// runs one block per CU; the others fit two.
-using TileBF16 = Tile<128, 128, 2>;
-using TileBF16Gated = Tile<128, 128, 1>;
-static_assert(TileBF16::BM == TileBF16Gated::BM && TileBF16::BN == TileBF16Gated::BN, "one tile map");
+// Row-tile height of the bf16 path: one BM for both expert GEMMs, so they
+// share one tile map.  256 (half the LDS bytes per MFMA of 128) only when an
+// expert holds at least 512 rows: a 256-row tile over a 257-row expert would
+// spend half its MFMAs on padding.
+int gemm_bm(int dtype_bf16, int64_t C) { return dtype_bf16 ? (C >= 512 ? 256 : 128) : FBM; }
 
-int gemm_bm(int dtype_bf16) { return dtype_bf16 ? TileBF16::BM : FBM; }
+// bf16 tile shapes: W = 256 output columns, N = 128, G = gated (128 columns
+// of each weight); the suffix is BM.  Stage rings fill about 128-144 KB of LDS.
+using TileW256 = Tile<256, 256, 2>;
+using TileN256 = Tile<256, 128, 3>;
+using TileG256 = Tile<256, 128, 2>;
+using TileW128 = Tile<128, 256, 3>;
+using TileN128 = Tile<128, 128, 4>;
+using TileG128 = Tile<128, 128, 3>;
 
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s) {
@@ -459,23 +550,44 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
                                int64_t rows_bound, void *out, hipStream_t s) {
     if (C == 0 || rows_bound == 0) return hipSuccess;
     if (dtype_bf16) {
-        const int tiles_n = (N + TileBF16::BN - 1) / TileBF16::BN;
-        const dim3 grid((unsigned)grid_for(C, E, TileBF16::BM, tiles_n, rows_bound));
+        const int bm = gemm_bm(1, C);
         const uint16_t *a = (const uint16_t *)A, *b = (const uint16_t *)B, *b3 = (const uint16_t *)B3,
                        *bi = (const uint16_t *)bias;
         uint16_t *o = (uint16_t *)out;
-#define MOE_GEMM(TL, ACTV, BIASV)                                                              \
-    do {                                                                                       \
-        if (K % 64 == 0)                                                                       \
-            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, false>), grid, dim3(256), 0, s, \
-                               a, b, b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);   \
-        else                                                                                   \
-            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, true>), grid, dim3(256), 0, s, \
-                               a, b, b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);   \
+        // row tiles an expert-parallel launch can expect (for the column-tile choice)
+        const int64_t mt_est = (rows_bound + bm - 1) / bm;
+#define MOE_GEMM(TL, ACTV, BIASV)                                                                   \
+    do {                                                                                            \
+        const int tiles_n = (N + TL::BN - 1) / TL::BN;                                              \
+        const dim3 grid((unsigned)grid_for(C, E, TL::BM, tiles_n, rows_bound));                     \
+        if (K % 64 == 0)                                                                            \
+            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, false>), grid, dim3(256), 0, s, a, b, \
+                               b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);             \
+        else                                                                                        \
+            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, true>), grid, dim3(256), 0, s, a, b, \
+                               b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);             \
     } while (0)
-        if (act == 0) { if (bias) MOE_GEMM(TileBF16, 0, true); else MOE_GEMM(TileBF16, 0, false); }
-        else if (act == 1) { if (bias) MOE_GEMM(TileBF16, 1, true); else MOE_GEMM(TileBF16, 1, false); }
-        else MOE_GEMM(TileBF16Gated, 2, false);
+        // 256 output columns per tile unless that leaves fewer tiles than CUs
+        const bool wide = mt_est * ((N + 255) / 256) >= 256;
+        if (bm == 256) {
+            if (act == 2) MOE_GEMM(TileG256, 2, false);
+            else if (wide) {
+                if (act == 1) { if (bias) MOE_GEMM(TileW256, 1, true); else MOE_GEMM(TileW256, 1, false); }
+                else { if (bias) MOE_GEMM(TileW256, 0, true); else MOE_GEMM(TileW256, 0, false); }
+            } else {
+                if (act == 1) { if (bias) MOE_GEMM(TileN256, 1, true); else MOE_GEMM(TileN256, 1, false); }
+                else { if (bias) MOE_GEMM(TileN256, 0, true); else MOE_GEMM(TileN256, 0, false); }
+            }
+        } else {
+            if (act == 2) MOE_GEMM(TileG128, 2, false);
+            else if (wide) {
+                if (act == 1) { if (bias) MOE_GEMM(TileW128, 1, true); else MOE_GEMM(TileW128, 1, false); }
+                else { if (bias) MOE_GEMM(TileW128, 0, true); else MOE_GEMM(TileW128, 0, false); }
+            } else {
+                if (act == 1) { if (bias) MOE_GEMM(TileN128, 1, true); else MOE_GEMM(TileN128, 1, false); }
+                else { if (bias) MOE_GEMM(TileN128, 0, true); else MOE_GEMM(TileN128, 0, false); }
+            }
+        }
 #undef MOE_GEMM
     } else {
         const int tiles_n = (N + FBN - 1) / FBN;

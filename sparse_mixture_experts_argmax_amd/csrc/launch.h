@@ -31,8 +31,8 @@ hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_i
 
 // ---- experts ----------------------------------------------------------
 // Row-tile height of the grouped GEMM; tile_map holds E+1 prefix sums of
-// ceil(expert_count / GEMM_BM).
-int gemm_bm(int dtype_bf16);
+// ceil(expert_count / gemm_bm(dtype, C)).
+int gemm_bm(int dtype_bf16, int64_t C);
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s);
 // out[e, m, :] = act(A[e, m, :] . B[e]^T (+ bias[e]))  for m < count[e]

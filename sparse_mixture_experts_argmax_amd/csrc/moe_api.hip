@@ -164,7 +164,7 @@ moe_status run_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count, 
     int32_t *tile_map = reinterpret_cast<int32_t *>(ws + w.tile_map);
     void *H = ws + w.h;
     const int bf16 = dt == MOE_BF16;
-    MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16), tile_map, stream));
+    MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16, C), tile_map, stream));
     const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
     MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, E, C,
                                      dff, d, rows_bound, H, stream));
@@ -356,7 +356,7 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     if (!mark(1)) return MOE_ERR_HIP;
     MOE_CHECK(run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
                            base + w.dispatch, stream));
-    if (C > 0) MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16), tile_map, stream));
+    if (C > 0) MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16, C), tile_map, stream));
     if (!mark(2)) return MOE_ERR_HIP;
     if (C > 0) {
         const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;

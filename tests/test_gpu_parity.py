@@ -12,7 +12,7 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
-from gpu_util import (AUX_RTOL, check_routing, check_y, device_inputs, host_bits, host_f64)
+from gpu_util import (AUX_RTOL, Y_TOL, check_routing, check_y, device_inputs, host_bits, host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,9 @@ SMALL = {
     "e300_generic": (400, 32, 64, 300, 2, 2.0, "bf16", "relu", False, False, 2.0),
     "f32_swiglu": (150, 16, 24, 6, 2, 1.5, "f32", "swiglu", False, True, 4.0),
     "tiles": (4096, 256, 384, 16, 1, 1.25, "bf16", "relu", True, False, 1.0),
+    # experts of at least 512 rows: the 256-row GEMM tiles, with K and N tails
+    "big_tiles": (3000, 200, 328, 4, 2, 1.0, "bf16", "relu", True, False, 1.0),
+    "big_swiglu": (2048, 136, 200, 2, 1, 1.0, "bf16", "swiglu", False, False, 1.0),
 }
 
 
@@ -212,3 +215,55 @@ def test_deterministic(name):
                     [plan.intermediate("slot").cpu().numpy().copy()])
     for a, b in zip(*outs):
         assert (a == b).all()
+
+
+def _ffn_rows(cfg, sample=None, seed=7):
+    """Expert FFN outputs, element by element, on the GPU's own dispatch buffer.
+
+    Every kept (expert, row) when `sample` is None, else a seeded sample of
+    that many rows plus the first and last row of every non-empty expert."""
+    t = device_inputs(cfg)
+    C = moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
+    idx, gate, ps, rc = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    slot, drop, count, xbuf = moe.dispatch(t["x"], idx, cfg["E"], C)
+    ybuf = moe.expert_ffn(xbuf, count, t["W1"], t["W2"], W3=t["W3"], b1=t["b1"], b2=t["b2"],
+                          act=cfg["act"])
+    torch.cuda.synchronize()
+    cnt = count.cpu().numpy()
+    rows = [(e, m) for e in range(cfg["E"]) for m in range(int(cnt[e]))]
+    if sample is not None and len(rows) > sample:
+        rng = np.random.default_rng(seed)
+        pick = set(rng.choice(len(rows), size=sample, replace=False).tolist())
+        ends = {(e, 0) for e in range(cfg["E"]) if cnt[e]} | {(e, int(cnt[e]) - 1) for e in range(cfg["E"]) if cnt[e]}
+        rows = sorted({rows[i] for i in pick} | ends)
+    xb = host_f64(xbuf)
+    yb = host_f64(ybuf)
+    got, ref = [], []
+    for e in sorted({e for e, _ in rows}):
+        ms = np.array([m for ee, m in rows if ee == e])
+        W3 = None if cfg["W3"] is None else O.widen(cfg["W3"][e], cfg["dtype"])
+        b1 = None if cfg["b1"] is None else O.widen(cfg["b1"][e], cfg["dtype"])
+        b2 = None if cfg["b2"] is None else O.widen(cfg["b2"][e], cfg["dtype"])
+        ref.append(O.expert_ffn(xb[e, ms], O.widen(cfg["W1"][e], cfg["dtype"]),
+                                O.widen(cfg["W2"][e], cfg["dtype"]), cfg["act"], b1=b1, b2=b2, W3=W3))
+        got.append(yb[e, ms])
+    return np.concatenate(got), np.concatenate(ref), len(rows)
+
+
+@pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "ragged_f32",
+                                  "switch_base", "mixtral"])
+def test_expert_ffn_elementwise(name):
+    """Each GEMM tile shape against the oracle's expert FFN, every element of the checked rows.
+
+    The bound is the forward's, scaled by the row magnitudes (expert outputs are
+    not damped by a gate): max-abs <= tol * max(1, max |ref|), L1 ratio <= tol."""
+    cfg = _full(name) if name in FULL else _small(name)
+    got, ref, n = _ffn_rows(cfg, sample=None if name not in FULL else 160)
+    max_abs, l1 = Y_TOL[cfg["dtype"]]
+    err = np.abs(got - ref)
+    scale = max(1.0, float(np.abs(ref).max()))
+    ratio = err.sum() / max(np.abs(ref).sum(), 1e-30)
+    print(f"expert FFN parity: {name}, {n} rows, max-abs {err.max():.3e} (scale {scale:.2f}), "
+          f"L1 ratio {ratio:.3e}", flush=True)
+    assert err.max() <= max_abs * scale
+    assert ratio <= l1
