@@ -32,6 +32,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// Workgroup barrier that orders LDS accesses only (waits lgkmcnt, not vmcnt):
+// global loads issued ahead for later steps stay in flight across it, which
+// __syncthreads (a full fence) would drain.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Argmax candidate: larger value wins, equal values go to the lower index.
 // `ok` false means "no candidate" and loses to any real one.
 struct Cand {

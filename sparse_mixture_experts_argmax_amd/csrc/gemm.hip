@@ -25,9 +25,6 @@
 //   * The epilogue adds the bias, applies the activation, rounds to bf16 and
 //     stages the tile in LDS so that rows go out as coalesced 16-byte stores.
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 x 16 tiles).
-#ifndef MOE_RD_PATTERN
-#define MOE_RD_PATTERN 0
-#endif
 #include "common.h"
 #include "launch.h"
 
@@ -68,6 +65,15 @@ __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ tile_map, i
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
+// SiLU for the bf16 epilogue: exp through the hardware exp2 and a hardware
+// reciprocal (each about 1 ulp of fp32); the result is rounded to bf16
+// (8 significand bits) right after, so the difference from silu() does not
+// survive.  Very negative a gives exp2 -> inf, rcp -> 0, result -0.
+__device__ __forceinline__ float silu_fast(float a) {
+    const float ex = __builtin_amdgcn_exp2f(-a * 1.44269504088896341f);   // e^-a = 2^(-a log2 e)
+    return a * __builtin_amdgcn_rcpf(1.0f + ex);
+}
+
 #define MOE_LDS_AS __attribute__((address_space(3)))
 #define MOE_GLB_AS __attribute__((address_space(1)))
 
@@ -80,14 +86,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-// Workgroup barrier that orders LDS accesses only (lgkmcnt), so DMA loads of
-// later stages stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Tile shape: block BM x BN (BN = output columns; the gated form also stages
 // the matching BN rows of the second weight), K step 64, an S-deep ring of
 // LDS stages filled by 16-byte DMA (global_load_lds).  4 waves in a 2 x 2
@@ -95,34 +93,47 @@ __device__ __forceinline__ void lds_barrier() {
 // v_mfma_f32_32x32x16_bf16 (on gfx950 one wave per SIMD keeps this form
 // issuing at nearly the full rate).  Large wave tiles keep the LDS bytes read
 // per MFMA low: a 128 x 128 wave tile reads 16 KB of fragments per 64 MFMAs.
-// LDS rows are 64 bf16 = 128 bytes = 8 pieces of 16 bytes; piece c of row r
-// is stored at position c ^ (r % 8), so the 8 rows of a fragment read phase
-// and of a DMA instruction each touch every bank group once.
-template <int BM_, int BN_, int S_>
+// A stage holds BK columns of K: LDS rows of BK bf16 = 8 (BK = 64) or 4
+// (BK = 32) pieces of 16 bytes.  Piece c of row r is stored at position
+// c ^ swz(r), swz(r) = r % 8 for 128-byte rows and (r / 2) % 4 for 64-byte
+// rows, so the 8 rows of a fragment read phase and the rows of a DMA
+// instruction each touch every bank group once.  MINB = 2 sizes the ring and
+// the registers for two blocks per CU, so that one block's prologue and
+// epilogue overlap the other's MFMAs.
+template <int BM_, int BN_, int S_, int BK_ = 64, int MINB_ = 1>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, S = S_;
+    static constexpr int BM = BM_, BN = BN_, S = S_, BK = BK_, MINB = MINB_;
+    static constexpr int ROWB = BK * 2;                 // bytes per LDS row
+    static constexpr int PIECES = BK / 8;               // 16-byte pieces per row
+    static constexpr int KS = BK / 16;                  // MFMA k steps per stage
     static constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 fragments per wave
-    static constexpr int AI = BM / 32, BI = BN / 32;    // 1 KB DMA instructions per wave per stage
+    static constexpr int AI = BM * ROWB / 4096;         // 1 KB DMA instructions per wave per stage (A)
+    static constexpr int BI = BN * ROWB / 4096;         // (B)
     static_assert(BM % 64 == 0 && BN % 64 == 0 && S >= 2 && S <= 4, "tile");
+    static_assert((BK == 64 || BK == 32) && (MINB == 1 || MINB == 2), "tile");
+    static __device__ __forceinline__ int swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 };
 
 template <class TL, int ACT, bool BIAS, bool KTAIL>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
+__global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ B3,
     const uint16_t *__restrict__ bias, const int32_t *__restrict__ count,
     const int32_t *__restrict__ tile_map, int E, int64_t C, int N, int K, int tiles_n,
     uint16_t *__restrict__ out) {
-    constexpr int BM = TL::BM, BN = TL::BN, S = TL::S;
+    constexpr int BM = TL::BM, BN = TL::BN, S = TL::S, BK = TL::BK;
+    constexpr int ROWB = TL::ROWB, PIECES = TL::PIECES, KS = TL::KS;
     constexpr int FM = TL::FM, FN = TL::FN, AI = TL::AI, BI = TL::BI;
     constexpr bool DUAL = (ACT == 2);
     constexpr int NBT = DUAL ? 2 : 1;                    // weight tiles per stage
-    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
     constexpr int STAGE = A_BYTES + NBT * B_BYTES;
     constexpr int PER = AI + NBT * BI;                   // DMA instructions per wave per stage
     // DMA instructions a wave issues after a stage's own before that stage is
     // waited for: those of the S - 2 newer stages
     constexpr int NEWER = (S - 2) * PER;
-    static_assert(BM * BN <= STAGE, "an output half-tile must fit one stage buffer");
+    // the output tile is staged through two stage buffers (a row half each)
+    // when it fits, else stored from registers
+    constexpr bool STAGED_OUT = BM * BN <= STAGE;
     // one LDS array per stage: the compiler then sees that the fragment reads of
     // one stage cannot alias the DMA in flight into another and adds no wait
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
@@ -144,12 +155,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     const int wn = wave & 1;
     const int64_t b3off = DUAL ? (int64_t)(B3 - B) : 0;
 
-    // DMA sources: wave instruction i fills LDS rows [8 (wave * AI + i), +8);
-    // lane l lands at byte 16 l of that 1 KB block = row l / 8, position l % 8,
-    // which holds logical piece (l % 8) ^ (l / 8) of its row.  Rows past the
-    // count / past N read a valid row; their results are never stored.
-    const int lr = lane >> 3;
-    const int lc = (lane & 7) ^ lr;
+    // DMA sources: wave instruction i fills the RPI LDS rows starting at
+    // RPI (wave * AI + i); lane l lands at byte 16 l of that 1 KB block = row
+    // l / PIECES, position l % PIECES, which holds logical piece
+    // (l % PIECES) ^ swz(row) of its row (RPI is a multiple of 8, so swz of
+    // the row is swz(l / PIECES)).  Rows past the count / past N read a
+    // valid row; their results are never stored.
+    constexpr int RPI = 1024 / ROWB;                     // LDS rows per DMA instruction
+    const int lr = lane / PIECES;
+    const int lc = (lane % PIECES) ^ TL::swz(lr);
     const uint16_t *asrc[AI];
     const uint16_t *bsrc[BI];
     {
@@ -157,24 +171,24 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
         const uint16_t *Be = B + (int64_t)e * N * K;
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
-            int am = m0 + (wave * AI + i) * 8 + lr;
+            int am = m0 + (wave * AI + i) * RPI + lr;
             am = am < cnt ? am : cnt - 1;
             asrc[i] = Ae + (int64_t)am * K + lc * 8;
         }
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
-            int bn = n0 + (wave * BI + j) * 8 + lr;
+            int bn = n0 + (wave * BI + j) * RPI + lr;
             bn = bn < N ? bn : N - 1;
             bsrc[j] = Be + (int64_t)bn * K + lc * 8;
         }
     }
-    const int nk = (K + 63) >> 6;
-    // with K % 64 != 0 the pieces of the last K tile that lie past K are read
+    const int nk = (K + BK - 1) / BK;
+    // with K % BK != 0 the pieces of the last K tile that lie past K are read
     // from column 0 and cleared in LDS once they have landed
-    const bool tail_piece = KTAIL && ((nk - 1) * 64 + lc * 8 >= K);
+    const bool tail_piece = KTAIL && ((nk - 1) * BK + lc * 8 >= K);
 
     auto issue = [&](uint8_t *base, int kt) {
-        const int k0 = (KTAIL && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * 64;
+        const int k0 = (KTAIL && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * BK;
 #pragma unroll
         for (int i = 0; i < AI; ++i)
             __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(asrc[i] + k0),
@@ -228,26 +242,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
 
     // fragment reads (32 x 16 operands): row (base + lane % 32), logical piece
     // 2 ks + lane / 32; fragment bases are multiples of 32, so the stored
-    // position is piece ^ (lane % 8)
-    const int arow = (wm * (BM / 2) + (lane & 31)) * 128;
-    const int brow = (wn * (BN / 2) + (lane & 31)) * 128;
+    // position is piece ^ swz(lane % 32)
+    const int arow = (wm * (BM / 2) + (lane & 31)) * ROWB;
+    const int brow = (wn * (BN / 2) + (lane & 31)) * ROWB;
+    const int fswz = TL::swz(lane & 31);
     // fragments of two k steps: the reads of k step ks + 1 are issued between
     // the MFMAs of k step ks
     bf16x8 af[2][FM], bfr[2][FN], bf3[DUAL ? 2 : 1][DUAL ? FN : 1];
     auto rd = [&](const uint8_t *sa, int ks, int sl) {
         const uint8_t *sb = sa + A_BYTES;
-        const int pofs = ((ks * 2 + (lane >> 5)) ^ (lane & 7)) << 4;
+        const int pofs = ((ks * 2 + (lane >> 5)) ^ fswz) << 4;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[sl][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 32 * 128 + pofs));
+            af[sl][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 32 * ROWB + pofs));
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            bfr[sl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 32 * 128 + pofs));
+            bfr[sl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 32 * ROWB + pofs));
         if (DUAL) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 bf3[DUAL ? sl : 0][DUAL ? j : 0] =
-                    as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + B_BYTES + brow + j * 32 * 128 + pofs));
+                    as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + B_BYTES + brow + j * 32 * ROWB + pofs));
         }
     };
     // per k step: R fragment reads (of the next k step) and M MFMAs; one read
@@ -258,9 +273,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     // the MFMAs of one K tile; the fragments of its k step 0 are already read
     auto compute = [&](const uint8_t *sa) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const int sl = ks & 1;
-            if (ks < 3) rd(sa, ks + 1, sl ^ 1);
+            if (ks < KS - 1) rd(sa, ks + 1, sl ^ 1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -274,25 +289,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
                         acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf3[DUAL ? sl : 0][j], af[sl][i],
                                                                              acc3[i][j], 0, 0, 0);
             }
-            if (ks < 3) {
-#if MOE_RD_PATTERN == 1
-                __builtin_amdgcn_sched_group_barrier(0x100, R, 0);       // the reads first
-                __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
-#elif MOE_RD_PATTERN == 2
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
-#else
+            if (ks < KS - 1) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
-#endif
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -364,12 +367,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
     }
 #undef MOE_TAIL
 
-    // ---- epilogue: bias, activation, bf16; the tile is staged in LDS (row
-    // half wm in stage buffer wm, pieces of 16 bytes swizzled by row) so that
-    // rows go out as coalesced 16-byte stores
+    // ---- epilogue: bias, activation, bf16.  With STAGED_OUT the tile is staged
+    // in LDS (row half wm in stage buffer wm, 16-byte pieces swizzled by row)
+    // so that rows go out as coalesced 16-byte stores; otherwise each lane
+    // stores its four consecutive columns (8 bytes) directly.
     constexpr int P = BN / 8;                            // 16-byte pieces per output row
-    lds_barrier();                                       // every wave is past its last fragment read
+    if (STAGED_OUT) lds_barrier();                       // every wave is past its last fragment read
     uint8_t *so = wm ? st1 : st0;
+    uint16_t *oe = out + (int64_t)e * C * N;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -394,30 +399,37 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
                 for (int q = 0; q < 4; ++q) {
                     float t = acc[i][j][4 * g + q] + bv[q];
                     if (ACT == 1) t = fmaxf(t, 0.f);
-                    if (ACT == 2) t = silu(t) * acc3[DUAL ? i : 0][DUAL ? j : 0][4 * g + q];
+                    if (ACT == 2) t = silu_fast(t) * acc3[DUAL ? i : 0][DUAL ? j : 0][4 * g + q];
                     v[q] = t;
                 }
                 uint2 pk;
                 pk.x = pack_bf16x2(v[0], v[1]);
                 pk.y = pack_bf16x2(v[2], v[3]);
-                const int pc = (nl >> 3) ^ (r & (P - 1));
-                *reinterpret_cast<uint2 *>(so + r * (BN * 2) + (pc << 4) + ((nl & 4) << 1)) = pk;
+                if (STAGED_OUT) {
+                    const int pc = (nl >> 3) ^ (r & (P - 1));
+                    *reinterpret_cast<uint2 *>(so + r * (BN * 2) + (pc << 4) + ((nl & 4) << 1)) = pk;
+                } else {
+                    const int m = m0 + wm * (BM / 2) + r;
+                    const int n = n0 + nl;
+                    if (m < cnt && n < N) *reinterpret_cast<uint2 *>(oe + (int64_t)m * N + n) = pk;
+                }
             }
         }
     }
-    lds_barrier();
-    uint16_t *oe = out + (int64_t)e * C * N;
-    static_assert((BM * P) % 256 == 0, "whole store rounds");
+    if (STAGED_OUT) {
+        lds_barrier();
+        static_assert(!STAGED_OUT || (BM * P) % 256 == 0, "whole store rounds");
 #pragma unroll
-    for (int it = 0; it < BM * P / 256; ++it) {
-        const int q = tid + it * 256;
-        const int R = q / P;                             // tile row
-        const int p = q % P;
-        const int r = R % (BM / 2);
-        const uint8_t *src = (R < BM / 2 ? st0 : st1) + r * (BN * 2) + ((p ^ (r & (P - 1))) << 4);
-        const int m = m0 + R;
-        const int n = n0 + p * 8;
-        if (m < cnt && n < N) st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(src));
+        for (int it = 0; it < BM * P / 256; ++it) {
+            const int q = tid + it * 256;
+            const int R = q / P;                         // tile row
+            const int p = q % P;
+            const int r = R % (BM / 2);
+            const uint8_t *src = (R < BM / 2 ? st0 : st1) + r * (BN * 2) + ((p ^ (r & (P - 1))) << 4);
+            const int m = m0 + R;
+            const int n = n0 + p * 8;
+            if (m < cnt && n < N) st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(src));
+        }
     }
 }
 
@@ -530,13 +542,17 @@ int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_bound) {
 int gemm_bm(int dtype_bf16, int64_t C) { return dtype_bf16 ? (C >= 512 ? 256 : 128) : FBM; }
 
 // bf16 tile shapes: W = 256 output columns, N = 128, G = gated (128 columns
-// of each weight); the suffix is BM.  Stage rings fill about 128-144 KB of LDS.
-using TileW256 = Tile<256, 256, 2>;
-using TileN256 = Tile<256, 128, 3>;
-using TileG256 = Tile<256, 128, 2>;
-using TileW128 = Tile<128, 256, 3>;
-using TileN128 = Tile<128, 128, 4>;
-using TileG128 = Tile<128, 128, 3>;
+// of each weight); the suffix is BM.  The 128-row shapes (and the narrow
+// 256-row one) use 32-wide K stages sized for two blocks per CU; the wide
+// 256-row shapes keep 64-wide K stages, one block per CU (half the LDS
+// bytes per MFMA of a 128-row tile, and enough MFMA work per step to hide
+// the DMA).  Each ring fills 128-144 KB of LDS per CU.
+using TileW256 = Tile<256, 256, 2, 64, 1>;
+using TileN256 = Tile<256, 128, 3, 32, 2>;
+using TileG256 = Tile<256, 128, 2, 64, 1>;
+using TileW128 = Tile<128, 256, 3, 32, 2>;
+using TileN128 = Tile<128, 128, 4, 32, 2>;
+using TileG128 = Tile<128, 128, 3, 32, 2>;
 
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s) {

@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) load(st[s], s < nchunk ? s : nchunk - 1);
     auto step = [&](RStage<WPER> &cur, int c) {
-        __syncthreads();                     // the previous chunk's MFMAs are done with sW
+        lds_barrier();                       // the previous chunk's MFMAs are done with sW
         store_w(cur, c);
-        __syncthreads();
+        lds_barrier();
         compute(cur);
         const int cn = c + DEPTH;
         load(cur, cn < nchunk ? cn : nchunk - 1);
