@@ -77,7 +77,7 @@ int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor);
 /* Workspace bytes needed by moe_router / moe_dispatch / moe_expert_ffn /
  * moe_forward for the given sizes (host functions).  0 means "none";
  * SIZE_MAX means the sizes are invalid. */
-size_t moe_router_workspace_bytes(int64_t T, int32_t E, int32_t k);
+size_t moe_router_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k);
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
 size_t moe_expert_ffn_workspace_bytes(int32_t E, int64_t C, int32_t dff, moe_dtype dt);
 size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
@@ -112,6 +112,9 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
  *   prob_sum    [E]     fp32 out, sum over tokens of the softmax p_i(x)
  *   route_count [E]     int32 out, number of (token, rank) choices per expert
  *                       (before capacity)
+ *   ws          moe_router_workspace_bytes(T, d, E, k) bytes of device scratch
+ *               (per-block partial sums, and for bf16 x with E <= 256 the
+ *               exact three-part bf16 split of W_r that the MFMA path reads)
  * Logits are fp32 ([SW-RES] section 2.1); non-finite inputs do not fault
  * and still give indices in [0, E).
  */

@@ -39,7 +39,7 @@ class WsLayout(C.Structure):
 SIGNATURES = {
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_capacity": (_i64, [_i64, _i32, _i32, C.c_double]),
-    "moe_router_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_router_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i32, _i64, _i32, C.c_int]),
     "moe_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i64, C.c_int, C.c_int]),

@@ -76,7 +76,7 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None):
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
     route_count = torch.empty(E, dtype=torch.int32, device=dev)
-    need = L.LIB.moe_router_workspace_bytes(T, E, k)
+    need = L.LIB.moe_router_workspace_bytes(T, d, E, k)
     if need == L.SIZE_MAX:
         raise ValueError("invalid router sizes")
     ws = workspace if workspace is not None else _workspace(need, dev)

@@ -32,6 +32,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+#define MOE_LDS_AS __attribute__((address_space(3)))
+#define MOE_GLB_AS __attribute__((address_space(1)))
+
+// s_waitcnt vmcnt(V) lgkmcnt(0) (expcnt left alone), gfx9 encoding.  The
+// 16-byte LDS DMA (global_load_lds) is counted by vmcnt; a waitcnt of our own
+// lets a stage be waited for while the newer stages stay in flight.
+template <int V>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 // Workgroup barrier that orders LDS accesses only (waits lgkmcnt, not vmcnt):
 // global loads issued ahead for later steps stay in flight across it, which
 // __syncthreads (a full fence) would drain.
@@ -55,12 +67,59 @@ __device__ __forceinline__ bool cand_better(const Cand &a, const Cand &b) {
     return a.i < b.i;
 }
 
+// Reductions over each row of 16 lanes with DPP lane moves (no LDS round
+// trip): swap neighbours, swap pairs, mirror within 8, mirror within 16.
+// After the four steps every lane of the row holds the same result (each
+// step combines two groups that already agree internally).
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    return v + dpp_f<DPP_MIRROR>(v);
+}
+
 __device__ __forceinline__ Cand cand_shfl_xor(const Cand &c, int m) {
     Cand o;
     o.v = __shfl_xor(c.v, m);
     o.i = __shfl_xor(c.i, m);
     o.ok = __shfl_xor(c.ok, m);
     return o;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Cand cand_dpp(const Cand &c) {
+    return Cand{dpp_f<CTRL>(c.v), dpp_i<CTRL>(c.i), dpp_i<CTRL>(c.ok)};
+}
+// the best candidate of each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ Cand row16_best(Cand c) {
+    Cand o = cand_dpp<DPP_XOR1>(c);
+    if (cand_better(o, c)) c = o;
+    o = cand_dpp<DPP_XOR2>(c);
+    if (cand_better(o, c)) c = o;
+    o = cand_dpp<DPP_HALF_MIRROR>(c);
+    if (cand_better(o, c)) c = o;
+    o = cand_dpp<DPP_MIRROR>(c);
+    if (cand_better(o, c)) c = o;
+    return c;
 }
 
 }  // namespace moe

@@ -74,18 +74,6 @@ __device__ __forceinline__ float silu_fast(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + ex);
 }
 
-#define MOE_LDS_AS __attribute__((address_space(3)))
-#define MOE_GLB_AS __attribute__((address_space(1)))
-
-// s_waitcnt vmcnt(V) lgkmcnt(0) (expcnt left alone), gfx9 encoding.  The
-// 16-byte LDS DMA below is counted by vmcnt; a waitcnt of our own lets a
-// stage be waited for while the newer stages stay in flight.
-template <int V>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(V >= 0 && V < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
 // Tile shape: block BM x BN (BN = output columns; the gated form also stages
 // the matching BN rows of the second weight), K step 64, an S-deep ring of
 // LDS stages filled by 16-byte DMA (global_load_lds).  4 waves in a 2 x 2

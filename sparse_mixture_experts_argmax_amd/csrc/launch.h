@@ -11,9 +11,10 @@ namespace moe {
 // ---- router -----------------------------------------------------------
 // Number of per-block partial rows the router writes for T tokens.
 int router_blocks(int64_t T, int dtype_bf16, int E);
+// w3: scratch of 3 * E * d bf16 for the exact three-part split of W_r.
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
-                         float *part_prob, int32_t *part_cnt, hipStream_t s);
+                         float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s);
 hipError_t launch_router_reduce(const float *part_prob, const int32_t *part_cnt, int nblk,
                                 int E, float *prob_sum, int32_t *route_count, hipStream_t s);
 

@@ -24,14 +24,15 @@ bool act_ok(int a) { return a == MOE_ACT_RELU || a == MOE_ACT_SWIGLU; }
 constexpr int64_t ROUTER_MIN_TOK = 8;
 
 struct RouterWs {
-    size_t part_prob, part_cnt, total;
+    size_t part_prob, part_cnt, w3, total;
 };
-RouterWs router_ws(int64_t T, int E) {
+RouterWs router_ws(int64_t T, int d, int E) {
     RouterWs w;
     const int64_t nblk = (T + ROUTER_MIN_TOK - 1) / ROUTER_MIN_TOK;
     w.part_prob = 0;
     w.part_cnt = up((size_t)nblk * E * 4);
-    w.total = w.part_cnt + up((size_t)nblk * E * 4);
+    w.w3 = w.part_cnt + up((size_t)nblk * E * 4);
+    w.total = w.w3 + up((size_t)3 * E * d * 2);     // three bf16 parts of W_r
     return w;
 }
 
@@ -65,7 +66,7 @@ struct ForwardWs {
 };
 ForwardWs forward_ws(int64_t T, int d, int dff, int E, int k, int64_t C, moe_dtype dt) {
     ForwardWs w;
-    w.r = router_ws(T, E);
+    w.r = router_ws(T, d, E);
     w.dsp = dispatch_ws(T, E, k);
     w.f = ffn_ws(E, C, dff, dt);
     size_t o = 0;
@@ -130,12 +131,13 @@ moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
                       float *gate, float *prob_sum, int32_t *route_count, char *ws,
                       hipStream_t stream) {
-    const RouterWs w = router_ws(T, E);
+    const RouterWs w = router_ws(T, d, E);
     float *part_prob = reinterpret_cast<float *>(ws + w.part_prob);
     int32_t *part_cnt = reinterpret_cast<int32_t *>(ws + w.part_cnt);
+    uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + w.w3);
     const int bf16 = dt == MOE_BF16;
     MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
-                               part_cnt, stream));
+                               part_cnt, w3, stream));
     MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
                                       prob_sum, route_count, stream));
     return MOE_OK;
@@ -197,9 +199,9 @@ int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor) {
     return (int64_t)c;
 }
 
-size_t moe_router_workspace_bytes(int64_t T, int32_t E, int32_t k) {
-    if (check_sizes(T, E, k) != MOE_OK) return SIZE_MAX;
-    return router_ws(T, E).total;
+size_t moe_router_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k) {
+    if (check_sizes(T, E, k) != MOE_OK || check_width(d) != MOE_OK) return SIZE_MAX;
+    return router_ws(T, d, E).total;
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
@@ -246,7 +248,7 @@ moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float
     if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr4_ok(expert_idx, empty) ||
         !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false))
         return MOE_ERR_INVALID_ARGUMENT;
-    const size_t need = router_ws(T, E).total;
+    const size_t need = router_ws(T, d, E).total;
     if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
     return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,

@@ -36,8 +36,7 @@ constexpr int MAXK = 8;
 constexpr int RM_WAVES = 4;
 constexpr int RM_TOK_WAVE = 16;
 constexpr int RM_TOK_BLOCK = RM_WAVES * RM_TOK_WAVE;
-constexpr int RM_KC = 32;                  // one 16x16x32 MFMA k-step per chunk
-constexpr int RM_STRIDE = RM_KC + 8;       // padded LDS row (bf16 elements)
+constexpr int RM_LDS = 128 * 1024;         // LDS bytes of the stage ring
 
 __device__ __forceinline__ void split3(float w, uint16_t &h, uint16_t &m, uint16_t &l) {
     h = f2bf(w);
@@ -47,133 +46,198 @@ __device__ __forceinline__ void split3(float w, uint16_t &h, uint16_t &m, uint16
     l = f2bf(r2);
 }
 
-// Register stage of one K chunk: this thread's share of the W_r chunk (fp32)
-// and its x fragment.  Loads are never conditional (indices are clamped and
-// out-of-range values zeroed when used) so that the compiler only waits for a
-// stage when it is consumed, DEPTH chunks after its loads were issued.
-template <int WPER>
-struct RStage {
-    float4 w[WPER];
-    u32x4 x;
-    bool xin;
+// W3[p][n][:] = part p of W_r[n][:] (p = 0 hi, 1 mid, 2 lo), once per call.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ Wr, int64_t n,
+                                                           uint16_t *__restrict__ W3) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        uint16_t h, m, l;
+        split3(Wr[i], h, m, l);
+        W3[i] = h;
+        W3[n + i] = m;
+        W3[2 * n + i] = l;
+    }
+}
+
+// Stage geometry of the MFMA router: a stage holds KC columns of the three
+// weight parts (3 x EP rows) and of the block's 64 token rows, in LDS rows of
+// KC bf16.  Piece c (16 bytes) of row r is stored at c ^ swz(r), as in the
+// expert GEMM: conflict-free 16-byte fragment reads and DMA writes.
+template <int NB, int KC>
+struct RGeo {
+    static constexpr int EP = NB * 16;
+    static constexpr int ROWB = KC * 2;
+    static constexpr int PIECES = KC / 8;
+    static constexpr int ROWS = 3 * EP + RM_TOK_BLOCK;
+    static constexpr int STAGE = ROWS * ROWB;
+    static constexpr int S = RM_LDS / STAGE > 4 ? 4 : RM_LDS / STAGE;
+    static constexpr int PERW = STAGE / 4096;            // 1 KB DMA instructions per wave per stage
+    static constexpr int RPI = 1024 / ROWB;              // rows per DMA instruction
+    static_assert(S >= 2 && STAGE % 4096 == 0, "router stage ring");
+    static __device__ __forceinline__ int swz(int r) { return KC == 64 ? (r & 7) : ((r >> 1) & 3); }
 };
 
-template <int NB>
-constexpr int router_depth() { return NB <= 4 ? 4 : (NB <= 8 ? 3 : 2); }
+template <int NB, int KC>
+constexpr bool rgeo_ok() { return RM_LDS / ((3 * NB * 16 + RM_TOK_BLOCK) * KC * 2) >= 2; }
 
-template <int NB>
+// One block = 64 tokens (4 waves x 16) and every expert.  The three bf16
+// parts of W_r (exact split, see router_split_kernel) and the token rows flow
+// through an S-deep ring of LDS stages filled by 16-byte DMA; bf16 x bf16
+// products are exact in fp32, so three v_mfma_f32_16x16x32_bf16 per 16
+// experts and 32 columns give the fp32 dot products.
+template <int NB, int KC, bool KTAIL, int KSEL>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
-    const uint16_t *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ br,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
     float *__restrict__ part_prob, int32_t *__restrict__ part_cnt) {
-    constexpr int EP = NB * 16;
-    constexpr int DEPTH = router_depth<NB>();
-    __shared__ __attribute__((aligned(16))) uint16_t sW[3][EP * RM_STRIDE];
+    using G = RGeo<NB, KC>;
+    constexpr int EP = G::EP, ROWB = G::ROWB, PIECES = G::PIECES, S = G::S, PERW = G::PERW;
+    constexpr int STAGE = G::STAGE, RPI = G::RPI;
+    constexpr int NEWER = (S - 2) * PERW;
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
     __shared__ float sProb[RM_WAVES][EP];
     __shared__ int sCnt[EP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;      // expert column within a 16-block / token row of A
     const int kg = lane >> 4;       // k group (A/B operands) or row group (D)
-    const int64_t tw = (int64_t)blockIdx.x * RM_TOK_BLOCK + wave * RM_TOK_WAVE;
-
+    const int64_t t0 = (int64_t)blockIdx.x * RM_TOK_BLOCK;
+    const int64_t tw = t0 + wave * RM_TOK_WAVE;
     for (int i = tid; i < EP; i += 256) sCnt[i] = 0;
 
-    constexpr int WPIECES = EP * (RM_KC / 4);           // float4 pieces per chunk
-    constexpr int WPER = (WPIECES + 255) / 256;
-    // this thread's W pieces: row p/8 (clamped to E-1), column (p%8)*4
-    const float *wrow[WPER];
-    bool wok[WPER];
+    // DMA sources: block instruction q = wave * PERW + i fills rows
+    // [q RPI, +RPI): rows 0 .. 3 EP - 1 are the weight parts (expert rows
+    // past E repeat row E - 1), the rest the block's tokens (past T: row T - 1)
+    const int lr = lane / PIECES;
+    const int lc = (lane % PIECES) ^ G::swz(lr);
+    const int64_t nW = (int64_t)E * d;
+    const uint16_t *src[PERW];
 #pragma unroll
-    for (int q = 0; q < WPER; ++q) {
-        const int p = tid + q * 256;
-        int row = p >> 3;
-        wok[q] = p < WPIECES && row < E;
-        row = row < E ? row : E - 1;
-        wrow[q] = Wr + (int64_t)row * d + (p & 7) * 4;
-    }
-    const int64_t txr = (tw + col < T) ? tw + col : T - 1;
-    const uint16_t *xrow = x + txr * d + 8 * kg;
-    const bool tok_in = tw + col < T;
-
-    auto load = [&](RStage<WPER> &st, int c) {
-        const int k0 = c * RM_KC;
-#pragma unroll
-        for (int q = 0; q < WPER; ++q) {
-            const int kc = k0 + ((tid + q * 256) & 7) * 4;
-            st.w[q] = *reinterpret_cast<const float4 *>(wrow[q] + (kc < d ? k0 : 0));
+    for (int i = 0; i < PERW; ++i) {
+        const int row = (wave * PERW + i) * RPI + lr;
+        if (row < 3 * EP) {
+            const int p = row / EP;
+            int n = row - p * EP;
+            n = n < E ? n : E - 1;
+            src[i] = W3 + p * nW + (int64_t)n * d + lc * 8;
+        } else {
+            int64_t t = t0 + (row - 3 * EP);
+            t = t < T ? t : T - 1;
+            src[i] = x + t * d + lc * 8;
         }
-        st.xin = tok_in && (k0 + 8 * kg < d);
-        st.x = ld16(xrow + (k0 + 8 * kg < d ? k0 : 0));
+    }
+    const int nk = (d + KC - 1) / KC;
+    const bool tail_piece = KTAIL && ((nk - 1) * KC + lc * 8 >= d);
+    auto issue = [&](uint8_t *base, int kt) {
+        const int k0 = (KTAIL && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * KC;
+#pragma unroll
+        for (int i = 0; i < PERW; ++i)
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(src[i] + k0),
+                                             (MOE_LDS_AS void *)(base + (wave * PERW + i) * 1024),
+                                             16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
-    auto store_w = [&](const RStage<WPER> &st, int c) {
-        const int k0 = c * RM_KC;
+    // the pieces past d were loaded from column 0: clear them (products with a
+    // zero operand on either side are zero)
+    auto clear_tail = [&](uint8_t *base) {
+        if (tail_piece) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int q = 0; q < WPER; ++q) {
-            const int p = tid + q * 256;
-            if (p < WPIECES) {
-                const int row = p >> 3;
-                const int c4 = (p & 7) * 4;
-                const bool ok = wok[q] && (k0 + c4 < d);
-                const float w[4] = {ok ? st.w[q].x : 0.f, ok ? st.w[q].y : 0.f,
-                                    ok ? st.w[q].z : 0.f, ok ? st.w[q].w : 0.f};
-                uint16_t h[4], m[4], l[4];
+            for (int i = 0; i < PERW; ++i) *reinterpret_cast<u32x4 *>(base + (wave * PERW + i) * 1024 + lane * 16) = z;
+        }
+    };
+
+    // wave w computes the logits of all 64 tokens (4 row blocks of 16) for its
+    // NBW groups of 16 experts, g = w NBW .. w NBW + NBW - 1: every weight
+    // fragment read from LDS feeds 4 MFMAs
+    constexpr int NBW = NB / RM_WAVES;
+    static_assert(NB % RM_WAVES == 0, "expert groups per wave");
+    f32x4 acc[4][NBW];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) split3(w[j], h[j], m[j], l[j]);
-                const int o = row * RM_STRIDE + c4;
-                uint2 vh, vm, vl;
-                vh.x = h[0] | ((uint32_t)h[1] << 16); vh.y = h[2] | ((uint32_t)h[3] << 16);
-                vm.x = m[0] | ((uint32_t)m[1] << 16); vm.y = m[2] | ((uint32_t)m[3] << 16);
-                vl.x = l[0] | ((uint32_t)l[1] << 16); vl.y = l[2] | ((uint32_t)l[3] << 16);
-                *reinterpret_cast<uint2 *>(&sW[0][o]) = vh;
-                *reinterpret_cast<uint2 *>(&sW[1][o]) = vm;
-                *reinterpret_cast<uint2 *>(&sW[2][o]) = vl;
+    for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+        for (int g = 0; g < NBW; ++g) acc[ab][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragment rows: A = token row ab 16 + col, B = weight row p EP + g 16 + col;
+    // row bases are multiples of 16, so swz(row) = swz(col)
+    const int fs = G::swz(col);
+    const int arow = (3 * EP + col) * ROWB;
+    const int brow = (wave * NBW * 16 + col) * ROWB;
+    auto compute = [&](const uint8_t *sb) {
+#pragma unroll
+        for (int sub = 0; sub < KC / 32; ++sub) {
+            const int po = ((sub * 4 + kg) ^ fs) << 4;
+            bf16x8 a[4];
+#pragma unroll
+            for (int ab = 0; ab < 4; ++ab)
+                a[ab] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + arow + ab * 16 * ROWB + po));
+#pragma unroll
+            for (int g = 0; g < NBW; ++g) {
+                const int o = brow + g * 16 * ROWB + po;
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + p * EP * ROWB + o));
+#pragma unroll
+                    for (int ab = 0; ab < 4; ++ab)
+                        acc[ab][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab], b, acc[ab][g], 0, 0, 0);
+                }
             }
         }
     };
 
-    f32x4 acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int boff = col * RM_STRIDE + 8 * kg;
-    auto compute = [&](const RStage<WPER> &st) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const bf16x8 a = as_bf16x8(st.xin ? st.x : z);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int o = nb * 16 * RM_STRIDE + boff;
-            const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sW[0][o]));
-            const bf16x8 bm = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sW[1][o]));
-            const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sW[2][o]));
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[nb], 0, 0, 0);
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, acc[nb], 0, 0, 0);
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[nb], 0, 0, 0);
-        }
-    };
-
-    // ring of DEPTH register stages; chunk c lives in stage c % DEPTH
-    const int nchunk = (d + RM_KC - 1) / RM_KC;
-    RStage<WPER> st[DEPTH];
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load(st[s], s < nchunk ? s : nchunk - 1);
-    auto step = [&](RStage<WPER> &cur, int c) {
-        lds_barrier();                       // the previous chunk's MFMAs are done with sW
-        store_w(cur, c);
-        lds_barrier();
-        compute(cur);
-        const int cn = c + DEPTH;
-        load(cur, cn < nchunk ? cn : nchunk - 1);
-    };
-    int c0 = 0;
-    for (; c0 + DEPTH <= nchunk; c0 += DEPTH) {      // whole rounds: no exits inside
-#pragma unroll
-        for (int s = 0; s < DEPTH; ++s) step(st[s], c0 + s);
+    // ---- the ring (same scheme as the expert GEMM): chunk kt lives in stage
+    // kt % S; a step waits for its own DMA, passes an LDS-only barrier,
+    // refills the stage of kt - 1 with kt + S - 1 and runs its MFMAs
+    issue(st0, 0);
+    if (S > 2 && nk > 1) issue(st1, 1);
+    if (S > 3 && nk > 2) issue(st2, 2);
+    int kt = 0;
+#define MOE_RSTEP(CUR, NXT)                                                     \
+    if (kt < nk) {                                                              \
+        if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
+        else wait_vm_lgkm0<0>();                                                \
+        if (KTAIL && kt == nk - 1) clear_tail(CUR);                             \
+        lds_barrier();                                                          \
+        if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
+        compute(CUR);                                                           \
+        ++kt;                                                                   \
     }
+    while (kt < nk) {
+        if constexpr (S == 2) {
+            MOE_RSTEP(st0, st1)
+            MOE_RSTEP(st1, st0)
+        } else if constexpr (S == 3) {
+            MOE_RSTEP(st0, st2)
+            MOE_RSTEP(st1, st0)
+            MOE_RSTEP(st2, st1)
+        } else {
+            MOE_RSTEP(st0, st3)
+            MOE_RSTEP(st1, st0)
+            MOE_RSTEP(st2, st1)
+            MOE_RSTEP(st3, st2)
+        }
+    }
+#undef MOE_RSTEP
+
+    // ---- logits to LDS (token rows 0..31 in st0, 32..63 in st1; the ring is
+    // drained), then each wave takes 16 tokens across all experts
+    constexpr int ZS = EP + 4;                           // fp32 row stride
+    static_assert(32 * ZS * 4 <= STAGE, "logit rows fit a stage buffer");
+    lds_barrier();
 #pragma unroll
-    for (int s = 0; s < DEPTH - 1; ++s)              // the last nchunk % DEPTH chunks
-        if (c0 + s < nchunk) step(st[s], c0 + s);
+    for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+        for (int g = 0; g < NBW; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = ab * 16 + 4 * kg + i;
+                float *zr = reinterpret_cast<float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
+                zr[(wave * NBW + g) * 16 + col] = acc[ab][g][i];
+            }
+    lds_barrier();
 
     // ---- epilogue: lane holds logits of tokens tw + 4*kg + i, experts nb*16 + col
     float bias[NB];
@@ -192,16 +256,17 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         const bool tok_ok = t < T;
         float v[NB];
         float mx = -INFINITY;
+        const int tok = wave * RM_TOK_WAVE + 4 * kg + i;
+        const float *zr = reinterpret_cast<const float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = nb * 16 + col;
-            float z = acc[nb][i] + bias[nb];
+            float z = zr[n] + bias[nb];
             if (z != z) z = -INFINITY;          // NaN ranks as -inf: indices stay in range
             v[nb] = z;
             if (n < E) mx = fmaxf(mx, z);
         }
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+        mx = row16_max(mx);
         float ex[NB];
         float s = 0.f;
 #pragma unroll
@@ -210,24 +275,27 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             ex[nb] = (n < E) ? expf(v[nb] - mx) : 0.f;
             s += ex[nb];
         }
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+        s = row16_sum(s);
         if (tok_ok) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) psum[nb] += ex[nb] / s;
         }
 
         // top-k by k rounds of a 16-lane argmax over the not-yet-chosen experts
+        // (KSEL = k when it is 1 or 2, so that the common cases stay small
+        // code; 0 = any k up to MAXK)
+        constexpr int KMAX = KSEL ? KSEL : MAXK;
+        const int kk = KSEL ? KSEL : k;
         uint32_t excl[(NB + 31) / 32];
 #pragma unroll
         for (int q = 0; q < (NB + 31) / 32; ++q) excl[q] = 0u;
-        float vsel[MAXK];
-        int isel[MAXK];
+        float vsel[KMAX];
+        int isel[KMAX];
 #pragma unroll
-        for (int j = 0; j < MAXK; ++j) {
+        for (int j = 0; j < KMAX; ++j) {
             vsel[j] = -INFINITY;
             isel[j] = 0;
-            if (j < k) {
+            if (j < kk) {
                 Cand c{-INFINITY, 0x7fffffff, 0};
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -238,11 +306,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                         if (cand_better(o, c)) c = o;
                     }
                 }
-#pragma unroll
-                for (int m = 8; m >= 1; m >>= 1) {
-                    const Cand o = cand_shfl_xor(c, m);
-                    if (cand_better(o, c)) c = o;
-                }
+                c = row16_best(c);
                 if ((c.i & 15) == col) {
                     const int nbw = c.i >> 4;
                     excl[nbw >> 5] |= 1u << (nbw & 31);
@@ -252,21 +316,21 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             }
         }
         if (tok_ok && col == 0) {
-            if (k == 1) {
+            if (kk == 1) {
                 out_idx[t] = isel[0];
                 out_gate[t] = 1.0f / s;        // p_{i*} = exp(0) / sum
                 atomicAdd(&sCnt[isel[0]], 1);
             } else {
-                float ek[MAXK];
+                float ek[KMAX];
                 float sk = 0.f;
 #pragma unroll
-                for (int j = 0; j < MAXK; ++j) {
-                    ek[j] = (j < k) ? expf(vsel[j] - vsel[0]) : 0.f;
+                for (int j = 0; j < KMAX; ++j) {
+                    ek[j] = (j < kk) ? expf(vsel[j] - vsel[0]) : 0.f;
                     sk += ek[j];
                 }
 #pragma unroll
-                for (int j = 0; j < MAXK; ++j) {
-                    if (j < k) {
+                for (int j = 0; j < KMAX; ++j) {
+                    if (j < kk) {
                         out_idx[t * k + j] = isel[j];
                         out_gate[t * k + j] = ek[j] / sk;
                         atomicAdd(&sCnt[isel[j]], 1);
@@ -440,24 +504,37 @@ int router_blocks(int64_t T, int dtype_bf16, int E) {
 
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
-                         float *part_prob, int32_t *part_cnt, hipStream_t s) {
+                         float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s) {
     const int nblk = router_blocks(T, dtype_bf16, E);
     if (nblk == 0) return hipSuccess;
     if (use_mfma(dtype_bf16, E)) {
+        const int64_t n = (int64_t)E * d;
+        const int sg = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+        hipLaunchKernelGGL(router_split_kernel, dim3(sg), dim3(256), 0, s, W_r, n, w3);
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
         const int nb = (E + 15) / 16;
-#define MOE_ROUTER_CASE(NBV)                                                                  \
-    if (nb <= NBV) {                                                                          \
-        hipLaunchKernelGGL(router_mfma_kernel<NBV>, dim3(nblk), dim3(256), 0, s, xb, W_r, b_r, \
-                           T, d, E, k, expert_idx, gate, part_prob, part_cnt);                \
-        return hipGetLastError();                                                             \
+#define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV)                                                \
+    hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV>), dim3(nblk), dim3(256), 0, s,  \
+                       xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt)
+#define MOE_ROUTER_K(NBV, KCV, TAILV)                                                          \
+    do {                                                                                       \
+        if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1);                                     \
+        else if (k == 2) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 2);                                \
+        else MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 0);                                            \
+    } while (0)
+#define MOE_ROUTER_CASE(NBV, KCV)                                                              \
+    if (nb <= NBV) {                                                                           \
+        static_assert(rgeo_ok<NBV, KCV>(), "router ring");                                     \
+        if (d % KCV == 0) MOE_ROUTER_K(NBV, KCV, false);                                       \
+        else MOE_ROUTER_K(NBV, KCV, true);                                                     \
+        return hipGetLastError();                                                              \
     }
-        MOE_ROUTER_CASE(1)
-        MOE_ROUTER_CASE(2)
-        MOE_ROUTER_CASE(4)
-        MOE_ROUTER_CASE(8)
-        MOE_ROUTER_CASE(16)
+        MOE_ROUTER_CASE(4, 64)
+        MOE_ROUTER_CASE(8, 64)
+        MOE_ROUTER_CASE(16, 32)
 #undef MOE_ROUTER_CASE
+#undef MOE_ROUTER_K
+#undef MOE_ROUTER_LAUNCH
         return hipErrorInvalidValue;
     }
     const size_t shm = (size_t)(RG_TOK + 1) * E * sizeof(float);

@@ -74,7 +74,9 @@ def test_workspace_sizes():
     assert L.LIB.moe_workspace_bytes(16384, 768, 3072, 64, 1, 320, 7, 0) == L.SIZE_MAX
     assert L.LIB.moe_workspace_bytes(16384, 770, 3072, 64, 1, 320, 1, 0) == L.SIZE_MAX
     assert L.LIB.moe_workspace_bytes(16, 768, 3072, 64, 1, 17, 1, 0) == L.SIZE_MAX   # C > T
-    assert L.LIB.moe_router_workspace_bytes(100, 2000, 1) == L.SIZE_MAX
+    assert L.LIB.moe_router_workspace_bytes(100, 64, 2000, 1) == L.SIZE_MAX
+    assert L.LIB.moe_router_workspace_bytes(100, 66, 8, 1) == L.SIZE_MAX      # d not a multiple of 8
+    assert L.LIB.moe_router_workspace_bytes(100, 64, 8, 1) >= 3 * 8 * 64 * 2
     lay = L.WsLayout()
     assert L.LIB.moe_forward_workspace_layout(16384, 768, 3072, 64, 1, 320, 1, 0, lay) == 0
     assert lay.total == n
