@@ -90,6 +90,12 @@ __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
     return fmaxf(v, dpp_f<DPP_MIRROR>(v));
 }
+__device__ __forceinline__ int row16_min(int v) {
+    v = min(v, dpp_i<DPP_XOR1>(v));
+    v = min(v, dpp_i<DPP_XOR2>(v));
+    v = min(v, dpp_i<DPP_HALF_MIRROR>(v));
+    return min(v, dpp_i<DPP_MIRROR>(v));
+}
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<DPP_XOR1>(v);
     v += dpp_f<DPP_XOR2>(v);
@@ -103,23 +109,6 @@ __device__ __forceinline__ Cand cand_shfl_xor(const Cand &c, int m) {
     o.i = __shfl_xor(c.i, m);
     o.ok = __shfl_xor(c.ok, m);
     return o;
-}
-
-template <int CTRL>
-__device__ __forceinline__ Cand cand_dpp(const Cand &c) {
-    return Cand{dpp_f<CTRL>(c.v), dpp_i<CTRL>(c.i), dpp_i<CTRL>(c.ok)};
-}
-// the best candidate of each row of 16 lanes, in every lane of the row
-__device__ __forceinline__ Cand row16_best(Cand c) {
-    Cand o = cand_dpp<DPP_XOR1>(c);
-    if (cand_better(o, c)) c = o;
-    o = cand_dpp<DPP_XOR2>(c);
-    if (cand_better(o, c)) c = o;
-    o = cand_dpp<DPP_HALF_MIRROR>(c);
-    if (cand_better(o, c)) c = o;
-    o = cand_dpp<DPP_MIRROR>(c);
-    if (cand_better(o, c)) c = o;
-    return c;
 }
 
 }  // namespace moe

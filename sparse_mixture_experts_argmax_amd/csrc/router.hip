@@ -267,28 +267,34 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             if (n < E) mx = fmaxf(mx, z);
         }
         mx = row16_max(mx);
+        // exp through the hardware exp2 (about 1 ulp): these terms only feed
+        // the sum s and the per-expert probability sums, whose bounds are far
+        // looser; the gate of the chosen expert is 1 / s with s from them
+        const float mxl = mx * 1.44269504088896341f;
         float ex[NB];
         float s = 0.f;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = nb * 16 + col;
-            ex[nb] = (n < E) ? expf(v[nb] - mx) : 0.f;
+            ex[nb] = (n < E) ? __builtin_amdgcn_exp2f(fmaf(v[nb], 1.44269504088896341f, -mxl)) : 0.f;
             s += ex[nb];
         }
         s = row16_sum(s);
         if (tok_ok) {
+            const float inv = 1.0f / s;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) psum[nb] += ex[nb] / s;
+            for (int nb = 0; nb < NB; ++nb) psum[nb] = fmaf(ex[nb], inv, psum[nb]);
         }
 
-        // top-k by k rounds of a 16-lane argmax over the not-yet-chosen experts
-        // (KSEL = k when it is 1 or 2, so that the common cases stay small
-        // code; 0 = any k up to MAXK)
+        // top-k by k rounds over the not-yet-chosen experts: the round's
+        // largest logit (a 16-lane max), then the lowest expert index holding
+        // it (a 16-lane min), so ties go to the lower index.  Round 0 reuses
+        // the softmax max.  (KSEL = k when it is 1 or 2, so that the common
+        // cases stay small code; 0 = any k up to MAXK.)
         constexpr int KMAX = KSEL ? KSEL : MAXK;
         const int kk = KSEL ? KSEL : k;
-        uint32_t excl[(NB + 31) / 32];
-#pragma unroll
-        for (int q = 0; q < (NB + 31) / 32; ++q) excl[q] = 0u;
+        uint32_t excl = 0u;                      // bit nb: this lane's expert nb*16+col is taken
+        static_assert(NB <= 32, "exclusion mask");
         float vsel[KMAX];
         int isel[KMAX];
 #pragma unroll
@@ -296,23 +302,25 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
             vsel[j] = -INFINITY;
             isel[j] = 0;
             if (j < kk) {
-                Cand c{-INFINITY, 0x7fffffff, 0};
+                float m = mx;
+                if (j > 0) {
+                    m = -INFINITY;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        if (nb * 16 + col < E && !((excl >> nb) & 1u)) m = fmaxf(m, v[nb]);
+                    m = row16_max(m);
+                }
+                int best = 0x7fffffff;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const int n = nb * 16 + col;
-                    const bool taken = (excl[nb >> 5] >> (nb & 31)) & 1u;
-                    if (n < E && !taken) {
-                        const Cand o{v[nb], n, 1};
-                        if (cand_better(o, c)) c = o;
-                    }
+                    const bool cand = n < E && !((excl >> nb) & 1u) && v[nb] == m;
+                    best = cand ? min(best, n) : best;
                 }
-                c = row16_best(c);
-                if ((c.i & 15) == col) {
-                    const int nbw = c.i >> 4;
-                    excl[nbw >> 5] |= 1u << (nbw & 31);
-                }
-                vsel[j] = c.v;
-                isel[j] = c.i;
+                best = row16_min(best);
+                if ((best & 15) == col) excl |= 1u << (best >> 4);
+                vsel[j] = m;
+                isel[j] = best;
             }
         }
         if (tok_ok && col == 0) {
