@@ -44,6 +44,18 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// Workgroup barrier for LDS rings filled by DMA.  The caller has already
+// waited (wait_vm_lgkm0) for its own LDS accesses and for the DMA of the stage
+// it needs; the barrier then makes every wave's part visible.  No fence: an
+// LDS fence would also wait for the DMA of the newer stages (the compiler
+// counts LDS DMA as LDS writes), draining the ring.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that orders LDS accesses only (waits lgkmcnt, not vmcnt):
 // global loads issued ahead for later steps stay in flight across it, which
 // __syncthreads (a full fence) would drain.

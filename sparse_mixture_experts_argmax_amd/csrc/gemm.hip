@@ -293,16 +293,21 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     // own DMA (the S - 2 newer stages stay in flight), passes one barrier (all
     // waves have landed their part of kt and finished reading kt - 1), refills
     // the stage of kt - 1 with kt + S - 1, then runs the MFMAs of kt.
+    // prologue: K tiles 0 .. S - 2, clamped to the last one when there are
+    // fewer (the duplicate loads are never read).  Unconditional on purpose:
+    // a conditional DMA here makes the compiler give up tracking which stage
+    // a pending DMA writes, and then it drains the whole ring before every
+    // fragment read.
     issue(st0, 0);
-    if (S > 2 && nk > 1) issue(st1, 1);
-    if (S > 3 && nk > 2) issue(st2, 2);
+    if (S > 2) issue(st1, nk > 1 ? 1 : nk - 1);
+    if (S > 3) issue(st2, nk > 2 ? 2 : nk - 1);
     int kt = 0;
     // steady state: every step refills a stage, so the wait count is fixed
     // and the loop body has no branch
 #define MOE_STEP(CUR, NXT)                                                      \
     {                                                                           \
         wait_vm_lgkm0<NEWER>();                                                 \
-        lds_barrier();                                                          \
+        ring_barrier();                                                         \
         rd(CUR, 0, 0);                                                          \
         issue(NXT, kt + S - 1);                                                 \
         compute(CUR);                                                           \
@@ -329,8 +334,11 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     if (kt < nk) {                                                              \
         if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
         else wait_vm_lgkm0<0>();                                                \
-        if (KTAIL && kt == nk - 1) clear_tail(CUR);                             \
-        lds_barrier();                                                          \
+        if (KTAIL && kt == nk - 1) {                                            \
+            clear_tail(CUR);                                                    \
+            wait_vm_lgkm0<63>();          /* the zeros are in LDS */            \
+        }                                                                       \
+        ring_barrier();                                                         \
         rd(CUR, 0, 0);                                                          \
         if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
         __builtin_amdgcn_sched_barrier(0);                                      \
@@ -530,17 +538,15 @@ int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_bound) {
 int gemm_bm(int dtype_bf16, int64_t C) { return dtype_bf16 ? (C >= 512 ? 256 : 128) : FBM; }
 
 // bf16 tile shapes: W = 256 output columns, N = 128, G = gated (128 columns
-// of each weight); the suffix is BM.  The 128-row shapes (and the narrow
-// 256-row one) use 32-wide K stages sized for two blocks per CU; the wide
-// 256-row shapes keep 64-wide K stages, one block per CU (half the LDS
-// bytes per MFMA of a 128-row tile, and enough MFMA work per step to hide
-// the DMA).  Each ring fills 128-144 KB of LDS per CU.
+// of each weight); the suffix is BM.  64-wide K stages, one block per CU and
+// 128-144 KB rings (two or three stages ahead of the MFMAs), except the
+// narrow 128-row shape, which runs two blocks per CU on 32-wide K stages.
 using TileW256 = Tile<256, 256, 2, 64, 1>;
-using TileN256 = Tile<256, 128, 3, 32, 2>;
+using TileN256 = Tile<256, 128, 3, 64, 1>;
 using TileG256 = Tile<256, 128, 2, 64, 1>;
-using TileW128 = Tile<128, 256, 3, 32, 2>;
+using TileW128 = Tile<128, 256, 3, 64, 1>;
 using TileN128 = Tile<128, 128, 4, 32, 2>;
-using TileG128 = Tile<128, 128, 3, 32, 2>;
+using TileG128 = Tile<128, 128, 3, 64, 1>;
 
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s) {

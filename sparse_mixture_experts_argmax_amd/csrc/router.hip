@@ -191,34 +191,70 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // ---- the ring (same scheme as the expert GEMM): chunk kt lives in stage
     // kt % S; a step waits for its own DMA, passes an LDS-only barrier,
     // refills the stage of kt - 1 with kt + S - 1 and runs its MFMAs
+    // prologue: K tiles 0 .. S - 2, clamped to the last one when there are
+    // fewer (the duplicate loads are never read).  Unconditional on purpose:
+    // a conditional DMA here makes the compiler give up tracking which stage
+    // a pending DMA writes, and then it drains the whole ring before every
+    // fragment read.
     issue(st0, 0);
-    if (S > 2 && nk > 1) issue(st1, 1);
-    if (S > 3 && nk > 2) issue(st2, 2);
+    if (S > 2) issue(st1, nk > 1 ? 1 : nk - 1);
+    if (S > 3) issue(st2, nk > 2 ? 2 : nk - 1);
     int kt = 0;
+    // steady state: every step refills a stage (no conditional DMA, which
+    // would make the compiler drain the ring before every fragment read)
+#define MOE_RSTEP_S(CUR, NXT)                                                   \
+    {                                                                           \
+        wait_vm_lgkm0<NEWER>();                                                 \
+        ring_barrier();                                                         \
+        issue(NXT, kt + S - 1);                                                 \
+        compute(CUR);                                                           \
+        ++kt;                                                                   \
+    }
+    for (; kt + 2 * S - 1 <= nk;) {
+        if constexpr (S == 2) {
+            MOE_RSTEP_S(st0, st1)
+            MOE_RSTEP_S(st1, st0)
+        } else if constexpr (S == 3) {
+            MOE_RSTEP_S(st0, st2)
+            MOE_RSTEP_S(st1, st0)
+            MOE_RSTEP_S(st2, st1)
+        } else {
+            MOE_RSTEP_S(st0, st3)
+            MOE_RSTEP_S(st1, st0)
+            MOE_RSTEP_S(st2, st1)
+            MOE_RSTEP_S(st3, st2)
+        }
+    }
+#undef MOE_RSTEP_S
+    // drain: at most 2 S - 2 steps, refilling while chunks remain; kt % S == 0 here
 #define MOE_RSTEP(CUR, NXT)                                                     \
     if (kt < nk) {                                                              \
         if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
         else wait_vm_lgkm0<0>();                                                \
-        if (KTAIL && kt == nk - 1) clear_tail(CUR);                             \
-        lds_barrier();                                                          \
+        if (KTAIL && kt == nk - 1) {                                            \
+            clear_tail(CUR);                                                    \
+            wait_vm_lgkm0<63>();          /* the zeros are in LDS */            \
+        }                                                                       \
+        ring_barrier();                                                         \
         if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
         compute(CUR);                                                           \
         ++kt;                                                                   \
     }
-    while (kt < nk) {
-        if constexpr (S == 2) {
-            MOE_RSTEP(st0, st1)
-            MOE_RSTEP(st1, st0)
-        } else if constexpr (S == 3) {
-            MOE_RSTEP(st0, st2)
-            MOE_RSTEP(st1, st0)
-            MOE_RSTEP(st2, st1)
-        } else {
-            MOE_RSTEP(st0, st3)
-            MOE_RSTEP(st1, st0)
-            MOE_RSTEP(st2, st1)
-            MOE_RSTEP(st3, st2)
-        }
+    if constexpr (S == 2) {
+        MOE_RSTEP(st0, st1)
+        MOE_RSTEP(st1, st0)
+    } else if constexpr (S == 3) {
+        MOE_RSTEP(st0, st2)
+        MOE_RSTEP(st1, st0)
+        MOE_RSTEP(st2, st1)
+        MOE_RSTEP(st0, st2)
+    } else {
+        MOE_RSTEP(st0, st3)
+        MOE_RSTEP(st1, st0)
+        MOE_RSTEP(st2, st1)
+        MOE_RSTEP(st3, st2)
+        MOE_RSTEP(st0, st3)
+        MOE_RSTEP(st1, st0)
     }
 #undef MOE_RSTEP
 
