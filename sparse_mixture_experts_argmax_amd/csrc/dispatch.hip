@@ -27,9 +27,11 @@ namespace {
 
 __global__ __launch_bounds__(DISPATCH_TOK_BLOCK) void slot_rank_kernel(
     const int32_t *__restrict__ expert_idx, int64_t T, int E, int k, int nbits,
-    int32_t *__restrict__ rank, int32_t *__restrict__ hist) {
+    int32_t *__restrict__ rank, int32_t *__restrict__ hist, unsigned *__restrict__ done) {
     extern __shared__ int sc[];                     // [4 waves][E]
     const int tid = threadIdx.x;
+    // the completion counter of the scan that follows starts at zero
+    if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *done = 0u;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int j = blockIdx.y;
@@ -65,25 +67,85 @@ __global__ __launch_bounds__(DISPATCH_TOK_BLOCK) void slot_rank_kernel(
 }
 
 // One wave per expert: exclusive scan over (rank, block), in place.
+// Optionally (the fused forward) also:
+//  * the router's per-expert totals, in the same order and precision as its
+//    own reduction, so that both give the same bits;
+//  * the expert GEMMs' tile map (tile_map[e] = sum over e' < e of
+//    ceil(expert_count[e'] / bm)), built by whichever block finishes last
+//    (a completion counter that slot_rank zeroed).
 __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hist, int L, int E,
-                                                        int64_t C, int32_t *__restrict__ expert_count) {
+                                                        int64_t C, int32_t *__restrict__ expert_count,
+                                                        const float *__restrict__ part_prob, int nblk_r,
+                                                        float *__restrict__ prob_sum,
+                                                        int32_t *__restrict__ route_count,
+                                                        int32_t *__restrict__ tile_map, int bm,
+                                                        unsigned *__restrict__ done) {
+    __shared__ int s_last;
+    __shared__ int s_wsum[4];
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
-    int32_t *h = hist + (int64_t)e * L;
-    int run = 0;
-    for (int b0 = 0; b0 < L; b0 += 64) {
-        const int b = b0 + lane;
-        const int v = (b < L) ? h[b] : 0;
-        int inc = v;
-        for (int m = 1; m < 64; m <<= 1) {
-            const int u = __shfl_up(inc, m);
-            if (lane >= m) inc += u;
+    const int wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    if (e < E) {
+        int32_t *h = hist + (int64_t)e * L;
+        int run = 0;
+        for (int b0 = 0; b0 < L; b0 += 64) {
+            const int b = b0 + lane;
+            const int v = (b < L) ? h[b] : 0;
+            int inc = v;
+            for (int m = 1; m < 64; m <<= 1) {
+                const int u = __shfl_up(inc, m);
+                if (lane >= m) inc += u;
+            }
+            if (b < L) h[b] = run + inc - v;
+            run += __shfl(inc, 63);
         }
-        if (b < L) h[b] = run + inc - v;
-        run += __shfl(inc, 63);
+        if (lane == 0) expert_count[e] = (int32_t)((int64_t)run < C ? (int64_t)run : C);
+        // run = number of choices of expert e before capacity
+        if (part_prob != nullptr) {
+            double sp = 0.0;
+            for (int b = lane; b < nblk_r; b += 64) sp += (double)part_prob[(int64_t)b * E + e];
+            for (int m = 32; m >= 1; m >>= 1) sp += __shfl_xor(sp, m);
+            if (lane == 0) {
+                prob_sum[e] = (float)sp;
+                route_count[e] = run;
+            }
+        }
     }
-    if (lane == 0) expert_count[e] = (int32_t)((int64_t)run < C ? (int64_t)run : C);
+    if (tile_map == nullptr) return;                 // uniform over the grid
+    __threadfence();                                 // this block's counts are visible ...
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(done, 1u) == gridDim.x - 1;   // ... before it counts
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    // thread t owns experts 4t .. 4t + 3 (E <= 1024): a wave scan, then the
+    // wave totals; counts are read from L2 (other blocks wrote them)
+    const int t = threadIdx.x;
+    int c[4];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ee = 4 * t + q;
+        const int n = ee < E ? __hip_atomic_load(expert_count + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        c[q] = (n + bm - 1) / bm;
+        local += c[q];
+    }
+    int inc = local;
+    for (int m = 1; m < 64; m <<= 1) {
+        const int u = __shfl_up(inc, m);
+        if (lane >= m) inc += u;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int run = inc - local;
+    for (int i = 0; i < wave; ++i) run += s_wsum[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ee = 4 * t + q;
+        if (ee < E) tile_map[ee] = run;
+        run += c[q];
+    }
+    if (E - 1 >= 4 * t && E - 1 < 4 * t + 4) tile_map[E] = run;
 }
 
 // One wave per (token, rank) choice; lanes move 16-byte pieces of the row.
@@ -126,18 +188,21 @@ int bits_for(int E) {
 }  // namespace
 
 hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, int32_t *rank,
-                            int32_t *hist, hipStream_t s) {
+                            int32_t *hist, unsigned *done, hipStream_t s) {
     const int nblk = dispatch_blocks(T);
     if (nblk == 0) return hipSuccess;
     hipLaunchKernelGGL(slot_rank_kernel, dim3(nblk, k), dim3(DISPATCH_TOK_BLOCK),
-                       (size_t)4 * E * sizeof(int), s, expert_idx, T, E, k, bits_for(E), rank, hist);
+                       (size_t)4 * E * sizeof(int), s, expert_idx, T, E, k, bits_for(E), rank, hist,
+                       done);
     return hipGetLastError();
 }
 
 hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
-                            int32_t *expert_count, hipStream_t s) {
+                            int32_t *expert_count, const float *part_prob, int nblk_r,
+                            float *prob_sum, int32_t *route_count, int32_t *tile_map, int bm,
+                            unsigned *done, hipStream_t s) {
     hipLaunchKernelGGL(slot_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, s, hist, nblk * k, E, C,
-                       expert_count);
+                       expert_count, part_prob, nblk_r, prob_sum, route_count, tile_map, bm, done);
     return hipGetLastError();
 }
 

@@ -7,23 +7,25 @@
 // [CMU-L16] section 5 / [CS25-L5] "Switch Layer": experts run as batched
 // matrix products over their slot lists (a dedicated grouped-GEMM kernel).
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulation):
-//   * 256 threads = 4 waves in a 2x2 grid; block tile 128 x 128 x 64, each
-//     wave 64 x 64 = 4 x 4 MFMA tiles (two 16x16 accumulators sets for SwiGLU).
+// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   * 256 threads = 4 waves in a 2x2 grid; block tiles of 128 or 256 rows by
+//     128 or 256 columns (see Tile), each wave owning a quarter.
 //   * A and B tiles are K-contiguous in HBM (x rows, nn.Linear-style weight
-//     rows), so both are staged through LDS the same way: 16-byte global
-//     loads into registers one K step ahead, stores into the other half of a
-//     double-buffered, row-padded LDS tile (conflict-free 16-byte reads).
+//     rows), so both are staged the same way: 16-byte LDS DMA
+//     (global_load_lds) into a ring of LDS stages two or three K tiles ahead
+//     of the MFMAs, 16-byte pieces of each LDS row XOR-swizzled by row
+//     (conflict-free fragment reads, no padding).
 //   * Only real row tiles are launched work: tile_map holds the prefix sums
-//     of ceil(count[e] / 128), read on the device, so an expert with few
-//     rows costs few tiles and an empty expert none.
+//     of ceil(count[e] / BM), built on the device, so an expert with few rows
+//     costs few tiles and an empty expert none.
 //   * Tile order is expert-major, then column tile, then row tile, so the
 //     row tiles that share a weight tile run next to each other; the block
 //     index is remapped so that each XCD (blocks are dealt to the 8 XCDs
 //     round-robin) gets one contiguous range of that order and its own L2
 //     keeps the weight and activation tiles it reuses.
-//   * The epilogue adds the bias, applies the activation, rounds to bf16 and
-//     stages the tile in LDS so that rows go out as coalesced 16-byte stores.
+//   * The epilogue adds the bias, applies the activation and rounds to bf16;
+//     the tile goes out through LDS as coalesced 16-byte row stores when it
+//     fits a stage buffer, else straight from registers.
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 x 16 tiles).
 #include "common.h"
 #include "launch.h"

@@ -21,10 +21,18 @@ hipError_t launch_router_reduce(const float *part_prob, const int32_t *part_cnt,
 // ---- dispatch ---------------------------------------------------------
 constexpr int DISPATCH_TOK_BLOCK = 256;
 inline int dispatch_blocks(int64_t T) { return (int)((T + DISPATCH_TOK_BLOCK - 1) / DISPATCH_TOK_BLOCK); }
+// done (may be null): zeroed here for the completion counter of the scan.
 hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, int32_t *rank,
-                            int32_t *hist, hipStream_t s);
+                            int32_t *hist, unsigned *done, hipStream_t s);
+// part_prob (nblk_r router partial rows) may be null; when given, the scan also
+// writes the router's prob_sum and route_count (what launch_router_reduce
+// would, bit for bit).  tile_map may be null; when given, the last block
+// also writes the GEMM tile map for row tiles of bm (what launch_tile_map
+// would), using the completion counter done that launch_slot_rank zeroed.
 hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
-                            int32_t *expert_count, hipStream_t s);
+                            int32_t *expert_count, const float *part_prob, int nblk_r,
+                            float *prob_sum, int32_t *route_count, int32_t *tile_map, int bm,
+                            unsigned *done, hipStream_t s);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,

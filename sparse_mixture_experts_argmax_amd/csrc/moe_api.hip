@@ -37,13 +37,14 @@ RouterWs router_ws(int64_t T, int d, int E) {
 }
 
 struct DispatchWs {
-    size_t rank, hist, total;
+    size_t rank, hist, done, total;
 };
 DispatchWs dispatch_ws(int64_t T, int E, int k) {
     DispatchWs w;
     w.rank = 0;
     w.hist = up((size_t)T * k * 4);
-    w.total = w.hist + up((size_t)E * k * moe::dispatch_blocks(T) * 4);
+    w.done = w.hist + up((size_t)E * k * moe::dispatch_blocks(T) * 4);
+    w.total = w.done + up(4);
     return w;
 }
 
@@ -127,10 +128,12 @@ moe_status check_ffn_args(moe_dtype dt, moe_act act, const void *W1, const void 
     return MOE_OK;
 }
 
+// reduce = false leaves prob_sum / route_count to the dispatch scan (the
+// fused forward), which reads the router's partials from ws.
 moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
                       float *gate, float *prob_sum, int32_t *route_count, char *ws,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool reduce = true) {
     const RouterWs w = router_ws(T, d, E);
     float *part_prob = reinterpret_cast<float *>(ws + w.part_prob);
     int32_t *part_cnt = reinterpret_cast<int32_t *>(ws + w.part_cnt);
@@ -138,20 +141,28 @@ moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float
     const int bf16 = dt == MOE_BF16;
     MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
                                part_cnt, w3, stream));
-    MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
-                                      prob_sum, route_count, stream));
+    if (reduce)
+        MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
+                                          prob_sum, route_count, stream));
     return MOE_OK;
 }
 
+// part_prob != null (the fused forward): the scan also finishes the router's
+// prob_sum / route_count from its nblk_r partial rows; tile_map != null: it
+// also writes the GEMM tile map for row tiles of bm.
 moe_status run_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, int64_t T,
                         int32_t d, int32_t E, int32_t k, int64_t C, int32_t *slot,
                         uint8_t *drop_mask, int32_t *expert_count, void *xbuf, char *ws,
-                        hipStream_t stream) {
+                        hipStream_t stream, const float *part_prob = nullptr, int nblk_r = 0,
+                        float *prob_sum = nullptr, int32_t *route_count = nullptr,
+                        int32_t *tile_map = nullptr, int bm = 0) {
     const DispatchWs w = dispatch_ws(T, E, k);
     int32_t *rank = reinterpret_cast<int32_t *>(ws + w.rank);
     int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
-    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, stream));
-    MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, C, expert_count, stream));
+    unsigned *done = reinterpret_cast<unsigned *>(ws + w.done);
+    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, tile_map ? done : nullptr, stream));
+    MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, C, expert_count, part_prob,
+                                  nblk_r, prob_sum, route_count, tile_map, bm, done, stream));
     MOE_HIP(moe::launch_permute(x, (int)esize(dt), expert_idx, rank, hist, T, d, E, k, C, slot,
                                 drop_mask, xbuf, stream));
     return MOE_OK;
@@ -353,12 +364,18 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     auto mark = [&](int i) -> bool { return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess; };
 
     if (!mark(0)) return MOE_ERR_HIP;
+    // the router's per-expert totals are finished by the dispatch scan (one
+    // launch fewer); with T = 0 there is no dispatch work, so the router does it
+    const bool fuse_reduce = T > 0;
     MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
-                         base + w.router, stream));
+                         base + w.router, stream, !fuse_reduce));
     if (!mark(1)) return MOE_ERR_HIP;
     MOE_CHECK(run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
-                           base + w.dispatch, stream));
-    if (C > 0) MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16, C), tile_map, stream));
+                           base + w.dispatch, stream,
+                           fuse_reduce ? reinterpret_cast<const float *>(base + w.router + w.r.part_prob)
+                                       : nullptr,
+                           moe::router_blocks(T, bf16, E), prob_sum, route_count,
+                           T > 0 && C > 0 ? tile_map : nullptr, moe::gemm_bm(bf16, C)));
     if (!mark(2)) return MOE_ERR_HIP;
     if (C > 0) {
         const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
