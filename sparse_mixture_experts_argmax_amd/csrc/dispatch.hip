@@ -14,6 +14,9 @@
 //                 earlier waves) and the block's per-expert histogram.
 //   slot_scan  -- per expert, an exclusive scan of the histograms in
 //                 (rank, block) order: the slots taken before each block.
+//                 In the fused forward it also sums the router's per-block
+//                 partials (probability sums, choice counts), and its last
+//                 block builds the GEMM tile map from the kept counts.
 //   permute    -- slot = scan + in-block position; slots >= C drop; kept
 //                 rows are copied x[t] -> xbuf[e, slot] with 16-byte moves.
 // [SW-GLaM] "All-to-All": the data-sharded -> expert-sharded relayout, done

@@ -13,10 +13,12 @@
 //    round-to-nearest bf16 of what the previous parts left, so the sum
 //    reproduces all 24 significand bits).  bf16 x bf16 products are exact
 //    in fp32, so three bf16 MFMAs with fp32 accumulation give an fp32 dot
-//    product without any fp32 vector FMA.  One wave owns 16 tokens and all
-//    experts; the W_r chunk is split once per block into LDS and shared by
-//    the four waves.  Row softmax and top-k run on the MFMA output layout
-//    with 16-lane butterflies.
+//    product without any fp32 vector FMA.  router_split makes the three
+//    parts once per call; a block of 64 tokens streams them and its token
+//    rows through a ring of LDS stages filled by 16-byte DMA, and each of
+//    its four waves computes the logits of all 64 tokens for a quarter of
+//    the experts.  The logits go through LDS to one wave per 16 tokens,
+//    where row softmax and top-k use 16-lane DPP row reductions.
 //  * router_generic (fp32 x, or E > 256): fp32 FMA dot products into LDS,
 //    then one wave per token row.
 #include "common.h"
