@@ -370,6 +370,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     // so that rows go out as coalesced 16-byte stores; otherwise each lane
     // stores its four consecutive columns (8 bytes) directly.
     constexpr int P = BN / 8;                            // 16-byte pieces per output row
+    constexpr int PSW = (P & (P - 1)) == 0 ? P - 1 : 7;  // piece swizzle mask (keeps a piece in its row)
     if (STAGED_OUT) lds_barrier();                       // every wave is past its last fragment read
     uint8_t *so = wm ? st1 : st0;
     uint16_t *oe = out + (int64_t)e * C * N;
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
                 pk.x = pack_bf16x2(v[0], v[1]);
                 pk.y = pack_bf16x2(v[2], v[3]);
                 if (STAGED_OUT) {
-                    const int pc = (nl >> 3) ^ (r & (P - 1));
+                    const int pc = (nl >> 3) ^ (r & PSW);
                     *reinterpret_cast<uint2 *>(so + r * (BN * 2) + (pc << 4) + ((nl & 4) << 1)) = pk;
                 } else {
                     const int m = m0 + wm * (BM / 2) + r;
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
             const int R = q / P;                         // tile row
             const int p = q % P;
             const int r = R % (BM / 2);
-            const uint8_t *src = (R < BM / 2 ? st0 : st1) + r * (BN * 2) + ((p ^ (r & (P - 1))) << 4);
+            const uint8_t *src = (R < BM / 2 ? st0 : st1) + r * (BN * 2) + ((p ^ (r & PSW)) << 4);
             const int m = m0 + R;
             const int n = n0 + p * 8;
             if (m < cnt && n < N) st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(src));
@@ -534,18 +535,33 @@ int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_bound) {
 }  // namespace
 
 // Row-tile height of the bf16 path: one BM for both expert GEMMs, so they
-// share one tile map.  256 (half the LDS bytes per MFMA of 128) only when an
-// expert holds at least 512 rows: a 256-row tile over a 257-row expert would
-// spend half its MFMAs on padding.
-int gemm_bm(int dtype_bf16, int64_t C) { return dtype_bf16 ? (C >= 512 ? 256 : 128) : FBM; }
+// share one tile map.  When an expert's capacity fits one tile of 192 or 320
+// rows, that tile covers all of its rows, so every weight tile is streamed
+// once (experts of about 256 rows would otherwise pay a third, mostly empty
+// 128-row tile and read their weights three times).  256 (half the LDS bytes
+// per MFMA of 128) when experts hold at least 512 rows: a 256-row tile over a
+// 257-row expert spends half its MFMAs on padding.  The gated SwiGLU tiles
+// exist for 128 and 256 rows only.
+int gemm_bm(int dtype_bf16, int64_t C, int act) {
+    if (!dtype_bf16) return FBM;
+    if (C >= 512) return 256;
+    if (act != 2 && C > 256 && C <= 320) return 320;
+    if (act != 2 && C > 128 && C <= 192) return 192;
+    return 128;
+}
 
-// bf16 tile shapes: W = 256 output columns, N = 128, G = gated (128 columns
-// of each weight); the suffix is BM.  64-wide K stages, one block per CU and
-// 128-144 KB rings (two or three stages ahead of the MFMAs), except the
-// narrow 128-row shape, which runs two blocks per CU on 32-wide K stages.
+// bf16 tile shapes: W = wide (192 or 256 output columns), N = 128 columns,
+// G = gated (128 columns of each weight); the suffix is BM.  64-wide K
+// stages, one block per CU and 112-144 KB rings (one or two stages ahead of
+// the MFMAs), except the narrow 128-row shape, which runs two blocks per CU
+// on 32-wide K stages.
+using TileW320 = Tile<320, 192, 2, 64, 1>;
+using TileN320 = Tile<320, 128, 2, 64, 1>;
 using TileW256 = Tile<256, 256, 2, 64, 1>;
 using TileN256 = Tile<256, 128, 3, 64, 1>;
 using TileG256 = Tile<256, 128, 2, 64, 1>;
+using TileW192 = Tile<192, 256, 2, 64, 1>;
+using TileN192 = Tile<192, 128, 3, 64, 1>;
 using TileW128 = Tile<128, 256, 3, 64, 1>;
 using TileN128 = Tile<128, 128, 4, 32, 2>;
 using TileG128 = Tile<128, 128, 3, 64, 1>;
@@ -558,16 +574,19 @@ hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *
 
 hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, const void *bias,
                                int dtype_bf16, int act, const int32_t *expert_count,
-                               const int32_t *tile_map, int E, int64_t C, int N, int K,
+                               const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
                                int64_t rows_bound, void *out, hipStream_t s) {
     if (C == 0 || rows_bound == 0) return hipSuccess;
     if (dtype_bf16) {
-        const int bm = gemm_bm(1, C);
+        // the gated tiles exist for 128 and 256 rows only
+        if ((bm != 128 && bm != 192 && bm != 256 && bm != 320) || (act == 2 && bm != 128 && bm != 256))
+            return hipErrorInvalidValue;
         const uint16_t *a = (const uint16_t *)A, *b = (const uint16_t *)B, *b3 = (const uint16_t *)B3,
                        *bi = (const uint16_t *)bias;
         uint16_t *o = (uint16_t *)out;
-        // row tiles an expert-parallel launch can expect (for the column-tile choice)
-        const int64_t mt_est = (rows_bound + bm - 1) / bm;
+        // row tiles an expert-parallel launch can expect (for the column-tile
+        // choice): one per expert when a tile holds the whole capacity
+        const int64_t mt_est = C <= bm ? (rows_bound < E ? rows_bound : E) : (rows_bound + bm - 1) / bm;
 #define MOE_GEMM(TL, ACTV, BIASV)                                                                   \
     do {                                                                                            \
         const int tiles_n = (N + TL::BN - 1) / TL::BN;                                              \
@@ -579,27 +598,31 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
             hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, true>), grid, dim3(256), 0, s, a, b, \
                                b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);             \
     } while (0)
-        // 256 output columns per tile unless that leaves fewer tiles than CUs
-        const bool wide = mt_est * ((N + 255) / 256) >= 256;
-        if (bm == 256) {
-            if (act == 2) MOE_GEMM(TileG256, 2, false);
-            else if (wide) {
-                if (act == 1) { if (bias) MOE_GEMM(TileW256, 1, true); else MOE_GEMM(TileW256, 1, false); }
-                else { if (bias) MOE_GEMM(TileW256, 0, true); else MOE_GEMM(TileW256, 0, false); }
-            } else {
-                if (act == 1) { if (bias) MOE_GEMM(TileN256, 1, true); else MOE_GEMM(TileN256, 1, false); }
-                else { if (bias) MOE_GEMM(TileN256, 0, true); else MOE_GEMM(TileN256, 0, false); }
-            }
+#define MOE_GEMM_ACT(TL)                                                                            \
+    do {                                                                                            \
+        if (act == 1) { if (bias) MOE_GEMM(TL, 1, true); else MOE_GEMM(TL, 1, false); }             \
+        else { if (bias) MOE_GEMM(TL, 0, true); else MOE_GEMM(TL, 0, false); }                      \
+    } while (0)
+        // wide column tiles unless that leaves fewer tiles than CUs
+        if (bm == 320) {
+            if (mt_est * ((N + 191) / 192) >= 256) MOE_GEMM_ACT(TileW320);
+            else MOE_GEMM_ACT(TileN320);
+        } else if (bm == 192) {
+            if (mt_est * ((N + 255) / 256) >= 256) MOE_GEMM_ACT(TileW192);
+            else MOE_GEMM_ACT(TileN192);
         } else {
-            if (act == 2) MOE_GEMM(TileG128, 2, false);
-            else if (wide) {
-                if (act == 1) { if (bias) MOE_GEMM(TileW128, 1, true); else MOE_GEMM(TileW128, 1, false); }
-                else { if (bias) MOE_GEMM(TileW128, 0, true); else MOE_GEMM(TileW128, 0, false); }
+            const bool wide = mt_est * ((N + 255) / 256) >= 256;
+            if (bm == 256) {
+                if (act == 2) MOE_GEMM(TileG256, 2, false);
+                else if (wide) MOE_GEMM_ACT(TileW256);
+                else MOE_GEMM_ACT(TileN256);
             } else {
-                if (act == 1) { if (bias) MOE_GEMM(TileN128, 1, true); else MOE_GEMM(TileN128, 1, false); }
-                else { if (bias) MOE_GEMM(TileN128, 0, true); else MOE_GEMM(TileN128, 0, false); }
+                if (act == 2) MOE_GEMM(TileG128, 2, false);
+                else if (wide) MOE_GEMM_ACT(TileW128);
+                else MOE_GEMM_ACT(TileN128);
             }
         }
+#undef MOE_GEMM_ACT
 #undef MOE_GEMM
     } else {
         const int tiles_n = (N + FBN - 1) / FBN;

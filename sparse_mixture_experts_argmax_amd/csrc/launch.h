@@ -39,17 +39,19 @@ hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_i
                           hipStream_t s);
 
 // ---- experts ----------------------------------------------------------
-// Row-tile height of the grouped GEMM; tile_map holds E+1 prefix sums of
-// ceil(expert_count / gemm_bm(dtype, C)).
-int gemm_bm(int dtype_bf16, int64_t C);
+// Row-tile height of the grouped GEMM (act: 0 none, 1 relu, 2 swiglu, the
+// activation of the first GEMM; both GEMMs use the same height); tile_map
+// holds E+1 prefix sums of ceil(expert_count / gemm_bm(dtype, C, act)).
+int gemm_bm(int dtype_bf16, int64_t C, int act);
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s);
 // out[e, m, :] = act(A[e, m, :] . B[e]^T (+ bias[e]))  for m < count[e]
 // act: 0 none, 1 relu, 2 swiglu (silu(A.B^T) * (A.B3^T)).
+// tile_map was built for row tiles of bm = gemm_bm(dtype, C, act of the first GEMM).
 // rows_bound: an upper bound of sum_e count[e] (sizes the grid).
 hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, const void *bias,
                                int dtype_bf16, int act, const int32_t *expert_count,
-                               const int32_t *tile_map, int E, int64_t C, int N, int K,
+                               const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
                                int64_t rows_bound, void *out, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------

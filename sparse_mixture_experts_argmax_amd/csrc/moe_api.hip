@@ -177,11 +177,12 @@ moe_status run_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count, 
     int32_t *tile_map = reinterpret_cast<int32_t *>(ws + w.tile_map);
     void *H = ws + w.h;
     const int bf16 = dt == MOE_BF16;
-    MOE_HIP(moe::launch_tile_map(expert_count, E, moe::gemm_bm(bf16, C), tile_map, stream));
     const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
-    MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, E, C,
+    const int bm = moe::gemm_bm(bf16, C, act1);
+    MOE_HIP(moe::launch_tile_map(expert_count, E, bm, tile_map, stream));
+    MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, bm, E, C,
                                      dff, d, rows_bound, H, stream));
-    MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, E, C,
+    MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, bm, E, C,
                                      d, dff, rows_bound, ybuf, stream));
     return MOE_OK;
 }
@@ -361,6 +362,8 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.ffn + w.f.tile_map);
     void *H = base + w.ffn + w.f.h;
     const int64_t rows = T * (int64_t)k;
+    const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
+    const int bm = moe::gemm_bm(bf16, C, act1);
     auto mark = [&](int i) -> bool { return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess; };
 
     if (!mark(0)) return MOE_ERR_HIP;
@@ -375,16 +378,14 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
                            fuse_reduce ? reinterpret_cast<const float *>(base + w.router + w.r.part_prob)
                                        : nullptr,
                            moe::router_blocks(T, bf16, E), prob_sum, route_count,
-                           T > 0 && C > 0 ? tile_map : nullptr, moe::gemm_bm(bf16, C)));
+                           T > 0 && C > 0 ? tile_map : nullptr, bm));
     if (!mark(2)) return MOE_ERR_HIP;
-    if (C > 0) {
-        const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
-        MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, E, C,
+    if (C > 0)
+        MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, bm, E, C,
                                          dff, d, rows, H, stream));
-    }
     if (!mark(3)) return MOE_ERR_HIP;
     if (C > 0)
-        MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, E, C, d,
+        MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, bm, E, C, d,
                                          dff, rows, ybuf, stream));
     if (!mark(4)) return MOE_ERR_HIP;
     MOE_HIP(moe::launch_combine(ybuf, bf16, expert_idx, slot, gate, prob_sum, route_count, T, d, E,

@@ -30,6 +30,10 @@ SMALL = {
     # experts of at least 512 rows: the 256-row GEMM tiles, with K and N tails
     "big_tiles": (3000, 200, 328, 4, 2, 1.0, "bf16", "relu", True, False, 1.0),
     "big_swiglu": (2048, 136, 200, 2, 1, 1.0, "bf16", "swiglu", False, False, 1.0),
+    # capacity 300 and 170: one 320- or 192-row tile per expert, in the wide
+    # column tiles (first GEMM) and the narrow ones (second), with K and N tails
+    "tiles_320": (19200, 72, 776, 64, 1, 1.0, "bf16", "relu", True, False, 1.0),
+    "tiles_192": (10880, 72, 776, 64, 1, 1.0, "bf16", "relu", True, False, 1.0),
 }
 
 
@@ -250,8 +254,8 @@ def _ffn_rows(cfg, sample=None, seed=7):
     return np.concatenate(got), np.concatenate(ref), len(rows)
 
 
-@pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "ragged_f32",
-                                  "switch_base", "mixtral"])
+@pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "tiles_320",
+                                  "tiles_192", "ragged_f32", "switch_base", "mixtral", "many_expert"])
 def test_expert_ffn_elementwise(name):
     """Each GEMM tile shape against the oracle's expert FFN, every element of the checked rows.
 
