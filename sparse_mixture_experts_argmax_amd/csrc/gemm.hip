@@ -104,107 +104,103 @@ struct Tile {
     static __device__ __forceinline__ int swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 };
 
-template <class TL, int ACT, bool BIAS, bool KTAIL>
-__global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ B3,
-    const uint16_t *__restrict__ bias, const int32_t *__restrict__ count,
-    const int32_t *__restrict__ tile_map, int E, int64_t C, int N, int K, int tiles_n,
-    uint16_t *__restrict__ out) {
-    constexpr int BM = TL::BM, BN = TL::BN, S = TL::S, BK = TL::BK;
-    constexpr int ROWB = TL::ROWB, PIECES = TL::PIECES, KS = TL::KS;
-    constexpr int FM = TL::FM, FN = TL::FN, AI = TL::AI, BI = TL::BI;
-    constexpr bool DUAL = (ACT == 2);
-    constexpr int NBT = DUAL ? 2 : 1;                    // weight tiles per stage
-    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-    constexpr int STAGE = A_BYTES + NBT * B_BYTES;
-    constexpr int PER = AI + NBT * BI;                   // DMA instructions per wave per stage
-    // DMA instructions a wave issues after a stage's own before that stage is
-    // waited for: those of the S - 2 newer stages
-    constexpr int NEWER = (S - 2) * PER;
-    // the output tile is staged through two stage buffers (a row half each)
-    // when it fits, else stored from registers
-    constexpr bool STAGED_OUT = BM * BN <= STAGE;
-    // one LDS array per stage: the compiler then sees that the fragment reads of
-    // one stage cannot alias the DMA in flight into another and adds no wait
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
-    __shared__ int s_map[MAX_E_LDS + 1];
-
-    int e, mt, nt;
-    if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt)) return;
-    const int cnt = count[e];
-    const int m0 = mt * BM;
-    const int n0 = nt * BN;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (DMA base)
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-    const int64_t b3off = DUAL ? (int64_t)(B3 - B) : 0;
-
-    // DMA sources: wave instruction i fills the RPI LDS rows starting at
-    // RPI (wave * AI + i); lane l lands at byte 16 l of that 1 KB block = row
-    // l / PIECES, position l % PIECES, which holds logical piece
-    // (l % PIECES) ^ swz(row) of its row (RPI is a multiple of 8, so swz of
-    // the row is swz(l / PIECES)).  Rows past the count / past N read a
-    // valid row; their results are never stored.
-    constexpr int RPI = 1024 / ROWB;                     // LDS rows per DMA instruction
-    const int lr = lane / PIECES;
-    const int lc = (lane % PIECES) ^ TL::swz(lr);
+// The state of one block's tile shared by the prologue and the K loop: the LDS
+// ring and the per-lane DMA sources.  A rows go to LDS in groups of RPI rows
+// (one 1 KB DMA instruction); group 4 i + w belongs to instruction i of wave
+// w, so the first instructions of every wave cover the first tile rows.
+template <class TL, int ACT>
+struct TileCtx {
+    static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, ROWB = TL::ROWB, PIECES = TL::PIECES;
+    static constexpr int AI = TL::AI, BI = TL::BI;
+    static constexpr bool DUAL = (ACT == 2);
+    static constexpr int NBT = DUAL ? 2 : 1;                       // weight tiles per stage
+    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    static constexpr int STAGE = A_BYTES + NBT * B_BYTES;
+    static constexpr int RPI = 1024 / ROWB;                        // LDS rows per DMA instruction
+    uint8_t *st0, *st1, *st2, *st3;
+    const uint16_t *Ae;                                            // the expert's rows of A
     const uint16_t *asrc[AI];
     const uint16_t *bsrc[BI];
-    {
-        const uint16_t *Ae = A + (int64_t)e * C * K;
-        const uint16_t *Be = B + (int64_t)e * N * K;
+    int64_t b3off;
+    int K, m0, lane, wave, lr, lc, nk;
+    bool tail_piece;
+
+    // A sources for tile rows m0 + row, the row clamped to last (rows past
+    // the count are computed but never stored)
+    __device__ __forceinline__ void set_a(int last) {
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
-            int am = m0 + (wave * AI + i) * RPI + lr;
-            am = am < cnt ? am : cnt - 1;
+            int am = m0 + (4 * i + wave) * RPI + lr;
+            am = am < last ? am : last;
             asrc[i] = Ae + (int64_t)am * K + lc * 8;
         }
-#pragma unroll
-        for (int j = 0; j < BI; ++j) {
-            int bn = n0 + (wave * BI + j) * RPI + lr;
-            bn = bn < N ? bn : N - 1;
-            bsrc[j] = Be + (int64_t)bn * K + lc * 8;
-        }
     }
-    const int nk = (K + BK - 1) / BK;
-    // with K % BK != 0 the pieces of the last K tile that lie past K are read
-    // from column 0 and cleared in LDS once they have landed
-    const bool tail_piece = KTAIL && ((nk - 1) * BK + lc * 8 >= K);
+};
 
-    auto issue = [&](uint8_t *base, int kt) {
-        const int k0 = (KTAIL && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * BK;
+// DMA of K tile kt into one stage: NA instructions of A, then those of B (and
+// B3).  Lane l lands at byte 16 l of its 1 KB group = row l / PIECES,
+// position l % PIECES, which holds logical piece (l % PIECES) ^ swz(row).  The
+// pieces past K (K % BK != 0) of the last K tile are read from column 0 and
+// cleared in LDS once they have landed.
+template <int NA, bool KTAIL, class CTX>
+__device__ __forceinline__ void tile_issue(const CTX &c, uint8_t *base, int kt) {
+    const int k0 = (KTAIL && kt == c.nk - 1 && c.tail_piece) ? -c.lc * 8 : kt * CTX::BK;
 #pragma unroll
-        for (int i = 0; i < AI; ++i)
-            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(asrc[i] + k0),
-                                             (MOE_LDS_AS void *)(base + (wave * AI + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < NA; ++i)
+        __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[i] + k0),
+                                         (MOE_LDS_AS void *)(base + (4 * i + c.wave) * 1024), 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < BI; ++j)
-            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(bsrc[j] + k0),
-                                             (MOE_LDS_AS void *)(base + A_BYTES + (wave * BI + j) * 1024),
-                                             16, 0, 0);
-        if (DUAL) {
+    for (int j = 0; j < CTX::BI; ++j)
+        __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.bsrc[j] + k0),
+                                         (MOE_LDS_AS void *)(base + CTX::A_BYTES + (c.wave * CTX::BI + j) * 1024),
+                                         16, 0, 0);
+    if (CTX::DUAL) {
 #pragma unroll
-            for (int j = 0; j < BI; ++j)
-                __builtin_amdgcn_global_load_lds(
-                    (const MOE_GLB_AS void *)(bsrc[j] + b3off + k0),
-                    (MOE_LDS_AS void *)(base + A_BYTES + B_BYTES + (wave * BI + j) * 1024), 16, 0, 0);
-        }
-        // keep every DMA of the stage ahead of the MFMAs that follow (left to
-        // itself the scheduler sinks them to the end of the step, which leaves
-        // almost no time for them to land)
-        __builtin_amdgcn_sched_barrier(0);
-    };
+        for (int j = 0; j < CTX::BI; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const MOE_GLB_AS void *)(c.bsrc[j] + c.b3off + k0),
+                (MOE_LDS_AS void *)(base + CTX::A_BYTES + CTX::B_BYTES + (c.wave * CTX::BI + j) * 1024), 16,
+                0, 0);
+    }
+    // keep every DMA of the stage ahead of the MFMAs that follow (left to
+    // itself the scheduler sinks them to the end of the step, which leaves
+    // almost no time for them to land)
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The K loop and epilogue of a tile whose rows that hold data lie in
+// [0, 64 FV): FV 32-row fragments per wave (wave row wm owns tile rows
+// 64 i + 32 wm + 0..31) and the A-DMA instructions of those rows only.  The
+// caller has issued K tiles 0 .. S - 2 with every A instruction.
+template <class TL, int FV, int ACT, bool BIAS, bool KTAIL>
+__device__ __forceinline__ void tile_body(TileCtx<TL, ACT> &c, const uint16_t *__restrict__ bias_e, int cnt,
+                                          int n0, int N, uint16_t *__restrict__ oe) {
+    using X = TileCtx<TL, ACT>;
+    constexpr int BN = TL::BN, S = TL::S, ROWB = TL::ROWB, KS = TL::KS, FN = TL::FN, BI = TL::BI;
+    constexpr bool DUAL = X::DUAL;
+    constexpr int NBT = X::NBT, A_BYTES = X::A_BYTES, B_BYTES = X::B_BYTES;
+    constexpr int NA = FV * 64 / (4 * X::RPI);           // A-DMA instructions per wave
+    static_assert(NA >= 1 && NA <= TL::AI && NA * 4 * X::RPI == FV * 64, "A rows per wave");
+    constexpr int PER = NA + NBT * BI;
+    // DMA instructions a wave issues after a stage's own before that stage is
+    // waited for: those of the S - 2 newer stages (the prologue's stages hold
+    // more, which only makes the first waits stricter)
+    constexpr int NEWER = (S - 2) * PER;
+    constexpr int ROWS = FV * 64;                        // tile rows computed and stored
+    // the output rows are staged through two stage buffers (one per wave row)
+    // when they fit, else stored from registers
+    constexpr bool STAGED_OUT = TL::BM * BN <= X::STAGE;
+    const int lane = c.lane, wave = c.wave, nk = c.nk;
+    const int wm = wave >> 1, wn = wave & 1;
+    uint8_t *const st0 = c.st0, *const st1 = c.st1, *const st2 = c.st2, *const st3 = c.st3;
+    c.set_a(cnt - 1);
+
+    auto issue = [&](uint8_t *base, int kt) { tile_issue<NA, KTAIL>(c, base, kt); };
     auto clear_tail = [&](uint8_t *base) {
-        if (tail_piece) {
+        if (c.tail_piece) {
             const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < AI; ++i) *reinterpret_cast<u32x4 *>(base + (wave * AI + i) * 1024 + lane * 16) = z;
+            for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4 *>(base + (4 * i + wave) * 1024 + lane * 16) = z;
 #pragma unroll
             for (int j = 0; j < NBT * BI; ++j)
                 *reinterpret_cast<u32x4 *>(base + A_BYTES + (j / BI) * B_BYTES + (wave * BI + (j % BI)) * 1024 +
@@ -215,16 +211,16 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     // accumulators hold C^T fragments: acc[i][j] = weight rows (n) x x rows (m);
     // lane l holds output row m = l % 32 of the fragment and, for g = 0..3, the
     // four consecutive columns n = 8 g + 4 (l / 32) + 0..3 in elements 4g..4g+3
-    f32x16 acc[FM][FN];
-    f32x16 acc3[DUAL ? FM : 1][DUAL ? FN : 1];
+    f32x16 acc[FV][FN];
+    f32x16 acc3[DUAL ? FV : 1][DUAL ? FN : 1];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FV; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 #pragma unroll
-    for (int i = 0; i < (DUAL ? FM : 1); ++i)
+    for (int i = 0; i < (DUAL ? FV : 1); ++i)
 #pragma unroll
         for (int j = 0; j < (DUAL ? FN : 1); ++j)
 #pragma unroll
@@ -233,18 +229,18 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     // fragment reads (32 x 16 operands): row (base + lane % 32), logical piece
     // 2 ks + lane / 32; fragment bases are multiples of 32, so the stored
     // position is piece ^ swz(lane % 32)
-    const int arow = (wm * (BM / 2) + (lane & 31)) * ROWB;
+    const int arow = (32 * wm + (lane & 31)) * ROWB;
     const int brow = (wn * (BN / 2) + (lane & 31)) * ROWB;
     const int fswz = TL::swz(lane & 31);
     // fragments of two k steps: the reads of k step ks + 1 are issued between
     // the MFMAs of k step ks
-    bf16x8 af[2][FM], bfr[2][FN], bf3[DUAL ? 2 : 1][DUAL ? FN : 1];
+    bf16x8 af[2][FV], bfr[2][FN], bf3[DUAL ? 2 : 1][DUAL ? FN : 1];
     auto rd = [&](const uint8_t *sa, int ks, int sl) {
         const uint8_t *sb = sa + A_BYTES;
         const int pofs = ((ks * 2 + (lane >> 5)) ^ fswz) << 4;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[sl][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 32 * ROWB + pofs));
+        for (int i = 0; i < FV; ++i)
+            af[sl][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + arow + i * 64 * ROWB + pofs));
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             bfr[sl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + brow + j * 32 * ROWB + pofs));
@@ -255,11 +251,11 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
                     as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + B_BYTES + brow + j * 32 * ROWB + pofs));
         }
     };
-    // per k step: R fragment reads (of the next k step) and M MFMAs; one read
-    // goes after each of the first R MFMAs
-    constexpr int R = FM + (DUAL ? 2 : 1) * FN;
-    constexpr int M = FM * FN * (DUAL ? 2 : 1);
-    static_assert(M >= R, "read/MFMA interleave");
+    // per k step: R fragment reads (of the next k step) and M MFMAs, paired
+    // one read after each MFMA while both last
+    constexpr int R = FV + NBT * FN;
+    constexpr int M = FV * FN * NBT;
+    constexpr int RM = R > M ? R : M;
     // the MFMAs of one K tile; the fragments of its k step 0 are already read
     auto compute = [&](const uint8_t *sa) {
 #pragma unroll
@@ -267,13 +263,13 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
             const int sl = ks & 1;
             if (ks < KS - 1) rd(sa, ks + 1, sl ^ 1);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FV; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[sl][j], af[sl][i], acc[i][j], 0, 0, 0);
             if (DUAL) {
 #pragma unroll
-                for (int i = 0; i < (DUAL ? FM : 1); ++i)
+                for (int i = 0; i < (DUAL ? FV : 1); ++i)
 #pragma unroll
                     for (int j = 0; j < (DUAL ? FN : 1); ++j)
                         acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf3[DUAL ? sl : 0][j], af[sl][i],
@@ -281,11 +277,10 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
             }
             if (ks < KS - 1) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                for (int r = 0; r < RM; ++r) {
+                    if (r < M) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    if (r < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -295,14 +290,6 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     // own DMA (the S - 2 newer stages stay in flight), passes one barrier (all
     // waves have landed their part of kt and finished reading kt - 1), refills
     // the stage of kt - 1 with kt + S - 1, then runs the MFMAs of kt.
-    // prologue: K tiles 0 .. S - 2, clamped to the last one when there are
-    // fewer (the duplicate loads are never read).  Unconditional on purpose:
-    // a conditional DMA here makes the compiler give up tracking which stage
-    // a pending DMA writes, and then it drains the whole ring before every
-    // fragment read.
-    issue(st0, 0);
-    if (S > 2) issue(st1, nk > 1 ? 1 : nk - 1);
-    if (S > 3) issue(st2, nk > 2 ? 2 : nk - 1);
     int kt = 0;
     // steady state: every step refills a stage, so the wait count is fixed
     // and the loop body has no branch
@@ -365,15 +352,15 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     }
 #undef MOE_TAIL
 
-    // ---- epilogue: bias, activation, bf16.  With STAGED_OUT the tile is staged
-    // in LDS (row half wm in stage buffer wm, 16-byte pieces swizzled by row)
-    // so that rows go out as coalesced 16-byte stores; otherwise each lane
-    // stores its four consecutive columns (8 bytes) directly.
+    // ---- epilogue: bias, activation, bf16.  With STAGED_OUT the rows of wave
+    // row wm go to stage buffer wm (16-byte pieces swizzled by row), so that
+    // rows leave as coalesced 16-byte stores; otherwise each lane stores its
+    // four consecutive columns (8 bytes) directly.
     constexpr int P = BN / 8;                            // 16-byte pieces per output row
     constexpr int PSW = (P & (P - 1)) == 0 ? P - 1 : 7;  // piece swizzle mask (keeps a piece in its row)
     if (STAGED_OUT) lds_barrier();                       // every wave is past its last fragment read
     uint8_t *so = wm ? st1 : st0;
-    uint16_t *oe = out + (int64_t)e * C * N;
+    const int m0 = c.m0;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -383,7 +370,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
             if (BIAS) {
                 const int n = n0 + nl;
                 if (n < N) {
-                    const uint2 bb = *reinterpret_cast<const uint2 *>(bias + (int64_t)e * N + n);
+                    const uint2 bb = *reinterpret_cast<const uint2 *>(bias_e + n);
                     bv[0] = bf2f((uint16_t)(bb.x & 0xFFFFu));
                     bv[1] = bf2f((uint16_t)(bb.x >> 16));
                     bv[2] = bf2f((uint16_t)(bb.y & 0xFFFFu));
@@ -391,8 +378,8 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
                 }
             }
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = i * 32 + (lane & 31);      // row within the half
+            for (int i = 0; i < FV; ++i) {
+                const int r = i * 32 + (lane & 31);      // row within the wave row's buffer
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -408,7 +395,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
                     const int pc = (nl >> 3) ^ (r & PSW);
                     *reinterpret_cast<uint2 *>(so + r * (BN * 2) + (pc << 4) + ((nl & 4) << 1)) = pk;
                 } else {
-                    const int m = m0 + wm * (BM / 2) + r;
+                    const int m = m0 + 64 * i + 32 * wm + (lane & 31);
                     const int n = n0 + nl;
                     if (m < cnt && n < N) *reinterpret_cast<uint2 *>(oe + (int64_t)m * N + n) = pk;
                 }
@@ -417,19 +404,106 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     }
     if (STAGED_OUT) {
         lds_barrier();
-        static_assert(!STAGED_OUT || (BM * P) % 256 == 0, "whole store rounds");
+        static_assert(!STAGED_OUT || (ROWS * P) % 256 == 0, "whole store rounds");
 #pragma unroll
-        for (int it = 0; it < BM * P / 256; ++it) {
-            const int q = tid + it * 256;
-            const int R = q / P;                         // tile row
+        for (int it = 0; it < ROWS * P / 256; ++it) {
+            const int q = threadIdx.x + it * 256;
+            const int Rw = q / P;                        // tile row
             const int p = q % P;
-            const int r = R % (BM / 2);
-            const uint8_t *src = (R < BM / 2 ? st0 : st1) + r * (BN * 2) + ((p ^ (r & PSW)) << 4);
-            const int m = m0 + R;
+            const int r = ((Rw >> 6) << 5) | (Rw & 31);  // its row in the wave row's buffer
+            const uint8_t *src = (((Rw >> 5) & 1) ? st1 : st0) + r * (BN * 2) + ((p ^ (r & PSW)) << 4);
+            const int m = m0 + Rw;
             const int n = n0 + p * 8;
             if (m < cnt && n < N) st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(src));
         }
     }
+}
+
+// One tile per block.  EXPERT: the tile covers all rows of an expert (BM >= C),
+// block -> (expert, column tile) directly, and the first stages are issued
+// before the expert's count is known; else the block finds its (expert, row
+// tile, column tile) in tile_map.  The K loop then runs in the specialization
+// for the 64-row chunks of the tile that hold data.
+template <class TL, int ACT, bool BIAS, bool KTAIL, bool EXPERT>
+__global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ B3,
+    const uint16_t *__restrict__ bias, const int32_t *__restrict__ count,
+    const int32_t *__restrict__ tile_map, int E, int64_t C, int N, int K, int tiles_n,
+    uint16_t *__restrict__ out) {
+    using X = TileCtx<TL, ACT>;
+    constexpr int BM = TL::BM, BN = TL::BN, S = TL::S, FM = TL::FM;
+    constexpr int STAGE = X::STAGE;
+    // one LDS array per stage: the compiler then sees that the fragment reads of
+    // one stage cannot alias the DMA in flight into another and adds no wait
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
+    __shared__ int s_map[EXPERT ? 1 : MAX_E_LDS + 1];
+
+    int e, mt, nt;
+    if (EXPERT) {
+        // expert-major, then column tile; block b of XCD b % 8 takes the
+        // (b / 8)-th tile of that XCD's contiguous share
+        const int total = E * tiles_n;
+        const int per_xcd = (total + 7) >> 3;
+        const int slot = blockIdx.x >> 3;
+        const int L = (blockIdx.x & 7) * per_xcd + slot;
+        if (slot >= per_xcd || L >= total) return;
+        e = L / tiles_n;
+        nt = L - e * tiles_n;
+        mt = 0;
+    } else {
+        if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt)) return;
+    }
+
+    X c;
+    c.st0 = st0; c.st1 = st1; c.st2 = st2; c.st3 = st3;
+    c.lane = threadIdx.x & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (DMA base)
+    c.lr = c.lane / TL::PIECES;
+    c.lc = (c.lane % TL::PIECES) ^ TL::swz(c.lr);
+    c.K = K;
+    c.m0 = mt * BM;
+    c.nk = (K + TL::BK - 1) / TL::BK;
+    c.tail_piece = KTAIL && ((c.nk - 1) * TL::BK + c.lc * 8 >= K);
+    c.b3off = X::DUAL ? (int64_t)(B3 - B) : 0;
+    c.Ae = A + (int64_t)e * C * K;
+    const int n0 = nt * BN;
+    {
+        const uint16_t *Be = B + (int64_t)e * N * K;
+#pragma unroll
+        for (int j = 0; j < TL::BI; ++j) {
+            int bn = n0 + (c.wave * TL::BI + j) * X::RPI + c.lr;
+            bn = bn < N ? bn : N - 1;
+            c.bsrc[j] = Be + (int64_t)bn * K + c.lc * 8;
+        }
+    }
+    // prologue: K tiles 0 .. S - 2 with every A row (clamped to the last row
+    // of the capacity), each clamped to the last K tile when there are fewer
+    // (the duplicate loads are never read).  Unconditional on purpose: a
+    // conditional DMA here makes the compiler give up tracking which stage a
+    // pending DMA writes, and then it drains the whole ring before every
+    // fragment read.
+    c.set_a((int)C - 1);
+    tile_issue<TL::AI, KTAIL>(c, st0, 0);
+    if (S > 2) tile_issue<TL::AI, KTAIL>(c, st1, c.nk > 1 ? 1 : c.nk - 1);
+    if (S > 3) tile_issue<TL::AI, KTAIL>(c, st2, c.nk > 2 ? 2 : c.nk - 1);
+
+    const int cnt = count[e];
+    const int rows = cnt - c.m0;                         // > 0 for every mapped tile
+    if (rows <= 0) {
+        wait_vm_lgkm0<0>();                              // no DMA may land after the block ends
+        return;
+    }
+    const int fv = rows >= BM ? FM : (rows + 63) >> 6;
+    const uint16_t *bias_e = BIAS ? bias + (int64_t)e * N : nullptr;
+    uint16_t *oe = out + (int64_t)e * C * N;
+    if constexpr (FM >= 5) if (fv == 5) { tile_body<TL, 5, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
+    if constexpr (FM >= 4) if (fv == 4) { tile_body<TL, 4, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
+    if constexpr (FM >= 3) if (fv == 3) { tile_body<TL, 3, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
+    if (fv == 2) { tile_body<TL, 2, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
+    tile_body<TL, 1, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe);
 }
 
 // ---------------------------------------------------------------------------
@@ -587,16 +661,28 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
         // row tiles an expert-parallel launch can expect (for the column-tile
         // choice): one per expert when a tile holds the whole capacity
         const int64_t mt_est = C <= bm ? (rows_bound < E ? rows_bound : E) : (rows_bound + bm - 1) / bm;
+        // a tile that holds the whole capacity goes by (expert, column tile)
+        // without the tile map
+        const bool expert = C <= bm;
+#define MOE_GEMM_K(TL, ACTV, BIASV, EXP)                                                            \
+    do {                                                                                            \
+        if (K % 64 == 0)                                                                            \
+            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, false, EXP>), grid, dim3(256), 0, s, a, \
+                               b, b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);          \
+        else                                                                                        \
+            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, true, EXP>), grid, dim3(256), 0, s, a, \
+                               b, b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);          \
+    } while (0)
 #define MOE_GEMM(TL, ACTV, BIASV)                                                                   \
     do {                                                                                            \
         const int tiles_n = (N + TL::BN - 1) / TL::BN;                                              \
-        const dim3 grid((unsigned)grid_for(C, E, TL::BM, tiles_n, rows_bound));                     \
-        if (K % 64 == 0)                                                                            \
-            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, false>), grid, dim3(256), 0, s, a, b, \
-                               b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);             \
-        else                                                                                        \
-            hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, true>), grid, dim3(256), 0, s, a, b, \
-                               b3, bi, expert_count, tile_map, E, C, N, K, tiles_n, o);             \
+        if (expert) {                                                                               \
+            const dim3 grid((unsigned)((((int64_t)E * tiles_n + 7) / 8) * 8));                      \
+            MOE_GEMM_K(TL, ACTV, BIASV, true);                                                      \
+        } else {                                                                                    \
+            const dim3 grid((unsigned)grid_for(C, E, TL::BM, tiles_n, rows_bound));                 \
+            MOE_GEMM_K(TL, ACTV, BIASV, false);                                                     \
+        }                                                                                           \
     } while (0)
 #define MOE_GEMM_ACT(TL)                                                                            \
     do {                                                                                            \
@@ -623,6 +709,7 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
             }
         }
 #undef MOE_GEMM_ACT
+#undef MOE_GEMM_K
 #undef MOE_GEMM
     } else {
         const int tiles_n = (N + FBN - 1) / FBN;
