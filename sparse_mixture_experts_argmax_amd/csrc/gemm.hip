@@ -31,6 +31,7 @@
 #include "launch.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace moe {
 
@@ -90,9 +91,13 @@ __device__ __forceinline__ float silu_fast(float a) {
 // instruction each touch every bank group once.  MINB = 2 sizes the ring and
 // the registers for two blocks per CU, so that one block's prologue and
 // epilogue overlap the other's MFMAs.
-template <int BM_, int BN_, int S_, int BK_ = 64, int MINB_ = 1>
+template <int BM_, int BN_, int S_, int BK_ = 64, int MINB_ = 1, int ILV_ = 0>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, S = S_, BK = BK_, MINB = MINB_;
+    // > 0: the DMA of the next stage is spread over the MFMAs of the first ILV
+    // k steps instead of issued in one burst (a wave stalls while the address
+    // unit is busy, so a burst delays the MFMAs behind it)
+    static constexpr int ILV = ILV_;
     static constexpr int ROWB = BK * 2;                 // bytes per LDS row
     static constexpr int PIECES = BK / 8;               // 16-byte pieces per row
     static constexpr int KS = BK / 16;                  // MFMA k steps per stage
@@ -256,11 +261,36 @@ __device__ __forceinline__ void tile_body(TileCtx<TL, ACT> &c, const uint16_t *_
     constexpr int R = FV + NBT * FN;
     constexpr int M = FV * FN * NBT;
     constexpr int RM = R > M ? R : M;
-    // the MFMAs of one K tile; the fragments of its k step 0 are already read
-    auto compute = [&](const uint8_t *sa) {
+    // DMA instruction q of a stage (A rows, then B, then B3), for spreading a
+    // stage's DMA over the MFMAs of the first ILV k steps
+    auto dma_one = [&](uint8_t *base, int kt2, int q) {
+        const int k0 = (KTAIL && kt2 == nk - 1 && c.tail_piece) ? -c.lc * 8 : kt2 * TL::BK;
+        if (q < NA)
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[q] + k0),
+                                             (MOE_LDS_AS void *)(base + (4 * q + wave) * 1024), 16, 0, 0);
+        else if (q < NA + BI)
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.bsrc[q - NA] + k0),
+                                             (MOE_LDS_AS void *)(base + A_BYTES + (wave * BI + q - NA) * 1024),
+                                             16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(
+                (const MOE_GLB_AS void *)(c.bsrc[q - NA - BI] + c.b3off + k0),
+                (MOE_LDS_AS void *)(base + A_BYTES + B_BYTES + (wave * BI + q - NA - BI) * 1024), 16, 0, 0);
+    };
+    constexpr int ILV = TL::ILV < KS ? TL::ILV : KS;
+    constexpr int SLOTS = (ILV > 0 ? ILV : 1) * M;
+    // the MFMAs of one K tile; the fragments of its k step 0 are already read.
+    // With ILV, the DMA of K tile kt2 into nxt is spread over its first k steps.
+    auto compute = [&](const uint8_t *sa, uint8_t *nxt, int kt2, auto with_dma) {
+        constexpr bool IL = decltype(with_dma)::value && ILV > 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int sl = ks & 1;
+            if (IL) {
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    if ((q * SLOTS / PER) / M == ks) dma_one(nxt, kt2, q);
+            }
             if (ks < KS - 1) rd(sa, ks + 1, sl ^ 1);
 #pragma unroll
             for (int i = 0; i < FV; ++i)
@@ -275,7 +305,16 @@ __device__ __forceinline__ void tile_body(TileCtx<TL, ACT> &c, const uint16_t *_
                         acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf3[DUAL ? sl : 0][j], af[sl][i],
                                                                              acc3[i][j], 0, 0, 0);
             }
-            if (ks < KS - 1) {
+            if (IL) {
+#pragma unroll
+                for (int r = 0; r < RM; ++r) {
+                    if (r < M) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    if (ks < KS - 1 && r < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+#pragma unroll
+                    for (int q = 0; q < PER; ++q)
+                        if (q * SLOTS / PER == ks * M + r) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            } else if (ks < KS - 1) {
 #pragma unroll
                 for (int r = 0; r < RM; ++r) {
                     if (r < M) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -298,8 +337,8 @@ __device__ __forceinline__ void tile_body(TileCtx<TL, ACT> &c, const uint16_t *_
         wait_vm_lgkm0<NEWER>();                                                 \
         ring_barrier();                                                         \
         rd(CUR, 0, 0);                                                          \
-        issue(NXT, kt + S - 1);                                                 \
-        compute(CUR);                                                           \
+        if (ILV == 0) issue(NXT, kt + S - 1);                                   \
+        compute(CUR, NXT, kt + S - 1, std::integral_constant<bool, true>());   \
         ++kt;                                                                   \
     }
     for (; kt + 2 * S - 1 <= nk;) {
@@ -331,7 +370,7 @@ __device__ __forceinline__ void tile_body(TileCtx<TL, ACT> &c, const uint16_t *_
         rd(CUR, 0, 0);                                                          \
         if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
         __builtin_amdgcn_sched_barrier(0);                                      \
-        compute(CUR);                                                           \
+        compute(CUR, NXT, 0, std::integral_constant<bool, false>());           \
         ++kt;                                                                   \
     }
     if constexpr (S == 2) {
@@ -628,17 +667,19 @@ int gemm_bm(int dtype_bf16, int64_t C, int act) {
 // G = gated (128 columns of each weight); the suffix is BM.  64-wide K
 // stages, one block per CU and 112-144 KB rings (one or two stages ahead of
 // the MFMAs), except the narrow 128-row shape, which runs two blocks per CU
-// on 32-wide K stages.
-using TileW320 = Tile<320, 192, 2, 64, 1>;
-using TileN320 = Tile<320, 128, 2, 64, 1>;
-using TileW256 = Tile<256, 256, 2, 64, 1>;
-using TileN256 = Tile<256, 128, 3, 64, 1>;
-using TileG256 = Tile<256, 128, 2, 64, 1>;
-using TileW192 = Tile<192, 256, 2, 64, 1>;
-using TileN192 = Tile<192, 128, 3, 64, 1>;
-using TileW128 = Tile<128, 256, 3, 64, 1>;
-using TileN128 = Tile<128, 128, 4, 32, 2>;
-using TileG128 = Tile<128, 128, 3, 64, 1>;
+// on 32-wide K stages.  The 256- and 320-row tiles spread each stage's DMA
+// over the MFMAs of the first two k steps (measured faster there; neutral to
+// slower on the 128- and 192-row ones).
+using TileW320 = Tile<320, 192, 2, 64, 1, 2>;
+using TileN320 = Tile<320, 128, 2, 64, 1, 2>;
+using TileW256 = Tile<256, 256, 2, 64, 1, 2>;
+using TileN256 = Tile<256, 128, 3, 64, 1, 2>;
+using TileG256 = Tile<256, 128, 2, 64, 1, 2>;
+using TileW192 = Tile<192, 256, 2, 64, 1, 0>;
+using TileN192 = Tile<192, 128, 3, 64, 1, 0>;
+using TileW128 = Tile<128, 256, 3, 64, 1, 0>;
+using TileN128 = Tile<128, 128, 4, 32, 2, 0>;
+using TileG128 = Tile<128, 128, 3, 64, 1, 0>;
 
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s) {
