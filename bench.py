@@ -42,6 +42,16 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 METRIC = "MoE-layer fwd tokens/s (1 GPU) + grouped-GEMM MFMA % of peak + permute GB/s"
 
 
+def fused_forward(cfg: dict) -> tuple[bool, bool]:
+    """(gather, scatter): what the library's forward fuses for this workload.
+
+    bf16 with tokens: the first GEMM gathers the token rows of x (no dispatch
+    copy); with k = 1 also the second GEMM writes gated rows to y (no combine
+    pass).  Mirrors the choice in moe_forward."""
+    gather = cfg["dtype"] == "bf16" and cfg["T"] > 0
+    return gather, gather and cfg["k"] == 1
+
+
 def stage_work(cfg: dict, A: int) -> dict:
     """Algorithmic bytes and flops of each stage for one forward.
 
@@ -49,30 +59,38 @@ def stage_work(cfg: dict, A: int) -> dict:
     activations each stage must read or write, no padding, no re-reads.
       router   x [T,d] + W_r [E,d] fp32 read, expert_idx + gate [T,k] written;
                flops 2 T d E (fp32)
-      dispatch 2 A d s (x rows read, xbuf rows written) + T k (4 + 4 + 1)
-               (indices read, slots and drop flags written)
+      dispatch T k (4 + 4 + 1) (indices read, slots and drop flags written)
+               + 2 A d s (x rows read, xbuf rows written), or, fused,
+               + 4 A (row index written) [+ (T - A) d s, dropped rows of y cleared]
       gemm1    W1 (+W3) [E,f,d] + A d s read + A f s written;
                flops 2 A d f (x2 for SwiGLU)
       gemm2    W2 [E,d,f] + A f s read + A d s written; flops 2 A f d
-      combine  A d s read + T d s written + T k 12 (indices, slots, gates)
+               [fused: + 8 A, the row's token and gate]
+      combine  A d s read + T d s written + T k 12 (indices, slots, gates);
+               nothing when the second GEMM wrote y
     """
     T, d, f, E, k = cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"]
     s = 2 if cfg["dtype"] == "bf16" else 4
     m = 2 if cfg["act"] == "swiglu" else 1
+    gather, scatter = fused_forward(cfg)
+    disp = T * k * 9 + (4 * A + (T - A) * d * s * scatter if gather else 2 * A * d * s)
     return {
         "router": dict(bytes=T * d * s + E * d * 4 + T * k * 8, flops=2 * T * d * E, dtype="f32"),
-        "dispatch": dict(bytes=2 * A * d * s + T * k * 9, flops=0, dtype=cfg["dtype"]),
+        "dispatch": dict(bytes=disp, flops=0, dtype=cfg["dtype"]),
         "expert_gemm1": dict(bytes=m * E * f * d * s + A * d * s + A * f * s, flops=2 * m * A * d * f,
                              dtype=cfg["dtype"]),
-        "expert_gemm2": dict(bytes=E * d * f * s + A * f * s + A * d * s, flops=2 * A * f * d,
-                             dtype=cfg["dtype"]),
-        "combine": dict(bytes=A * d * s + T * d * s + T * k * 12, flops=0, dtype=cfg["dtype"]),
+        "expert_gemm2": dict(bytes=E * d * f * s + A * f * s + A * d * s + 8 * A * scatter,
+                             flops=2 * A * f * d, dtype=cfg["dtype"]),
+        "combine": dict(bytes=0 if scatter else A * d * s + T * d * s + T * k * 12, flops=0,
+                        dtype=cfg["dtype"]),
     }
 
 
 def roofline_of(work: dict, seconds: float) -> dict:
     """Which roofline bounds a stage, and the achieved rate against that peak."""
     peak_f = PEAK_TFLOPS[work["dtype"]]
+    if work["bytes"] == 0 and work["flops"] == 0:
+        return dict(bound="none", achieved=None, peak=None, unit=None, frac=None)
     t_mem = work["bytes"] / (PEAK_HBM_GBS * 1e9)
     t_flop = work["flops"] / (peak_f * 1e12) if work["flops"] else 0.0
     if t_flop > t_mem:
@@ -131,7 +149,7 @@ def kernel_stage(name: str) -> str:
     """The forward stage a kernel belongs to, from its (demangled) name."""
     if "router" in name:
         return "router"
-    if any(t in name for t in ("slot_rank", "slot_scan", "permute_kernel", "tile_map")):
+    if any(t in name for t in ("slot_rank", "slot_scan", "slot_index", "permute_kernel", "tile_map")):
         return "dispatch"
     m = _GEMM_ACT.search(name)
     if m:
@@ -237,6 +255,11 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def create(self, n):
         out = []
@@ -353,10 +376,16 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # the stage breakdown: the same steps again through moe_forward_staged,
+    # which records a HIP event at every stage boundary (the events cost
+    # time of their own, so the timed steps above run without them)
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
 
     stage_ms = {name: 0.0 for name in L.STAGES}
     for i in range(args.steps):
@@ -368,6 +397,20 @@ def main(argv=None):
     A = int(plan.intermediate("expert_count").sum().item())
     drops = int(plan.drop_mask.sum().item())
     work = stage_work(cfg, A)
+    # the standalone dispatch (slots + permutation into xbuf), timed on its
+    # own outside the steps: the forward itself gathers rows inside the first
+    # GEMM when it can, so it has no permutation to time
+    n_disp = 10
+    disp_ev = hip.create(2)
+    moe.dispatch(x, plan.expert_idx, cfg["E"], plan.C)
+    hip.record(disp_ev[0], stream.cuda_stream)
+    for _ in range(n_disp):
+        moe.dispatch(x, plan.expert_idx, cfg["E"], plan.C)
+    hip.record(disp_ev[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    disp_s = hip.elapsed_ms(disp_ev[0], disp_ev[1]) / n_disp / 1e3
+    hip.destroy(disp_ev)
+    disp_bytes = 2 * A * cfg["d"] * (2 if cfg["dtype"] == "bf16" else 4) + cfg["T"] * cfg["k"] * 9
     stages = {}
     for name in L.STAGES:
         r = roofline_of(work[name], stage_ms[name] / 1e3)
@@ -403,7 +446,8 @@ def main(argv=None):
                    "capacity": plan.C, "act": cfg["act"], "router": "fp32",
                    "kept_assignments": A, "dropped": drops},
         "grouped_gemm_mfma_pct": round(100.0 * ffn_flops / ffn_s / 1e12 / peak, 2),
-        "permute_GBps": round(work["dispatch"]["bytes"] / (stage_ms["dispatch"] / 1e3) / 1e9, 1),
+        "permute_GBps": round(disp_bytes / disp_s / 1e9, 1),
+        "permute_us": round(disp_s * 1e6, 2),
         "stages": stages,
         "roofline": roofline,
     }

@@ -87,11 +87,16 @@ size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t
  * Where moe_forward keeps its intermediates inside `ws` (byte offsets), so
  * a caller can read them after the call: slot [T,k] int32, expert_count [E]
  * int32, route_count [E] int32, prob_sum [E] fp32, the dispatch buffer
- * xbuf [E,C,d] and the expert outputs ybuf [E,C,d] (storage dtype).
+ * xbuf [E,C,d] and the expert outputs ybuf [E,C,d] (storage dtype), and
+ * row_tok [E,C] int32 (the token of each kept expert row).
+ * With bf16 and T, C > 0 the forward does not write xbuf (the first expert
+ * GEMM reads the token rows of x through row_tok); with bf16, T, C > 0 and
+ * k = 1 it does not write ybuf either (the second GEMM writes each gated row
+ * straight to y).  The f32 forward writes xbuf and ybuf, not row_tok.
  * Returns MOE_OK or MOE_ERR_INVALID_ARGUMENT.  Host function.
  */
 typedef struct {
-    size_t slot, expert_count, route_count, prob_sum, xbuf, ybuf, total;
+    size_t slot, expert_count, route_count, prob_sum, xbuf, ybuf, row_tok, total;
 } moe_ws_layout;
 moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32_t E,
                                         int32_t k, int64_t C, moe_dtype dt, moe_act act,
@@ -183,6 +188,11 @@ moe_status moe_combine(const void *ybuf, moe_dtype dt, const int32_t *expert_idx
  * y [T,d] (storage dtype, MoE branch only), aux_loss [1] fp32,
  * expert_idx [T,k] int32, gate [T,k] fp32, drop_mask [T,k] uint8; every
  * other intermediate stays in `ws` (see moe_forward_workspace_layout).
+ * The results are those of moe_router, moe_dispatch, moe_expert_ffn and
+ * moe_combine called in turn, bit for bit; with bf16 the forward fuses the
+ * dispatch copy into the first expert GEMM (it reads the token rows of x
+ * directly) and, with k = 1, the combine into the second (each expert row is
+ * scaled by its gate and written to its token's row of y).
  */
 moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                        const void *W1, const void *b1, const void *W3, const void *W2,
@@ -197,9 +207,11 @@ moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const floa
  * stages of the layer ([CS25-L5] "Capacity Factor" asks that dispatch
  * traffic and step time be logged alongside the routing statistics).
  * stage_events [MOE_STAGE_EVENTS] host array of caller-created events:
- *   [0] start  [1] after router  [2] after dispatch (slots, permutation,
- *   GEMM tile map)  [3] after expert GEMM 1 (+activation)  [4] after expert
- *   GEMM 2  [5] after combine and loss.
+ *   [0] start  [1] after router  [2] after dispatch (slots, permutation or
+ *   row index, GEMM tile map)  [3] after expert GEMM 1 (+activation)  [4]
+ *   after expert GEMM 2 (+gated scatter to y when fused)  [5] after combine
+ *   and loss (nothing is enqueued between [4] and [5] when the second GEMM
+ *   wrote y).
  * NULL array or NULL entries -> MOE_ERR_INVALID_ARGUMENT, nothing enqueued.
  */
 #define MOE_STAGE_EVENTS 6

@@ -32,7 +32,7 @@ _sz = C.c_size_t
 
 class WsLayout(C.Structure):
     _fields_ = [("slot", _sz), ("expert_count", _sz), ("route_count", _sz),
-                ("prob_sum", _sz), ("xbuf", _sz), ("ybuf", _sz), ("total", _sz)]
+                ("prob_sum", _sz), ("xbuf", _sz), ("ybuf", _sz), ("row_tok", _sz), ("total", _sz)]
 
 
 # name -> (restype, argtypes); mirrors include/moe.h

@@ -189,6 +189,7 @@ class ForwardPlan:
             "prob_sum": (lay.prob_sum, (E,), torch.float32, 4),
             "xbuf": (lay.xbuf, (E, C, d), self.dtype, es),
             "ybuf": (lay.ybuf, (E, C, d), self.dtype, es),
+            "row_tok": (lay.row_tok, (E, C), torch.int32, 4),
         }[name]
         off, shape, dt, sz = spec
         n = 1

@@ -28,13 +28,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int wave = threadIdx.x >> 6;
 
     if (blockIdx.x == 0 && wave == 0) {
-        double s = 0.0;
-        for (int e = lane; e < E; e += 64) s += (double)route_count[e] * (double)prob_sum[e];
-        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-        if (lane == 0) {
-            const double Td = (double)T;
-            aux[0] = (T > 0) ? (float)((double)alpha * (double)E * s / ((double)k * Td * Td)) : 0.0f;
-        }
+        const float a = aux_loss_wave<false>(route_count, prob_sum, E, T, k, alpha, lane);
+        if (lane == 0) aux[0] = a;
     }
 
     const int pieces = d / EPP;

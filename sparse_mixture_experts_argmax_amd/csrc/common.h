@@ -32,6 +32,32 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// Auxiliary load-balancing loss alpha * E * sum_i f_i P_i with
+// f_i = route_count_i / (k T) and P_i = prob_sum_i / T ([SW-GLaM] "负载均衡"),
+// in fp64 by one whole wave in a fixed order (lane l sums experts l, l + 64,
+// ..., then a butterfly), so every caller gets the same bits.  COHERENT reads
+// totals that other blocks of the running kernel wrote.
+template <bool COHERENT>
+__device__ __forceinline__ float aux_loss_wave(const int32_t *route_count, const float *prob_sum, int E,
+                                               int64_t T, int k, float alpha, int lane) {
+    double s = 0.0;
+    for (int e = lane; e < E; e += 64) {
+        int32_t rc;
+        float ps;
+        if (COHERENT) {
+            rc = __hip_atomic_load(route_count + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ps = __hip_atomic_load(prob_sum + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            rc = route_count[e];
+            ps = prob_sum[e];
+        }
+        s += (double)rc * (double)ps;
+    }
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    const double Td = (double)T;
+    return (T > 0) ? (float)((double)alpha * (double)E * s / ((double)k * Td * Td)) : 0.0f;
+}
+
 #define MOE_LDS_AS __attribute__((address_space(3)))
 #define MOE_GLB_AS __attribute__((address_space(1)))
 

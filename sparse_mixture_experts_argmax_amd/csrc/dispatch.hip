@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hi
                                                         float *__restrict__ prob_sum,
                                                         int32_t *__restrict__ route_count,
                                                         int32_t *__restrict__ tile_map, int bm,
-                                                        unsigned *__restrict__ done) {
+                                                        unsigned *__restrict__ done, float alpha,
+                                                        int64_t T, int k, float *__restrict__ aux) {
     __shared__ int s_last;
     __shared__ int s_wsum[4];
     const int lane = threadIdx.x & 63;
@@ -149,6 +150,10 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hi
         run += c[q];
     }
     if (E - 1 >= 4 * t && E - 1 < 4 * t + 4) tile_map[E] = run;
+    if (aux != nullptr && wave == 0) {
+        const float a = aux_loss_wave<true>(route_count, prob_sum, E, T, k, alpha, lane);
+        if (lane == 0) aux[0] = a;
+    }
 }
 
 // One wave per (token, rank) choice; lanes move 16-byte pieces of the row.
@@ -182,6 +187,53 @@ __global__ __launch_bounds__(256) void permute_kernel(
     }
 }
 
+// The fused forward's dispatch: slots and drops exactly as permute_kernel
+// computes them, one choice per thread, but no row is copied: each kept
+// choice records the token of its expert row (row_tok[e C + slot] = t), from
+// which the first expert GEMM gathers x.  With one choice per token, y_zero
+// (= y) gets the rows of dropped tokens cleared, since the second GEMM then
+// writes only kept rows; the wave clears each such row together.
+__global__ __launch_bounds__(256) void slot_index_kernel(
+    const int32_t *__restrict__ expert_idx, const int32_t *__restrict__ rank,
+    const int32_t *__restrict__ base, int64_t T, int E, int k, int nblk, int64_t C,
+    int32_t *__restrict__ slot, uint8_t *__restrict__ drop, int32_t *__restrict__ row_tok,
+    const float *__restrict__ gate, float *__restrict__ row_gate, uint8_t *__restrict__ y_zero,
+    int row_bytes) {
+    const int lane = threadIdx.x & 63;
+    const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    bool dropped = false;
+    if (a < T * k) {
+        const int64_t t = a / k;
+        const int j = (int)(a - t * k);
+        const int e = expert_idx[a];
+        int64_t s = -1;
+        if (e >= 0 && e < E) {
+            const int blk = (int)(t / DISPATCH_TOK_BLOCK);
+            s = (int64_t)base[(int64_t)e * k * nblk + (int64_t)j * nblk + blk] + rank[(int64_t)j * T + t];
+            if (s >= C) s = -1;
+        }
+        slot[a] = (int32_t)s;
+        drop[a] = (s < 0) ? 1 : 0;
+        if (s >= 0) {
+            row_tok[(int64_t)e * C + s] = (int32_t)t;
+            if (row_gate != nullptr) row_gate[(int64_t)e * C + s] = gate[a];
+        }
+        dropped = s < 0;
+    }
+    if (y_zero != nullptr) {
+        // k = 1: choice a is token a
+        uint64_t m = __ballot(dropped);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const int pieces = row_bytes >> 4;
+        while (m != 0) {
+            const int l = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            const int64_t t = a - lane + l;
+            for (int p = lane; p < pieces; p += 64) st16(y_zero + t * row_bytes + p * 16, z);
+        }
+    }
+}
+
 int bits_for(int E) {
     int b = 0;
     while ((1 << b) < E) ++b;
@@ -203,9 +255,22 @@ hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, 
 hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
                             int32_t *expert_count, const float *part_prob, int nblk_r,
                             float *prob_sum, int32_t *route_count, int32_t *tile_map, int bm,
-                            unsigned *done, hipStream_t s) {
+                            unsigned *done, hipStream_t s, int64_t T, float alpha, float *aux) {
     hipLaunchKernelGGL(slot_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, s, hist, nblk * k, E, C,
-                       expert_count, part_prob, nblk_r, prob_sum, route_count, tile_map, bm, done);
+                       expert_count, part_prob, nblk_r, prob_sum, route_count, tile_map, bm, done,
+                       alpha, T, k, aux);
+    return hipGetLastError();
+}
+
+hipError_t launch_slot_index(const int32_t *expert_idx, const int32_t *rank, const int32_t *base,
+                             int64_t T, int E, int k, int64_t C, int32_t *slot, uint8_t *drop_mask,
+                             int32_t *row_tok, const float *gate, float *row_gate, void *y_zero,
+                             int row_bytes, hipStream_t s) {
+    const int64_t n = T * k;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(slot_index_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, expert_idx,
+                       rank, base, T, E, k, dispatch_blocks(T), C, slot, drop_mask, row_tok, gate,
+                       row_gate, reinterpret_cast<uint8_t *>(y_zero), row_bytes);
     return hipGetLastError();
 }
 

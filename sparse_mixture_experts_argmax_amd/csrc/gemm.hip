@@ -77,6 +77,12 @@ __device__ __forceinline__ float silu_fast(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + ex);
 }
 
+// Two bf16 values times a gate, rounded back to bf16: the combine step's
+// arithmetic for one kept choice (fp32 fma onto zero, one rounding).
+__device__ __forceinline__ uint32_t scale_bf16x2(uint32_t p, float g) {
+    return pack_bf16x2(fmaf(g, bf2f((uint16_t)(p & 0xFFFFu)), 0.f), fmaf(g, bf2f((uint16_t)(p >> 16)), 0.f));
+}
+
 // Tile shape: block BM x BN (BN = output columns; the gated form also stages
 // the matching BN rows of the second weight), K step 64, an S-deep ring of
 // LDS stages filled by 16-byte DMA (global_load_lds).  4 waves in a 2 x 2
@@ -124,6 +130,18 @@ __device__ __forceinline__ void dma16(const uint16_t *src, uint8_t *dst) {
         __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)src, (MOE_LDS_AS void *)dst, 16, 0, 0);
 }
 
+// The fused forward's extras (mode 0: none): mode 1 gathers the A rows of
+// expert e straight from x (row m of the expert is token row_tok[e C + m]);
+// mode 2 scales output row m by row_gate[e C + m] (its token's gate) and
+// writes it to row row_tok[e C + m] of y (one expert choice per token).
+struct FuseArgs {
+    const int32_t *row_tok;
+    int64_t T;
+    const float *gate;                                   // row_gate [E, C]
+    uint16_t *y;
+    int mode;
+};
+
 // The state of one block's tile shared by the prologue and the K loop: the LDS
 // ring and the per-lane DMA sources.  A rows go to LDS in groups of RPI rows
 // (one 1 KB DMA instruction); group 4 i + w belongs to instruction i of wave
@@ -141,7 +159,15 @@ struct TileCtx {
     static constexpr int STAGE = A_BYTES + NBT * B_BYTES;
     static constexpr int RPI = 1024 / ROWB;                        // LDS rows per DMA instruction
     uint8_t *st0, *st1, *st2, *st3;
-    const uint16_t *Ae;                                            // the expert's rows of A
+    const uint16_t *Ae;                                            // the expert's rows of A (or all of x)
+    // fused forward: row m of the expert is token rtok[m] (its A row is row
+    // rtok[m] of x when gathering; its output goes to row rtok[m] of y,
+    // times gate[m] (that token's gate), when scattering)
+    const int32_t *rtok;
+    const float *gate;
+    uint16_t *y;
+    int64_t T, arows;                                              // tokens; rows A may index
+    bool gather, scatter;
     const uint16_t *asrc[AI];
     const uint16_t *bsrc[BI];
     int64_t b3off;
@@ -172,14 +198,34 @@ struct TileCtx {
         tailB[1] = (nk - 1) * BK + lcB[1] * 8 >= K;
     }
 
-    // A sources for tile rows m0 + row, the row clamped to last (rows past
-    // the count are computed but never stored)
+    // A sources of the first NA instructions: tile rows m0 + row, the row
+    // clamped to last (rows past the count are computed but never stored).
+    // Gathering, the row's token comes from rtok; an entry past the count
+    // may hold anything, so the token is clamped into [0, T).
+    template <int NA>
     __device__ __forceinline__ void set_a(int last) {
 #pragma unroll
-        for (int i = 0; i < AI; ++i) {
+        for (int i = 0; i < NA; ++i) {
             int am = m0 + (4 * i + wave) * RPI + lr;
             am = am < last ? am : last;
             asrc[i] = Ae + (int64_t)am * K + lcA * 8;
+        }
+    }
+    // gathering: the tokens of the rows the A instructions cover (rows past
+    // last repeat row last), loaded first so that their latency overlaps the
+    // weight DMA issued next; set_a_tok then points the A sources at them
+    __device__ __forceinline__ void load_tok(int last, int32_t (&tok)[AI]) const {
+#pragma unroll
+        for (int i = 0; i < AI; ++i) {
+            int am = m0 + (4 * i + wave) * RPI + lr;
+            tok[i] = rtok[am < last ? am : last];
+        }
+    }
+    __device__ __forceinline__ void set_a_tok(const int32_t (&tok)[AI]) {
+#pragma unroll
+        for (int i = 0; i < AI; ++i) {
+            const int64_t t = (uint32_t)tok[i];
+            asrc[i] = Ae + (t < arows ? t : arows - 1) * K + lcA * 8;
         }
     }
     // K offset (elements) of K tile kt for A and for B group j: the pieces
@@ -199,13 +245,22 @@ struct TileCtx {
 // position l % PIECES, which holds logical piece (l % PIECES) ^ swz(row).  The
 // pieces past K (K % BK != 0) of the last K tile are read from column 0 and
 // cleared in LDS once they have landed.
-template <int NA, bool KTAIL, class CTX>
+// PARTS: 1 = the A instructions, 2 = the weight instructions, 3 = both
+// (a stage's instructions must still go out back to back: the waits count
+// the instructions issued after a stage's own).
+template <int NA, bool KTAIL, class CTX, int PARTS = 3>
 __device__ __forceinline__ void tile_issue(const CTX &c, uint8_t *base, int kt) {
     const int ka = c.template ka<KTAIL>(kt);
+    if (PARTS & 1) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-        __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[i] + ka),
-                                         (MOE_LDS_AS void *)(base + (4 * i + c.wave) * 1024), 16, 0, 0);
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[i] + ka),
+                                             (MOE_LDS_AS void *)(base + (4 * i + c.wave) * 1024), 16, 0, 0);
+    }
+    if (!(PARTS & 2)) {
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < CTX::BI; ++j)
         dma16<CTX::WAUX>(c.bsrc[j] + c.template kb<KTAIL>(kt, j), base + CTX::A_BYTES + (c.wave * CTX::BI + j) * 1024);
@@ -227,7 +282,7 @@ __device__ __forceinline__ void tile_issue(const CTX &c, uint8_t *base, int kt) 
 // caller has issued K tiles 0 .. S - 2 with every A instruction.
 template <class TL, int FV, int ACT, bool BIAS, bool KTAIL, class X>
 __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bias_e, int cnt, int n0, int N,
-                                          uint16_t *__restrict__ oe) {
+                                          uint16_t *__restrict__ oe, int *s_tok, float *s_g) {
     constexpr int BN = TL::BN, S = TL::S, ROWB = TL::ROWB, KS = TL::KS, FN = TL::FN, BI = TL::BI;
     constexpr bool DUAL = X::DUAL;
     constexpr int NBT = X::NBT, A_BYTES = X::A_BYTES, B_BYTES = X::B_BYTES;
@@ -245,7 +300,24 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     const int lane = c.lane, wave = c.wave, nk = c.nk;
     const int wm = wave >> 1, wn = wave & 1;
     uint8_t *const st0 = c.st0, *const st1 = c.st1, *const st2 = c.st2, *const st3 = c.st3;
-    c.set_a(cnt - 1);
+    // A sources of the data rows, clamped to the expert's last row (rows past
+    // the count are computed but never stored); gathering keeps the prologue's
+    // sources, whose rows past the count hold valid tokens too
+    if (!c.gather) c.template set_a<NA>(cnt - 1);
+    // scattering: each thread fetches the token and gate of up to two stored
+    // rows now; they land during the K loop and go to LDS in the epilogue
+    int ptok[2] = {0, 0};
+    float pgate[2] = {0.f, 0.f};
+    if (c.scatter) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = threadIdx.x + 256 * h;
+            if (r < ROWS && c.m0 + r < cnt) {
+                ptok[h] = c.rtok[c.m0 + r];
+                pgate[h] = c.gate[c.m0 + r];
+            }
+        }
+    }
 
     auto issue = [&](uint8_t *base, int kt) { tile_issue<NA, KTAIL>(c, base, kt); };
     auto clear_tail = [&](uint8_t *base) {
@@ -445,9 +517,23 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     // a store phase fall in distinct 16-byte bank groups (rows of 384 bytes
     // alternate between the two 128-byte halves of a 256-byte bank line)
     auto esw = [](int r) { return (P & (P - 1)) == 0 ? (r & (P - 1)) : ((r >> 1) & 7); };
-    if (STAGED_OUT) lds_barrier();                       // every wave is past its last fragment read
-    uint8_t *so = wm ? st1 : st0;
     const int m0 = c.m0;
+    // scattering: the token and gate of every stored row, staged once
+    const bool scatter = c.scatter;
+    if (scatter) {
+        static_assert(ROWS <= 512, "two rows per thread");
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = threadIdx.x + 256 * h;
+            if (r < ROWS) {
+                const int64_t tt = (uint32_t)ptok[h];
+                s_tok[r] = (int)(tt < c.T ? tt : c.T - 1);
+                s_g[r] = pgate[h];
+            }
+        }
+    }
+    if (STAGED_OUT || scatter) lds_barrier();            // every wave is past its last fragment read
+    uint8_t *so = wm ? st1 : st0;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -482,9 +568,19 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
                     const int pc = (nl >> 3) ^ esw(r);
                     *reinterpret_cast<uint2 *>(so + r * (BN * 2) + (pc << 4) + ((nl & 4) << 1)) = pk;
                 } else {
-                    const int m = m0 + 64 * i + 32 * wm + (lane & 31);
+                    const int rr = 64 * i + 32 * wm + (lane & 31);
+                    const int m = m0 + rr;
                     const int n = n0 + nl;
-                    if (m < cnt && n < N) *reinterpret_cast<uint2 *>(oe + (int64_t)m * N + n) = pk;
+                    if (m < cnt && n < N) {
+                        if (scatter) {
+                            const float gg = s_g[rr];
+                            pk.x = scale_bf16x2(pk.x, gg);
+                            pk.y = scale_bf16x2(pk.y, gg);
+                            *reinterpret_cast<uint2 *>(c.y + (int64_t)s_tok[rr] * N + n) = pk;
+                        } else {
+                            *reinterpret_cast<uint2 *>(oe + (int64_t)m * N + n) = pk;
+                        }
+                    }
                 }
             }
         }
@@ -501,7 +597,17 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
             const uint8_t *src = (((Rw >> 5) & 1) ? st1 : st0) + r * (BN * 2) + ((p ^ esw(r)) << 4);
             const int m = m0 + Rw;
             const int n = n0 + p * 8;
-            if (m < cnt && n < N) st16(oe + (int64_t)m * N + n, *reinterpret_cast<const u32x4 *>(src));
+            if (m < cnt && n < N) {
+                u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                if (scatter) {
+                    const float gg = s_g[Rw];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = scale_bf16x2(v[q], gg);
+                    st16(c.y + (int64_t)s_tok[Rw] * N + n, v);
+                } else {
+                    st16(oe + (int64_t)m * N + n, v);
+                }
+            }
         }
     }
 }
@@ -516,7 +622,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ B3,
     const uint16_t *__restrict__ bias, const int32_t *__restrict__ count,
     const int32_t *__restrict__ tile_map, int E, int64_t C, int N, int K, int tiles_n,
-    uint16_t *__restrict__ out) {
+    uint16_t *__restrict__ out, FuseArgs fz) {
     using X = TileCtx<TL, ACT, WNT>;
     constexpr int BM = TL::BM, BN = TL::BN, S = TL::S, FM = TL::FM;
     constexpr int STAGE = X::STAGE;
@@ -527,6 +633,8 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
     __shared__ int s_map[EXPERT ? 1 : MAX_E_LDS + 1];
+    __shared__ int s_tok[BM];                            // scattering: token and gate of each row
+    __shared__ float s_g[BM];
 
     int e, mt, nt;
     if (EXPERT) {
@@ -550,7 +658,14 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     c.set_lanes(threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), K);
     c.m0 = mt * BM;
     c.b3off = X::DUAL ? (int64_t)(B3 - B) : 0;
-    c.Ae = A + (int64_t)e * C * K;
+    c.gather = fz.mode == 1;
+    c.scatter = fz.mode == 2;
+    c.rtok = fz.row_tok != nullptr ? fz.row_tok + (int64_t)e * C : nullptr;
+    c.T = fz.T;
+    c.arows = c.gather ? fz.T : C;                       // bound of the A row index
+    c.gate = fz.gate != nullptr ? fz.gate + (int64_t)e * C : nullptr;
+    c.y = fz.y;
+    c.Ae = c.gather ? A : A + (int64_t)e * C * K;
     const int n0 = nt * BN;
     {
         const uint16_t *Be = B + (int64_t)e * N * K;
@@ -567,8 +682,25 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     // conditional DMA here makes the compiler give up tracking which stage a
     // pending DMA writes, and then it drains the whole ring before every
     // fragment read.
-    c.set_a((int)C - 1);
-    tile_issue<TL::AI, KTAIL>(c, st0, 0);
+    // The A rows: gathering, the row tokens are loaded first and stage 0's
+    // weight DMA goes out while they land; otherwise the row indices
+    // themselves (the DMA is issued the same way on both paths, with no
+    // branch around it: a conditional DMA costs the ring its lookahead).
+    {
+        int32_t tok[TL::AI];
+        if (c.gather) {
+            c.load_tok((int)C - 1, tok);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TL::AI; ++i) {
+                const int am = c.m0 + (4 * i + c.wave) * X::RPI + c.lr;
+                tok[i] = am < (int)C - 1 ? am : (int)C - 1;
+            }
+        }
+        tile_issue<TL::AI, KTAIL, X, 2>(c, st0, 0);
+        c.set_a_tok(tok);
+        tile_issue<TL::AI, KTAIL, X, 1>(c, st0, 0);
+    }
     if (S > 2) tile_issue<TL::AI, KTAIL>(c, st1, c.nk > 1 ? 1 : c.nk - 1);
     if (S > 3) tile_issue<TL::AI, KTAIL>(c, st2, c.nk > 2 ? 2 : c.nk - 1);
 
@@ -581,11 +713,11 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     const int fv = rows >= BM ? FM : (rows + 63) >> 6;
     const uint16_t *bias_e = BIAS ? bias + (int64_t)e * N : nullptr;
     uint16_t *oe = out + (int64_t)e * C * N;
-    if constexpr (FM >= 5) if (fv == 5) { tile_body<TL, 5, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
-    if constexpr (FM >= 4) if (fv == 4) { tile_body<TL, 4, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
-    if constexpr (FM >= 3) if (fv == 3) { tile_body<TL, 3, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
-    if (fv == 2) { tile_body<TL, 2, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe); return; }
-    tile_body<TL, 1, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe);
+    if constexpr (FM >= 5) if (fv == 5) { tile_body<TL, 5, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe, s_tok, s_g); return; }
+    if constexpr (FM >= 4) if (fv == 4) { tile_body<TL, 4, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe, s_tok, s_g); return; }
+    if constexpr (FM >= 3) if (fv == 3) { tile_body<TL, 3, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe, s_tok, s_g); return; }
+    if (fv == 2) { tile_body<TL, 2, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe, s_tok, s_g); return; }
+    tile_body<TL, 1, ACT, BIAS, KTAIL>(c, bias_e, cnt, n0, N, oe, s_tok, s_g);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,9 +865,15 @@ hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *
 hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, const void *bias,
                                int dtype_bf16, int act, const int32_t *expert_count,
                                const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
-                               int64_t rows_bound, void *out, hipStream_t s) {
+                               int64_t rows_bound, void *out, hipStream_t s, const int32_t *row_tok,
+                               int64_t T, const float *gate) {
     if (C == 0 || rows_bound == 0) return hipSuccess;
+    if (row_tok != nullptr && (!dtype_bf16 || T < 1 || (act == 0 && gate == nullptr)))
+        return hipErrorInvalidValue;
     if (dtype_bf16) {
+        // fused forward: the first GEMM gathers token rows, the second
+        // scatters gated rows to y (out is then y)
+        FuseArgs fz{row_tok, T, gate, (uint16_t *)out, row_tok == nullptr ? 0 : (act == 0 ? 2 : 1)};
         // the gated tiles exist for 128 and 256 rows only
         if ((bm != 128 && bm != 192 && bm != 256 && bm != 320) || (act == 2 && bm != 128 && bm != 256))
             return hipErrorInvalidValue;
@@ -757,7 +895,7 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
         const bool wnt = expert && rows_bound * (int64_t)K * 2 <= (int64_t(128) << 20);
 #define MOE_GEMM_L(TL, ACTV, BIASV, KT, EXP, NT)                                                    \
     hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACTV, BIASV, KT, EXP, NT>), grid, dim3(256), 0, s, a, b, b3,  \
-                       bi, expert_count, tile_map, E, C, N, K, tiles_n, o)
+                       bi, expert_count, tile_map, E, C, N, K, tiles_n, o, fz)
 #define MOE_GEMM_K(TL, ACTV, BIASV, EXP)                                                            \
     do {                                                                                            \
         if (!(EXP)) {                                                                               \

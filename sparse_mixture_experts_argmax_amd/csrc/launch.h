@@ -29,10 +29,21 @@ hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, 
 // would, bit for bit).  tile_map may be null; when given, the last block
 // also writes the GEMM tile map for row tiles of bm (what launch_tile_map
 // would), using the completion counter done that launch_slot_rank zeroed.
+// aux (may be null; needs tile_map): the last block also writes the
+// auxiliary loss from the totals it finished (what launch_combine would).
 hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
                             int32_t *expert_count, const float *part_prob, int nblk_r,
                             float *prob_sum, int32_t *route_count, int32_t *tile_map, int bm,
-                            unsigned *done, hipStream_t s);
+                            unsigned *done, hipStream_t s, int64_t T = 0, float alpha = 0.f,
+                            float *aux = nullptr);
+// Slots and drops as launch_permute, but rows are not copied: row_tok[e C +
+// slot] = token for every kept choice.  k = 1 only (both may be null):
+// row_gate[e C + slot] = gate of that choice, and y_zero gets the rows
+// (row_bytes each) of dropped tokens cleared.
+hipError_t launch_slot_index(const int32_t *expert_idx, const int32_t *rank, const int32_t *base,
+                             int64_t T, int E, int k, int64_t C, int32_t *slot, uint8_t *drop_mask,
+                             int32_t *row_tok, const float *gate, float *row_gate, void *y_zero,
+                             int row_bytes, hipStream_t s);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,
@@ -49,10 +60,16 @@ hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *
 // act: 0 none, 1 relu, 2 swiglu (silu(A.B^T) * (A.B3^T)).
 // tile_map was built for row tiles of bm = gemm_bm(dtype, C, act of the first GEMM).
 // rows_bound: an upper bound of sum_e count[e] (sizes the grid).
+// row_tok [E, C] (bf16 only; null = off): row m of expert e is token
+// row_tok[e C + m].  With act != 0, A is x [T, K] and the expert rows are
+// gathered from it; with act == 0, out is y [T, N] and each output row goes
+// to its token's row scaled by row_gate[e C + m] (one choice per token).
 hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, const void *bias,
                                int dtype_bf16, int act, const int32_t *expert_count,
                                const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
-                               int64_t rows_bound, void *out, hipStream_t s);
+                               int64_t rows_bound, void *out, hipStream_t s,
+                               const int32_t *row_tok = nullptr, int64_t T = 0,
+                               const float *row_gate = nullptr);
 
 // ---- combine ----------------------------------------------------------
 hipError_t launch_combine(const void *ybuf, int dtype_bf16, const int32_t *expert_idx,

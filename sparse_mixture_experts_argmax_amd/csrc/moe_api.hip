@@ -63,7 +63,8 @@ struct ForwardWs {
     RouterWs r;
     DispatchWs dsp;
     FfnWs f;
-    size_t router, prob_sum, route_count, dispatch, expert_count, slot, xbuf, ffn, ybuf, total;
+    size_t router, prob_sum, route_count, dispatch, expert_count, slot, xbuf, ffn, ybuf, row_tok,
+        row_gate, total;
 };
 ForwardWs forward_ws(int64_t T, int d, int dff, int E, int k, int64_t C, moe_dtype dt) {
     ForwardWs w;
@@ -80,6 +81,8 @@ ForwardWs forward_ws(int64_t T, int d, int dff, int E, int k, int64_t C, moe_dty
     w.xbuf = o;          o += up((size_t)E * C * d * esize(dt));
     w.ffn = o;           o += w.f.total;
     w.ybuf = o;          o += up((size_t)E * C * d * esize(dt));
+    w.row_tok = o;       o += up((size_t)E * C * 4);
+    w.row_gate = o;      o += up((size_t)E * C * 4);
     w.total = o;
     return w;
 }
@@ -155,16 +158,23 @@ moe_status run_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, 
                         uint8_t *drop_mask, int32_t *expert_count, void *xbuf, char *ws,
                         hipStream_t stream, const float *part_prob = nullptr, int nblk_r = 0,
                         float *prob_sum = nullptr, int32_t *route_count = nullptr,
-                        int32_t *tile_map = nullptr, int bm = 0) {
+                        int32_t *tile_map = nullptr, int bm = 0, int32_t *row_tok = nullptr,
+                        void *y_zero = nullptr, float alpha = 0.f, float *aux = nullptr,
+                        const float *gate = nullptr, float *row_gate = nullptr) {
     const DispatchWs w = dispatch_ws(T, E, k);
     int32_t *rank = reinterpret_cast<int32_t *>(ws + w.rank);
     int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
     unsigned *done = reinterpret_cast<unsigned *>(ws + w.done);
     MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, tile_map ? done : nullptr, stream));
     MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, C, expert_count, part_prob,
-                                  nblk_r, prob_sum, route_count, tile_map, bm, done, stream));
-    MOE_HIP(moe::launch_permute(x, (int)esize(dt), expert_idx, rank, hist, T, d, E, k, C, slot,
-                                drop_mask, xbuf, stream));
+                                  nblk_r, prob_sum, route_count, tile_map, bm, done, stream, T, alpha,
+                                  aux));
+    if (row_tok != nullptr)
+        MOE_HIP(moe::launch_slot_index(expert_idx, rank, hist, T, E, k, C, slot, drop_mask, row_tok,
+                                       gate, row_gate, y_zero, d * (int)esize(dt), stream));
+    else
+        MOE_HIP(moe::launch_permute(x, (int)esize(dt), expert_idx, rank, hist, T, d, E, k, C, slot,
+                                    drop_mask, xbuf, stream));
     return MOE_OK;
 }
 
@@ -245,6 +255,7 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
     out->prob_sum = w.prob_sum;
     out->xbuf = w.xbuf;
     out->ybuf = w.ybuf;
+    out->row_tok = w.row_tok;
     out->total = w.total;
     return MOE_OK;
 }
@@ -370,6 +381,14 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     // the router's per-expert totals are finished by the dispatch scan (one
     // launch fewer); with T = 0 there is no dispatch work, so the router does it
     const bool fuse_reduce = T > 0;
+    // bf16 with work to do: no dispatch copy (the first GEMM gathers the
+    // token rows through row_tok) and, with one choice per token, no combine
+    // pass (the second GEMM writes gated rows straight to y; the scan writes
+    // the auxiliary loss and the index pass clears the rows of dropped tokens)
+    const bool gather = bf16 && T > 0 && C > 0;
+    const bool scatter = gather && k == 1;
+    int32_t *row_tok = gather ? reinterpret_cast<int32_t *>(base + w.row_tok) : nullptr;
+    float *row_gate = scatter ? reinterpret_cast<float *>(base + w.row_gate) : nullptr;
     MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
                          base + w.router, stream, !fuse_reduce));
     if (!mark(1)) return MOE_ERR_HIP;
@@ -378,18 +397,21 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
                            fuse_reduce ? reinterpret_cast<const float *>(base + w.router + w.r.part_prob)
                                        : nullptr,
                            moe::router_blocks(T, bf16, E), prob_sum, route_count,
-                           T > 0 && C > 0 ? tile_map : nullptr, bm));
+                           T > 0 && C > 0 ? tile_map : nullptr, bm, row_tok, scatter ? y : nullptr,
+                           alpha, scatter ? aux_loss : nullptr, gate, row_gate));
     if (!mark(2)) return MOE_ERR_HIP;
     if (C > 0)
-        MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, bm, E, C,
-                                         dff, d, rows, H, stream));
+        MOE_HIP(moe::launch_grouped_gemm(gather ? x : xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map,
+                                         bm, E, C, dff, d, rows, H, stream, row_tok, T));
     if (!mark(3)) return MOE_ERR_HIP;
     if (C > 0)
         MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, bm, E, C, d,
-                                         dff, rows, ybuf, stream));
+                                         dff, rows, scatter ? y : ybuf, stream, scatter ? row_tok : nullptr,
+                                         T, row_gate));
     if (!mark(4)) return MOE_ERR_HIP;
-    MOE_HIP(moe::launch_combine(ybuf, bf16, expert_idx, slot, gate, prob_sum, route_count, T, d, E,
-                                k, C, alpha, y, aux_loss, stream));
+    if (!scatter)
+        MOE_HIP(moe::launch_combine(ybuf, bf16, expert_idx, slot, gate, prob_sum, route_count, T, d, E,
+                                    k, C, alpha, y, aux_loss, stream));
     if (!mark(5)) return MOE_ERR_HIP;
     return MOE_OK;
 }

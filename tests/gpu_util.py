@@ -41,10 +41,12 @@ def dev(a, dtype):
 
 
 def host_f64(t: torch.Tensor) -> np.ndarray:
-    if t.dtype == torch.bfloat16:
-        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        return datagen.bf16_bits_to_f32(bits).astype(np.float64)
-    return t.cpu().numpy().astype(np.float64)
+    """fp64 copy; buffers may hold unwritten rows (any bits), which the callers never compare."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        if t.dtype == torch.bfloat16:
+            bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            return datagen.bf16_bits_to_f32(bits).astype(np.float64)
+        return t.cpu().numpy().astype(np.float64)
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:

@@ -80,8 +80,10 @@ def test_workspace_sizes():
     lay = L.WsLayout()
     assert L.LIB.moe_forward_workspace_layout(16384, 768, 3072, 64, 1, 320, 1, 0, lay) == 0
     assert lay.total == n
-    offs = sorted([lay.slot, lay.expert_count, lay.route_count, lay.prob_sum, lay.xbuf, lay.ybuf])
-    assert len(set(offs)) == 6 and all(o % 256 == 0 for o in offs) and offs[-1] < n
+    offs = sorted([lay.slot, lay.expert_count, lay.route_count, lay.prob_sum, lay.xbuf, lay.ybuf,
+                   lay.row_tok])
+    assert len(set(offs)) == 7 and all(o % 256 == 0 for o in offs) and offs[-1] < n
+    assert n - lay.row_tok >= 64 * 320 * 4
 
 
 _no_gpu = pytest.mark.skipif(
