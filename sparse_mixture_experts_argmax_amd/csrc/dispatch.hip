@@ -16,9 +16,13 @@
 //                 (rank, block) order: the slots taken before each block.
 //                 In the fused forward it also sums the router's per-block
 //                 partials (probability sums, choice counts), and its last
-//                 block builds the GEMM tile map from the kept counts.
+//                 block builds the GEMM tile map from the kept counts (and,
+//                 when the second GEMM writes y, the auxiliary loss).
 //   permute    -- slot = scan + in-block position; slots >= C drop; kept
 //                 rows are copied x[t] -> xbuf[e, slot] with 16-byte moves.
+//   slot_index -- the bf16 forward's alternative to permute: the same slots,
+//                 but only the token of each expert row is recorded (the
+//                 first GEMM gathers the rows from x itself).
 // [SW-GLaM] "All-to-All": the data-sharded -> expert-sharded relayout, done
 // here as a permutation inside one GPU's memory.
 #include "common.h"
