@@ -101,9 +101,14 @@ __device__ __forceinline__ uint32_t scale_bf16x2(uint32_t p, float g) {
 // under any placement.  MINB = 2 sizes the ring and
 // the registers for two blocks per CU, so that one block's prologue and
 // epilogue overlap the other's MFMAs.
-template <int BM_, int BN_, int S_, int BK_ = 64, int MINB_ = 1, int ILV_ = 0>
+template <int BM_, int BN_, int S_, int BK_ = 64, int MINB_ = 1, int ILV_ = 0, int SB_ = 0>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, S = S_, BK = BK_, MINB = MINB_;
+    // > 0: split ring.  A and the weights get rings of their own: S = 2
+    // stages of A (one K tile ahead) and SB = 3 of weights (two ahead), so
+    // the weight stream from HBM has twice the lead of the activations, which
+    // come from the caches
+    static constexpr int SB = SB_;
     // > 0: the DMA of the next stage is spread over the MFMAs of the first ILV
     // k steps instead of issued in one burst (a wave stalls while the address
     // unit is busy, so a burst delays the MFMAs behind it)
@@ -117,6 +122,7 @@ struct Tile {
     static_assert(BM % 64 == 0 && BN % 64 == 0 && S >= 2 && S <= 4, "tile");
     static_assert((BK == 64 || BK == 32) && (MINB == 1 || MINB == 2), "tile");
     static_assert(BK == 32 || BI % 2 == 0, "B groups alternate the swizzle parity");
+    static_assert(SB == 0 || (SB == 3 && S == 2), "split ring: 2 stages of A, 3 of weights");
     static __device__ __forceinline__ int swz(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 };
 
@@ -158,7 +164,7 @@ struct TileCtx {
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
     static constexpr int STAGE = A_BYTES + NBT * B_BYTES;
     static constexpr int RPI = 1024 / ROWB;                        // LDS rows per DMA instruction
-    uint8_t *st0, *st1, *st2, *st3;
+    uint8_t *st0, *st1, *st2, *st3, *st4;
     const uint16_t *Ae;                                            // the expert's rows of A (or all of x)
     // fused forward: row m of the expert is token rtok[m] (its A row is row
     // rtok[m] of x when gathering; its output goes to row rtok[m] of y,
@@ -245,35 +251,38 @@ struct TileCtx {
 // position l % PIECES, which holds logical piece (l % PIECES) ^ swz(row).  The
 // pieces past K (K % BK != 0) of the last K tile are read from column 0 and
 // cleared in LDS once they have landed.
-// PARTS: 1 = the A instructions, 2 = the weight instructions, 3 = both
-// (a stage's instructions must still go out back to back: the waits count
-// the instructions issued after a stage's own).
+// PARTS: 1 = the A instructions (K tile kta into abase), 2 = the weight
+// instructions (K tile ktb into bbase), 3 = both (the waits count the
+// instructions issued after a stage's own, so the order matters).
 template <int NA, bool KTAIL, class CTX, int PARTS = 3>
-__device__ __forceinline__ void tile_issue(const CTX &c, uint8_t *base, int kt) {
-    const int ka = c.template ka<KTAIL>(kt);
+__device__ __forceinline__ void tile_issue2(const CTX &c, uint8_t *abase, uint8_t *bbase, int kta, int ktb) {
     if (PARTS & 1) {
+        const int ka = c.template ka<KTAIL>(kta);
 #pragma unroll
         for (int i = 0; i < NA; ++i)
             __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[i] + ka),
-                                             (MOE_LDS_AS void *)(base + (4 * i + c.wave) * 1024), 16, 0, 0);
+                                             (MOE_LDS_AS void *)(abase + (4 * i + c.wave) * 1024), 16, 0, 0);
     }
-    if (!(PARTS & 2)) {
-        __builtin_amdgcn_sched_barrier(0);
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < CTX::BI; ++j)
-        dma16<CTX::WAUX>(c.bsrc[j] + c.template kb<KTAIL>(kt, j), base + CTX::A_BYTES + (c.wave * CTX::BI + j) * 1024);
-    if (CTX::DUAL) {
+    if (PARTS & 2) {
 #pragma unroll
         for (int j = 0; j < CTX::BI; ++j)
-            dma16<CTX::WAUX>(c.bsrc[j] + c.b3off + c.template kb<KTAIL>(kt, j),
-                             base + CTX::A_BYTES + CTX::B_BYTES + (c.wave * CTX::BI + j) * 1024);
+            dma16<CTX::WAUX>(c.bsrc[j] + c.template kb<KTAIL>(ktb, j), bbase + (c.wave * CTX::BI + j) * 1024);
+        if (CTX::DUAL) {
+#pragma unroll
+            for (int j = 0; j < CTX::BI; ++j)
+                dma16<CTX::WAUX>(c.bsrc[j] + c.b3off + c.template kb<KTAIL>(ktb, j),
+                                 bbase + CTX::B_BYTES + (c.wave * CTX::BI + j) * 1024);
+        }
     }
     // keep every DMA of the stage ahead of the MFMAs that follow (left to
     // itself the scheduler sinks them to the end of the step, which leaves
     // almost no time for them to land)
     __builtin_amdgcn_sched_barrier(0);
+}
+// A stage holding both operands: A at base, the weights after it.
+template <int NA, bool KTAIL, class CTX, int PARTS = 3>
+__device__ __forceinline__ void tile_issue(const CTX &c, uint8_t *base, int kt) {
+    tile_issue2<NA, KTAIL, CTX, PARTS>(c, base, base + CTX::A_BYTES, kt, kt);
 }
 
 // The K loop and epilogue of a tile whose rows that hold data lie in
@@ -289,17 +298,24 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     constexpr int NA = FV * 64 / (4 * X::RPI);           // A-DMA instructions per wave
     static_assert(NA >= 1 && NA <= TL::AI && NA * 4 * X::RPI == FV * 64, "A rows per wave");
     constexpr int PER = NA + NBT * BI;
+    constexpr bool SPLIT = TL::SB > 0;
     // DMA instructions a wave issues after a stage's own before that stage is
     // waited for: those of the S - 2 newer stages (the prologue's stages hold
-    // more, which only makes the first waits stricter)
-    constexpr int NEWER = (S - 2) * PER;
+    // more, which only makes the first waits stricter).  Split ring: step kt
+    // needs A(kt) and the weights of kt, and only the weights of kt + 1 were
+    // issued after A(kt).
+    constexpr int NEWER = SPLIT ? NBT * BI : (S - 2) * PER;
     constexpr int ROWS = FV * 64;                        // tile rows computed and stored
-    // the output rows are staged through two stage buffers (one per wave row)
-    // when they fit, else stored from registers
-    constexpr bool STAGED_OUT = TL::BM * BN <= X::STAGE;
+    // the output rows are staged in LDS when they fit, else stored from
+    // registers: two stage buffers (one per wave row), or with the split ring
+    // five buffers of one 64-row chunk each
+    constexpr int CHUNK = 64 * BN * 2;
+    constexpr bool STAGED_OUT = SPLIT ? (TL::FM <= 5 && CHUNK <= A_BYTES && CHUNK <= NBT * B_BYTES)
+                                      : TL::BM * BN <= X::STAGE;
     const int lane = c.lane, wave = c.wave, nk = c.nk;
     const int wm = wave >> 1, wn = wave & 1;
-    uint8_t *const st0 = c.st0, *const st1 = c.st1, *const st2 = c.st2, *const st3 = c.st3;
+    uint8_t *const st0 = c.st0, *const st1 = c.st1, *const st2 = c.st2, *const st3 = c.st3,
+                   *const st4 = c.st4;
     // A sources of the data rows, clamped to the expert's last row (rows past
     // the count are computed but never stored); gathering keeps the prologue's
     // sources, whose rows past the count hold valid tokens too
@@ -319,18 +335,18 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
         }
     }
 
-    auto issue = [&](uint8_t *base, int kt) { tile_issue<NA, KTAIL>(c, base, kt); };
-    auto clear_tail = [&](uint8_t *base) {
+    // na / nb: where A of K tile kta and the weights of K tile ktb go
+    auto issue = [&](uint8_t *na, uint8_t *nb, int kta, int ktb) { tile_issue2<NA, KTAIL>(c, na, nb, kta, ktb); };
+    auto clear_tail = [&](uint8_t *sa, uint8_t *sb) {
         const u32x4 z = {0u, 0u, 0u, 0u};
         if (c.tailA) {
 #pragma unroll
-            for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4 *>(base + (4 * i + wave) * 1024 + lane * 16) = z;
+            for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4 *>(sa + (4 * i + wave) * 1024 + lane * 16) = z;
         }
 #pragma unroll
         for (int j = 0; j < NBT * BI; ++j)
             if (c.tailB[(j % BI) & 1])
-                *reinterpret_cast<u32x4 *>(base + A_BYTES + (j / BI) * B_BYTES + (wave * BI + (j % BI)) * 1024 +
-                                           lane * 16) = z;
+                *reinterpret_cast<u32x4 *>(sb + (j / BI) * B_BYTES + (wave * BI + (j % BI)) * 1024 + lane * 16) = z;
     };
 
     // accumulators hold C^T fragments: acc[i][j] = weight rows (n) x x rows (m);
@@ -360,8 +376,7 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     // fragments of two k steps: the reads of k step ks + 1 are issued between
     // the MFMAs of k step ks
     bf16x8 af[2][FV], bfr[2][FN], bf3[DUAL ? 2 : 1][DUAL ? FN : 1];
-    auto rd = [&](const uint8_t *sa, int ks, int sl) {
-        const uint8_t *sb = sa + A_BYTES;
+    auto rd = [&](const uint8_t *sa, const uint8_t *sb, int ks, int sl) {
         const int pofs = ((ks * 2 + (lane >> 5)) ^ fswz) << 4;
 #pragma unroll
         for (int i = 0; i < FV; ++i)
@@ -383,22 +398,23 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     constexpr int RM = R > M ? R : M;
     // DMA instruction q of a stage (A rows, then B, then B3), for spreading a
     // stage's DMA over the MFMAs of the first ILV k steps
-    auto dma_one = [&](uint8_t *base, int kt2, int q) {
+    auto dma_one = [&](uint8_t *na, uint8_t *nb, int kta, int ktb, int q) {
         if (q < NA)
-            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[q] + c.template ka<KTAIL>(kt2)),
-                                             (MOE_LDS_AS void *)(base + (4 * q + wave) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(c.asrc[q] + c.template ka<KTAIL>(kta)),
+                                             (MOE_LDS_AS void *)(na + (4 * q + wave) * 1024), 16, 0, 0);
         else if (q < NA + BI)
-            dma16<X::WAUX>(c.bsrc[q - NA] + c.template kb<KTAIL>(kt2, q - NA),
-                           base + A_BYTES + (wave * BI + q - NA) * 1024);
+            dma16<X::WAUX>(c.bsrc[q - NA] + c.template kb<KTAIL>(ktb, q - NA), nb + (wave * BI + q - NA) * 1024);
         else
-            dma16<X::WAUX>(c.bsrc[q - NA - BI] + c.b3off + c.template kb<KTAIL>(kt2, q - NA - BI),
-                           base + A_BYTES + B_BYTES + (wave * BI + q - NA - BI) * 1024);
+            dma16<X::WAUX>(c.bsrc[q - NA - BI] + c.b3off + c.template kb<KTAIL>(ktb, q - NA - BI),
+                           nb + B_BYTES + (wave * BI + q - NA - BI) * 1024);
     };
     constexpr int ILV = TL::ILV < KS ? TL::ILV : KS;
     constexpr int SLOTS = (ILV > 0 ? ILV : 1) * M;
     // the MFMAs of one K tile; the fragments of its k step 0 are already read.
-    // With ILV, the DMA of K tile kt2 into nxt is spread over its first k steps.
-    auto compute = [&](const uint8_t *sa, uint8_t *nxt, int kt2, auto with_dma) {
+    // With ILV, the DMA of A (K tile kta into na) and of the weights (ktb
+    // into nb) is spread over its first k steps.
+    auto compute = [&](const uint8_t *sa, const uint8_t *sb, uint8_t *na, uint8_t *nb, int kta, int ktb,
+                       auto with_dma) {
         constexpr bool IL = decltype(with_dma)::value && ILV > 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -406,9 +422,9 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
             if (IL) {
 #pragma unroll
                 for (int q = 0; q < PER; ++q)
-                    if ((q * SLOTS / PER) / M == ks) dma_one(nxt, kt2, q);
+                    if ((q * SLOTS / PER) / M == ks) dma_one(na, nb, kta, ktb, q);
             }
-            if (ks < KS - 1) rd(sa, ks + 1, sl ^ 1);
+            if (ks < KS - 1) rd(sa, sb, ks + 1, sl ^ 1);
 #pragma unroll
             for (int i = 0; i < FV; ++i)
 #pragma unroll
@@ -445,52 +461,97 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     // ---- the ring: K tile kt lives in stage kt % S.  Step kt waits for its
     // own DMA (the S - 2 newer stages stay in flight), passes one barrier (all
     // waves have landed their part of kt and finished reading kt - 1), refills
-    // the stage of kt - 1 with kt + S - 1, then runs the MFMAs of kt.
+    // the stage of kt - 1 with kt + S - 1, then runs the MFMAs of kt.  Split
+    // ring: A of kt is in a[kt % 2] (st0, st1), its weights in b[kt % 3]
+    // (st2, st3, st4); step kt refills a[(kt + 1) % 2] with A of kt + 1 and
+    // b[(kt + 2) % 3] with the weights of kt + 2, both consumed at kt - 1.
     int kt = 0;
-    // steady state: every step refills a stage, so the wait count is fixed
-    // and the loop body has no branch
-#define MOE_STEP(CUR, NXT)                                                      \
+    constexpr auto DMA_ON = std::integral_constant<bool, true>();
+    constexpr auto DMA_OFF = std::integral_constant<bool, false>();
+    // steady state: every step refills, so the wait count is fixed and the
+    // loop body has no branch
+#define MOE_STEP2(CA, CB, NA_, NB_, KA, KB)                                     \
     {                                                                           \
         wait_vm_lgkm0<NEWER>();                                                 \
         ring_barrier();                                                         \
-        rd(CUR, 0, 0);                                                          \
-        if (ILV == 0) issue(NXT, kt + S - 1);                                   \
-        compute(CUR, NXT, kt + S - 1, std::integral_constant<bool, true>());   \
+        rd(CA, CB, 0, 0);                                                       \
+        if (ILV == 0) issue(NA_, NB_, KA, KB);                                  \
+        compute(CA, CB, NA_, NB_, KA, KB, DMA_ON);                              \
         ++kt;                                                                   \
     }
-    for (; kt + 2 * S - 1 <= nk;) {
-        if constexpr (S == 2) {
-            MOE_STEP(st0, st1)
-            MOE_STEP(st1, st0)
-        } else if constexpr (S == 3) {
-            MOE_STEP(st0, st2)
-            MOE_STEP(st1, st0)
-            MOE_STEP(st2, st1)
-        } else {
-            MOE_STEP(st0, st3)
-            MOE_STEP(st1, st0)
-            MOE_STEP(st2, st1)
-            MOE_STEP(st3, st2)
+#define MOE_STEP(CUR, NXT) MOE_STEP2(CUR, CUR + A_BYTES, NXT, NXT + A_BYTES, kt + S - 1, kt + S - 1)
+#define MOE_STEPS(CA, CB, NA_, NB_) MOE_STEP2(CA, CB, NA_, NB_, kt + 1, kt + 2)
+    if constexpr (SPLIT) {
+        for (; kt + 8 <= nk;) {
+            MOE_STEPS(st0, st2, st1, st4)
+            MOE_STEPS(st1, st3, st0, st2)
+            MOE_STEPS(st0, st4, st1, st3)
+            MOE_STEPS(st1, st2, st0, st4)
+            MOE_STEPS(st0, st3, st1, st2)
+            MOE_STEPS(st1, st4, st0, st3)
+        }
+    } else {
+        for (; kt + 2 * S - 1 <= nk;) {
+            if constexpr (S == 2) {
+                MOE_STEP(st0, st1)
+                MOE_STEP(st1, st0)
+            } else if constexpr (S == 3) {
+                MOE_STEP(st0, st2)
+                MOE_STEP(st1, st0)
+                MOE_STEP(st2, st1)
+            } else {
+                MOE_STEP(st0, st3)
+                MOE_STEP(st1, st0)
+                MOE_STEP(st2, st1)
+                MOE_STEP(st3, st2)
+            }
         }
     }
+#undef MOE_STEPS
 #undef MOE_STEP
-    // drain: at most 2 S - 2 steps, refilling while K tiles remain; kt % S == 0 here
+#undef MOE_STEP2
+    // drain, refilling while K tiles remain: at most 2 S - 2 steps with
+    // kt % S == 0 at the start, or 7 split steps with kt % 6 == 0
 #define MOE_TAIL(CUR, NXT)                                                      \
     if (kt < nk) {                                                              \
         if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
         else wait_vm_lgkm0<0>();                                                \
         if (KTAIL && kt == nk - 1) {                                            \
-            clear_tail(CUR);                                                    \
+            clear_tail(CUR, CUR + A_BYTES);                                     \
             wait_vm_lgkm0<63>();          /* the zeros are in LDS */            \
         }                                                                       \
         ring_barrier();                                                         \
-        rd(CUR, 0, 0);                                                          \
-        if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
+        rd(CUR, CUR + A_BYTES, 0, 0);                                           \
+        if (kt + S - 1 < nk) issue(NXT, NXT + A_BYTES, kt + S - 1, kt + S - 1); \
         __builtin_amdgcn_sched_barrier(0);                                      \
-        compute(CUR, NXT, 0, std::integral_constant<bool, false>());           \
+        compute(CUR, CUR + A_BYTES, NXT, NXT + A_BYTES, 0, 0, DMA_OFF);         \
         ++kt;                                                                   \
     }
-    if constexpr (S == 2) {
+#define MOE_TAILS(CA, CB, NA_, NB_)                                             \
+    if (kt < nk) {                                                              \
+        if (kt + 1 < nk) wait_vm_lgkm0<NEWER>();                                \
+        else wait_vm_lgkm0<0>();                                                \
+        if (KTAIL && kt == nk - 1) {                                            \
+            clear_tail(CA, CB);                                                 \
+            wait_vm_lgkm0<63>();          /* the zeros are in LDS */            \
+        }                                                                       \
+        ring_barrier();                                                         \
+        rd(CA, CB, 0, 0);                                                       \
+        if (kt + 1 < nk) tile_issue2<NA, KTAIL, X, 1>(c, NA_, NB_, kt + 1, 0);  \
+        if (kt + 2 < nk) tile_issue2<NA, KTAIL, X, 2>(c, NA_, NB_, 0, kt + 2);  \
+        __builtin_amdgcn_sched_barrier(0);                                      \
+        compute(CA, CB, NA_, NB_, 0, 0, DMA_OFF);                               \
+        ++kt;                                                                   \
+    }
+    if constexpr (SPLIT) {
+        MOE_TAILS(st0, st2, st1, st4)
+        MOE_TAILS(st1, st3, st0, st2)
+        MOE_TAILS(st0, st4, st1, st3)
+        MOE_TAILS(st1, st2, st0, st4)
+        MOE_TAILS(st0, st3, st1, st2)
+        MOE_TAILS(st1, st4, st0, st3)
+        MOE_TAILS(st0, st2, st1, st4)
+    } else if constexpr (S == 2) {
         MOE_TAIL(st0, st1)
         MOE_TAIL(st1, st0)
     } else if constexpr (S == 3) {
@@ -506,6 +567,7 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
         MOE_TAIL(st0, st3)
         MOE_TAIL(st1, st0)
     }
+#undef MOE_TAILS
 #undef MOE_TAIL
 
     // ---- epilogue: bias, activation, bf16.  With STAGED_OUT the rows of wave
@@ -533,7 +595,10 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
         }
     }
     if (STAGED_OUT || scatter) lds_barrier();            // every wave is past its last fragment read
-    uint8_t *so = wm ? st1 : st0;
+    // the staging buffer of 64-row chunk i (split ring)
+    auto chunk_buf = [&](int i) -> uint8_t * {
+        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : st4;
+    };
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -552,7 +617,9 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
             }
 #pragma unroll
             for (int i = 0; i < FV; ++i) {
-                const int r = i * 32 + (lane & 31);      // row within the wave row's buffer
+                // staged row: within the wave row's buffer, or within chunk i's
+                const int r = SPLIT ? 32 * wm + (lane & 31) : i * 32 + (lane & 31);
+                uint8_t *so = SPLIT ? chunk_buf(i) : (wm ? st1 : st0);
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -593,8 +660,10 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
             const int q = threadIdx.x + it * 256;
             const int Rw = q / P;                        // tile row
             const int p = q % P;
-            const int r = ((Rw >> 6) << 5) | (Rw & 31);  // its row in the wave row's buffer
-            const uint8_t *src = (((Rw >> 5) & 1) ? st1 : st0) + r * (BN * 2) + ((p ^ esw(r)) << 4);
+            // its row in the wave row's buffer, or in its 64-row chunk's
+            const int r = SPLIT ? (Rw & 63) : (((Rw >> 6) << 5) | (Rw & 31));
+            const uint8_t *sbuf = SPLIT ? chunk_buf(Rw >> 6) : (((Rw >> 5) & 1) ? st1 : st0);
+            const uint8_t *src = sbuf + r * (BN * 2) + ((p ^ esw(r)) << 4);
             const int m = m0 + Rw;
             const int n = n0 + p * 8;
             if (m < cnt && n < N) {
@@ -626,12 +695,15 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     using X = TileCtx<TL, ACT, WNT>;
     constexpr int BM = TL::BM, BN = TL::BN, S = TL::S, FM = TL::FM;
     constexpr int STAGE = X::STAGE;
+    constexpr bool SPLIT = TL::SB > 0;
+    constexpr int SA = X::A_BYTES, SBW = X::NBT * X::B_BYTES;   // split ring: A and weight stages
     // one LDS array per stage: the compiler then sees that the fragment reads of
     // one stage cannot alias the DMA in flight into another and adds no wait
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[SPLIT ? SA : STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[SPLIT ? SA : STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[SPLIT ? SBW : (S > 2 ? STAGE : 16)];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[SPLIT ? SBW : (S > 3 ? STAGE : 16)];
+    __shared__ __attribute__((aligned(1024))) uint8_t st4[SPLIT ? SBW : 16];
     __shared__ int s_map[EXPERT ? 1 : MAX_E_LDS + 1];
     __shared__ int s_tok[BM];                            // scattering: token and gate of each row
     __shared__ float s_g[BM];
@@ -653,7 +725,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     }
 
     X c;
-    c.st0 = st0; c.st1 = st1; c.st2 = st2; c.st3 = st3;
+    c.st0 = st0; c.st1 = st1; c.st2 = st2; c.st3 = st3; c.st4 = st4;
     // wave-uniform wave index (DMA base)
     c.set_lanes(threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), K);
     c.m0 = mt * BM;
@@ -697,12 +769,19 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
                 tok[i] = am < (int)C - 1 ? am : (int)C - 1;
             }
         }
-        tile_issue<TL::AI, KTAIL, X, 2>(c, st0, 0);
+        // stage 0: weights, then A (split ring: A into st0, weights into st2)
+        uint8_t *b0 = SPLIT ? st2 : st0 + X::A_BYTES;
+        tile_issue2<TL::AI, KTAIL, X, 2>(c, st0, b0, 0, 0);
         c.set_a_tok(tok);
-        tile_issue<TL::AI, KTAIL, X, 1>(c, st0, 0);
+        tile_issue2<TL::AI, KTAIL, X, 1>(c, st0, b0, 0, 0);
     }
-    if (S > 2) tile_issue<TL::AI, KTAIL>(c, st1, c.nk > 1 ? 1 : c.nk - 1);
-    if (S > 3) tile_issue<TL::AI, KTAIL>(c, st2, c.nk > 2 ? 2 : c.nk - 1);
+    if (SPLIT) {
+        // the weights of K tile 1 (clamped), one stage further ahead
+        tile_issue2<TL::AI, KTAIL, X, 2>(c, st1, st3, 0, c.nk > 1 ? 1 : c.nk - 1);
+    } else {
+        if (S > 2) tile_issue<TL::AI, KTAIL>(c, st1, c.nk > 1 ? 1 : c.nk - 1);
+        if (S > 3) tile_issue<TL::AI, KTAIL>(c, st2, c.nk > 2 ? 2 : c.nk - 1);
+    }
 
     const int cnt = count[e];
     const int rows = cnt - c.m0;                         // > 0 for every mapped tile
@@ -838,6 +917,9 @@ int gemm_bm(int dtype_bf16, int64_t C, int act) {
     return 128;
 }
 
+#ifndef MOE_SPLIT320
+#define MOE_SPLIT320 3
+#endif
 // bf16 tile shapes: W = wide (192 or 256 output columns), N = 128 columns,
 // G = gated (128 columns of each weight); the suffix is BM.  64-wide K
 // stages, one block per CU and 112-144 KB rings (one or two stages ahead of
@@ -845,7 +927,7 @@ int gemm_bm(int dtype_bf16, int64_t C, int act) {
 // on 32-wide K stages.  The 256- and 320-row tiles spread each stage's DMA
 // over the MFMAs of the first two k steps (measured faster there; neutral to
 // slower on the 128- and 192-row ones).
-using TileW320 = Tile<320, 192, 2, 64, 1, 2>;
+using TileW320 = Tile<320, 192, 2, 64, 1, 2, MOE_SPLIT320>;
 using TileN320 = Tile<320, 128, 2, 64, 1, 2>;
 using TileW256 = Tile<256, 256, 2, 64, 1, 2>;
 using TileN256 = Tile<256, 128, 3, 64, 1, 2>;
