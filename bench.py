@@ -5,14 +5,20 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload switch_base]
 
 A step is one whole layer forward (router, dispatch, expert FFN, combine
 and loss) over one batch of seeded synthetic inputs already resident in
-HBM.  W untimed steps, then K timed steps bracketed by device
+HBM.  First the GPU settles: untimed forwards run for --settle-seconds
+(0.3 s), since the chip leaves its idle clocks only under load and the
+first ~100 forwards after even 0.2 s of idle run up to 25 % slower.  Then W
+untimed warm-up steps, then exactly K timed steps bracketed by device
 synchronisation; value = tokens per second over the K steps.
 
-Each timed step records HIP events at the stage boundaries on the stream the
-kernels run on (moe_forward_staged), giving each stage's average duration
-over the timed region; the roofline object reports the stage that takes the
-longest, with its algorithmic bytes / flops per launch (see `stage_work`).
-The CPU baseline times the CPU oracle on the same workload, on this host.
+After the timed steps the same K steps run again through
+moe_forward_staged, which records HIP events at the stage boundaries on the
+stream the kernels run on, giving each stage's average duration (the
+events cost time of their own, so the timed steps run without them); the
+roofline object reports the stage that takes the longest, with its
+algorithmic bytes / flops per launch (see `stage_work`).  step_ms gives the
+spread of single forwards, warm and with a cold last-level cache.  The CPU
+baseline times the CPU oracle on the same workload, on this host.
 
 Prints one JSON line.
 """
@@ -28,6 +34,8 @@ import os
 import re
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -305,6 +313,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="untimed forwards before the warm-up steps, to bring the GPU to its load clocks")
     ap.add_argument("--workload", default="switch_base", choices=datagen.CONFIG_ORDER)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline (0 disables it)")
@@ -372,6 +382,14 @@ def main(argv=None):
             _ptr(plan.gate), _ptr(plan.drop_mask), _ptr(plan.ws), plan.ws.numel(),
             stream.cuda_stream, arr))
 
+    # settle: untimed forwards in rounds of 10 until settle_seconds have passed
+    n_settle, t_s = 0, time.perf_counter()
+    while n_settle == 0 or time.perf_counter() - t_s < args.settle_seconds:
+        for _ in range(10):
+            step()
+        n_settle += 10
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_s
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -393,6 +411,35 @@ def main(argv=None):
         for j, name in enumerate(L.STAGES):
             stage_ms[name] += hip.elapsed_ms(ev[j], ev[j + 1]) / args.steps
     hip.destroy(events)
+
+    # per-step spread (warm): one HIP event between consecutive forwards, so
+    # each interval holds one forward and one event record (~4.5 us)
+    step_ev = hip.create(args.steps + 1)
+    hip.record(step_ev[0], stream.cuda_stream)
+    for i in range(args.steps):
+        step()
+        hip.record(step_ev[i + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    warm_ms = [hip.elapsed_ms(step_ev[i], step_ev[i + 1]) for i in range(args.steps)]
+    hip.destroy(step_ev)
+    # cold last-level cache: 512 MB of scratch written before each timed forward
+    n_cold = min(args.steps, 10)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_ev = hip.create(2 * n_cold)
+    for i in range(n_cold):
+        scratch.fill_(i & 0xFF)
+        hip.record(cold_ev[2 * i], stream.cuda_stream)
+        step()
+        hip.record(cold_ev[2 * i + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    cold_ms = [hip.elapsed_ms(cold_ev[2 * i], cold_ev[2 * i + 1]) for i in range(n_cold)]
+    hip.destroy(cold_ev)
+    del scratch
+
+    def spread(v):
+        q = np.percentile(np.asarray(v, dtype=np.float64), [50, 10, 90])
+        return dict(median=round(float(q[0]), 4), p10=round(float(q[1]), 4), p90=round(float(q[2]), 4),
+                    n=len(v), tokens_per_s=round(cfg["T"] / (float(q[0]) / 1e3), 1))
 
     A = int(plan.intermediate("expert_count").sum().item())
     drops = int(plan.drop_mask.sum().item())
@@ -449,6 +496,10 @@ def main(argv=None):
         "permute_GBps": round(disp_bytes / disp_s / 1e9, 1),
         "permute_us": round(disp_s * 1e6, 2),
         "stages": stages,
+        "settle": {"seconds": round(settle_s, 3), "forwards": n_settle},
+        "step_ms": {"warm": spread(warm_ms), "cold_mall": spread(cold_ms),
+                    "note": "per-forward HIP event intervals (each holds one event record, "
+                            "about 4.5 us); cold_mall writes 512 MB of scratch before each forward"},
         "roofline": roofline,
     }
     if args.cpu_seconds > 0:
