@@ -250,7 +250,7 @@ def committed_traffic(workload: str, stage: str):
                 if rec.get("source_digest") != source_digest():
                     return None, "kernel sources changed since the counters were taken"
                 st = rec["stages"].get(stage)
-                return (st["traffic_bytes"] if st else None), path
+                return (st["traffic_bytes"] if st else None), os.path.relpath(path, ROOT)
     return None, "no traffic record"
 
 
