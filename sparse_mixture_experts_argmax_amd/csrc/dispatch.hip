@@ -80,6 +80,44 @@ __global__ __launch_bounds__(DISPATCH_TOK_BLOCK) void slot_rank_kernel(
 //  * the expert GEMMs' tile map (tile_map[e] = sum over e' < e of
 //    ceil(expert_count[e'] / bm)), built by whichever block finishes last
 //    (a completion counter that slot_rank zeroed).
+// The GEMM tile map from the clipped counts, by one whole block of 256
+// threads: thread t owns experts 4t .. 4t + 3 (E <= 1024), a wave scan, then
+// the wave totals.  COHERENT: the counts come from other blocks of the same
+// launch, so they are read from L2 (agent-scope atomic loads).
+template <bool COHERENT>
+__device__ void tile_map_block(const int32_t *expert_count, int E, int bm, int32_t *tile_map, int *s_wsum) {
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    int c[4];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ee = 4 * t + q;
+        int n = 0;
+        if (ee < E)
+            n = COHERENT ? __hip_atomic_load(expert_count + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : expert_count[ee];
+        c[q] = (n + bm - 1) / bm;
+        local += c[q];
+    }
+    int inc = local;
+    for (int m = 1; m < 64; m <<= 1) {
+        const int u = __shfl_up(inc, m);
+        if (lane >= m) inc += u;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int run = inc - local;
+    for (int i = 0; i < wave; ++i) run += s_wsum[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ee = 4 * t + q;
+        if (ee < E) tile_map[ee] = run;
+        run += c[q];
+    }
+    if (E - 1 >= 4 * t && E - 1 < 4 * t + 4) tile_map[E] = run;
+}
+
 __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hist, int L, int E,
                                                         int64_t C, int32_t *__restrict__ expert_count,
                                                         const float *__restrict__ part_prob, int nblk_r,
@@ -126,34 +164,7 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hi
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    // thread t owns experts 4t .. 4t + 3 (E <= 1024): a wave scan, then the
-    // wave totals; counts are read from L2 (other blocks wrote them)
-    const int t = threadIdx.x;
-    int c[4];
-    int local = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int ee = 4 * t + q;
-        const int n = ee < E ? __hip_atomic_load(expert_count + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        c[q] = (n + bm - 1) / bm;
-        local += c[q];
-    }
-    int inc = local;
-    for (int m = 1; m < 64; m <<= 1) {
-        const int u = __shfl_up(inc, m);
-        if (lane >= m) inc += u;
-    }
-    if (lane == 63) s_wsum[wave] = inc;
-    __syncthreads();
-    int run = inc - local;
-    for (int i = 0; i < wave; ++i) run += s_wsum[i];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int ee = 4 * t + q;
-        if (ee < E) tile_map[ee] = run;
-        run += c[q];
-    }
-    if (E - 1 >= 4 * t && E - 1 < 4 * t + 4) tile_map[E] = run;
+    tile_map_block<true>(expert_count, E, bm, tile_map, s_wsum);
     if (aux != nullptr && wave == 0) {
         const float a = aux_loss_wave<true>(route_count, prob_sum, E, T, k, alpha, lane);
         if (lane == 0) aux[0] = a;
@@ -202,8 +213,20 @@ __global__ __launch_bounds__(256) void slot_index_kernel(
     const int32_t *__restrict__ base, int64_t T, int E, int k, int nblk, int64_t C,
     int32_t *__restrict__ slot, uint8_t *__restrict__ drop, int32_t *__restrict__ row_tok,
     const float *__restrict__ gate, float *__restrict__ row_gate, uint8_t *__restrict__ y_zero,
-    int row_bytes) {
+    int row_bytes, const int32_t *__restrict__ expert_count, const float *__restrict__ prob_sum,
+    const int32_t *__restrict__ route_count, int32_t *__restrict__ tile_map, int bm, float alpha,
+    float *__restrict__ aux) {
+    __shared__ int s_wsum[4];
     const int lane = threadIdx.x & 63;
+    // block 0 also writes the GEMM tile map and the loss from the totals
+    // the scan finished (a launch earlier, so plain loads see them)
+    if (blockIdx.x == 0) {
+        if (tile_map != nullptr) tile_map_block<false>(expert_count, E, bm, tile_map, s_wsum);
+        if (aux != nullptr && threadIdx.x < 64) {
+            const float av = aux_loss_wave<false>(route_count, prob_sum, E, T, k, alpha, lane);
+            if (lane == 0) aux[0] = av;
+        }
+    }
     const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
     bool dropped = false;
     if (a < T * k) {
@@ -269,12 +292,17 @@ hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
 hipError_t launch_slot_index(const int32_t *expert_idx, const int32_t *rank, const int32_t *base,
                              int64_t T, int E, int k, int64_t C, int32_t *slot, uint8_t *drop_mask,
                              int32_t *row_tok, const float *gate, float *row_gate, void *y_zero,
-                             int row_bytes, hipStream_t s) {
+                             int row_bytes, hipStream_t s, const int32_t *expert_count,
+                             const float *prob_sum, const int32_t *route_count, int32_t *tile_map,
+                             int bm, float alpha, float *aux) {
     const int64_t n = T * k;
     if (n == 0) return hipSuccess;
+    if (tile_map != nullptr && (E > 1024 || bm < 1 || expert_count == nullptr)) return hipErrorInvalidValue;
+    if (aux != nullptr && (prob_sum == nullptr || route_count == nullptr)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(slot_index_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, expert_idx,
                        rank, base, T, E, k, dispatch_blocks(T), C, slot, drop_mask, row_tok, gate,
-                       row_gate, reinterpret_cast<uint8_t *>(y_zero), row_bytes);
+                       row_gate, reinterpret_cast<uint8_t *>(y_zero), row_bytes, expert_count, prob_sum,
+                       route_count, tile_map, bm, alpha, aux);
     return hipGetLastError();
 }
 

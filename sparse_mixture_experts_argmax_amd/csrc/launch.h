@@ -39,11 +39,18 @@ hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
 // Slots and drops as launch_permute, but rows are not copied: row_tok[e C +
 // slot] = token for every kept choice.  k = 1 only (both may be null):
 // row_gate[e C + slot] = gate of that choice, and y_zero gets the rows
-// (row_bytes each) of dropped tokens cleared.
+// (row_bytes each) of dropped tokens cleared.  tile_map (may be null): block
+// 0 also writes the GEMM tile map for row tiles of bm from expert_count (what
+// launch_tile_map would); aux (may be null): block 0 also writes the
+// auxiliary loss from prob_sum and route_count (what launch_combine would).
+// The totals come from the scan, a launch earlier.
 hipError_t launch_slot_index(const int32_t *expert_idx, const int32_t *rank, const int32_t *base,
                              int64_t T, int E, int k, int64_t C, int32_t *slot, uint8_t *drop_mask,
                              int32_t *row_tok, const float *gate, float *row_gate, void *y_zero,
-                             int row_bytes, hipStream_t s);
+                             int row_bytes, hipStream_t s, const int32_t *expert_count = nullptr,
+                             const float *prob_sum = nullptr, const int32_t *route_count = nullptr,
+                             int32_t *tile_map = nullptr, int bm = 0, float alpha = 0.f,
+                             float *aux = nullptr);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,

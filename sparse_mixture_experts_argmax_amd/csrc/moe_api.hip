@@ -165,13 +165,18 @@ moe_status run_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, 
     int32_t *rank = reinterpret_cast<int32_t *>(ws + w.rank);
     int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
     unsigned *done = reinterpret_cast<unsigned *>(ws + w.done);
-    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, tile_map ? done : nullptr, stream));
+    // with row_tok the index pass (a launch after the scan) writes the tile
+    // map and the loss, so the scan needs no completion counter
+    const bool late = row_tok != nullptr;
+    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, tile_map && !late ? done : nullptr,
+                                  stream));
     MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, C, expert_count, part_prob,
-                                  nblk_r, prob_sum, route_count, tile_map, bm, done, stream, T, alpha,
-                                  aux));
-    if (row_tok != nullptr)
+                                  nblk_r, prob_sum, route_count, late ? nullptr : tile_map, bm, done,
+                                  stream, T, alpha, late ? nullptr : aux));
+    if (late)
         MOE_HIP(moe::launch_slot_index(expert_idx, rank, hist, T, E, k, C, slot, drop_mask, row_tok,
-                                       gate, row_gate, y_zero, d * (int)esize(dt), stream));
+                                       gate, row_gate, y_zero, d * (int)esize(dt), stream, expert_count,
+                                       prob_sum, route_count, tile_map, bm, alpha, aux));
     else
         MOE_HIP(moe::launch_permute(x, (int)esize(dt), expert_idx, rank, hist, T, d, E, k, C, slot,
                                     drop_mask, xbuf, stream));
