@@ -309,9 +309,11 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     constexpr int ROWS = FV * 64;                        // tile rows computed and stored
     // the output rows are staged in LDS when they fit, else stored from
     // registers: two stage buffers (one per wave row), or with the split ring
-    // five buffers of one 64-row chunk each
+    // one buffer per 64-row chunk: all five stages, or the three weight
+    // stages when a chunk is larger than an A stage (tiles of 192 rows)
     constexpr int CHUNK = 64 * BN * 2;
-    constexpr bool STAGED_OUT = SPLIT ? (TL::FM <= 5 && CHUNK <= A_BYTES && CHUNK <= NBT * B_BYTES)
+    constexpr bool CH_IN_A = CHUNK <= A_BYTES;
+    constexpr bool STAGED_OUT = SPLIT ? (CHUNK <= NBT * B_BYTES && TL::FM <= (CH_IN_A ? 5 : 3))
                                       : TL::BM * BN <= X::STAGE;
     const int lane = c.lane, wave = c.wave, nk = c.nk;
     const int wm = wave >> 1, wn = wave & 1;
@@ -620,6 +622,7 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     if (STAGED_OUT || scatter) lds_barrier();            // every wave is past its last fragment read
     // the staging buffer of 64-row chunk i (split ring)
     auto chunk_buf = [&](int i) -> uint8_t * {
+        if (!CH_IN_A) return i == 0 ? st2 : i == 1 ? st3 : st4;
         return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : i == 3 ? st3 : st4;
     };
 #pragma unroll
@@ -840,11 +843,16 @@ inline int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_boun
 #endif
 // bf16 tile shapes: W = wide (192 or 256 output columns), N = 128 columns,
 // G = gated (128 columns of each weight); the suffix is BM.  64-wide K
-// stages, one block per CU and 112-144 KB rings (one or two stages ahead of
+// stages, one block per CU and 112-152 KB rings (one or two stages ahead of
 // the MFMAs), except the narrow 128-row shape, which runs two blocks per CU
 // on 32-wide K stages.  The 256- and 320-row tiles spread each stage's DMA
 // over the MFMAs of the first two k steps (measured faster there; neutral to
-// slower on the 128- and 192-row ones).
+// slower on the 128-row ones).  The wide 320- and 192-row tiles (one tile per
+// expert, weights streamed once) use the split ring, which keeps the weights
+// two K tiles ahead: 3 % off both many-expert GEMMs for the 192-row one,
+// where the two-stage ring left the weight stream waiting on HBM latency;
+// the wide 128-row tile measured 6 % slower with it and keeps three uniform
+// stages.
 #ifndef MOE_W320
 #define MOE_W320 2, MOE_SPLIT320, 0
 #endif
@@ -853,7 +861,10 @@ using TileN320 = Tile<320, 128, 2, 64, 1, 2>;
 using TileW256 = Tile<256, 256, 2, 64, 1, 2>;
 using TileN256 = Tile<256, 128, 3, 64, 1, 2>;
 using TileG256 = Tile<256, 128, 2, 64, 1, 2>;
-using TileW192 = Tile<192, 256, 2, 64, 1, 0>;
+#ifndef MOE_W192
+#define MOE_W192 2, 3, 2
+#endif
+using TileW192 = Tile<192, 256, 2, 64, 1, MOE_W192>;
 using TileN192 = Tile<192, 128, 3, 64, 1, 0>;
 using TileW128 = Tile<128, 256, 3, 64, 1, 0>;
 using TileN128 = Tile<128, 128, 4, 32, 2, 0>;

@@ -3,7 +3,8 @@
 Workloads: the five seeded configurations at full size, plus small ragged
 cases (token counts that are not multiples of any tile, expert counts that
 are not multiples of 16, widths that leave K and N tails in the GEMMs,
-k = 2 and 3, forced drops, the router bias, more than 256 experts).
+k = 2 and 3, forced drops, the router bias, more than 256 experts, and
+capacities that select each row-tile height).
 """
 import numpy as np
 import pytest
@@ -34,6 +35,9 @@ SMALL = {
     # column tiles (first GEMM) and the narrow ones (second), with K and N tails
     "tiles_320": (19200, 72, 776, 64, 1, 1.0, "bf16", "relu", True, False, 1.0),
     "tiles_192": (10880, 72, 776, 64, 1, 1.0, "bf16", "relu", True, False, 1.0),
+    # capacity 240: row tiles of 128 from the tile map, in the wide column
+    # tiles (first GEMM), with K and N tails
+    "tiles_128": (12288, 72, 776, 64, 1, 1.25, "bf16", "relu", True, False, 1.0),
 }
 
 
@@ -255,7 +259,8 @@ def _ffn_rows(cfg, sample=None, seed=7):
 
 
 @pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "tiles_320",
-                                  "tiles_192", "ragged_f32", "switch_base", "mixtral", "many_expert"])
+                                  "tiles_192", "tiles_128", "ragged_f32", "switch_base", "zipf_skew",
+                                  "mixtral", "many_expert"])
 def test_expert_ffn_elementwise(name):
     """Each GEMM tile shape against the oracle's expert FFN, every element of the checked rows.
 
