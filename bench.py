@@ -66,7 +66,10 @@ def stage_work(cfg: dict, A: int) -> dict:
     A = kept (token, rank) choices.  Only real rows count: weights once, the
     activations each stage must read or write, no padding, no re-reads.
       router   x [T,d] + W_r [E,d] fp32 read, expert_idx + gate [T,k] written;
-               flops 2 T d E (fp32)
+               flops 2 T d E (fp32).  With bf16 tokens and E <= 256 the router
+               forms each fp32 product exactly as three bf16 MFMA products
+               (W_r split into three bf16 parts), so its bound is the bf16
+               MFMA peak over 3 x 2 T d E flops; otherwise fp32 vector ALU
       dispatch T k (4 + 4 + 1) (indices read, slots and drop flags written)
                + 2 A d s (x rows read, xbuf rows written), or, fused,
                + 4 A (row index written) [+ (T - A) d s, dropped rows of y cleared]
@@ -81,9 +84,12 @@ def stage_work(cfg: dict, A: int) -> dict:
     s = 2 if cfg["dtype"] == "bf16" else 4
     m = 2 if cfg["act"] == "swiglu" else 1
     gather, scatter = fused_forward(cfg)
+    mfma_router = cfg["dtype"] == "bf16" and E <= 256
     disp = T * k * 9 + (4 * A + (T - A) * d * s * scatter if gather else 2 * A * d * s)
     return {
-        "router": dict(bytes=T * d * s + E * d * 4 + T * k * 8, flops=2 * T * d * E, dtype="f32"),
+        "router": dict(bytes=T * d * s + E * d * 4 + T * k * 8,
+                       flops=(3 if mfma_router else 1) * 2 * T * d * E,
+                       dtype="bf16" if mfma_router else "f32"),
         "dispatch": dict(bytes=disp, flops=0, dtype=cfg["dtype"]),
         "expert_gemm1": dict(bytes=m * E * f * d * s + A * d * s + A * f * s, flops=2 * m * A * d * f,
                              dtype=cfg["dtype"]),
