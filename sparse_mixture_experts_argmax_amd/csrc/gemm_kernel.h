@@ -493,19 +493,10 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
         compute(CA, CB, NA_, NB_, KA, KB, DMA_ON);                              \
         ++kt;                                                                   \
     }
-    // Split ring without a K tail: the steady loop also runs the last steps.
-    // Their refills past the last K tile are clamped to it and land in
-    // stages no later step reads (as in the prologue), so the loop stays
-    // branch-free to the end (the drain then only takes nk % 6 steps) and
-    // every K tile gets the spread DMA: 1-2 % on the 320-row GEMMs.  The
-    // uniform rings keep the drain: their duplicate stages cost more than
-    // the drain does (6 % on 128-row tiles over 12 K tiles).  With a K tail
-    // the last tile's pieces past K must be cleared, which the drain does.
-    auto kc = [&](int t) { return t < nk ? t : nk - 1; };
 #define MOE_STEP(CUR, NXT) MOE_STEP2(CUR, CUR + A_BYTES, NXT, NXT + A_BYTES, kt + S - 1, kt + S - 1)
-#define MOE_STEPS(CA, CB, NA_, NB_) MOE_STEP2(CA, CB, NA_, NB_, kc(kt + 1), kc(kt + 2))
+#define MOE_STEPS(CA, CB, NA_, NB_) MOE_STEP2(CA, CB, NA_, NB_, kt + 1, kt + 2)
     if constexpr (SPLIT) {
-        for (; kt + (KTAIL ? 8 : 6) <= nk;) {
+        for (; kt + 8 <= nk;) {
             MOE_STEPS(st0, st2, st1, st4)
             MOE_STEPS(st1, st3, st0, st2)
             MOE_STEPS(st0, st4, st1, st3)
@@ -592,8 +583,6 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
     }
 #undef MOE_TAILS
 #undef MOE_TAIL
-    // clamped refills of the last steps may still be in flight
-    wait_vm_lgkm0<0>();
 
     // ---- epilogue: bias, activation, bf16.  With STAGED_OUT the rows of wave
     // row wm go to stage buffer wm (16-byte pieces swizzled by row), so that
