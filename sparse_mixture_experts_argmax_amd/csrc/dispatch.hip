@@ -15,14 +15,17 @@
 //   slot_scan  -- per expert, an exclusive scan of the histograms in
 //                 (rank, block) order: the slots taken before each block.
 //                 In the fused forward it also sums the router's per-block
-//                 partials (probability sums, choice counts), and its last
-//                 block builds the GEMM tile map from the kept counts (and,
-//                 when the second GEMM writes y, the auxiliary loss).
+//                 partials (probability sums, choice counts).  On the f32
+//                 path its last block builds the GEMM tile map from the kept
+//                 counts; the bf16 forward leaves that to slot_index.
 //   permute    -- slot = scan + in-block position; slots >= C drop; kept
 //                 rows are copied x[t] -> xbuf[e, slot] with 16-byte moves.
 //   slot_index -- the bf16 forward's alternative to permute: the same slots,
 //                 but only the token of each expert row is recorded (the
-//                 first GEMM gathers the rows from x itself).
+//                 first GEMM gathers the rows from x itself).  Its block 0
+//                 also writes the GEMM tile map and, when the second GEMM
+//                 writes y, the auxiliary loss, from the totals the scan
+//                 finished a launch earlier.
 // [SW-GLaM] "All-to-All": the data-sharded -> expert-sharded relayout, done
 // here as a permutation inside one GPU's memory.
 #include "common.h"
@@ -73,13 +76,6 @@ __global__ __launch_bounds__(DISPATCH_TOK_BLOCK) void slot_rank_kernel(
             ((sc[n] + sc[E + n]) + sc[2 * E + n]) + sc[3 * E + n];
 }
 
-// One wave per expert: exclusive scan over (rank, block), in place.
-// Optionally (the fused forward) also:
-//  * the router's per-expert totals, in the same order and precision as its
-//    own reduction, so that both give the same bits;
-//  * the expert GEMMs' tile map (tile_map[e] = sum over e' < e of
-//    ceil(expert_count[e'] / bm)), built by whichever block finishes last
-//    (a completion counter that slot_rank zeroed).
 // The GEMM tile map from the clipped counts, by one whole block of 256
 // threads: thread t owns experts 4t .. 4t + 3 (E <= 1024), a wave scan, then
 // the wave totals.  COHERENT: the counts come from other blocks of the same
@@ -118,6 +114,13 @@ __device__ void tile_map_block(const int32_t *expert_count, int E, int bm, int32
     if (E - 1 >= 4 * t && E - 1 < 4 * t + 4) tile_map[E] = run;
 }
 
+// One wave per expert: exclusive scan over (rank, block), in place.
+// Optionally (the fused forward) also:
+//  * the router's per-expert totals, in the same order and precision as its
+//    own reduction, so that both give the same bits;
+//  * the expert GEMMs' tile map (tile_map[e] = sum over e' < e of
+//    ceil(expert_count[e'] / bm)), built by whichever block finishes last
+//    (a completion counter that slot_rank zeroed).
 __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hist, int L, int E,
                                                         int64_t C, int32_t *__restrict__ expert_count,
                                                         const float *__restrict__ part_prob, int nblk_r,

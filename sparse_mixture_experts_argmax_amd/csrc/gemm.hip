@@ -8,16 +8,23 @@
 // matrix products over their slot lists (a dedicated grouped-GEMM kernel).
 //
 // bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * 256 threads = 4 waves in a 2x2 grid; block tiles of 128 or 256 rows by
-//     128 or 256 columns (see Tile), each wave owning a quarter.
+//   * 256 threads = 4 waves in a 2x2 grid; block tiles of 128 to 320 rows by
+//     128 to 256 columns (the shapes at the end of gemm_kernel.h), each wave
+//     owning a quarter.
 //   * A and B tiles are K-contiguous in HBM (x rows, nn.Linear-style weight
 //     rows), so both are staged the same way: 16-byte LDS DMA
-//     (global_load_lds) into a ring of LDS stages two or three K tiles ahead
-//     of the MFMAs, 16-byte pieces of each LDS row XOR-swizzled by row
-//     (conflict-free fragment reads, no padding).
-//   * Only real row tiles are launched work: tile_map holds the prefix sums
-//     of ceil(count[e] / BM), built on the device, so an expert with few rows
-//     costs few tiles and an empty expert none.
+//     (global_load_lds) into a ring of LDS stages one to three K tiles ahead
+//     of the MFMAs (the wide 320- and 192-row tiles keep the weights two
+//     ahead and the activations one), 16-byte pieces of each LDS row
+//     XOR-swizzled by row (conflict-free fragment reads, no padding).
+//   * Only real row tiles are launched work: a tile that holds a whole
+//     expert's capacity maps blocks to (expert, column tile) directly;
+//     otherwise tile_map holds the prefix sums of ceil(count[e] / BM), built
+//     on the device, so an expert with few rows costs few tiles and an empty
+//     expert none.
+//   * The first GEMM of the fused forward gathers its rows of x by token
+//     index; the second scales each output row by its token's gate and
+//     writes it to that token's row of y.
 //   * Tile order is expert-major, then column tile, then row tile, so the
 //     row tiles that share a weight tile run next to each other; the block
 //     index is remapped so that each XCD (blocks are dealt to the 8 XCDs

@@ -827,9 +827,6 @@ inline int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_boun
 
 }  // namespace
 
-#ifndef MOE_SPLIT320
-#define MOE_SPLIT320 3
-#endif
 // bf16 tile shapes: W = wide (192 or 256 output columns), N = 128 columns,
 // G = gated (128 columns of each weight); the suffix is BM.  64-wide K
 // stages, one block per CU and 112-152 KB rings (one or two stages ahead of
@@ -842,18 +839,12 @@ inline int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_boun
 // where the two-stage ring left the weight stream waiting on HBM latency;
 // the wide 128-row tile measured 6 % slower with it and keeps three uniform
 // stages.
-#ifndef MOE_W320
-#define MOE_W320 2, MOE_SPLIT320, 0
-#endif
-using TileW320 = Tile<320, 192, 2, 64, 1, MOE_W320>;
+using TileW320 = Tile<320, 192, 2, 64, 1, 2, 3>;
 using TileN320 = Tile<320, 128, 2, 64, 1, 2>;
 using TileW256 = Tile<256, 256, 2, 64, 1, 2>;
 using TileN256 = Tile<256, 128, 3, 64, 1, 2>;
 using TileG256 = Tile<256, 128, 2, 64, 1, 2>;
-#ifndef MOE_W192
-#define MOE_W192 2, 3, 2
-#endif
-using TileW192 = Tile<192, 256, 2, 64, 1, MOE_W192>;
+using TileW192 = Tile<192, 256, 2, 64, 1, 2, 3, 2>;
 using TileN192 = Tile<192, 128, 3, 64, 1, 0>;
 using TileW128 = Tile<128, 256, 3, 64, 1, 0>;
 using TileN128 = Tile<128, 128, 4, 32, 2, 0>;

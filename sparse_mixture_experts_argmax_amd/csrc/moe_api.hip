@@ -388,8 +388,8 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     const bool fuse_reduce = T > 0;
     // bf16 with work to do: no dispatch copy (the first GEMM gathers the
     // token rows through row_tok) and, with one choice per token, no combine
-    // pass (the second GEMM writes gated rows straight to y; the scan writes
-    // the auxiliary loss and the index pass clears the rows of dropped tokens)
+    // pass (the second GEMM writes gated rows straight to y; the index pass
+    // writes the auxiliary loss and clears the rows of dropped tokens)
     const bool gather = bf16 && T > 0 && C > 0;
     const bool scatter = gather && k == 1;
     int32_t *row_tok = gather ? reinterpret_cast<int32_t *>(base + w.row_tok) : nullptr;
