@@ -140,6 +140,25 @@ def aux_loss(p: np.ndarray, idx: np.ndarray, E: int, alpha: float) -> float:
     return float(alpha * E * np.sum(f * P))
 
 
+def router_z_loss(z: np.ndarray) -> float:
+    """The router z-loss: the mean over tokens of the squared log-sum-exp
+    of that token's router logits, (1/T) sum_t (log sum_i exp z_ti)^2.
+
+    [CMU-L16] section 4.2 (the two regularisers): the z-loss of Zoph et al.
+    (2022) penalises large router logits through their logsumexp squared;
+    the section's experiment reports this quantity itself (10.2 falling to
+    0.2) and the OLMoE weight 0.001 that multiplies it in the training loss,
+    so the value here carries no weight.  The page's formula image is
+    missing; the definition is the one its text names.  The logits are the
+    fp32 ones of router_logits, widened exactly; the log-sum-exp subtracts
+    the row maximum first, which leaves it unchanged.
+    """
+    z64 = np.asarray(z, dtype=np.float64)
+    m = np.max(z64, axis=-1)
+    lse = m + np.log(np.sum(np.exp(z64 - m[:, None]), axis=-1))
+    return float(np.mean(lse * lse))
+
+
 # ---------------------------------------------------------------------------
 # O6 capacity
 # ---------------------------------------------------------------------------
@@ -310,7 +329,7 @@ def forward(x, W_r, W1, W2, *, k, cf, alpha, act, dtype, W3=None, b1=None, b2=No
 
     Keys: z (fp32 logits), p (float64 probabilities), expert_idx, gate,
     prob_sum (sum_t p), route_count, C, slot, drop_mask, expert_count,
-    ybuf [E, C, d], y [T, d] (float64, MoE branch only), aux_loss.
+    ybuf [E, C, d], y [T, d] (float64, MoE branch only), aux_loss, z_loss.
     With `tokens` (or `experts`) given, expert outputs, ybuf and y are only
     evaluated for those tokens (experts); the routing is always complete.
     """
@@ -325,7 +344,7 @@ def forward(x, W_r, W1, W2, *, k, cf, alpha, act, dtype, W3=None, b1=None, b2=No
     return dict(z=z, p=p, expert_idx=idx, gate=g, prob_sum=p.sum(axis=0),
                 route_count=route_count(idx, E), C=C, slot=slot, drop_mask=drop,
                 expert_count=count, ybuf=ybuf, y=y,
-                aux_loss=aux_loss(p, idx, E, alpha))
+                aux_loss=aux_loss(p, idx, E, alpha), z_loss=router_z_loss(z))
 
 
 def forward_cfg(cfg: dict, experts=None, tokens=None) -> dict:

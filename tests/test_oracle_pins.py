@@ -383,6 +383,47 @@ def test_mixtral_sizes():
 
 
 # ---------------------------------------------------------------------------
+# router z-loss ([CMU-L16] section 4.2): mean over tokens of logsumexp^2
+# ---------------------------------------------------------------------------
+
+def check_z_loss_zero_router():
+    """W_r = 0: every logit is 0, so each token's log-sum-exp is ln E exactly."""
+    for E in (1, 2, 8, 64, 256):
+        x = np.ones((7, 16))
+        z = O.router_logits(x, np.zeros((E, 16), np.float32))
+        assert abs(O.router_z_loss(z) - math.log(E) ** 2) <= 1e-12 * max(1.0, math.log(E) ** 2)
+
+
+def check_z_loss_equal_logits():
+    """A row of E equal logits a has log-sum-exp a + ln E: the value is
+    mean_t (a_t + ln E)^2, also where exp(a) overflows fp32 and fp64 (a = 800)."""
+    E = 8
+    a = np.array([0.0, 1.5, -3.0, 80.0, -100.0, 800.0, -800.0])
+    z = np.repeat(a[:, None], E, axis=1).astype(np.float32)
+    want = float(np.mean((a.astype(np.float32).astype(np.float64) + math.log(E)) ** 2))
+    assert abs(O.router_z_loss(z) - want) <= 1e-12 * want
+
+
+def test_z_loss_zero_router():
+    check_z_loss_zero_router()
+
+
+def test_z_loss_equal_logits():
+    check_z_loss_equal_logits()
+
+
+def test_z_loss_brute_force():
+    """Tiny random logits against a pure-Python log-sum-exp, token by token."""
+    rng = np.random.default_rng(4)
+    z = (rng.standard_normal((9, 5)) * 3).astype(np.float32)
+    tot = 0.0
+    for row in z.tolist():
+        lse = math.log(sum(math.exp(v) for v in row))
+        tot += lse * lse
+    assert abs(O.router_z_loss(z) - tot / z.shape[0]) <= 1e-12 * tot
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -475,3 +516,26 @@ def test_planted_first_rank_only_aux_is_caught(monkeypatch):
     monkeypatch.setattr(O, "aux_loss", lambda p, idx, E, a: orig(p, idx[:, :1], E, a))
     with pytest.raises(AssertionError):
         test_aux_k2_counts_both_ranks()
+
+
+def _z_loss_max_not_lse(z):
+    m = np.max(np.asarray(z, np.float64), axis=-1)
+    return float(np.mean(m * m))
+
+
+def _z_loss_unsquared(z):
+    z64 = np.asarray(z, np.float64)
+    m = np.max(z64, axis=-1)
+    return float(np.mean(m + np.log(np.sum(np.exp(z64 - m[:, None]), axis=-1))))
+
+
+@pytest.mark.parametrize("repl", [_z_loss_max_not_lse, _z_loss_unsquared])
+def test_planted_z_loss_mistake_is_caught(monkeypatch, repl):
+    monkeypatch.setattr(O, "router_z_loss", repl)
+    failed = 0
+    for check in (check_z_loss_zero_router, check_z_loss_equal_logits):
+        try:
+            check()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
