@@ -384,7 +384,8 @@ def main(argv=None):
         L.check("moe_forward_staged", L.LIB.moe_forward_staged(
             _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
             _ptr(b2), _ACT[cfg["act"]], cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"],
-            plan.capacity_factor, plan.alpha, _ptr(plan.y), _ptr(plan.aux), _ptr(plan.expert_idx),
+            plan.capacity_factor, plan.alpha, _ptr(plan.y), _ptr(plan.aux), _ptr(plan.z_loss),
+            _ptr(plan.expert_idx),
             _ptr(plan.gate), _ptr(plan.drop_mask), _ptr(plan.ws), plan.ws.numel(),
             stream.cuda_stream, arr))
 

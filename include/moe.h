@@ -117,6 +117,11 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
  *   prob_sum    [E]     fp32 out, sum over tokens of the softmax p_i(x)
  *   route_count [E]     int32 out, number of (token, rank) choices per expert
  *                       (before capacity)
+ *   z_loss      [1]     fp32 out, or NULL: the router z-loss
+ *                       (1/T) sum_t (log sum_i exp z_ti)^2 over the fp32
+ *                       logits z ([CMU-L16] section 4.2, the z-loss of Zoph
+ *                       et al.; unweighted: the training loss multiplies it,
+ *                       by 0.001 in OLMoE); 0 for T = 0
  *   ws          moe_router_workspace_bytes(T, d, E, k) bytes of device scratch
  *               (per-block partial sums, and for bf16 x with E <= 256 the
  *               exact three-part bf16 split of W_r that the MFMA path reads)
@@ -126,7 +131,7 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
 moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k,
                       int32_t *expert_idx, float *gate, float *prob_sum, int32_t *route_count,
-                      void *ws, size_t ws_bytes, hipStream_t stream);
+                      float *z_loss, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Dispatch: capacity slots in token order and the expert-major permutation.
@@ -185,9 +190,10 @@ moe_status moe_combine(const void *ybuf, moe_dtype dt, const int32_t *expert_idx
 /*
  * The whole layer: router, dispatch, experts, combine and loss, enqueued
  * back to back with C = moe_capacity(T, E, k, capacity_factor).  Outputs
- * y [T,d] (storage dtype, MoE branch only), aux_loss [1] fp32,
- * expert_idx [T,k] int32, gate [T,k] fp32, drop_mask [T,k] uint8; every
- * other intermediate stays in `ws` (see moe_forward_workspace_layout).
+ * y [T,d] (storage dtype, MoE branch only), aux_loss [1] fp32, z_loss [1]
+ * fp32 or NULL (the router z-loss, as moe_router), expert_idx [T,k] int32,
+ * gate [T,k] fp32, drop_mask [T,k] uint8; every other intermediate stays in
+ * `ws` (see moe_forward_workspace_layout).
  * The results are those of moe_router, moe_dispatch, moe_expert_ffn and
  * moe_combine called in turn, bit for bit; with bf16 the forward fuses the
  * dispatch copy into the first expert GEMM (it reads the token rows of x
@@ -198,7 +204,7 @@ moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const floa
                        const void *W1, const void *b1, const void *W3, const void *W2,
                        const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
                        int32_t E, int32_t k, double capacity_factor, float alpha,
-                       void *y, float *aux_loss, int32_t *expert_idx, float *gate,
+                       void *y, float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
                        uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -219,9 +225,9 @@ moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, con
                               const void *W1, const void *b1, const void *W3, const void *W2,
                               const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
                               int32_t E, int32_t k, double capacity_factor, float alpha,
-                              void *y, float *aux_loss, int32_t *expert_idx, float *gate,
-                              uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream,
-                              hipEvent_t *stage_events);
+                              void *y, float *aux_loss, float *z_loss, int32_t *expert_idx,
+                              float *gate, uint8_t *drop_mask, void *ws, size_t ws_bytes,
+                              hipStream_t stream, hipEvent_t *stage_events);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ SIGNATURES = {
     "moe_forward_workspace_layout": (C.c_int, [_i64, _i32, _i32, _i32, _i32, _i64, C.c_int,
                                                C.c_int, C.POINTER(WsLayout)]),
     "moe_router": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p,
-                             _p, _sz, _p]),
+                             _p, _p, _sz, _p]),
     "moe_dispatch": (C.c_int, [_p, C.c_int, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p, _p,
                                _p, _sz, _p]),
     "moe_expert_ffn": (C.c_int, [_p, C.c_int, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p, _p,
@@ -54,10 +54,11 @@ SIGNATURES = {
     "moe_combine": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64,
                               C.c_float, _p, _p, _p]),
     "moe_forward": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _p, C.c_int, _i64, _i32, _i32,
-                              _i32, _i32, C.c_double, C.c_float, _p, _p, _p, _p, _p, _p, _sz, _p]),
+                              _i32, _i32, C.c_double, C.c_float, _p, _p, _p, _p, _p, _p, _p, _sz,
+                              _p]),
     "moe_forward_staged": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _p, C.c_int, _i64, _i32,
                                      _i32, _i32, _i32, C.c_double, C.c_float, _p, _p, _p, _p, _p, _p,
-                                     _sz, _p, _p]),
+                                     _p, _sz, _p, _p]),
 }
 
 MOE_STAGE_EVENTS = 6

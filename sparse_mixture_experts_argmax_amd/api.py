@@ -66,8 +66,10 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
 
 
-def router(x, W_r, k: int = 1, b_r=None, workspace=None):
-    """Router: returns (expert_idx [T,k] int32, gate [T,k] fp32, prob_sum [E] fp32, route_count [E] int32)."""
+def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False):
+    """Router: returns (expert_idx [T,k] int32, gate [T,k] fp32, prob_sum [E] fp32, route_count [E] int32),
+    and with z_loss=True also the router z-loss [1] fp32 (mean over tokens of the squared
+    log-sum-exp of the logits)."""
     T, d = x.shape
     E = W_r.shape[0]
     dev = x.device
@@ -76,13 +78,16 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None):
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
     route_count = torch.empty(E, dtype=torch.int32, device=dev)
+    zl = torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None
     need = L.LIB.moe_router_workspace_bytes(T, d, E, k)
     if need == L.SIZE_MAX:
         raise ValueError("invalid router sizes")
     ws = workspace if workspace is not None else _workspace(need, dev)
     L.check("moe_router", L.LIB.moe_router(
         _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
-        _ptr(prob_sum), _ptr(route_count), _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(ws), ws.numel(), _stream(dev)))
+    if z_loss:
+        return idx, gate, prob_sum, route_count, zl
     return idx, gate, prob_sum, route_count
 
 
@@ -142,7 +147,8 @@ class ForwardPlan:
 
     plan = ForwardPlan(T, d, dff, E, k, dtype, act=..., capacity_factor=..., alpha=...)
     y, aux, idx, gate, drop = plan(x, W_r, W1, W2, W3=..., b1=..., b2=..., b_r=...)
-    Each call overwrites the same output tensors.
+    Each call overwrites the same output tensors; plan.z_loss holds the
+    router z-loss of the last call.
     """
 
     def __init__(self, T, d, dff, E, k, dtype, *, act="relu", capacity_factor=1.25, alpha=1e-2,
@@ -155,6 +161,7 @@ class ForwardPlan:
         self.device = dev
         self.y = torch.empty((T, d), dtype=dtype, device=dev)
         self.aux = torch.empty(1, dtype=torch.float32, device=dev)
+        self.z_loss = torch.empty(1, dtype=torch.float32, device=dev)
         self.expert_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.gate = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.drop_mask = torch.empty((T, k), dtype=torch.uint8, device=dev)
@@ -174,7 +181,8 @@ class ForwardPlan:
         L.check("moe_forward", L.LIB.moe_forward(
             _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
             _ptr(b2), _ACT[self.act], self.T, self.d, self.dff, self.E, self.k,
-            self.capacity_factor, self.alpha, _ptr(self.y), _ptr(self.aux), _ptr(self.expert_idx),
+            self.capacity_factor, self.alpha, _ptr(self.y), _ptr(self.aux), _ptr(self.z_loss),
+            _ptr(self.expert_idx),
             _ptr(self.gate), _ptr(self.drop_mask), _ptr(self.ws), self.ws.numel(), s))
         return self.y, self.aux, self.expert_idx, self.gate, self.drop_mask
 

@@ -32,6 +32,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// The router z-loss (1/T) sum_t (log sum_i exp z_ti)^2 from per-block
+// partial sums of the squared log-sum-exps ([CMU-L16] section 4.2), in fp64
+// by one whole wave in a fixed order (lane-strided sums, then a butterfly),
+// so the router's own reduction and the dispatch scan give the same bits;
+// 0 for T = 0.  Every lane returns the value.
+__device__ __forceinline__ float z_loss_wave(const float *part_z, int nblk, int64_t T, int lane) {
+    double s = 0.0;
+    for (int b = lane; b < nblk; b += 64) s += (double)part_z[b];
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    return T > 0 ? (float)(s / (double)T) : 0.f;
+}
+
 // Auxiliary load-balancing loss alpha * E * sum_i f_i P_i with
 // f_i = route_count_i / (k T) and P_i = prob_sum_i / T ([SW-GLaM] "负载均衡"),
 // in fp64 by one whole wave in a fixed order (lane l sums experts l, l + 64,

@@ -128,7 +128,9 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hi
                                                         int32_t *__restrict__ route_count,
                                                         int32_t *__restrict__ tile_map, int bm,
                                                         unsigned *__restrict__ done, float alpha,
-                                                        int64_t T, int k, float *__restrict__ aux) {
+                                                        int64_t T, int k, float *__restrict__ aux,
+                                                        const float *__restrict__ part_z,
+                                                        float *__restrict__ z_loss) {
     __shared__ int s_last;
     __shared__ int s_wsum[4];
     const int lane = threadIdx.x & 63;
@@ -157,6 +159,11 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(int32_t *__restrict__ hi
             if (lane == 0) {
                 prob_sum[e] = (float)sp;
                 route_count[e] = run;
+            }
+            // the router's z-loss from its block partials (expert 0's wave)
+            if (z_loss != nullptr && e == 0) {
+                const float zl = z_loss_wave(part_z, nblk_r, T, lane);
+                if (lane == 0) z_loss[0] = zl;
             }
         }
     }
@@ -285,10 +292,12 @@ hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, 
 hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
                             int32_t *expert_count, const float *part_prob, int nblk_r,
                             float *prob_sum, int32_t *route_count, int32_t *tile_map, int bm,
-                            unsigned *done, hipStream_t s, int64_t T, float alpha, float *aux) {
+                            unsigned *done, hipStream_t s, int64_t T, float alpha, float *aux,
+                            const float *part_z, float *z_loss) {
+    if (z_loss != nullptr && (part_prob == nullptr || part_z == nullptr)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(slot_scan_kernel, dim3((E + 3) / 4), dim3(256), 0, s, hist, nblk * k, E, C,
                        expert_count, part_prob, nblk_r, prob_sum, route_count, tile_map, bm, done,
-                       alpha, T, k, aux);
+                       alpha, T, k, aux, part_z, z_loss);
     return hipGetLastError();
 }
 

@@ -12,11 +12,16 @@ namespace moe {
 // Number of per-block partial rows the router writes for T tokens.
 int router_blocks(int64_t T, int dtype_bf16, int E);
 // w3: scratch of 3 * E * d bf16 for the exact three-part split of W_r.
+// part_z [router_blocks]: each block's sum of its tokens' squared
+// log-sum-exps (the router z-loss partials).
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
-                         float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s);
+                         float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s,
+                         float *part_z);
+// z_loss (may be null): (1/T) sum of the part_z partials.
 hipError_t launch_router_reduce(const float *part_prob, const int32_t *part_cnt, int nblk,
-                                int E, float *prob_sum, int32_t *route_count, hipStream_t s);
+                                int E, float *prob_sum, int32_t *route_count, hipStream_t s,
+                                const float *part_z, int64_t T, float *z_loss);
 
 // ---- dispatch ---------------------------------------------------------
 constexpr int DISPATCH_TOK_BLOCK = 256;
@@ -31,11 +36,14 @@ hipError_t launch_slot_rank(const int32_t *expert_idx, int64_t T, int E, int k, 
 // would), using the completion counter done that launch_slot_rank zeroed.
 // aux (may be null; needs tile_map): the last block also writes the
 // auxiliary loss from the totals it finished (what launch_combine would).
+// z_loss (may be null; needs part_prob): the router's z-loss from its part_z
+// partials (what launch_router_reduce would, bit for bit).
 hipError_t launch_slot_scan(int32_t *hist, int nblk, int E, int k, int64_t C,
                             int32_t *expert_count, const float *part_prob, int nblk_r,
                             float *prob_sum, int32_t *route_count, int32_t *tile_map, int bm,
                             unsigned *done, hipStream_t s, int64_t T = 0, float alpha = 0.f,
-                            float *aux = nullptr);
+                            float *aux = nullptr, const float *part_z = nullptr,
+                            float *z_loss = nullptr);
 // Slots and drops as launch_permute, but rows are not copied: row_tok[e C +
 // slot] = token for every kept choice.  k = 1 only (both may be null):
 // row_gate[e C + slot] = gate of that choice, and y_zero gets the rows

@@ -24,14 +24,15 @@ bool act_ok(int a) { return a == MOE_ACT_RELU || a == MOE_ACT_SWIGLU; }
 constexpr int64_t ROUTER_MIN_TOK = 8;
 
 struct RouterWs {
-    size_t part_prob, part_cnt, w3, total;
+    size_t part_prob, part_cnt, part_z, w3, total;
 };
 RouterWs router_ws(int64_t T, int d, int E) {
     RouterWs w;
     const int64_t nblk = (T + ROUTER_MIN_TOK - 1) / ROUTER_MIN_TOK;
     w.part_prob = 0;
     w.part_cnt = up((size_t)nblk * E * 4);
-    w.w3 = w.part_cnt + up((size_t)nblk * E * 4);
+    w.part_z = w.part_cnt + up((size_t)nblk * E * 4);
+    w.w3 = w.part_z + up((size_t)nblk * 4);
     w.total = w.w3 + up((size_t)3 * E * d * 2);     // three bf16 parts of W_r
     return w;
 }
@@ -131,22 +132,23 @@ moe_status check_ffn_args(moe_dtype dt, moe_act act, const void *W1, const void 
     return MOE_OK;
 }
 
-// reduce = false leaves prob_sum / route_count to the dispatch scan (the
-// fused forward), which reads the router's partials from ws.
+// reduce = false leaves prob_sum / route_count / z_loss to the dispatch scan
+// (the fused forward), which reads the router's partials from ws.
 moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
-                      float *gate, float *prob_sum, int32_t *route_count, char *ws,
+                      float *gate, float *prob_sum, int32_t *route_count, float *z_loss, char *ws,
                       hipStream_t stream, bool reduce = true) {
     const RouterWs w = router_ws(T, d, E);
     float *part_prob = reinterpret_cast<float *>(ws + w.part_prob);
     int32_t *part_cnt = reinterpret_cast<int32_t *>(ws + w.part_cnt);
+    float *part_z = reinterpret_cast<float *>(ws + w.part_z);
     uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + w.w3);
     const int bf16 = dt == MOE_BF16;
     MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
-                               part_cnt, w3, stream));
+                               part_cnt, w3, stream, part_z));
     if (reduce)
         MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
-                                          prob_sum, route_count, stream));
+                                          prob_sum, route_count, stream, part_z, T, z_loss));
     return MOE_OK;
 }
 
@@ -160,7 +162,8 @@ moe_status run_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, 
                         float *prob_sum = nullptr, int32_t *route_count = nullptr,
                         int32_t *tile_map = nullptr, int bm = 0, int32_t *row_tok = nullptr,
                         void *y_zero = nullptr, float alpha = 0.f, float *aux = nullptr,
-                        const float *gate = nullptr, float *row_gate = nullptr) {
+                        const float *gate = nullptr, float *row_gate = nullptr,
+                        const float *part_z = nullptr, float *z_loss = nullptr) {
     const DispatchWs w = dispatch_ws(T, E, k);
     int32_t *rank = reinterpret_cast<int32_t *>(ws + w.rank);
     int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
@@ -172,7 +175,7 @@ moe_status run_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, 
                                   stream));
     MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, C, expert_count, part_prob,
                                   nblk_r, prob_sum, route_count, late ? nullptr : tile_map, bm, done,
-                                  stream, T, alpha, late ? nullptr : aux));
+                                  stream, T, alpha, late ? nullptr : aux, part_z, z_loss));
     if (late)
         MOE_HIP(moe::launch_slot_index(expert_idx, rank, hist, T, E, k, C, slot, drop_mask, row_tok,
                                        gate, row_gate, y_zero, d * (int)esize(dt), stream, expert_count,
@@ -267,19 +270,20 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
 
 moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
-                      float *gate, float *prob_sum, int32_t *route_count, void *ws,
-                      size_t ws_bytes, hipStream_t stream) {
+                      float *gate, float *prob_sum, int32_t *route_count, float *z_loss,
+                      void *ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK(check_sizes(T, E, k));
     MOE_CHECK(check_width(d));
     if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
     const bool empty = T == 0;
     if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr4_ok(expert_idx, empty) ||
-        !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false))
+        !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false) ||
+        !(z_loss == nullptr || ptr4_ok(z_loss, false)))
         return MOE_ERR_INVALID_ARGUMENT;
     const size_t need = router_ws(T, d, E).total;
     if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
-    return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
+    return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count, z_loss,
                       static_cast<char *>(ws), stream);
 }
 
@@ -346,8 +350,8 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
                         const void *W1, const void *b1, const void *W3, const void *W2,
                         const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff, int32_t E,
                         int32_t k, double capacity_factor, float alpha, void *y, float *aux_loss,
-                        int32_t *expert_idx, float *gate, uint8_t *drop_mask, void *ws,
-                        size_t ws_bytes, hipStream_t stream, hipEvent_t *ev) {
+                        float *z_loss, int32_t *expert_idx, float *gate, uint8_t *drop_mask,
+                        void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *ev) {
     MOE_CHECK(check_sizes(T, E, k));
     MOE_CHECK(check_width(d));
     MOE_CHECK(check_width(dff));
@@ -357,8 +361,8 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     if (C < 0) return MOE_ERR_INVALID_ARGUMENT;
     const bool empty = T == 0;
     if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr_ok(y, empty) ||
-        !ptr4_ok(aux_loss, false) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(gate, empty) ||
-        (drop_mask == nullptr && !empty))
+        !ptr4_ok(aux_loss, false) || !(z_loss == nullptr || ptr4_ok(z_loss, false)) || !ptr4_ok(expert_idx, empty) ||
+        !ptr4_ok(gate, empty) || (drop_mask == nullptr && !empty))
         return MOE_ERR_INVALID_ARGUMENT;
     if (ev != nullptr) {
         for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
@@ -395,7 +399,7 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     int32_t *row_tok = gather ? reinterpret_cast<int32_t *>(base + w.row_tok) : nullptr;
     float *row_gate = scatter ? reinterpret_cast<float *>(base + w.row_gate) : nullptr;
     MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
-                         base + w.router, stream, !fuse_reduce));
+                         z_loss, base + w.router, stream, !fuse_reduce));
     if (!mark(1)) return MOE_ERR_HIP;
     MOE_CHECK(run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
                            base + w.dispatch, stream,
@@ -403,7 +407,10 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
                                        : nullptr,
                            moe::router_blocks(T, bf16, E), prob_sum, route_count,
                            T > 0 && C > 0 ? tile_map : nullptr, bm, row_tok, scatter ? y : nullptr,
-                           alpha, scatter ? aux_loss : nullptr, gate, row_gate));
+                           alpha, scatter ? aux_loss : nullptr, gate, row_gate,
+                           fuse_reduce ? reinterpret_cast<const float *>(base + w.router + w.r.part_z)
+                                       : nullptr,
+                           fuse_reduce ? z_loss : nullptr));
     if (!mark(2)) return MOE_ERR_HIP;
     if (C > 0)
         MOE_HIP(moe::launch_grouped_gemm(gather ? x : xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map,
@@ -429,10 +436,10 @@ moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const floa
                        const void *W1, const void *b1, const void *W3, const void *W2,
                        const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
                        int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
-                       float *aux_loss, int32_t *expert_idx, float *gate, uint8_t *drop_mask,
-                       void *ws, size_t ws_bytes, hipStream_t stream) {
+                       float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
+                       uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream) {
     return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k,
-                        capacity_factor, alpha, y, aux_loss, expert_idx, gate, drop_mask, ws,
+                        capacity_factor, alpha, y, aux_loss, z_loss, expert_idx, gate, drop_mask, ws,
                         ws_bytes, stream, nullptr);
 }
 
@@ -440,12 +447,12 @@ moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, con
                               const void *W1, const void *b1, const void *W3, const void *W2,
                               const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,
                               int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
-                              float *aux_loss, int32_t *expert_idx, float *gate,
+                              float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
                               uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t *stage_events) {
     if (stage_events == nullptr) return MOE_ERR_INVALID_ARGUMENT;
     return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k,
-                        capacity_factor, alpha, y, aux_loss, expert_idx, gate, drop_mask, ws,
+                        capacity_factor, alpha, y, aux_loss, z_loss, expert_idx, gate, drop_mask, ws,
                         ws_bytes, stream, stage_events);
 }
 

@@ -90,7 +90,7 @@ template <int NB, int KC, bool KTAIL, int KSEL>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
-    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt) {
+    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z) {
     using G = RGeo<NB, KC>;
     constexpr int EP = G::EP, ROWB = G::ROWB, PIECES = G::PIECES, S = G::S, PERW = G::PERW;
     constexpr int STAGE = G::STAGE, RPI = G::RPI;
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
     __shared__ float sProb[RM_WAVES][EP];
     __shared__ int sCnt[EP];
+    __shared__ float sLz[RM_TOK_BLOCK];                 // each token's log-sum-exp, squared
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -323,6 +324,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) psum[nb] = fmaf(ex[nb], inv, psum[nb]);
         }
+        if (col == 0) {
+            // z-loss term: log sum_i exp z_i = max + log sum_i exp(z_i - max)
+            const float l = mx + logf(s);
+            sLz[tok] = tok_ok ? l * l : 0.f;
+        }
 
         // top-k by k rounds over the not-yet-chosen experts: the round's
         // largest logit (a 16-lane max), then the lowest expert index holding
@@ -402,6 +408,13 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         part_prob[(int64_t)blockIdx.x * E + n] = s;
         part_cnt[(int64_t)blockIdx.x * E + n] = sCnt[n];
     }
+    // the block's z-loss partial, summed in a fixed order
+    if (tid < RM_TOK_BLOCK) {
+        static_assert(RM_TOK_BLOCK == 64, "one wave sums the block's tokens");
+        float v = sLz[tid];
+        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+        if (tid == 0) part_z[blockIdx.x] = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -413,8 +426,9 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void router_generic_kernel(
     const void *__restrict__ xv, const float *__restrict__ Wr, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
-    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt) {
+    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z) {
     extern __shared__ float smem[];
+    __shared__ float sLz[RG_TOK];                       // each token's log-sum-exp, squared
     float *sZ = smem;                                   // [RG_TOK][E]
     int *sCnt = reinterpret_cast<int *>(smem + RG_TOK * E);   // [E]
 
@@ -456,6 +470,10 @@ __global__ __launch_bounds__(256) void router_generic_kernel(
             float s = 0.f;
             for (int n = lane; n < E; n += 64) s += expf(row[n] - mx);
             for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+            if (lane == 0) {
+                const float l = mx + logf(s);           // log sum_i exp z_i
+                sLz[r] = l * l;
+            }
             float vsel[MAXK];
             int isel[MAXK];
             for (int j = 0; j < MAXK; ++j) {
@@ -503,9 +521,15 @@ __global__ __launch_bounds__(256) void router_generic_kernel(
             }
         } else {
             for (int n = lane; n < E; n += 64) row[n] = 0.f;
+            if (lane == 0) sLz[r] = 0.f;
         }
     }
     __syncthreads();
+    if (tid == 0) {
+        float v = 0.f;
+        for (int r = 0; r < RG_TOK; ++r) v += sLz[r];
+        part_z[blockIdx.x] = v;
+    }
     for (int n = tid; n < E; n += 256) {
         float s = 0.f;
         for (int r = 0; r < RG_TOK; ++r) s += sZ[r * E + n];
@@ -519,7 +543,8 @@ __global__ __launch_bounds__(256) void router_generic_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void router_reduce_kernel(
     const float *__restrict__ part_prob, const int32_t *__restrict__ part_cnt, int nblk, int E,
-    float *__restrict__ prob_sum, int32_t *__restrict__ route_count) {
+    float *__restrict__ prob_sum, int32_t *__restrict__ route_count, const float *__restrict__ part_z,
+    int64_t T, float *__restrict__ z_loss) {
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
@@ -537,6 +562,10 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(
         prob_sum[e] = (float)s;
         route_count[e] = (int32_t)c;
     }
+    if (z_loss != nullptr && e == 0) {
+        const float zl = z_loss_wave(part_z, nblk, T, lane);
+        if (lane == 0) z_loss[0] = zl;
+    }
 }
 
 bool use_mfma(int dtype_bf16, int E) { return dtype_bf16 && E <= 256; }
@@ -550,7 +579,8 @@ int router_blocks(int64_t T, int dtype_bf16, int E) {
 
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
-                         float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s) {
+                         float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s,
+                         float *part_z) {
     const int nblk = router_blocks(T, dtype_bf16, E);
     if (nblk == 0) return hipSuccess;
     if (use_mfma(dtype_bf16, E)) {
@@ -561,7 +591,7 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
         const int nb = (E + 15) / 16;
 #define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV)                                                \
     hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV>), dim3(nblk), dim3(256), 0, s,  \
-                       xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt)
+                       xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z)
 #define MOE_ROUTER_K(NBV, KCV, TAILV)                                                          \
     do {                                                                                       \
         if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1);                                     \
@@ -586,17 +616,18 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
     const size_t shm = (size_t)(RG_TOK + 1) * E * sizeof(float);
     if (dtype_bf16)
         hipLaunchKernelGGL(router_generic_kernel<true>, dim3(nblk), dim3(256), shm, s, x, W_r,
-                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt);
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z);
     else
         hipLaunchKernelGGL(router_generic_kernel<false>, dim3(nblk), dim3(256), shm, s, x, W_r,
-                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt);
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z);
     return hipGetLastError();
 }
 
 hipError_t launch_router_reduce(const float *part_prob, const int32_t *part_cnt, int nblk,
-                                int E, float *prob_sum, int32_t *route_count, hipStream_t s) {
+                                int E, float *prob_sum, int32_t *route_count, hipStream_t s,
+                                const float *part_z, int64_t T, float *z_loss) {
     hipLaunchKernelGGL(router_reduce_kernel, dim3((E + 3) / 4), dim3(256), 0, s, part_prob,
-                       part_cnt, nblk, E, prob_sum, route_count);
+                       part_cnt, nblk, E, prob_sum, route_count, part_z, T, z_loss);
     return hipGetLastError();
 }
 

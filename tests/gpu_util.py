@@ -13,6 +13,8 @@ Comparison rules
   * y: on tokens whose choices agree; bf16 storage: max-abs 2e-2 and
     sum|dy| / sum|y_ref| <= 5e-3; fp32 storage: 1e-5 for both.
   * aux_loss: relative 1e-5 against the oracle's loss on the GPU's choices.
+  * z_loss: relative 1e-5 against the oracle's on the same fp32 logits (the
+    per-token log-sum-exp is fp32 on the GPU, the sums fp64).
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ DEV = "cuda:0"
 Y_TOL = {"bf16": (2e-2, 5e-3), "f32": (1e-5, 1e-5)}
 GATE_RTOL = 1e-5
 AUX_RTOL = 1e-5
+Z_RTOL = 1e-5
 NEAR_TIE_GAP = 1e-5
 MAX_TIE_FRACTION = 1e-4
 

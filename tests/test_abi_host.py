@@ -104,13 +104,14 @@ P = 4096          # an aligned stand-in address (never dereferenced: every case 
     (dict(x=P + 2), L.MOE_ERR_INVALID_ARGUMENT),              # misaligned
     (dict(W_r=None), L.MOE_ERR_INVALID_ARGUMENT),
     (dict(ws_bytes=0), L.MOE_ERR_WORKSPACE_TOO_SMALL),
+    (dict(zl=P + 1), L.MOE_ERR_INVALID_ARGUMENT),              # misaligned z-loss output
 ])
 def test_router_rejects(case, expect):
     a = dict(x=P, dt=L.MOE_BF16, W_r=P, b_r=None, T=64, d=64, E=8, k=1, idx=P, gate=P, ps=P, rc=P,
-             ws=P, ws_bytes=1 << 30)
+             zl=None, ws=P, ws_bytes=1 << 30)
     a.update(case)
     st = L.LIB.moe_router(a["x"], a["dt"], a["W_r"], a["b_r"], a["T"], a["d"], a["E"], a["k"],
-                          a["idx"], a["gate"], a["ps"], a["rc"], a["ws"], a["ws_bytes"], None)
+                          a["idx"], a["gate"], a["ps"], a["rc"], a["zl"], a["ws"], a["ws_bytes"], None)
     assert st == expect
 
 
@@ -132,12 +133,12 @@ def test_router_rejects(case, expect):
 def test_forward_rejects(case, expect):
     a = dict(x=P, dt=L.MOE_BF16, W_r=P, b_r=None, W1=P, b1=None, W3=None, W2=P, b2=None,
              act=L.MOE_ACT_RELU, T=64, d=64, dff=128, E=8, k=1, cf=1.25, alpha=0.01, y=P, aux=P,
-             idx=P, gate=P, drop=P, ws=P, ws_bytes=1 << 40)
+             zl=None, idx=P, gate=P, drop=P, ws=P, ws_bytes=1 << 40)
     a.update(case)
     st = L.LIB.moe_forward(a["x"], a["dt"], a["W_r"], a["b_r"], a["W1"], a["b1"], a["W3"], a["W2"],
                            a["b2"], a["act"], a["T"], a["d"], a["dff"], a["E"], a["k"], a["cf"],
-                           a["alpha"], a["y"], a["aux"], a["idx"], a["gate"], a["drop"], a["ws"],
-                           a["ws_bytes"], None)
+                           a["alpha"], a["y"], a["aux"], a["zl"], a["idx"], a["gate"], a["drop"],
+                           a["ws"], a["ws_bytes"], None)
     assert st == expect
 
 

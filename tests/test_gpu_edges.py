@@ -4,7 +4,8 @@ Each case has a result fixed by the method's definition, checked directly,
 on top of the usual parity with the oracle:
   * all logits tied (W_r = 0): every token takes experts 0 .. k-1 (the lower
     index wins ties), so the capacity rule keeps exactly the first C tokens of
-    each rank, and aux / alpha = 1 (P_i = 1/E for every i);
+    each rank, aux / alpha = 1 (P_i = 1/E for every i), and the router
+    z-loss is (ln E)^2;
   * the fp32 router: logits 4.00 and 4.01, which bf16 rounding would tie,
     route to expert 1;
   * one token, one expert, k = E, a capacity of one row, the largest E and
@@ -63,6 +64,8 @@ def test_all_ties_take_the_lowest_indices(k):
     for j in range(k):
         assert (slot[:, j] == np.where(ar < C, ar, -1)).all()
     assert abs(float(aux.cpu()[0]) / cfg["alpha"] - 1.0) <= 1e-5
+    # every log-sum-exp is ln E: the z-loss is (ln E)^2
+    assert abs(float(plan.z_loss.cpu()[0]) - np.log(E) ** 2) <= 1e-6 * np.log(E) ** 2
     _forward_checks(cfg)
 
 

@@ -13,7 +13,8 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
-from gpu_util import (AUX_RTOL, Y_TOL, check_routing, check_y, device_inputs, host_bits, host_f64)
+from gpu_util import (AUX_RTOL, Y_TOL, Z_RTOL, check_routing, check_y, device_inputs, host_bits,
+                      host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,12 +61,20 @@ def _full(name, with_experts=True):
 
 def _run_router(cfg):
     t = device_inputs(cfg)
-    idx, gate, prob_sum, route_count = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    idx, gate, prob_sum, route_count, zl = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"],
+                                                      z_loss=True)
     torch.cuda.synchronize()
+    t["z_loss"] = zl
     return t, idx, gate, prob_sum, route_count
 
 
-def _router_checks(cfg, idx, gate, prob_sum, route_count):
+def _check_z_loss(z_gpu, z_logits):
+    """The router z-loss against the oracle's on the same fp32 logits."""
+    ref = O.router_z_loss(z_logits)
+    assert abs(float(z_gpu) - ref) <= Z_RTOL * abs(ref), (float(z_gpu), ref)
+
+
+def _router_checks(cfg, idx, gate, prob_sum, route_count, z_loss=None):
     x64 = O.widen(cfg["x"], cfg["dtype"])
     z = O.router_logits(x64, cfg["W_r"], cfg["b_r"])
     p = O.softmax(z)
@@ -76,6 +85,8 @@ def _router_checks(cfg, idx, gate, prob_sum, route_count):
     E = cfg["E"]
     assert (route_count.cpu().numpy() == O.route_count(gi, E)).all()
     np.testing.assert_allclose(prob_sum.cpu().numpy(), p.sum(axis=0), rtol=2e-6, atol=1e-6)
+    if z_loss is not None:
+        _check_z_loss(z_loss.cpu()[0], z)
     return z, p, gi, agree
 
 
@@ -84,14 +95,14 @@ def test_router_full(name):
     cfg = _full(name, with_experts=False)
     print(f"router parity: {name} T={cfg['T']} E={cfg['E']} k={cfg['k']}", flush=True)
     t, idx, gate, ps, rc = _run_router(cfg)
-    _router_checks(cfg, idx, gate, ps, rc)
+    _router_checks(cfg, idx, gate, ps, rc, t["z_loss"])
 
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_router_small(name):
     cfg = _small(name)
     t, idx, gate, ps, rc = _run_router(cfg)
-    _router_checks(cfg, idx, gate, ps, rc)
+    _router_checks(cfg, idx, gate, ps, rc, t["z_loss"])
 
 
 def _dispatch_checks(cfg, t, gi, C):
@@ -157,6 +168,8 @@ def _forward_checks(cfg, tokens=None):
     # the loss: the oracle's definition on the GPU's choices
     aux_ref = O.aux_loss(ref["p"], gi, cfg["E"], cfg["alpha"])
     assert abs(float(aux.cpu()[0]) - aux_ref) <= AUX_RTOL * abs(aux_ref)
+    # the router z-loss (independent of the selection)
+    _check_z_loss(plan.z_loss.cpu()[0], ref["z"])
     # dropped everywhere -> y == 0
     all_dropped = np.all(rd == 1, axis=1)
     if all_dropped.any():
@@ -194,7 +207,7 @@ def test_split_api_equals_forward():
     cfg = _small("top2_swiglu", seed=3)
     t = device_inputs(cfg)
     C = moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
-    idx, gate, ps, rc = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    idx, gate, ps, rc, zl = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"], z_loss=True)
     slot, drop, count, xbuf = moe.dispatch(t["x"], idx, cfg["E"], C)
     ybuf = moe.expert_ffn(xbuf, count, t["W1"], t["W2"], W3=t["W3"], act=cfg["act"])
     y, aux = moe.combine(ybuf, idx, slot, gate, ps, rc, cfg["T"], alpha=cfg["alpha"])
@@ -206,6 +219,11 @@ def test_split_api_equals_forward():
     assert torch.equal(gate.view(torch.int32), gate2.view(torch.int32))
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(aux.view(torch.int32), aux2.view(torch.int32))
+    plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"], t["x"].dtype,
+                           act=cfg["act"], capacity_factor=cfg["cf"], alpha=cfg["alpha"])
+    plan(t["x"], t["W_r"], t["W1"], t["W2"], W3=t["W3"], b_r=t["b_r"])
+    torch.cuda.synchronize()
+    assert torch.equal(zl.view(torch.int32), plan.z_loss.view(torch.int32))
 
 
 @pytest.mark.parametrize("name", ["switch_base", "top2_swiglu"])
@@ -232,7 +250,7 @@ def _ffn_rows(cfg, sample=None, seed=7):
     that many rows plus the first and last row of every non-empty expert."""
     t = device_inputs(cfg)
     C = moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
-    idx, gate, ps, rc = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    idx, gate, ps, rc, zl = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"], z_loss=True)
     slot, drop, count, xbuf = moe.dispatch(t["x"], idx, cfg["E"], C)
     ybuf = moe.expert_ffn(xbuf, count, t["W1"], t["W2"], W3=t["W3"], b1=t["b1"], b2=t["b2"],
                           act=cfg["act"])
