@@ -56,6 +56,32 @@ def router_logits(x64: np.ndarray, W_r: np.ndarray, b_r: np.ndarray | None = Non
     return z.astype(np.float32)
 
 
+def softplus(a: np.ndarray) -> np.ndarray:
+    """log(1 + exp(a)) in float64, without overflow for large a."""
+    a = np.asarray(a, dtype=np.float64)
+    return np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a)))
+
+
+def noisy_router_logits(x64: np.ndarray, W_r: np.ndarray, b_r: np.ndarray | None,
+                        W_noise: np.ndarray, eps: np.ndarray) -> np.ndarray:
+    """Noisy top-k logits H = W_r x (+ b_r) + eps * softplus(W_noise x), as fp32.
+
+    [CMU-L16] section 2.3 (noisy top-k of Shazeer et al.): a learned,
+    input-dependent noise scale softplus(W_noise x) times standard normal
+    draws eps is added to the router logits before the top-k, so a token
+    sometimes goes to a lower choice; W_g and W_noise start at zero.  The
+    page's formula image is missing; this is the form of the paper it
+    cites.  eps [T, E] is an input (the method's random numbers are passed
+    in).  The clean logit and the noise logit are the correctly rounded fp32
+    values of router_logits; H is formed from them in float64 and rounded
+    once to fp32.  H then takes the place of the logits everywhere
+    downstream: softmax, selection, gates, the loss statistics and z-loss.
+    """
+    z = router_logits(x64, W_r, b_r).astype(np.float64)
+    zn = router_logits(x64, W_noise).astype(np.float64)
+    return (z + np.asarray(eps, dtype=np.float64) * softplus(zn)).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # O2 softmax
 # ---------------------------------------------------------------------------

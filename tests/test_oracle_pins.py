@@ -424,6 +424,66 @@ def test_z_loss_brute_force():
 
 
 # ---------------------------------------------------------------------------
+# noisy top-k ([CMU-L16] section 2.3): H = W_r x + eps * softplus(W_noise x)
+# ---------------------------------------------------------------------------
+
+def _noisy_case(seed=5, T=40, d=16, E=6):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    W_r = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    W_n = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    eps = rng.standard_normal((T, E)).astype(np.float32)
+    return x, W_r, W_n, eps
+
+
+def check_noisy_without_noise():
+    """eps = 0: the noisy logits are the clean ones, bit for bit."""
+    x, W_r, W_n, eps = _noisy_case()
+    H = O.noisy_router_logits(x, W_r, None, W_n, np.zeros_like(eps))
+    assert np.array_equal(H, O.router_logits(x, W_r))
+
+
+def check_noisy_zero_noise_weights():
+    """W_noise = 0: softplus(0) = ln 2, so H = z + eps ln 2 (rounded once to fp32)."""
+    x, W_r, W_n, eps = _noisy_case()
+    H = O.noisy_router_logits(x, W_r, None, np.zeros_like(W_n), eps)
+    want = (O.router_logits(x, W_r).astype(np.float64) + eps.astype(np.float64) * math.log(2.0))
+    assert np.array_equal(H, want.astype(np.float32))
+
+
+def check_noisy_zero_init_routes_by_noise():
+    """W_r = W_noise = 0 (the page's initialisation): H = eps ln 2, so each
+    token goes to the expert of its largest draw (lowest index on ties) --
+    the random, even assignment the page describes."""
+    x, W_r, W_n, eps = _noisy_case(T=2000, E=8)
+    H = O.noisy_router_logits(x, np.zeros_like(W_r), None, np.zeros_like(W_n), eps)
+    assert (O.top_k(H, 1)[:, 0] == np.argmax(eps, axis=1)).all()
+    load = np.bincount(O.top_k(H, 1)[:, 0], minlength=8) / 2000
+    assert np.all(np.abs(load - 1 / 8) < 0.03)
+
+
+def test_noisy_without_noise():
+    check_noisy_without_noise()
+
+
+def test_noisy_zero_noise_weights():
+    check_noisy_zero_noise_weights()
+
+
+def test_noisy_zero_init_routes_by_noise():
+    check_noisy_zero_init_routes_by_noise()
+
+
+def test_softplus_values():
+    """softplus(0) = ln 2, softplus(a) - softplus(-a) = a, and no overflow at +-1000."""
+    a = np.array([0.0, 1.0, -3.0, 20.0, 1000.0, -1000.0])
+    sp = O.softplus(a)
+    assert sp[0] == math.log(2.0)
+    assert np.allclose(O.softplus(a) - O.softplus(-a), a, rtol=0, atol=1e-12)
+    assert sp[4] == 1000.0 and sp[5] == 0.0 and abs(sp[1] - math.log1p(math.e)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -539,3 +599,21 @@ def test_planted_z_loss_mistake_is_caught(monkeypatch, repl):
         except AssertionError:
             failed += 1
     assert failed >= 1
+
+
+def _noisy_exp_scale(x64, W_r, b_r, W_noise, eps):
+    z = O.router_logits(x64, W_r, b_r).astype(np.float64)
+    zn = O.router_logits(x64, W_noise).astype(np.float64)
+    return (z + np.asarray(eps, np.float64) * np.exp(zn)).astype(np.float32)   # exp, not softplus
+
+
+def _noisy_unscaled(x64, W_r, b_r, W_noise, eps):
+    z = O.router_logits(x64, W_r, b_r).astype(np.float64)
+    return (z + np.asarray(eps, np.float64)).astype(np.float32)               # no learned scale
+
+
+@pytest.mark.parametrize("repl", [_noisy_exp_scale, _noisy_unscaled])
+def test_planted_noisy_mistake_is_caught(monkeypatch, repl):
+    monkeypatch.setattr(O, "noisy_router_logits", repl)
+    with pytest.raises(AssertionError):
+        check_noisy_zero_noise_weights()
