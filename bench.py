@@ -100,6 +100,23 @@ def stage_work(cfg: dict, A: int) -> dict:
     }
 
 
+def noisy_router_work(cfg: dict) -> dict:
+    """Algorithmic bytes and flops of one noisy top-k router call.
+
+    x [T,d] + W_r and W_noise [E,d] fp32 + the draws eps [T,E] fp32 read,
+    expert_idx + gate [T,k] written; flops 2 x 2 T d E (the clean and the
+    noise logits).  With bf16 tokens and E <= 256 both are exact fp32 dot
+    products from three bf16 MFMA products each, as in the plain router, so
+    the bound is the bf16 MFMA peak over 3 x 4 T d E flops; otherwise fp32
+    vector ALU.
+    """
+    T, d, E, k = cfg["T"], cfg["d"], cfg["E"], cfg["k"]
+    s = 2 if cfg["dtype"] == "bf16" else 4
+    mfma = cfg["dtype"] == "bf16" and E <= 256
+    return dict(bytes=T * d * s + 2 * E * d * 4 + T * E * 4 + T * k * 8,
+                flops=(3 if mfma else 1) * 4 * T * d * E, dtype="bf16" if mfma else "f32")
+
+
 def roofline_of(work: dict, seconds: float) -> dict:
     """Which roofline bounds a stage, and the achieved rate against that peak."""
     peak_f = PEAK_TFLOPS[work["dtype"]]
@@ -159,8 +176,18 @@ def source_digest() -> str:
 _GEMM_ACT = re.compile(r"gemm_(?:bf16|f32)_kernel<(?:[^<>]*<[^<>]*>, )?(\d+),")
 
 
+_NOISY = re.compile(r"router_generic_kernel<\w+, true>|router_mfma_kernel<\d+, \d+, \w+, \d+, [12]>"
+                    r"|router_split_noisy_kernel|router_reduce_kernel")
+
+
 def kernel_stage(name: str) -> str:
-    """The forward stage a kernel belongs to, from its (demangled) name."""
+    """The forward stage a kernel belongs to, from its (demangled) name.
+
+    The noisy router and the standalone router reduction run only in the
+    noisy-router measurement (the forward sums the router's partials in its
+    dispatch scan), so they form a stage of their own."""
+    if _NOISY.search(name):
+        return "noisy_router"
     if "router" in name:
         return "router"
     if any(t in name for t in ("slot_rank", "slot_scan", "slot_index", "permute_kernel", "tile_map")):
@@ -236,7 +263,7 @@ def summarize(prof_dir: str, workload: str) -> str:
         lines.append(f"| {st} | {fetch.get(st, 0):.1f} | {write.get(st, 0):.1f} | {fb:.0f} | {wb:.0f} "
                      f"| {fb + wb:.0f} |")
     lines += ["", "Per launch means the mean over that stage's kernel launches in the profiled steps; "
-              "the dispatch stage is several kernels, each counted as one launch.", "",
+              "the dispatch and noisy_router stages are several kernels, each counted as one launch.", "",
               TRAFFIC_TAG + json.dumps(dict(workload=workload, source_digest=source_digest(),
                                              fetch_scale=round(f_scale, 5), write_scale=round(w_scale, 5),
                                              stages=traffic)), ""]
@@ -324,6 +351,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="switch_base", choices=datagen.CONFIG_ORDER)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--noisy-calls", type=int, default=20,
+                    help="noisy top-k router calls timed after the steps (0 skips them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel that scales the HBM byte counters), then exit")
@@ -465,6 +494,28 @@ def main(argv=None):
     disp_s = hip.elapsed_ms(disp_ev[0], disp_ev[1]) / n_disp / 1e3
     hip.destroy(disp_ev)
     disp_bytes = 2 * A * cfg["d"] * (2 if cfg["dtype"] == "bf16" else 4) + cfg["T"] * cfg["k"] * 9
+    # the noisy top-k router variant, timed on its own outside the steps:
+    # the same tokens and W_r, seeded W_noise and standard normal draws
+    variants = {}
+    if args.noisy_calls > 0:
+        rng = np.random.default_rng(1)
+        W_n = todev((rng.standard_normal((cfg["E"], cfg["d"])) * np.sqrt(0.1 / cfg["d"])).astype(np.float32))
+        eps = todev(rng.standard_normal((cfg["T"], cfg["E"])).astype(np.float32))
+        rws = torch.empty(L.LIB.moe_router_workspace_bytes(cfg["T"], cfg["d"], cfg["E"], cfg["k"]), dtype=torch.uint8,
+                          device=dev)
+        moe.router(x, W_r, k=cfg["k"], b_r=b_r, workspace=rws, z_loss=True, W_noise=W_n, noise=eps)
+        nz_ev = hip.create(2)
+        hip.record(nz_ev[0], stream.cuda_stream)
+        for _ in range(args.noisy_calls):
+            moe.router(x, W_r, k=cfg["k"], b_r=b_r, workspace=rws, z_loss=True, W_noise=W_n, noise=eps)
+        hip.record(nz_ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        nz_s = hip.elapsed_ms(nz_ev[0], nz_ev[1]) / args.noisy_calls / 1e3
+        hip.destroy(nz_ev)
+        nw = noisy_router_work(cfg)
+        variants["noisy_router"] = dict(us=round(nz_s * 1e6, 2), bytes=nw["bytes"], flops=nw["flops"],
+                                        calls=args.noisy_calls, **roofline_of(nw, nz_s))
+        del W_n, eps, rws
     stages = {}
     for name in L.STAGES:
         r = roofline_of(work[name], stage_ms[name] / 1e3)
@@ -503,6 +554,7 @@ def main(argv=None):
         "permute_GBps": round(disp_bytes / disp_s / 1e9, 1),
         "permute_us": round(disp_s * 1e6, 2),
         "stages": stages,
+        "variants": variants,
         "settle": {"seconds": round(settle_s, 3), "forwards": n_settle},
         "step_ms": {"warm": spread(warm_ms), "cold_mall": spread(cold_ms),
                     "note": "per-forward HIP event intervals (each holds one event record, "

@@ -134,6 +134,27 @@ moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float
                       float *z_loss, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Noisy top-k router: moe_router on the logits
+ *   H = W_r x (+ b_r) + noise * softplus(W_noise x)
+ * ([CMU-L16] section 2.3, the noisy top-k of Shazeer et al.: a learned,
+ * input-dependent noise scale lets a token reach a lower choice; the page's
+ * formula image is missing, and this is the form of the paper it cites).
+ * H takes the place of the logits for the softmax, the selection and its
+ * tie rule, the gates, prob_sum, route_count and z_loss.
+ *   W_noise     [E, d]  fp32 noise weights
+ *   noise       [T, E]  fp32 standard normal draws (the caller draws them)
+ * Other arguments and the workspace as moe_router.  bf16 x with E <= 256
+ * runs the MFMA router on W_r and W_noise (the same exact fp32 products as
+ * moe_router); fp32 x, or E up to 1024, the fp32 FMA path.
+ * The dispatch, expert and combine entry points take its outputs unchanged.
+ */
+moe_status moe_router_noisy(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                            const float *W_noise, const float *noise, int64_t T, int32_t d,
+                            int32_t E, int32_t k, int32_t *expert_idx, float *gate,
+                            float *prob_sum, int32_t *route_count, float *z_loss, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
  * Dispatch: capacity slots in token order and the expert-major permutation.
  * [CS25-L5] "Capacity Factor 与 Token Dropping" (capacity-aware dispatch:
  * tokens in order fill their expert's C slots, overflow skips the expert);

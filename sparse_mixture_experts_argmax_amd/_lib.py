@@ -47,6 +47,8 @@ SIGNATURES = {
                                                C.c_int, C.POINTER(WsLayout)]),
     "moe_router": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p,
                              _p, _p, _sz, _p]),
+    "moe_router_noisy": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p,
+                                   _p, _p, _p, _sz, _p]),
     "moe_dispatch": (C.c_int, [_p, C.c_int, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p, _p,
                                _p, _sz, _p]),
     "moe_expert_ffn": (C.c_int, [_p, C.c_int, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p, _p,

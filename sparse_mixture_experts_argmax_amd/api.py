@@ -66,14 +66,20 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
 
 
-def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False):
+def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W_noise=None,
+           noise=None):
     """Router: returns (expert_idx [T,k] int32, gate [T,k] fp32, prob_sum [E] fp32, route_count [E] int32),
     and with z_loss=True also the router z-loss [1] fp32 (mean over tokens of the squared
-    log-sum-exp of the logits)."""
+    log-sum-exp of the logits).  With W_noise [E,d] fp32 and noise [T,E] fp32 (standard normal
+    draws) the noisy top-k router: the logits become W_r x + noise * softplus(W_noise x)."""
     T, d = x.shape
     E = W_r.shape[0]
     dev = x.device
-    _same(torch.float32, W_r, b_r)
+    _same(torch.float32, W_r, b_r, W_noise, noise)
+    if (W_noise is None) != (noise is None):
+        raise ValueError("the noisy router needs both W_noise and noise")
+    if noise is not None and tuple(noise.shape) != (T, E):
+        raise ValueError("noise must be [T, E]")
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
@@ -83,9 +89,15 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False):
     if need == L.SIZE_MAX:
         raise ValueError("invalid router sizes")
     ws = workspace if workspace is not None else _workspace(need, dev)
-    L.check("moe_router", L.LIB.moe_router(
-        _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
-        _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(ws), ws.numel(), _stream(dev)))
+    if W_noise is None:
+        L.check("moe_router", L.LIB.moe_router(
+            _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
+            _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(ws), ws.numel(), _stream(dev)))
+    else:
+        L.check("moe_router_noisy", L.LIB.moe_router_noisy(
+            _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W_noise), _ptr(noise), T, d, E, k,
+            _ptr(idx), _ptr(gate), _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(ws), ws.numel(),
+            _stream(dev)))
     if z_loss:
         return idx, gate, prob_sum, route_count, zl
     return idx, gate, prob_sum, route_count

@@ -11,13 +11,24 @@ namespace moe {
 // ---- router -----------------------------------------------------------
 // Number of per-block partial rows the router writes for T tokens.
 int router_blocks(int64_t T, int dtype_bf16, int E);
-// w3: scratch of 3 * E * d bf16 for the exact three-part split of W_r.
+// w3: scratch of 3 * router_w3_rows(E) * d bf16 for the exact three-part
+// split of W_r (or of the stacked noisy weight).
+int router_w3_rows(int E);
 // part_z [router_blocks]: each block's sum of its tokens' squared
 // log-sum-exps (the router z-loss partials).
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
                          float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s,
                          float *part_z);
+// Noisy top-k router (any dtype and E; MFMA for bf16 x and E <= 256):
+// logits H = W_r x (+ b_r) + eps * softplus(W_noise x), eps [T, E] given;
+// partial rows as launch_router, router_noisy_blocks(T, dtype_bf16, E) of
+// them; w3 as launch_router.
+int router_noisy_blocks(int64_t T, int dtype_bf16, int E);
+hipError_t launch_router_noisy(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
+                               const float *W_noise, const float *eps, int64_t T, int d, int E,
+                               int k, int32_t *expert_idx, float *gate, float *part_prob,
+                               int32_t *part_cnt, float *part_z, uint16_t *w3, hipStream_t s);
 // z_loss (may be null): (1/T) sum of the part_z partials.
 hipError_t launch_router_reduce(const float *part_prob, const int32_t *part_cnt, int nblk,
                                 int E, float *prob_sum, int32_t *route_count, hipStream_t s,

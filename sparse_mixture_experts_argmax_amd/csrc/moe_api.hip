@@ -33,7 +33,8 @@ RouterWs router_ws(int64_t T, int d, int E) {
     w.part_cnt = up((size_t)nblk * E * 4);
     w.part_z = w.part_cnt + up((size_t)nblk * E * 4);
     w.w3 = w.part_z + up((size_t)nblk * 4);
-    w.total = w.w3 + up((size_t)3 * E * d * 2);     // three bf16 parts of W_r
+    // three bf16 parts of W_r, or of the stacked noisy weight
+    w.total = w.w3 + up((size_t)3 * moe::router_w3_rows(E) * d * 2);
     return w;
 }
 
@@ -285,6 +286,36 @@ moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
     return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count, z_loss,
                       static_cast<char *>(ws), stream);
+}
+
+moe_status moe_router_noisy(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                            const float *W_noise, const float *noise, int64_t T, int32_t d,
+                            int32_t E, int32_t k, int32_t *expert_idx, float *gate,
+                            float *prob_sum, int32_t *route_count, float *z_loss, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr_ok(W_noise, false) ||
+        !ptr4_ok(noise, empty) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(gate, empty) ||
+        !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false) ||
+        !(z_loss == nullptr || ptr4_ok(z_loss, false)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const RouterWs w = router_ws(T, d, E);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    char *base = static_cast<char *>(ws);
+    float *part_prob = reinterpret_cast<float *>(base + w.part_prob);
+    int32_t *part_cnt = reinterpret_cast<int32_t *>(base + w.part_cnt);
+    float *part_z = reinterpret_cast<float *>(base + w.part_z);
+    uint16_t *w3 = reinterpret_cast<uint16_t *>(base + w.w3);
+    const int bf16 = dt == MOE_BF16;
+    MOE_HIP(moe::launch_router_noisy(x, bf16, W_r, b_r, W_noise, noise, T, d, E, k, expert_idx, gate,
+                                     part_prob, part_cnt, part_z, w3, stream));
+    MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_noisy_blocks(T, bf16, E), E, prob_sum,
+                                      route_count, stream, part_z, T, z_loss));
+    return MOE_OK;
 }
 
 moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, int64_t T,

@@ -21,6 +21,16 @@
 //    where row softmax and top-k use 16-lane DPP row reductions.
 //  * router_generic (fp32 x, or E > 256): fp32 FMA dot products into LDS,
 //    then one wave per token row.
+//
+// Noisy top-k ([CMU-L16] section 2.3, after Shazeer et al.): the logit
+// becomes H = W_r x + eps * softplus(W_noise x) with the standard normal
+// draws eps [T, E] given by the caller, and H replaces the logits in
+// everything that follows.  With bf16 x and E <= 128 the MFMA router runs
+// on the stacked weight [W_r; W_noise]: each half padded to a whole number
+// of 16-expert groups (32, 64 or 128 rows), so the lane that holds expert
+// n's logit also holds its noise logit and H is formed lane by lane.  With
+// E <= 256 it runs its K loop twice, over W_r and then W_noise, keeping the
+// first pass's logits in registers.  Otherwise router_generic.
 #include "common.h"
 #include "launch.h"
 
@@ -60,6 +70,26 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
     }
 }
 
+// The stacked noisy weight: rows [0, EH) are W_r, rows [EH, 2 EH) W_noise,
+// rows past E in either half zero; the same three-part split into W3.
+__global__ __launch_bounds__(256) void router_split_noisy_kernel(const float *__restrict__ Wr,
+                                                                 const float *__restrict__ Wn, int E,
+                                                                 int d, int EH, uint16_t *__restrict__ W3) {
+    const int64_t n = (int64_t)2 * EH * d;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int r = (int)(i / d);
+        const int c = (int)(i - (int64_t)r * d);
+        const int h = r < EH ? r : r - EH;
+        const float *src = r < EH ? Wr : Wn;
+        const float w = h < E ? src[(int64_t)h * d + c] : 0.f;
+        uint16_t hi, mid, lo;
+        split3(w, hi, mid, lo);
+        W3[i] = hi;
+        W3[n + i] = mid;
+        W3[2 * n + i] = lo;
+    }
+}
+
 // Stage geometry of the MFMA router: a stage holds KC columns of the three
 // weight parts (3 x EP rows) and of the block's 64 token rows, in LDS rows of
 // KC bf16.  Piece c (16 bytes) of row r is stored at c ^ swz(r), as in the
@@ -86,11 +116,22 @@ constexpr bool rgeo_ok() { return RM_LDS / ((3 * NB * 16 + RM_TOK_BLOCK) * KC * 
 // through an S-deep ring of LDS stages filled by 16-byte DMA; bf16 x bf16
 // products are exact in fp32, so three v_mfma_f32_16x16x32_bf16 per 16
 // experts and 32 columns give the fp32 dot products.
-template <int NB, int KC, bool KTAIL, int KSEL>
+//
+// NZ (noisy top-k, W3 from router_split_noisy_kernel):
+//  0  the plain router;
+//  1  W3 is the stacked weight with NB / 2 groups of 16 rows per half; lane
+//     col's column nb is expert nb 16 + col and column NB / 2 + nb its noise
+//     logit, combined in the epilogue;
+//  2  W3 holds NB 16 rows of W_r, then NB 16 of W_noise; the K loop runs
+//     twice (the token rows are re-read, mostly from L2) and the first
+//     pass's logits stay in registers, so each lane forms H for its own
+//     (token, expert) entries before they go to LDS.
+template <int NB, int KC, bool KTAIL, int KSEL, int NZ>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
-    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z) {
+    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z,
+    const float *__restrict__ eps) {
     using G = RGeo<NB, KC>;
     constexpr int EP = G::EP, ROWB = G::ROWB, PIECES = G::PIECES, S = G::S, PERW = G::PERW;
     constexpr int STAGE = G::STAGE, RPI = G::RPI;
@@ -113,11 +154,13 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     for (int i = tid; i < EP; i += 256) sCnt[i] = 0;
 
     // DMA sources: block instruction q = wave * PERW + i fills rows
-    // [q RPI, +RPI): rows 0 .. 3 EP - 1 are the weight parts (expert rows
-    // past E repeat row E - 1), the rest the block's tokens (past T: row T - 1)
+    // [q RPI, +RPI): rows 0 .. 3 EP - 1 are the weight parts (rows past the
+    // part's EW rows repeat its last one), the rest the block's tokens (past
+    // T: row T - 1)
     const int lr = lane / PIECES;
     const int lc = (lane % PIECES) ^ G::swz(lr);
-    const int64_t nW = (int64_t)E * d;
+    const int EW = NZ == 1 ? EP : NZ == 2 ? 2 * EP : E;
+    const int64_t nW = (int64_t)EW * d;
     const uint16_t *src[PERW];
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
@@ -125,7 +168,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         if (row < 3 * EP) {
             const int p = row / EP;
             int n = row - p * EP;
-            n = n < E ? n : E - 1;
+            n = n < EW ? n : EW - 1;
             src[i] = W3 + p * nW + (int64_t)n * d + lc * 8;
         } else {
             int64_t t = t0 + (row - 3 * EP);
@@ -199,67 +242,87 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // a conditional DMA here makes the compiler give up tracking which stage
     // a pending DMA writes, and then it drains the whole ring before every
     // fragment read.
-    issue(st0, 0);
-    if (S > 2) issue(st1, nk > 1 ? 1 : nk - 1);
-    if (S > 3) issue(st2, nk > 2 ? 2 : nk - 1);
+    constexpr int NPASS = NZ == 2 ? 2 : 1;
     int kt = 0;
-    // steady state: every step refills a stage (no conditional DMA, which
-    // would make the compiler drain the ring before every fragment read)
-#define MOE_RSTEP_S(CUR, NXT)                                                   \
-    {                                                                           \
-        wait_vm_lgkm0<NEWER>();                                                 \
-        ring_barrier();                                                         \
-        issue(NXT, kt + S - 1);                                                 \
-        compute(CUR);                                                           \
-        ++kt;                                                                   \
-    }
-    for (; kt + 2 * S - 1 <= nk;) {
-        if constexpr (S == 2) {
-            MOE_RSTEP_S(st0, st1)
-            MOE_RSTEP_S(st1, st0)
-        } else if constexpr (S == 3) {
-            MOE_RSTEP_S(st0, st2)
-            MOE_RSTEP_S(st1, st0)
-            MOE_RSTEP_S(st2, st1)
-        } else {
-            MOE_RSTEP_S(st0, st3)
-            MOE_RSTEP_S(st1, st0)
-            MOE_RSTEP_S(st2, st1)
-            MOE_RSTEP_S(st3, st2)
+    f32x4 acc0[4][NBW];                                  // NZ 2: the first pass's logits
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        if (pass == 1) {
+            // the ring is drained; keep the W_r logits, restart on the W_noise rows
+#pragma unroll
+            for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+                for (int g = 0; g < NBW; ++g) {
+                    acc0[ab][g] = acc[ab][g];
+                    acc[ab][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int i = 0; i < PERW; ++i)
+                if ((wave * PERW + i) * RPI + lr < 3 * EP) src[i] += (int64_t)EP * d;
+            lds_barrier();                               // every wave is done with the last stage
         }
-    }
+        issue(st0, 0);
+        if (S > 2) issue(st1, nk > 1 ? 1 : nk - 1);
+        if (S > 3) issue(st2, nk > 2 ? 2 : nk - 1);
+        kt = 0;
+        // steady state: every step refills a stage (no conditional DMA, which
+        // would make the compiler drain the ring before every fragment read)
+#define MOE_RSTEP_S(CUR, NXT)                                                   \
+        {                                                                           \
+            wait_vm_lgkm0<NEWER>();                                                 \
+            ring_barrier();                                                         \
+            issue(NXT, kt + S - 1);                                                 \
+            compute(CUR);                                                           \
+            ++kt;                                                                   \
+        }
+        for (; kt + 2 * S - 1 <= nk;) {
+            if constexpr (S == 2) {
+                MOE_RSTEP_S(st0, st1)
+                MOE_RSTEP_S(st1, st0)
+            } else if constexpr (S == 3) {
+                MOE_RSTEP_S(st0, st2)
+                MOE_RSTEP_S(st1, st0)
+                MOE_RSTEP_S(st2, st1)
+            } else {
+                MOE_RSTEP_S(st0, st3)
+                MOE_RSTEP_S(st1, st0)
+                MOE_RSTEP_S(st2, st1)
+                MOE_RSTEP_S(st3, st2)
+            }
+        }
 #undef MOE_RSTEP_S
-    // drain: at most 2 S - 2 steps, refilling while chunks remain; kt % S == 0 here
+        // drain: at most 2 S - 2 steps, refilling while chunks remain; kt % S == 0 here
 #define MOE_RSTEP(CUR, NXT)                                                     \
-    if (kt < nk) {                                                              \
-        if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
-        else wait_vm_lgkm0<0>();                                                \
-        if (KTAIL && kt == nk - 1) {                                            \
-            clear_tail(CUR);                                                    \
-            wait_vm_lgkm0<63>();          /* the zeros are in LDS */            \
-        }                                                                       \
-        ring_barrier();                                                         \
-        if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
-        compute(CUR);                                                           \
-        ++kt;                                                                   \
-    }
-    if constexpr (S == 2) {
-        MOE_RSTEP(st0, st1)
-        MOE_RSTEP(st1, st0)
-    } else if constexpr (S == 3) {
-        MOE_RSTEP(st0, st2)
-        MOE_RSTEP(st1, st0)
-        MOE_RSTEP(st2, st1)
-        MOE_RSTEP(st0, st2)
-    } else {
-        MOE_RSTEP(st0, st3)
-        MOE_RSTEP(st1, st0)
-        MOE_RSTEP(st2, st1)
-        MOE_RSTEP(st3, st2)
-        MOE_RSTEP(st0, st3)
-        MOE_RSTEP(st1, st0)
-    }
+        if (kt < nk) {                                                              \
+            if (kt + S - 2 < nk) wait_vm_lgkm0<NEWER>();                            \
+            else wait_vm_lgkm0<0>();                                                \
+            if (KTAIL && kt == nk - 1) {                                            \
+                clear_tail(CUR);                                                    \
+                wait_vm_lgkm0<63>();          /* the zeros are in LDS */            \
+            }                                                                       \
+            ring_barrier();                                                         \
+            if (kt + S - 1 < nk) issue(NXT, kt + S - 1);                            \
+            compute(CUR);                                                           \
+            ++kt;                                                                   \
+        }
+        if constexpr (S == 2) {
+            MOE_RSTEP(st0, st1)
+            MOE_RSTEP(st1, st0)
+        } else if constexpr (S == 3) {
+            MOE_RSTEP(st0, st2)
+            MOE_RSTEP(st1, st0)
+            MOE_RSTEP(st2, st1)
+            MOE_RSTEP(st0, st2)
+        } else {
+            MOE_RSTEP(st0, st3)
+            MOE_RSTEP(st1, st0)
+            MOE_RSTEP(st2, st1)
+            MOE_RSTEP(st3, st2)
+            MOE_RSTEP(st0, st3)
+            MOE_RSTEP(st1, st0)
+        }
 #undef MOE_RSTEP
+    }
 
     // ---- logits to LDS (token rows 0..31 in st0, 32..63 in st1; the ring is
     // drained), then each wave takes 16 tokens across all experts
@@ -273,34 +336,57 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = ab * 16 + 4 * kg + i;
+                const int n = (wave * NBW + g) * 16 + col;
                 float *zr = reinterpret_cast<float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
-                zr[(wave * NBW + g) * 16 + col] = acc[ab][g][i];
+                if constexpr (NZ == 2) {
+                    // H = (W_r x + b) + eps softplus(W_noise x), softplus as
+                    // max(a, 0) + log(1 + exp(-|a|)) (no overflow)
+                    const int64_t t = t0 + tok;
+                    const bool ok = t < T && n < E;
+                    const float zn = acc[ab][g][i];
+                    const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
+                    const float b = (br != nullptr && n < E) ? br[n] : 0.f;
+                    const float e = ok ? eps[t * E + n] : 0.f;
+                    zr[n] = fmaf(e, sp, acc0[ab][g][i] + b);
+                } else {
+                    zr[n] = acc[ab][g][i];
+                }
             }
     lds_barrier();
 
     // ---- epilogue: lane holds logits of tokens tw + 4*kg + i, experts nb*16 + col
-    float bias[NB];
+    constexpr int NE = NZ == 1 ? NB / 2 : NB;            // expert groups
+    static_assert(NZ != 1 || NB % 2 == 0, "noisy halves");
+    float bias[NE];                                      // (NZ 2: already in the logits)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NE; ++nb) {
         const int n = nb * 16 + col;
-        bias[nb] = (br != nullptr && n < E) ? br[n] : 0.f;
+        bias[nb] = (NZ != 2 && br != nullptr && n < E) ? br[n] : 0.f;
     }
-    float psum[NB];
+    float psum[NE];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) psum[nb] = 0.f;
+    for (int nb = 0; nb < NE; ++nb) psum[nb] = 0.f;
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t t = tw + 4 * kg + i;
         const bool tok_ok = t < T;
-        float v[NB];
+        float v[NE];
         float mx = -INFINITY;
         const int tok = wave * RM_TOK_WAVE + 4 * kg + i;
         const float *zr = reinterpret_cast<const float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int nb = 0; nb < NE; ++nb) {
             const int n = nb * 16 + col;
             float z = zr[n] + bias[nb];
+            if (NZ == 1) {
+                // H = z + eps softplus(zn); softplus without overflow:
+                // max(a, 0) + log(1 + exp(-|a|))
+                const float zn = zr[NE * 16 + n];
+                const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
+                const float e = (tok_ok && n < E) ? eps[t * E + n] : 0.f;
+                z = fmaf(e, sp, z);
+            }
             if (z != z) z = -INFINITY;          // NaN ranks as -inf: indices stay in range
             v[nb] = z;
             if (n < E) mx = fmaxf(mx, z);
@@ -310,10 +396,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         // the sum s and the per-expert probability sums, whose bounds are far
         // looser; the gate of the chosen expert is 1 / s with s from them
         const float mxl = mx * 1.44269504088896341f;
-        float ex[NB];
+        float ex[NE];
         float s = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int nb = 0; nb < NE; ++nb) {
             const int n = nb * 16 + col;
             ex[nb] = (n < E) ? __builtin_amdgcn_exp2f(fmaf(v[nb], 1.44269504088896341f, -mxl)) : 0.f;
             s += ex[nb];
@@ -322,7 +408,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         if (tok_ok) {
             const float inv = 1.0f / s;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) psum[nb] = fmaf(ex[nb], inv, psum[nb]);
+            for (int nb = 0; nb < NE; ++nb) psum[nb] = fmaf(ex[nb], inv, psum[nb]);
         }
         if (col == 0) {
             // z-loss term: log sum_i exp z_i = max + log sum_i exp(z_i - max)
@@ -338,7 +424,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         constexpr int KMAX = KSEL ? KSEL : MAXK;
         const int kk = KSEL ? KSEL : k;
         uint32_t excl = 0u;                      // bit nb: this lane's expert nb*16+col is taken
-        static_assert(NB <= 32, "exclusion mask");
+        static_assert(NE <= 32, "exclusion mask");
         float vsel[KMAX];
         int isel[KMAX];
 #pragma unroll
@@ -350,13 +436,13 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                 if (j > 0) {
                     m = -INFINITY;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
+                    for (int nb = 0; nb < NE; ++nb)
                         if (nb * 16 + col < E && !((excl >> nb) & 1u)) m = fmaxf(m, v[nb]);
                     m = row16_max(m);
                 }
                 int best = 0x7fffffff;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
+                for (int nb = 0; nb < NE; ++nb) {
                     const int n = nb * 16 + col;
                     const bool cand = n < E && !((excl >> nb) & 1u) && v[nb] == m;
                     best = cand ? min(best, n) : best;
@@ -394,13 +480,13 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 
     // ---- block partials: probability sums and choice counts per expert
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NE; ++nb) {
         psum[nb] += __shfl_xor(psum[nb], 16);
         psum[nb] += __shfl_xor(psum[nb], 32);
     }
     if (lane < 16) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sProb[wave][nb * 16 + lane] = psum[nb];
+        for (int nb = 0; nb < NE; ++nb) sProb[wave][nb * 16 + lane] = psum[nb];
     }
     __syncthreads();
     for (int n = tid; n < E; n += 256) {
@@ -422,11 +508,15 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 // ---------------------------------------------------------------------------
 constexpr int RG_TOK = 8;   // tokens per block, two rows per wave
 
-template <bool BF16>
+// NOISY: noisy top-k ([CMU-L16] section 2.3, Shazeer et al.): the logit
+// becomes H = z + eps * softplus(W_noise x), with eps [T, E] standard normal
+// draws given by the caller, and H replaces z in everything that follows.
+template <bool BF16, bool NOISY>
 __global__ __launch_bounds__(256) void router_generic_kernel(
     const void *__restrict__ xv, const float *__restrict__ Wr, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
-    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z) {
+    float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z,
+    const float *__restrict__ Wn, const float *__restrict__ eps) {
     extern __shared__ float smem[];
     __shared__ float sLz[RG_TOK];                       // each token's log-sum-exp, squared
     float *sZ = smem;                                   // [RG_TOK][E]
@@ -445,14 +535,28 @@ __global__ __launch_bounds__(256) void router_generic_kernel(
         float z = 0.f;
         if (t < T) {
             const float *w = Wr + (int64_t)n * d;
+            const float *wn = NOISY ? Wn + (int64_t)n * d : nullptr;
+            float zn = 0.f;
             if (BF16) {
                 const uint16_t *xr = reinterpret_cast<const uint16_t *>(xv) + t * d;
-                for (int q = 0; q < d; ++q) z = fmaf(bf2f(xr[q]), w[q], z);
+                for (int q = 0; q < d; ++q) {
+                    const float xq = bf2f(xr[q]);
+                    z = fmaf(xq, w[q], z);
+                    if (NOISY) zn = fmaf(xq, wn[q], zn);
+                }
             } else {
                 const float *xr = reinterpret_cast<const float *>(xv) + t * d;
-                for (int q = 0; q < d; ++q) z = fmaf(xr[q], w[q], z);
+                for (int q = 0; q < d; ++q) {
+                    z = fmaf(xr[q], w[q], z);
+                    if (NOISY) zn = fmaf(xr[q], wn[q], zn);
+                }
             }
             if (br != nullptr) z += br[n];
+            if (NOISY) {
+                // softplus without overflow: max(a, 0) + log(1 + exp(-|a|))
+                const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
+                z = fmaf(eps[t * E + n], sp, z);
+            }
             if (z != z) z = -INFINITY;
         }
         sZ[p] = z;
@@ -569,6 +673,12 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(
 }
 
 bool use_mfma(int dtype_bf16, int E) { return dtype_bf16 && E <= 256; }
+bool use_mfma_noisy(int dtype_bf16, int E) { return dtype_bf16 && E <= 256; }
+// rows of each half of the noisy weight in W3.  E <= 128 (stacked, one K
+// pass): half of one of the MFMA router's widths (64, 128, 256 rows), so
+// that the noise half starts at the kernel's column NB / 2 * 16 and the four
+// waves split the rows evenly.  E <= 256 (two K passes): the full width 256.
+int noisy_half_rows(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256; }
 
 }  // namespace
 
@@ -589,14 +699,15 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
         hipLaunchKernelGGL(router_split_kernel, dim3(sg), dim3(256), 0, s, W_r, n, w3);
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
         const int nb = (E + 15) / 16;
-#define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV)                                                \
-    hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV>), dim3(nblk), dim3(256), 0, s,  \
-                       xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z)
+#define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
+    hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
+                       0, s, xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt,     \
+                       part_z, nullptr)
 #define MOE_ROUTER_K(NBV, KCV, TAILV)                                                          \
     do {                                                                                       \
-        if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1);                                     \
-        else if (k == 2) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 2);                                \
-        else MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 0);                                            \
+        if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, 0);                                  \
+        else if (k == 2) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 2, 0);                             \
+        else MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 0, 0);                                         \
     } while (0)
 #define MOE_ROUTER_CASE(NBV, KCV)                                                              \
     if (nb <= NBV) {                                                                           \
@@ -615,11 +726,69 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
     }
     const size_t shm = (size_t)(RG_TOK + 1) * E * sizeof(float);
     if (dtype_bf16)
-        hipLaunchKernelGGL(router_generic_kernel<true>, dim3(nblk), dim3(256), shm, s, x, W_r,
-                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z);
+        hipLaunchKernelGGL((router_generic_kernel<true, false>), dim3(nblk), dim3(256), shm, s, x, W_r,
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, nullptr,
+                           nullptr);
     else
-        hipLaunchKernelGGL(router_generic_kernel<false>, dim3(nblk), dim3(256), shm, s, x, W_r,
-                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z);
+        hipLaunchKernelGGL((router_generic_kernel<false, false>), dim3(nblk), dim3(256), shm, s, x, W_r,
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, nullptr,
+                           nullptr);
+    return hipGetLastError();
+}
+
+int router_w3_rows(int E) { return use_mfma_noisy(1, E) ? 2 * noisy_half_rows(E) : E; }
+
+int router_noisy_blocks(int64_t T, int dtype_bf16, int E) {
+    const int per = use_mfma_noisy(dtype_bf16, E) ? RM_TOK_BLOCK : RG_TOK;
+    return (int)((T + per - 1) / per);
+}
+
+hipError_t launch_router_noisy(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
+                               const float *W_noise, const float *eps, int64_t T, int d, int E,
+                               int k, int32_t *expert_idx, float *gate, float *part_prob,
+                               int32_t *part_cnt, float *part_z, uint16_t *w3, hipStream_t s) {
+    const int nblk = router_noisy_blocks(T, dtype_bf16, E);
+    if (nblk == 0) return hipSuccess;
+    if (use_mfma_noisy(dtype_bf16, E)) {
+        const int EH = noisy_half_rows(E);
+        const int64_t n = (int64_t)2 * EH * d;
+        const int sg = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+        hipLaunchKernelGGL(router_split_noisy_kernel, dim3(sg), dim3(256), 0, s, W_r, W_noise, E, d, EH,
+                           w3);
+        const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
+#define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
+    hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
+                       0, s, xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt,     \
+                       part_z, eps)
+#define MOE_ROUTER_K(NBV, KCV, TAILV, NZV)                                                     \
+    do {                                                                                       \
+        if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, NZV);                                \
+        else if (k == 2) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 2, NZV);                           \
+        else MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 0, NZV);                                       \
+    } while (0)
+#define MOE_ROUTER_CASE(NBV, KCV, NZV)                                                         \
+    if (EH == (NZV == 1 ? NBV * 8 : NBV * 16)) {                                               \
+        static_assert(rgeo_ok<NBV, KCV>(), "router ring");                                     \
+        if (d % KCV == 0) MOE_ROUTER_K(NBV, KCV, false, NZV);                                  \
+        else MOE_ROUTER_K(NBV, KCV, true, NZV);                                                \
+        return hipGetLastError();                                                              \
+    }
+        MOE_ROUTER_CASE(4, 64, 1)
+        MOE_ROUTER_CASE(8, 64, 1)
+        MOE_ROUTER_CASE(16, 32, 1)
+        MOE_ROUTER_CASE(16, 32, 2)
+#undef MOE_ROUTER_CASE
+#undef MOE_ROUTER_K
+#undef MOE_ROUTER_LAUNCH
+        return hipErrorInvalidValue;
+    }
+    const size_t shm = (size_t)(RG_TOK + 1) * E * sizeof(float);
+    if (dtype_bf16)
+        hipLaunchKernelGGL((router_generic_kernel<true, true>), dim3(nblk), dim3(256), shm, s, x, W_r,
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, W_noise, eps);
+    else
+        hipLaunchKernelGGL((router_generic_kernel<false, true>), dim3(nblk), dim3(256), shm, s, x, W_r,
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, W_noise, eps);
     return hipGetLastError();
 }
 

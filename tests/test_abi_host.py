@@ -117,6 +117,24 @@ def test_router_rejects(case, expect):
 
 @_no_gpu
 @pytest.mark.parametrize("case,expect", [
+    (dict(Wn=None), L.MOE_ERR_INVALID_ARGUMENT),               # no noise weights
+    (dict(eps=None), L.MOE_ERR_INVALID_ARGUMENT),              # no draws
+    (dict(eps=P + 2), L.MOE_ERR_INVALID_ARGUMENT),             # misaligned draws
+    (dict(E=1025), L.MOE_ERR_UNSUPPORTED),
+    (dict(ws_bytes=0), L.MOE_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_noisy_router_rejects(case, expect):
+    a = dict(x=P, dt=L.MOE_BF16, W_r=P, b_r=None, Wn=P, eps=P, T=64, d=64, E=8, k=1, idx=P, gate=P,
+             ps=P, rc=P, zl=None, ws=P, ws_bytes=1 << 30)
+    a.update(case)
+    st = L.LIB.moe_router_noisy(a["x"], a["dt"], a["W_r"], a["b_r"], a["Wn"], a["eps"], a["T"], a["d"],
+                                a["E"], a["k"], a["idx"], a["gate"], a["ps"], a["rc"], a["zl"], a["ws"],
+                                a["ws_bytes"], None)
+    assert st == expect
+
+
+@_no_gpu
+@pytest.mark.parametrize("case,expect", [
     (dict(act=L.MOE_ACT_SWIGLU), L.MOE_ERR_INVALID_ARGUMENT),           # SwiGLU without W3
     (dict(act=L.MOE_ACT_SWIGLU, W3=P, b1=P), L.MOE_ERR_UNSUPPORTED),     # SwiGLU with biases
     (dict(W3=P), L.MOE_ERR_INVALID_ARGUMENT),                           # W3 given to ReLU
