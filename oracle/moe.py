@@ -237,6 +237,47 @@ def assign_slots(idx: np.ndarray, E: int, C: int):
     return slot, drop, np.asarray(fill, dtype=np.int64)
 
 
+def priority_order(priority: np.ndarray) -> np.ndarray:
+    """Token visit order of priority routing: descending priority, equal
+    priorities in token order; NaN scores come last (in token order)."""
+    pr = np.asarray(priority, dtype=np.float64)
+    nan = np.isnan(pr)
+    return np.lexsort((np.arange(pr.shape[0]), np.where(nan, 0.0, -pr), nan))
+
+
+def assign_slots_priority(idx: np.ndarray, E: int, C: int, priority: np.ndarray):
+    """Capacity slots under priority routing; overflowing choices are dropped.
+
+    [CS25-L5], the V-MoE part after "什么是视觉 token": with a capacity
+    factor below 1 the tokens are first ranked by importance and the
+    high-priority ones take the expert slots, so the capacity becomes a
+    budget spent on the most important tokens.  This is the capacity rule of
+    assign_slots with the token visit order replaced by priority_order
+    (descending score, ties to the lower token index), still rank-major for
+    k > 1.  The page leaves the score open (a learned hypothesis); the
+    default score is the router's gate of the token's first choice, and any
+    fp32 score [T] may be given.
+
+    Returns slot [T, k] int32 (-1 if dropped), drop [T, k] uint8 and
+    expert_count [E] int64, as assign_slots.
+    """
+    T, k = idx.shape
+    order = priority_order(priority).tolist()
+    fill = [0] * E
+    slot = np.full((T, k), -1, dtype=np.int32)
+    drop = np.zeros((T, k), dtype=np.uint8)
+    idx_list = np.asarray(idx).tolist()
+    for j in range(k):
+        for t in order:
+            e = idx_list[t][j]
+            if fill[e] < C:
+                slot[t, j] = fill[e]
+                fill[e] += 1
+            else:
+                drop[t, j] = 1
+    return slot, drop, np.asarray(fill, dtype=np.int64)
+
+
 # ---------------------------------------------------------------------------
 # O8 experts
 # ---------------------------------------------------------------------------

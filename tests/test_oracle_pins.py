@@ -484,6 +484,108 @@ def test_softplus_values():
 
 
 # ---------------------------------------------------------------------------
+# priority routing ([CS25-L5], V-MoE part): capacity goes to the highest
+# scores first; ties to the lower token index; rank-major for k > 1
+# ---------------------------------------------------------------------------
+
+def _priority_case(seed=9, T=300, E=5, k=2):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((T, E))
+    idx = np.argsort(-z, axis=1, kind="stable")[:, :k].astype(np.int32)
+    pr = rng.random(T).astype(np.float32)
+    return idx, pr
+
+
+def check_priority_equal_scores_is_token_order():
+    """One score for every token: the visit order is token order, so the
+    slots are those of the plain capacity rule."""
+    idx, _ = _priority_case()
+    C = 50
+    got = O.assign_slots_priority(idx, 5, C, np.full(idx.shape[0], 0.25, np.float32))
+    ref = O.assign_slots(idx, 5, C)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)
+
+
+def check_priority_increasing_is_reversed_token_order():
+    """Scores increasing with t: the last token goes first, which is the plain
+    rule on the reversed token sequence."""
+    idx, _ = _priority_case(seed=3)
+    T, C = idx.shape[0], 40
+    got_s, got_d, got_c = O.assign_slots_priority(idx, 5, C, np.arange(T, dtype=np.float32))
+    ref_s, ref_d, ref_c = O.assign_slots(idx[::-1].copy(), 5, C)
+    assert np.array_equal(got_s, ref_s[::-1]) and np.array_equal(got_d, ref_d[::-1])
+    assert np.array_equal(got_c, ref_c)
+
+
+def check_priority_keeps_the_highest():
+    """k = 1 with half the even split (the page's gamma = 0.5): each expert
+    keeps exactly its C highest-scoring tokens (ties: lower index), and its
+    slots number them from the highest down; found here per expert by a
+    selection over that expert's tokens instead of one sequential fill."""
+    rng = np.random.default_rng(17)
+    T, E = 400, 4
+    idx = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    pr = np.round(rng.random(T), 2).astype(np.float32)     # many equal scores
+    C = O.capacity(T, E, 1, 0.5)
+    slot, drop, cnt = O.assign_slots_priority(idx, E, C, pr)
+    for e in range(E):
+        toks = [t for t in range(T) if idx[t, 0] == e]
+        ranked = sorted(toks, key=lambda t: (-float(pr[t]), t))
+        kept = ranked[:C]
+        assert cnt[e] == len(kept)
+        for r, t in enumerate(ranked):
+            if r < C:
+                assert slot[t, 0] == r and drop[t, 0] == 0
+            else:
+                assert slot[t, 0] == -1 and drop[t, 0] == 1
+
+
+def check_priority_rank_major():
+    """k = 2: every token's first choice is placed before any second choice,
+    so no expert keeps a second choice while it drops a first choice."""
+    idx, pr = _priority_case(seed=21, T=500, E=4)
+    slot, drop, _ = O.assign_slots_priority(idx, 4, 200, pr)
+    for e in range(4):
+        first_dropped = np.any((idx[:, 0] == e) & (drop[:, 0] == 1))
+        second_kept = np.any((idx[:, 1] == e) & (drop[:, 1] == 0))
+        assert not (first_dropped and second_kept)
+        # kept second choices sit after every kept first choice of the expert
+        s0 = slot[(idx[:, 0] == e) & (drop[:, 0] == 0), 0]
+        s1 = slot[(idx[:, 1] == e) & (drop[:, 1] == 0), 1]
+        if s0.size and s1.size:
+            assert s1.min() > s0.max()
+
+
+def test_priority_equal_scores_is_token_order():
+    check_priority_equal_scores_is_token_order()
+
+
+def test_priority_increasing_is_reversed_token_order():
+    check_priority_increasing_is_reversed_token_order()
+
+
+def test_priority_keeps_the_highest():
+    check_priority_keeps_the_highest()
+
+
+def test_priority_rank_major():
+    check_priority_rank_major()
+
+
+def test_priority_worked_example():
+    """By hand: one expert, C = 2, scores [NaN, 0.1, 0.5, -inf, 0.5, -0.0, 0.0].
+    Order: t2 and t4 (0.5; lower index first), t1, the zeros t5 and t6 (equal:
+    -0 = +0), t3 (-inf), t0 (NaN last).  Kept: t2 slot 0, t4 slot 1."""
+    pr = np.array([np.nan, 0.1, 0.5, -np.inf, 0.5, -0.0, 0.0], np.float32)
+    idx = np.zeros((7, 1), np.int32)
+    assert O.priority_order(pr).tolist() == [2, 4, 1, 5, 6, 3, 0]
+    slot, drop, cnt = O.assign_slots_priority(idx, 1, 2, pr)
+    assert slot[:, 0].tolist() == [-1, -1, 0, -1, 1, -1, -1]
+    assert drop[:, 0].tolist() == [1, 1, 0, 1, 0, 1, 1] and cnt.tolist() == [2]
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -617,3 +719,42 @@ def test_planted_noisy_mistake_is_caught(monkeypatch, repl):
     monkeypatch.setattr(O, "noisy_router_logits", repl)
     with pytest.raises(AssertionError):
         check_noisy_zero_noise_weights()
+
+
+def _priority_ascending(priority):
+    pr = np.asarray(priority, dtype=np.float64)
+    nan = np.isnan(pr)
+    return np.lexsort((np.arange(pr.shape[0]), np.where(nan, 0.0, pr), nan))
+
+
+def _priority_high_tie(priority):
+    pr = np.asarray(priority, dtype=np.float64)
+    nan = np.isnan(pr)
+    return np.lexsort((-np.arange(pr.shape[0]), np.where(nan, 0.0, -pr), nan))
+
+
+def _priority_token_major(idx, E, C, priority):
+    T, k = idx.shape
+    fill = [0] * E
+    slot = np.full((T, k), -1, np.int32)
+    drop = np.zeros((T, k), np.uint8)
+    for t in O.priority_order(priority).tolist():
+        for j in range(k):
+            e = idx[t, j]
+            if fill[e] < C:
+                slot[t, j] = fill[e]
+                fill[e] += 1
+            else:
+                drop[t, j] = 1
+    return slot, drop, np.array(fill)
+
+
+@pytest.mark.parametrize("name,repl,check", [
+    ("priority_order", _priority_ascending, check_priority_keeps_the_highest),
+    ("priority_order", _priority_high_tie, check_priority_equal_scores_is_token_order),
+    ("assign_slots_priority", _priority_token_major, check_priority_rank_major),
+])
+def test_planted_priority_mistake_is_caught(monkeypatch, name, repl, check):
+    monkeypatch.setattr(O, name, repl)
+    with pytest.raises(AssertionError):
+        check()
