@@ -190,6 +190,8 @@ def kernel_stage(name: str) -> str:
         return "noisy_router"
     if "router" in name:
         return "router"
+    if any(t in name for t in ("priority_list", "priority_slot", "permute_slots")):
+        return "priority_dispatch"
     if any(t in name for t in ("slot_rank", "slot_scan", "slot_index", "permute_kernel", "tile_map")):
         return "dispatch"
     m = _GEMM_ACT.search(name)
@@ -353,6 +355,8 @@ def main(argv=None):
                     help="minimum CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--noisy-calls", type=int, default=20,
                     help="noisy top-k router calls timed after the steps (0 skips them)")
+    ap.add_argument("--priority-calls", type=int, default=20,
+                    help="priority-routing dispatch calls timed after the steps (0 skips them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel that scales the HBM byte counters), then exit")
@@ -516,6 +520,27 @@ def main(argv=None):
         variants["noisy_router"] = dict(us=round(nz_s * 1e6, 2), bytes=nw["bytes"], flops=nw["flops"],
                                         calls=args.noisy_calls, **roofline_of(nw, nz_s))
         del W_n, eps, rws
+    # priority routing: the plain dispatch's work with the capacity filled in
+    # descending first-gate order, timed on its own like the dispatch above
+    if args.priority_calls > 0:
+        pr = plan.gate[:, 0].contiguous()
+        pws = torch.empty(L.LIB.moe_dispatch_priority_workspace_bytes(cfg["T"], cfg["E"], cfg["k"]),
+                          dtype=torch.uint8, device=dev)
+        moe.dispatch_priority(x, plan.expert_idx, pr, cfg["E"], plan.C, workspace=pws)
+        pr_ev = hip.create(2)
+        hip.record(pr_ev[0], stream.cuda_stream)
+        for _ in range(args.priority_calls):
+            moe.dispatch_priority(x, plan.expert_idx, pr, cfg["E"], plan.C, workspace=pws)
+        hip.record(pr_ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        pr_s = hip.elapsed_ms(pr_ev[0], pr_ev[1]) / args.priority_calls / 1e3
+        hip.destroy(pr_ev)
+        A_pr = int(moe.dispatch_priority(x, plan.expert_idx, pr, cfg["E"], plan.C, workspace=pws)[2].sum().item())
+        pw = dict(bytes=2 * A_pr * cfg["d"] * (2 if cfg["dtype"] == "bf16" else 4) + cfg["T"] * cfg["k"] * 9
+                  + cfg["T"] * 4, flops=0, dtype=cfg["dtype"])
+        variants["priority_dispatch"] = dict(us=round(pr_s * 1e6, 2), bytes=pw["bytes"], kept=A_pr,
+                                             calls=args.priority_calls, **roofline_of(pw, pr_s))
+        del pws
     stages = {}
     for name in L.STAGES:
         r = roofline_of(work[name], stage_ms[name] / 1e3)

@@ -79,6 +79,7 @@ int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor);
  * SIZE_MAX means the sizes are invalid. */
 size_t moe_router_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k);
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
+size_t moe_dispatch_priority_workspace_bytes(int64_t T, int32_t E, int32_t k);
 size_t moe_expert_ffn_workspace_bytes(int32_t E, int64_t C, int32_t dff, moe_dtype dt);
 size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
                            int64_t C, moe_dtype dt, moe_act act);
@@ -174,6 +175,27 @@ moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx,
                         int64_t T, int32_t d, int32_t E, int32_t k, int64_t C,
                         int32_t *slot, uint8_t *drop_mask, int32_t *expert_count, void *xbuf,
                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Priority dispatch: moe_dispatch with the capacity spent on the highest
+ * scores first.  [CS25-L5], the V-MoE part after "什么是视觉 token" (with a
+ * capacity factor below 1, tokens are ranked by importance and the
+ * high-priority ones take the expert slots).  Tokens are visited in
+ * descending priority[t] (equal scores: lower token index first; NaN scores
+ * last; -0 equals +0), every first choice before any second choice; each
+ * takes its expert's next free slot while fewer than C are taken.
+ *   priority     [T]  fp32 in, the tokens' scores (the page leaves the score
+ *                     open; the router's gate of each token's first choice,
+ *                     gate[:, 0], is the plain one)
+ * Other arguments as moe_dispatch; the workspace is
+ * moe_dispatch_priority_workspace_bytes(T, E, k) bytes (8 T k + small).
+ * E <= 1024.  Cost: about n_e^2 / 2 key compares per expert (n_e its
+ * choices before capacity), at most T^2 / 2 when all tokens pick one expert.
+ */
+moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *expert_idx,
+                                 const float *priority, int64_t T, int32_t d, int32_t E, int32_t k,
+                                 int64_t C, int32_t *slot, uint8_t *drop_mask, int32_t *expert_count,
+                                 void *xbuf, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Experts: every expert's FFN on its kept rows, as grouped GEMMs.

@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_capacity": (_i64, [_i64, _i32, _i32, C.c_double]),
     "moe_router_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_dispatch_priority_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i32, _i64, _i32, C.c_int]),
     "moe_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i64, C.c_int, C.c_int]),
     "moe_forward_workspace_layout": (C.c_int, [_i64, _i32, _i32, _i32, _i32, _i64, C.c_int,
@@ -51,6 +52,8 @@ SIGNATURES = {
                                    _p, _p, _p, _sz, _p]),
     "moe_dispatch": (C.c_int, [_p, C.c_int, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p, _p,
                                _p, _sz, _p]),
+    "moe_dispatch_priority": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p,
+                                        _p, _p, _sz, _p]),
     "moe_expert_ffn": (C.c_int, [_p, C.c_int, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p, _p,
                                  C.c_int, _p, _p, _sz, _p]),
     "moe_combine": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64,

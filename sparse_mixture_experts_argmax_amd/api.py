@@ -122,6 +122,30 @@ def dispatch(x, expert_idx, E: int, C: int, workspace=None):
     return slot, drop, count, xbuf
 
 
+def dispatch_priority(x, expert_idx, priority, E: int, C: int, workspace=None):
+    """Priority dispatch: as dispatch, with the capacity filled in descending
+    priority [T] fp32 (ties: lower token index; NaN last), rank-major.
+    Returns (slot, drop_mask, expert_count, xbuf)."""
+    T, d = x.shape
+    k = expert_idx.shape[1]
+    dev = x.device
+    _same(torch.float32, priority)
+    if tuple(priority.shape) != (T,):
+        raise ValueError("priority must be [T]")
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+    drop = torch.empty((T, k), dtype=torch.uint8, device=dev)
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    xbuf = torch.empty((E, C, d), dtype=x.dtype, device=dev)
+    need = L.LIB.moe_dispatch_priority_workspace_bytes(T, E, k)
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid dispatch sizes")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    L.check("moe_dispatch_priority", L.LIB.moe_dispatch_priority(
+        _ptr(x), _dtype_code(x), _ptr(expert_idx), _ptr(priority), T, d, E, k, C, _ptr(slot), _ptr(drop),
+        _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
+    return slot, drop, count, xbuf
+
+
 def expert_ffn(xbuf, expert_count, W1, W2, *, W3=None, b1=None, b2=None, act="relu",
                workspace=None, ybuf=None):
     """Grouped expert FFN: returns ybuf [E, C, d] (rows >= expert_count[e] untouched)."""

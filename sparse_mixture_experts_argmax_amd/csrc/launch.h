@@ -70,6 +70,17 @@ hipError_t launch_slot_index(const int32_t *expert_idx, const int32_t *rank, con
                              const float *prob_sum = nullptr, const int32_t *route_count = nullptr,
                              int32_t *tile_map = nullptr, int bm = 0, float alpha = 0.f,
                              float *aux = nullptr);
+// Priority routing (priority.hip): after launch_slot_rank and a
+// launch_slot_scan with an unbounded capacity (n_e = each expert's choice
+// count), the slots of the capacity rule with tokens visited in descending
+// priority[t] (ties: lower index; NaN last), rank-major; also drop_mask,
+// expert_count = min(n_e, C) and the kept rows in xbuf.  list [T k] uint64
+// and off [E] are scratch.  E <= 1024.
+hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *expert_idx,
+                                 const float *priority, const int32_t *rank, const int32_t *base,
+                                 const int32_t *n_e, int64_t T, int d, int E, int k, int64_t C,
+                                 uint64_t *list, int32_t *off, int32_t *slot, uint8_t *drop_mask,
+                                 int32_t *expert_count, void *xbuf, hipStream_t s);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,

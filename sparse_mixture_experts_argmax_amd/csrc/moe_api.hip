@@ -50,6 +50,22 @@ DispatchWs dispatch_ws(int64_t T, int E, int k) {
     return w;
 }
 
+// Priority dispatch: the plain dispatch's rank and scan scratch, then the
+// per-expert order-key lists, the choice counts and the list offsets.
+struct PriorityWs {
+    DispatchWs d;
+    size_t list, cnt, off, total;
+};
+PriorityWs priority_ws(int64_t T, int E, int k) {
+    PriorityWs w;
+    w.d = dispatch_ws(T, E, k);
+    w.list = w.d.total;
+    w.cnt = w.list + up((size_t)T * k * 8);
+    w.off = w.cnt + up((size_t)E * 4);
+    w.total = w.off + up((size_t)E * 4);
+    return w;
+}
+
 struct FfnWs {
     size_t tile_map, h, total;
 };
@@ -335,6 +351,42 @@ moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, 
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
     return run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
                         static_cast<char *>(ws), stream);
+}
+
+size_t moe_dispatch_priority_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+    if (check_sizes(T, E, k) != MOE_OK) return SIZE_MAX;
+    return priority_ws(T, E, k).total;
+}
+
+moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *expert_idx,
+                                 const float *priority, int64_t T, int32_t d, int32_t E, int32_t k,
+                                 int64_t C, int32_t *slot, uint8_t *drop_mask, int32_t *expert_count,
+                                 void *xbuf, void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    if (C < 0 || C > T) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(priority, empty) ||
+        !ptr4_ok(slot, empty) || (drop_mask == nullptr && !empty) || !ptr4_ok(expert_count, false) ||
+        !ptr_ok(xbuf, C == 0))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const PriorityWs w = priority_ws(T, E, k);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    char *base = static_cast<char *>(ws);
+    int32_t *rank = reinterpret_cast<int32_t *>(base + w.d.rank);
+    int32_t *hist = reinterpret_cast<int32_t *>(base + w.d.hist);
+    int32_t *n_e = reinterpret_cast<int32_t *>(base + w.cnt);
+    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, nullptr, stream));
+    // an unbounded capacity: the scan's counts are the experts' choice counts
+    MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, T * k + 1, n_e, nullptr, 0, nullptr,
+                                  nullptr, nullptr, 0, nullptr, stream));
+    MOE_HIP(moe::launch_priority_slots(x, (int)esize(dt), expert_idx, priority, rank, hist, n_e, T, d, E, k,
+                                       C, reinterpret_cast<uint64_t *>(base + w.list),
+                                       reinterpret_cast<int32_t *>(base + w.off), slot, drop_mask,
+                                       expert_count, xbuf, stream));
+    return MOE_OK;
 }
 
 moe_status moe_expert_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count, int32_t E,

@@ -117,6 +117,24 @@ def test_router_rejects(case, expect):
 
 @_no_gpu
 @pytest.mark.parametrize("case,expect", [
+    (dict(pr=None), L.MOE_ERR_INVALID_ARGUMENT),               # no scores
+    (dict(pr=P + 2), L.MOE_ERR_INVALID_ARGUMENT),              # misaligned scores
+    (dict(C=65), L.MOE_ERR_INVALID_ARGUMENT),                  # C > T
+    (dict(E=1025), L.MOE_ERR_UNSUPPORTED),
+    (dict(ws_bytes=0), L.MOE_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_priority_dispatch_rejects(case, expect):
+    a = dict(x=P, dt=L.MOE_BF16, idx=P, pr=P, T=64, d=64, E=8, k=1, C=16, slot=P, drop=P, cnt=P, xbuf=P,
+             ws=P, ws_bytes=1 << 30)
+    a.update(case)
+    st = L.LIB.moe_dispatch_priority(a["x"], a["dt"], a["idx"], a["pr"], a["T"], a["d"], a["E"], a["k"],
+                                     a["C"], a["slot"], a["drop"], a["cnt"], a["xbuf"], a["ws"],
+                                     a["ws_bytes"], None)
+    assert st == expect
+
+
+@_no_gpu
+@pytest.mark.parametrize("case,expect", [
     (dict(Wn=None), L.MOE_ERR_INVALID_ARGUMENT),               # no noise weights
     (dict(eps=None), L.MOE_ERR_INVALID_ARGUMENT),              # no draws
     (dict(eps=P + 2), L.MOE_ERR_INVALID_ARGUMENT),             # misaligned draws
