@@ -377,6 +377,70 @@ def combine(gate: np.ndarray, drop: np.ndarray, out: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# O11 backward of the gate side: combine and router
+# ---------------------------------------------------------------------------
+
+def combine_backward(dy: np.ndarray, gate: np.ndarray, drop: np.ndarray, out: np.ndarray):
+    """Gradients of y = combine(gate, drop, out) given dL/dy, float64.
+
+    y_t = sum over kept j of g_tj E_tj(x_t) is linear in both factors:
+    dL/dg_tj = <dy_t, E_tj(x_t)> and dL/dE_tj = g_tj dy_t for kept
+    choices; a dropped choice gets zero for both.  Returns (dgate [T, k],
+    dout [T, k, d]).
+    """
+    keep = (np.asarray(drop) == 0).astype(np.float64)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    dgate = np.einsum("td,tjd->tj", dy64, np.asarray(out, dtype=np.float64)) * keep
+    dout = (np.asarray(gate, dtype=np.float64) * keep)[:, :, None] * dy64[:, None, :]
+    return dgate, dout
+
+
+def router_backward(x64: np.ndarray, W_r: np.ndarray, z: np.ndarray, idx: np.ndarray,
+                    dgate: np.ndarray, k: int, alpha: float, z_weight: float):
+    """Gradient of the router's part of the loss, with the choices held fixed.
+
+    L = sum_tj dgate_tj g_tj + alpha N sum_i f_i P_i + z_weight z_loss, where
+    g are the gates (gates(): the full-softmax probability of the choice for
+    k = 1, the softmax over the kept logits for k >= 2), f_i the fraction of
+    choices of expert i (a constant: the top-k is not differentiated) and
+    P_i the mean probability.  [CMU-L16] exercise 2 (the gradient of the
+    balance loss with respect to p_i(x) is N f_i / T, times alpha; f carries
+    no gradient); the z-loss as router_z_loss, d/dz_ti of (1/T) lse_t^2 being
+    (2/T) lse_t p_ti.  Each path goes through the softmax Jacobian to the
+    logits z; then dW_r = dz^T x, db_r = sum_t dz_t and the router's part of
+    dx is dz W_r.  All in float64 from the fp32 logits z.
+
+    Returns (dz [T, E], dW_r [E, d], db_r [E], dx [T, d]).
+    """
+    z64 = np.asarray(z, dtype=np.float64)
+    T, E = z64.shape
+    p = softmax(z64)
+    rows = np.arange(T)[:, None]
+    dg = np.asarray(dgate, dtype=np.float64)
+    dz = np.zeros((T, E))
+    if k == 1:
+        e = np.asarray(idx)[:, 0]
+        g = p[np.arange(T), e]
+        onehot = np.zeros((T, E))
+        onehot[np.arange(T), e] = 1.0
+        dz += (dg[:, 0] * g)[:, None] * (onehot - p)
+    else:
+        g = softmax(z64[rows, idx])
+        s = np.sum(g * dg, axis=1, keepdims=True)
+        np.add.at(dz, (np.broadcast_to(rows, idx.shape), idx), g * (dg - s))
+    f = route_count(idx, E).astype(np.float64) / (k * T)
+    a = alpha * E * f / T
+    dz += p * (a[None, :] - (p @ a)[:, None])
+    m = np.max(z64, axis=1)
+    lse = m + np.log(np.sum(np.exp(z64 - m[:, None]), axis=1))
+    dz += z_weight * (2.0 / T) * lse[:, None] * p
+    dW = dz.T @ np.asarray(x64, dtype=np.float64)
+    db = dz.sum(axis=0)
+    dx = dz @ np.asarray(W_r, dtype=np.float64)
+    return dz, dW, db, dx
+
+
+# ---------------------------------------------------------------------------
 # whole layer
 # ---------------------------------------------------------------------------
 

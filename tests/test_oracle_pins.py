@@ -586,6 +586,132 @@ def test_priority_worked_example():
 
 
 # ---------------------------------------------------------------------------
+# backward of the gate side: finite differences of the forward definitions
+# (routing held fixed), closed forms, and the page's exercise 2
+# ---------------------------------------------------------------------------
+
+def _bwd_case(k, seed=13, T=7, d=5, E=4, drops=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    W = rng.standard_normal((E, d)) * 0.8
+    z = x @ W.T
+    idx = np.argsort(-z, axis=1, kind="stable")[:, :k]
+    out = rng.standard_normal((T, k, 3))
+    dy = rng.standard_normal((T, 3))
+    drop = np.zeros((T, k), np.uint8)
+    if drops:
+        drop[1, 0] = 1
+        drop[4, k - 1] = 1
+    return x, W, idx, out, dy, drop
+
+
+def _router_loss(x, W, idx, out, dy, drop, k, alpha, zw):
+    """The router's loss from the oracle's forward pieces, all in float64:
+    <dy, combine(g, drop, out)> + aux + zw * z-loss, with fixed choices."""
+    z = x @ W.T
+    T = z.shape[0]
+    p = O.softmax(z)
+    rows = np.arange(T)[:, None]
+    g = p[rows, idx] if k == 1 else O.softmax(z[rows, idx])
+    y = O.combine(g, drop, out)
+    return float(np.sum(dy * y)) + O.aux_loss(p, idx, W.shape[0], alpha) + zw * O.router_z_loss(z)
+
+
+def check_router_backward_finite_differences(k):
+    x, W, idx, out, dy, drop = _bwd_case(k)
+    alpha, zw = 0.3, 0.2
+    T = x.shape[0]
+    rows = np.arange(T)[:, None]
+    z = x @ W.T
+    p = O.softmax(z)
+    g = p[rows, idx] if k == 1 else O.softmax(z[rows, idx])
+    dgate, _ = O.combine_backward(dy, g, drop, out)
+    dz, dW, db, dx = O.router_backward(x, W, z, idx, dgate, k, alpha, zw)
+    h = 1e-6
+    for (i, j) in [(0, 0), (1, 3), (2, 1), (3, 4)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[i, j] += h
+        Wm[i, j] -= h
+        fd = (_router_loss(x, Wp, idx, out, dy, drop, k, alpha, zw) -
+              _router_loss(x, Wm, idx, out, dy, drop, k, alpha, zw)) / (2 * h)
+        assert abs(fd - dW[i, j]) <= 1e-6 * max(1.0, abs(fd)), (i, j, fd, dW[i, j])
+    for (t, j) in [(0, 0), (4, 2), (6, 4)]:
+        xp, xm = x.copy(), x.copy()
+        xp[t, j] += h
+        xm[t, j] -= h
+        fd = (_router_loss(xp, W, idx, out, dy, drop, k, alpha, zw) -
+              _router_loss(xm, W, idx, out, dy, drop, k, alpha, zw)) / (2 * h)
+        assert abs(fd - dx[t, j]) <= 1e-6 * max(1.0, abs(fd)), (t, j, fd, dx[t, j])
+    assert np.allclose(db, dz.sum(axis=0), rtol=0, atol=1e-14)
+
+
+def check_combine_backward_finite_differences():
+    x, W, idx, out, dy, drop = _bwd_case(2)
+    rng = np.random.default_rng(2)
+    g = rng.random((x.shape[0], 2))
+    dgate, dout = O.combine_backward(dy, g, drop, out)
+    h = 1e-6
+    loss = lambda gg, oo: float(np.sum(dy * O.combine(gg, drop, oo)))
+    for (t, j) in [(0, 0), (1, 0), (4, 1), (5, 1)]:
+        gp, gm = g.copy(), g.copy()
+        gp[t, j] += h
+        gm[t, j] -= h
+        assert abs((loss(gp, out) - loss(gm, out)) / (2 * h) - dgate[t, j]) < 1e-8
+        op, om = out.copy(), out.copy()
+        op[t, j, 2] += h
+        om[t, j, 2] -= h
+        assert abs((loss(g, op) - loss(g, om)) / (2 * h) - dout[t, j, 2]) < 1e-8
+
+
+def test_router_backward_finite_differences_k1():
+    check_router_backward_finite_differences(1)
+
+
+def test_router_backward_finite_differences_k2():
+    check_router_backward_finite_differences(2)
+
+
+def test_combine_backward_finite_differences():
+    check_combine_backward_finite_differences()
+
+
+def test_aux_gradient_vanishes_at_uniform_load():
+    """f_i = 1/N: alpha N sum_i f_i P_i = alpha sum_i P_i = alpha, a constant,
+    so its gradient is zero whatever the probabilities."""
+    rng = np.random.default_rng(4)
+    T, E = 12, 4
+    z = rng.standard_normal((T, E))
+    idx = (np.arange(T) % E)[:, None]
+    dz, dW, _, _ = O.router_backward(rng.standard_normal((T, 3)), rng.standard_normal((E, 3)), z, idx,
+                                     np.zeros((T, 1)), 1, 0.5, 0.0)
+    assert np.abs(dz).max() < 1e-16
+
+
+def test_z_loss_gradient_at_zero_router():
+    """W_r = 0: every logit is 0, lse = ln N and p = 1/N, so d(w z-loss)/dz_ti
+    = w (2/T) ln N / N everywhere."""
+    T, E, w = 10, 8, 0.001
+    idx = np.zeros((T, 1), np.int64)
+    dz, _, _, _ = O.router_backward(np.ones((T, 2)), np.zeros((E, 2)), np.zeros((T, E)), idx,
+                                    np.zeros((T, 1)), 1, 0.0, w)
+    assert np.allclose(dz, w * 2.0 / T * math.log(E) / E, rtol=1e-14, atol=0)
+
+
+def test_overloaded_expert_is_pushed_down():
+    """[CMU-L16] exercise 2: the balance loss's gradient with respect to
+    p_i(x_t) is alpha N f_i / T, so the most loaded expert's logit has a
+    positive gradient for every token (descent lowers it) and the least
+    loaded one a negative one."""
+    rng = np.random.default_rng(8)
+    T, E = 40, 4
+    z = rng.standard_normal((T, E))
+    idx = np.where(np.arange(T) < 25, 0, 1 + np.arange(T) % 3)[:, None]     # expert 0 holds 25 of 40
+    dz, _, _, _ = O.router_backward(np.zeros((T, 2)), np.zeros((E, 2)), z, idx, np.zeros((T, 1)), 1, 0.1, 0.0)
+    f = O.route_count(idx, E)
+    assert np.all(dz[:, np.argmax(f)] > 0) and np.all(dz[:, np.argmin(f)] < 0)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -758,3 +884,53 @@ def test_planted_priority_mistake_is_caught(monkeypatch, name, repl, check):
     monkeypatch.setattr(O, name, repl)
     with pytest.raises(AssertionError):
         check()
+
+
+def _router_backward_no_minus_p(x64, W_r, z, idx, dgate, k, alpha, z_weight):
+    """The gate path without the -p term of the softmax Jacobian."""
+    dz, dW, db, dx = _ORIG_RB(x64, W_r, z, idx, dgate, k, alpha, z_weight)
+    T = dz.shape[0]
+    p = O.softmax(np.asarray(z, np.float64))
+    e = np.asarray(idx)[:, 0]
+    g = p[np.arange(T), e]
+    dz = dz - (np.asarray(dgate)[:, 0] * g)[:, None] * (-p)
+    return dz, dz.T @ x64, dz.sum(0), dz @ W_r
+
+
+def _router_backward_f_without_k(x64, W_r, z, idx, dgate, k, alpha, z_weight):
+    """f counted over kT choices but divided by T only."""
+    return _ORIG_RB(x64, W_r, z, idx, dgate, k, alpha * k, z_weight)
+
+
+def _router_backward_zloss_no_square(x64, W_r, z, idx, dgate, k, alpha, z_weight):
+    """The z-loss gradient of (1/T) sum lse instead of (1/T) sum lse^2."""
+    dz, _, _, _ = _ORIG_RB(x64, W_r, z, idx, dgate, k, alpha, 0.0)
+    p = O.softmax(np.asarray(z, np.float64))
+    dz = dz + z_weight * (1.0 / dz.shape[0]) * p
+    return dz, dz.T @ x64, dz.sum(0), dz @ W_r
+
+
+_ORIG_RB = O.router_backward
+
+
+@pytest.mark.parametrize("repl,check", [
+    (_router_backward_no_minus_p, lambda: check_router_backward_finite_differences(1)),
+    (_router_backward_f_without_k, lambda: check_router_backward_finite_differences(2)),
+    (_router_backward_zloss_no_square, lambda: check_router_backward_finite_differences(2)),
+])
+def test_planted_router_backward_mistake_is_caught(monkeypatch, repl, check):
+    monkeypatch.setattr(O, "router_backward", repl)
+    with pytest.raises(AssertionError):
+        check()
+
+
+def test_planted_combine_backward_drop_is_caught(monkeypatch):
+    """A combine backward that also sends gradient to dropped choices."""
+    def keep_all(dy, gate, drop, out):
+        return _ORIG_CB(dy, gate, np.zeros_like(drop), out)
+    monkeypatch.setattr(O, "combine_backward", keep_all)
+    with pytest.raises(AssertionError):
+        check_combine_backward_finite_differences()
+
+
+_ORIG_CB = O.combine_backward
