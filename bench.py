@@ -186,6 +186,8 @@ def kernel_stage(name: str) -> str:
     The noisy router and the standalone router reduction run only in the
     noisy-router measurement (the forward sums the router's partials in its
     dispatch scan), so they form a stage of their own."""
+    if "combine_backward" in name or "router_bwd" in name:
+        return "gate_backward"
     if _NOISY.search(name):
         return "noisy_router"
     if "router" in name:
@@ -357,6 +359,9 @@ def main(argv=None):
                     help="noisy top-k router calls timed after the steps (0 skips them)")
     ap.add_argument("--priority-calls", type=int, default=20,
                     help="priority-routing dispatch calls timed after the steps (0 skips them)")
+    ap.add_argument("--backward-calls", type=int, default=20,
+                    help="gate-side backward calls (combine + router backward) timed after the steps "
+                         "(0 skips them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel that scales the HBM byte counters), then exit")
@@ -541,6 +546,40 @@ def main(argv=None):
         variants["priority_dispatch"] = dict(us=round(pr_s * 1e6, 2), bytes=pw["bytes"], kept=A_pr,
                                              calls=args.priority_calls, **roofline_of(pw, pr_s))
         del pws
+    # the gate-side backward (combine backward, then router backward through
+    # the gates, the balance loss and the z-loss), on the split API's forward
+    # buffers, timed on its own
+    if args.backward_calls > 0:
+        idx_b, gate_b, _, rc_b, lg_b = moe.router(x, W_r, k=cfg["k"], b_r=b_r, logits=True)
+        slot_b, _, cnt_b, xbuf_b = moe.dispatch(x, idx_b, cfg["E"], plan.C)
+        ybuf_b = moe.expert_ffn(xbuf_b, cnt_b, W1, W2, W3=W3, b1=b1, b2=b2, act=cfg["act"])
+        del xbuf_b
+        dy_b = torch.randn((cfg["T"], cfg["d"]), device=dev).to(x.dtype)
+        dyb_b = torch.zeros_like(ybuf_b)
+        bws = torch.empty(max(L.LIB.moe_router_backward_workspace_bytes(cfg["T"], cfg["d"], cfg["E"]), 256),
+                          dtype=torch.uint8, device=dev)
+
+        def gate_backward():
+            dg, _ = moe.combine_backward(dy_b, ybuf_b, idx_b, slot_b, gate_b, dybuf=dyb_b)
+            moe.router_backward(x, W_r, lg_b, idx_b, gate_b, dg, rc_b, alpha=cfg["alpha"], z_weight=1e-3,
+                                workspace=bws)
+        gate_backward()
+        bw_ev = hip.create(2)
+        hip.record(bw_ev[0], stream.cuda_stream)
+        for _ in range(args.backward_calls):
+            gate_backward()
+        hip.record(bw_ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        bw_s = hip.elapsed_ms(bw_ev[0], bw_ev[1]) / args.backward_calls / 1e3
+        hip.destroy(bw_ev)
+        A_b = int(cnt_b.sum().item())
+        T_, d_, E_, k_ = cfg["T"], cfg["d"], cfg["E"], cfg["k"]
+        s_ = 2 if cfg["dtype"] == "bf16" else 4
+        bw = dict(bytes=3 * A_b * d_ * s_ + 16 * T_ * k_ + 8 * T_ * E_ + T_ * d_ * (s_ + 4) + 8 * E_ * d_
+                  + 12 * T_ * k_, flops=4 * T_ * E_ * d_, dtype="f32")
+        variants["gate_backward"] = dict(us=round(bw_s * 1e6, 2), bytes=bw["bytes"], flops=bw["flops"],
+                                         calls=args.backward_calls, **roofline_of(bw, bw_s))
+        del ybuf_b, dyb_b, bws
     stages = {}
     for name in L.STAGES:
         r = roofline_of(work[name], stage_ms[name] / 1e3)

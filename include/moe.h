@@ -80,6 +80,7 @@ int64_t moe_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor);
 size_t moe_router_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k);
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
 size_t moe_dispatch_priority_workspace_bytes(int64_t T, int32_t E, int32_t k);
+size_t moe_router_backward_workspace_bytes(int64_t T, int32_t d, int32_t E);
 size_t moe_expert_ffn_workspace_bytes(int32_t E, int64_t C, int32_t dff, moe_dtype dt);
 size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
                            int64_t C, moe_dtype dt, moe_act act);
@@ -123,6 +124,8 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
  *                       logits z ([CMU-L16] section 4.2, the z-loss of Zoph
  *                       et al.; unweighted: the training loss multiplies it,
  *                       by 0.001 in OLMoE); 0 for T = 0
+ *   logits      [T, E]  fp32 out, or NULL: the logits W_r x + b_r as the
+ *                       softmax sees them (what moe_router_backward takes)
  *   ws          moe_router_workspace_bytes(T, d, E, k) bytes of device scratch
  *               (per-block partial sums, and for bf16 x with E <= 256 the
  *               exact three-part bf16 split of W_r that the MFMA path reads)
@@ -132,7 +135,7 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
 moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k,
                       int32_t *expert_idx, float *gate, float *prob_sum, int32_t *route_count,
-                      float *z_loss, void *ws, size_t ws_bytes, hipStream_t stream);
+                      float *z_loss, float *logits, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Noisy top-k router: moe_router on the logits
@@ -196,6 +199,47 @@ moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *exp
                                  const float *priority, int64_t T, int32_t d, int32_t E, int32_t k,
                                  int64_t C, int32_t *slot, uint8_t *drop_mask, int32_t *expert_count,
                                  void *xbuf, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Combine backward: the gradients of moe_combine's y with respect to the
+ * gates and the expert outputs, given dy = dL/dy.  y is linear in both
+ * ([CS25-L5] "Switch Layer"): for a kept choice (t, j) at expert e, slot s,
+ *   dgate[t, j]        = <dy_t, ybuf[e, s]>   (fp32 sum over d)
+ *   dybuf[e, s, :]     = gate[t, j] * dy_t    (rounded to the storage dtype)
+ * and a dropped choice gets dgate = 0 (its dybuf rows are not written).
+ *   dy [T, d] and ybuf [E, C, d] in the storage dtype; expert_idx, slot,
+ *   gate as moe_combine; dgate [T, k] fp32 out; dybuf [E, C, d] out, only
+ *   the kept rows written (the caller clears it if it needs the rest).
+ */
+moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, const int32_t *expert_idx,
+                                const int32_t *slot, const float *gate, int64_t T, int32_t d, int32_t E,
+                                int32_t k, int64_t C, float *dgate, void *dybuf, hipStream_t stream);
+
+/*
+ * Router backward: the gradient of
+ *   L = sum_tj dgate[t, j] g_tj + alpha N sum_i f_i P_i + z_weight z_loss
+ * with the choices held fixed, to the logits, W_r, b_r and x.  g are the
+ * gates of moe_router (k = 1: full-softmax probability of the choice;
+ * k >= 2: softmax over the kept logits), f_i = route_count_i / (k T) is a
+ * constant ([CMU-L16] exercise 2: the balance loss's gradient with respect
+ * to p_i(x_t) is alpha N f_i / T) and z_loss is moe_router's.  The top-k
+ * choice carries no gradient.
+ *   x [T, d] (storage dtype), W_r [E, d] fp32, logits [T, E] fp32 (from
+ *   moe_router), expert_idx / gate / route_count from moe_router, dgate
+ *   [T, k] fp32 (from moe_combine_backward), alpha and z_weight the loss
+ *   weights (0 leaves a term out).
+ *   dlogits [T, E] fp32 out, dL/dz
+ *   dW_r    [E, d] fp32 out, dlogits^T x (fp32, fixed order: 512-token
+ *           partial sums, then their sum in order)
+ *   db_r    [E] fp32 out or NULL, sum_t dlogits_t
+ *   dx      [T, d] fp32 out or NULL, the router's part of dL/dx, dlogits W_r
+ *   ws      moe_router_backward_workspace_bytes(T, d, E) bytes of scratch
+ */
+moe_status moe_router_backward(const void *x, moe_dtype dt, const float *W_r, const float *logits,
+                               const int32_t *expert_idx, const float *gate, const float *dgate,
+                               const int32_t *route_count, int64_t T, int32_t d, int32_t E, int32_t k,
+                               float alpha, float z_weight, float *dlogits, float *dW_r, float *db_r,
+                               float *dx, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Experts: every expert's FFN on its kept rows, as grouped GEMMs.

@@ -42,12 +42,16 @@ SIGNATURES = {
     "moe_router_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_dispatch_priority_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_router_backward_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_combine_backward": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "moe_router_backward": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32,
+                                      C.c_float, C.c_float, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i32, _i64, _i32, C.c_int]),
     "moe_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i64, C.c_int, C.c_int]),
     "moe_forward_workspace_layout": (C.c_int, [_i64, _i32, _i32, _i32, _i32, _i64, C.c_int,
                                                C.c_int, C.POINTER(WsLayout)]),
     "moe_router": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p,
-                             _p, _p, _sz, _p]),
+                             _p, _p, _p, _sz, _p]),
     "moe_router_noisy": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p,
                                    _p, _p, _p, _sz, _p]),
     "moe_dispatch": (C.c_int, [_p, C.c_int, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p, _p,

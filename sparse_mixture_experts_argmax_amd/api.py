@@ -67,11 +67,12 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
 
 
 def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W_noise=None,
-           noise=None):
+           noise=None, logits: bool = False):
     """Router: returns (expert_idx [T,k] int32, gate [T,k] fp32, prob_sum [E] fp32, route_count [E] int32),
     and with z_loss=True also the router z-loss [1] fp32 (mean over tokens of the squared
     log-sum-exp of the logits).  With W_noise [E,d] fp32 and noise [T,E] fp32 (standard normal
-    draws) the noisy top-k router: the logits become W_r x + noise * softplus(W_noise x)."""
+    draws) the noisy top-k router: the logits become W_r x + noise * softplus(W_noise x).
+    With logits=True (plain router) the fp32 logits [T, E] are returned last."""
     T, d = x.shape
     E = W_r.shape[0]
     dev = x.device
@@ -85,6 +86,9 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W
     prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
     route_count = torch.empty(E, dtype=torch.int32, device=dev)
     zl = torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if logits else None
+    if logits and W_noise is not None:
+        raise ValueError("logits are returned by the plain router only")
     need = L.LIB.moe_router_workspace_bytes(T, d, E, k)
     if need == L.SIZE_MAX:
         raise ValueError("invalid router sizes")
@@ -92,15 +96,18 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W
     if W_noise is None:
         L.check("moe_router", L.LIB.moe_router(
             _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
-            _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(ws), ws.numel(), _stream(dev)))
+            _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(lg), _ptr(ws), ws.numel(), _stream(dev)))
     else:
         L.check("moe_router_noisy", L.LIB.moe_router_noisy(
             _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W_noise), _ptr(noise), T, d, E, k,
             _ptr(idx), _ptr(gate), _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(ws), ws.numel(),
             _stream(dev)))
+    out = (idx, gate, prob_sum, route_count)
     if z_loss:
-        return idx, gate, prob_sum, route_count, zl
-    return idx, gate, prob_sum, route_count
+        out += (zl,)
+    if logits:
+        out += (lg,)
+    return out
 
 
 def dispatch(x, expert_idx, E: int, C: int, workspace=None):
@@ -144,6 +151,44 @@ def dispatch_priority(x, expert_idx, priority, E: int, C: int, workspace=None):
         _ptr(x), _dtype_code(x), _ptr(expert_idx), _ptr(priority), T, d, E, k, C, _ptr(slot), _ptr(drop),
         _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
     return slot, drop, count, xbuf
+
+
+def combine_backward(dy, ybuf, expert_idx, slot, gate, dybuf=None):
+    """Combine backward: returns (dgate [T,k] fp32, dybuf [E,C,d]; kept rows written)."""
+    E, C, d = ybuf.shape
+    T, k = expert_idx.shape
+    dev = dy.device
+    _same(ybuf.dtype, dy)
+    dgate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if dybuf is None:
+        dybuf = torch.zeros_like(ybuf)
+    L.check("moe_combine_backward", L.LIB.moe_combine_backward(
+        _ptr(dy), _dtype_code(dy), _ptr(ybuf), _ptr(expert_idx), _ptr(slot), _ptr(gate), T, d, E, k, C,
+        _ptr(dgate), _ptr(dybuf), _stream(dev)))
+    return dgate, dybuf
+
+
+def router_backward(x, W_r, logits, expert_idx, gate, dgate, route_count, alpha=1e-2, z_weight=0.0,
+                    workspace=None):
+    """Router backward: returns (dlogits [T,E], dW_r [E,d], db_r [E], dx [T,d]), all fp32."""
+    T, d = x.shape
+    E = W_r.shape[0]
+    k = expert_idx.shape[1]
+    dev = x.device
+    _same(torch.float32, W_r, logits, gate, dgate)
+    dz = torch.empty((T, E), dtype=torch.float32, device=dev)
+    dW = torch.empty((E, d), dtype=torch.float32, device=dev)
+    db = torch.empty(E, dtype=torch.float32, device=dev)
+    dx = torch.empty((T, d), dtype=torch.float32, device=dev)
+    need = L.LIB.moe_router_backward_workspace_bytes(T, d, E)
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid router sizes")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    L.check("moe_router_backward", L.LIB.moe_router_backward(
+        _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(logits), _ptr(expert_idx), _ptr(gate), _ptr(dgate),
+        _ptr(route_count), T, d, E, k, alpha, z_weight, _ptr(dz), _ptr(dW), _ptr(db), _ptr(dx), _ptr(ws),
+        ws.numel(), _stream(dev)))
+    return dz, dW, db, dx
 
 
 def expert_ffn(xbuf, expert_count, W1, W2, *, W3=None, b1=None, b2=None, act="relu",

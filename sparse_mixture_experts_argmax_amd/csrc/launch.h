@@ -15,11 +15,13 @@ int router_blocks(int64_t T, int dtype_bf16, int E);
 // split of W_r (or of the stacked noisy weight).
 int router_w3_rows(int E);
 // part_z [router_blocks]: each block's sum of its tokens' squared
-// log-sum-exps (the router z-loss partials).
+// log-sum-exps (the router z-loss partials).  logits (may be null): the
+// fp32 logits W_r x + b_r [T, E] as the softmax sees them (before the
+// NaN-to-minus-infinity ranking rule).
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
                          float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s,
-                         float *part_z);
+                         float *part_z, float *logits = nullptr);
 // Noisy top-k router (any dtype and E; MFMA for bf16 x and E <= 256):
 // logits H = W_r x (+ b_r) + eps * softplus(W_noise x), eps [T, E] given;
 // partial rows as launch_router, router_noisy_blocks(T, dtype_bf16, E) of
@@ -81,6 +83,20 @@ hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *e
                                  const int32_t *n_e, int64_t T, int d, int E, int k, int64_t C,
                                  uint64_t *list, int32_t *off, int32_t *slot, uint8_t *drop_mask,
                                  int32_t *expert_count, void *xbuf, hipStream_t s);
+// Backward of the gate side (backward.hip).  Combine: dgate [T, k] fp32 and
+// the kept rows of dybuf [E, C, d] (g dy, storage dtype).  Router: dz [T, E]
+// from the logits, gates and dgate; dW [E, d], db [E] (may be null) and dx
+// [T, d] (may be null), fp32; part_w [router_bwd_chunks(T)][E][d] and part_b
+// [router_bwd_chunks(T)][E] are scratch.
+int router_bwd_chunks(int64_t T);
+hipError_t launch_combine_backward(const void *dy, int dtype_bf16, const void *ybuf, const int32_t *expert_idx,
+                                   const int32_t *slot, const float *gate, int64_t T, int d, int E, int k,
+                                   int64_t C, float *dgate, void *dybuf, hipStream_t s);
+hipError_t launch_router_backward(const void *x, int dtype_bf16, const float *W_r, const float *logits,
+                                  const int32_t *expert_idx, const float *gate, const float *dgate,
+                                  const int32_t *route_count, int64_t T, int d, int E, int k, float alpha,
+                                  float z_weight, float *dz, float *dW, float *db, float *dx, float *part_w,
+                                  float *part_b, hipStream_t s);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,

@@ -154,7 +154,7 @@ moe_status check_ffn_args(moe_dtype dt, moe_act act, const void *W1, const void 
 moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
                       float *gate, float *prob_sum, int32_t *route_count, float *z_loss, char *ws,
-                      hipStream_t stream, bool reduce = true) {
+                      hipStream_t stream, bool reduce = true, float *logits = nullptr) {
     const RouterWs w = router_ws(T, d, E);
     float *part_prob = reinterpret_cast<float *>(ws + w.part_prob);
     int32_t *part_cnt = reinterpret_cast<int32_t *>(ws + w.part_cnt);
@@ -162,7 +162,7 @@ moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float
     uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + w.w3);
     const int bf16 = dt == MOE_BF16;
     MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
-                               part_cnt, w3, stream, part_z));
+                               part_cnt, w3, stream, part_z, logits));
     if (reduce)
         MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
                                           prob_sum, route_count, stream, part_z, T, z_loss));
@@ -288,20 +288,20 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
 moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
                       float *gate, float *prob_sum, int32_t *route_count, float *z_loss,
-                      void *ws, size_t ws_bytes, hipStream_t stream) {
+                      float *logits, void *ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK(check_sizes(T, E, k));
     MOE_CHECK(check_width(d));
     if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
     const bool empty = T == 0;
     if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr4_ok(expert_idx, empty) ||
         !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false) ||
-        !(z_loss == nullptr || ptr4_ok(z_loss, false)))
+        !(z_loss == nullptr || ptr4_ok(z_loss, false)) || !(logits == nullptr || ptr4_ok(logits, empty)))
         return MOE_ERR_INVALID_ARGUMENT;
     const size_t need = router_ws(T, d, E).total;
     if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
     return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count, z_loss,
-                      static_cast<char *>(ws), stream);
+                      static_cast<char *>(ws), stream, true, logits);
 }
 
 moe_status moe_router_noisy(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
@@ -386,6 +386,52 @@ moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *exp
                                        C, reinterpret_cast<uint64_t *>(base + w.list),
                                        reinterpret_cast<int32_t *>(base + w.off), slot, drop_mask,
                                        expert_count, xbuf, stream));
+    return MOE_OK;
+}
+
+moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, const int32_t *expert_idx,
+                                const int32_t *slot, const float *gate, int64_t T, int32_t d, int32_t E,
+                                int32_t k, int64_t C, float *dgate, void *dybuf, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    if (C < 0 || C > T) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(dy, empty) || !ptr_ok(ybuf, C == 0) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(slot, empty) ||
+        !ptr4_ok(gate, empty) || !ptr4_ok(dgate, empty) || !ptr_ok(dybuf, C == 0))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_HIP(moe::launch_combine_backward(dy, dt == MOE_BF16, ybuf, expert_idx, slot, gate, T, d, E, k, C, dgate,
+                                         dybuf, stream));
+    return MOE_OK;
+}
+
+size_t moe_router_backward_workspace_bytes(int64_t T, int32_t d, int32_t E) {
+    if (check_sizes(T, E, 1) != MOE_OK || check_width(d) != MOE_OK) return SIZE_MAX;
+    const size_t nc = (size_t)moe::router_bwd_chunks(T);
+    return up(nc * E * d * 4) + up(nc * E * 4);
+}
+
+moe_status moe_router_backward(const void *x, moe_dtype dt, const float *W_r, const float *logits,
+                               const int32_t *expert_idx, const float *gate, const float *dgate,
+                               const int32_t *route_count, int64_t T, int32_t d, int32_t E, int32_t k,
+                               float alpha, float z_weight, float *dlogits, float *dW_r, float *db_r,
+                               float *dx, void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr4_ok(W_r, false) || !ptr4_ok(logits, empty) || !ptr4_ok(expert_idx, empty) ||
+        !ptr4_ok(gate, empty) || !ptr4_ok(dgate, empty) || !ptr4_ok(route_count, false) ||
+        !ptr4_ok(dlogits, empty) || !ptr4_ok(dW_r, false) || !(db_r == nullptr || ptr4_ok(db_r, false)) ||
+        !(dx == nullptr || ptr4_ok(dx, empty)) || !isfinite(alpha) || !isfinite(z_weight))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const size_t nc = (size_t)moe::router_bwd_chunks(T);
+    if (ws_bytes < up(nc * E * d * 4) + up(nc * E * 4)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    float *part_w = static_cast<float *>(ws);
+    float *part_b = reinterpret_cast<float *>(static_cast<char *>(ws) + up(nc * E * d * 4));
+    MOE_HIP(moe::launch_router_backward(x, dt == MOE_BF16, W_r, logits, expert_idx, gate, dgate, route_count, T, d,
+                                        E, k, alpha, z_weight, dlogits, dW_r, db_r, dx, part_w, part_b, stream));
     return MOE_OK;
 }
 

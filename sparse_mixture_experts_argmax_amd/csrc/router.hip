@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
     float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z,
-    const float *__restrict__ eps) {
+    const float *__restrict__ eps, float *__restrict__ logits) {
     using G = RGeo<NB, KC>;
     constexpr int EP = G::EP, ROWB = G::ROWB, PIECES = G::PIECES, S = G::S, PERW = G::PERW;
     constexpr int STAGE = G::STAGE, RPI = G::RPI;
@@ -387,6 +387,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                 const float e = (tok_ok && n < E) ? eps[t * E + n] : 0.f;
                 z = fmaf(e, sp, z);
             }
+            if (logits != nullptr && tok_ok && n < E) logits[t * E + n] = z;
             if (z != z) z = -INFINITY;          // NaN ranks as -inf: indices stay in range
             v[nb] = z;
             if (n < E) mx = fmaxf(mx, z);
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(256) void router_generic_kernel(
     const void *__restrict__ xv, const float *__restrict__ Wr, const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
     float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z,
-    const float *__restrict__ Wn, const float *__restrict__ eps) {
+    const float *__restrict__ Wn, const float *__restrict__ eps, float *__restrict__ logits) {
     extern __shared__ float smem[];
     __shared__ float sLz[RG_TOK];                       // each token's log-sum-exp, squared
     float *sZ = smem;                                   // [RG_TOK][E]
@@ -557,6 +558,7 @@ __global__ __launch_bounds__(256) void router_generic_kernel(
                 const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
                 z = fmaf(eps[t * E + n], sp, z);
             }
+            if (logits != nullptr) logits[t * E + n] = z;
             if (z != z) z = -INFINITY;
         }
         sZ[p] = z;
@@ -690,7 +692,7 @@ int router_blocks(int64_t T, int dtype_bf16, int E) {
 hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const float *b_r,
                          int64_t T, int d, int E, int k, int32_t *expert_idx, float *gate,
                          float *part_prob, int32_t *part_cnt, uint16_t *w3, hipStream_t s,
-                         float *part_z) {
+                         float *part_z, float *logits) {
     const int nblk = router_blocks(T, dtype_bf16, E);
     if (nblk == 0) return hipSuccess;
     if (use_mfma(dtype_bf16, E)) {
@@ -702,7 +704,7 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
 #define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
     hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
                        0, s, xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt,     \
-                       part_z, nullptr)
+                       part_z, nullptr, logits)
 #define MOE_ROUTER_K(NBV, KCV, TAILV)                                                          \
     do {                                                                                       \
         if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, 0);                                  \
@@ -728,11 +730,11 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
     if (dtype_bf16)
         hipLaunchKernelGGL((router_generic_kernel<true, false>), dim3(nblk), dim3(256), shm, s, x, W_r,
                            b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, nullptr,
-                           nullptr);
+                           nullptr, logits);
     else
         hipLaunchKernelGGL((router_generic_kernel<false, false>), dim3(nblk), dim3(256), shm, s, x, W_r,
                            b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, nullptr,
-                           nullptr);
+                           nullptr, logits);
     return hipGetLastError();
 }
 
@@ -759,7 +761,7 @@ hipError_t launch_router_noisy(const void *x, int dtype_bf16, const float *W_r, 
 #define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
     hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
                        0, s, xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt,     \
-                       part_z, eps)
+                       part_z, eps, nullptr)
 #define MOE_ROUTER_K(NBV, KCV, TAILV, NZV)                                                     \
     do {                                                                                       \
         if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, NZV);                                \
@@ -785,10 +787,12 @@ hipError_t launch_router_noisy(const void *x, int dtype_bf16, const float *W_r, 
     const size_t shm = (size_t)(RG_TOK + 1) * E * sizeof(float);
     if (dtype_bf16)
         hipLaunchKernelGGL((router_generic_kernel<true, true>), dim3(nblk), dim3(256), shm, s, x, W_r,
-                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, W_noise, eps);
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, W_noise, eps,
+                           nullptr);
     else
         hipLaunchKernelGGL((router_generic_kernel<false, true>), dim3(nblk), dim3(256), shm, s, x, W_r,
-                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, W_noise, eps);
+                           b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt, part_z, W_noise, eps,
+                           nullptr);
     return hipGetLastError();
 }
 

@@ -105,13 +105,15 @@ P = 4096          # an aligned stand-in address (never dereferenced: every case 
     (dict(W_r=None), L.MOE_ERR_INVALID_ARGUMENT),
     (dict(ws_bytes=0), L.MOE_ERR_WORKSPACE_TOO_SMALL),
     (dict(zl=P + 1), L.MOE_ERR_INVALID_ARGUMENT),              # misaligned z-loss output
+    (dict(lg=P + 2), L.MOE_ERR_INVALID_ARGUMENT),              # misaligned logits output
 ])
 def test_router_rejects(case, expect):
     a = dict(x=P, dt=L.MOE_BF16, W_r=P, b_r=None, T=64, d=64, E=8, k=1, idx=P, gate=P, ps=P, rc=P,
-             zl=None, ws=P, ws_bytes=1 << 30)
+             zl=None, lg=None, ws=P, ws_bytes=1 << 30)
     a.update(case)
     st = L.LIB.moe_router(a["x"], a["dt"], a["W_r"], a["b_r"], a["T"], a["d"], a["E"], a["k"],
-                          a["idx"], a["gate"], a["ps"], a["rc"], a["zl"], a["ws"], a["ws_bytes"], None)
+                          a["idx"], a["gate"], a["ps"], a["rc"], a["zl"], a["lg"], a["ws"], a["ws_bytes"],
+                          None)
     assert st == expect
 
 
