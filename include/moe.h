@@ -234,6 +234,8 @@ moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, 
  *   db_r    [E] fp32 out or NULL, sum_t dlogits_t
  *   dx      [T, d] fp32 out or NULL, the router's part of dL/dx, dlogits W_r
  *   ws      moe_router_backward_workspace_bytes(T, d, E) bytes of scratch
+ * W_r and dx must be 16-byte aligned; T up to 65535 * 512 tokens
+ * (MOE_ERR_UNSUPPORTED beyond).
  */
 moe_status moe_router_backward(const void *x, moe_dtype dt, const float *W_r, const float *logits,
                                const int32_t *expert_idx, const float *gate, const float *dgate,

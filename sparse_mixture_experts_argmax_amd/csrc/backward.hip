@@ -150,105 +150,148 @@ __global__ __launch_bounds__(256) void router_bwd_dz_kernel(
     }
 }
 
-// dx[t, :] = sum_n dz[t, n] W_r[n, :] for TOK tokens per block; W_r is
-// read from L2 once per block, four rows per step so the loads overlap.
-template <int TOK>
+// dx[t, :] = sum_n dz[t, n] W_r[n, :] (n in order), register-tiled: a
+// block covers 64 tokens x 128 columns and steps over the experts 32 at a
+// time through LDS; each thread owns 4 tokens x 8 columns, so an expert
+// costs it 16 bytes of dz and 32 bytes of W_r from LDS for 32 FMAs.
+constexpr int DX_TT = 64, DX_NC = 128, DX_KS = 32;
 __global__ __launch_bounds__(256) void router_bwd_dx_kernel(const float *__restrict__ dz,
                                                             const float *__restrict__ Wr, int64_t T, int d,
                                                             int E, float *__restrict__ dx) {
-    extern __shared__ float s_dz[];                  // [TOK][E]
-    const int64_t t0 = (int64_t)blockIdx.x * TOK;
-    for (int i = threadIdx.x; i < TOK * E; i += 256) {
-        const int r = i / E;
-        s_dz[i] = t0 + r < T ? dz[(t0 + r) * E + (i - r * E)] : 0.f;
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < d; c += 256) {
-        float acc[TOK];
+    __shared__ __attribute__((aligned(16))) float s_a[DX_KS][DX_TT];     // dz, transposed
+    __shared__ __attribute__((aligned(16))) float s_b[DX_KS][DX_NC];     // W_r rows
+    const int tid = threadIdx.x;
+    const int tx = tid % 16, ty = tid / 16;
+    const int c0 = blockIdx.y * DX_NC;
+    const int64_t t0 = (int64_t)blockIdx.x * DX_TT;
+    float acc[4][8];
 #pragma unroll
-        for (int r = 0; r < TOK; ++r) acc[r] = 0.f;
-        int n = 0;
-        for (; n + 4 <= E; n += 4) {
-            float w[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) w[u] = Wr[(int64_t)(n + u) * d + c];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int r = 0; r < TOK; ++r) acc[r] = fmaf(s_dz[r * E + n + u], w[u], acc[r]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int n0 = 0; n0 < E; n0 += DX_KS) {
+        for (int i = tid; i < DX_TT * DX_KS; i += 256) {
+            const int r = i / DX_KS, q = i - r * DX_KS;
+            const int64_t t = t0 + r;
+            s_a[q][r] = (t < T && n0 + q < E) ? dz[t * E + n0 + q] : 0.f;
         }
-        for (; n < E; ++n) {
-            const float w = Wr[(int64_t)n * d + c];
-#pragma unroll
-            for (int r = 0; r < TOK; ++r) acc[r] = fmaf(s_dz[r * E + n], w, acc[r]);
+        for (int i = tid; i < DX_KS * (DX_NC / 4); i += 256) {
+            const int q = i / (DX_NC / 4), pc = i - q * (DX_NC / 4);
+            const int c = c0 + pc * 4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (n0 + q < E && c < d) v = *reinterpret_cast<const float4 *>(Wr + (int64_t)(n0 + q) * d + c);
+            *reinterpret_cast<float4 *>(&s_b[q][pc * 4]) = v;
         }
+        __syncthreads();
+#pragma unroll 4
+        for (int q = 0; q < DX_KS; ++q) {
+            const float4 av = *reinterpret_cast<const float4 *>(&s_a[q][ty * 4]);
+            const float4 ba = *reinterpret_cast<const float4 *>(&s_b[q][tx * 8]);
+            const float4 bb = *reinterpret_cast<const float4 *>(&s_b[q][tx * 8 + 4]);
+            const float as[4] = {av.x, av.y, av.z, av.w};
+            const float bs[8] = {ba.x, ba.y, ba.z, ba.w, bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-        for (int r = 0; r < TOK; ++r)
-            if (t0 + r < T) dx[(t0 + r) * d + c] = acc[r];
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(as[i], bs[j], acc[i][j]);
+        }
+        __syncthreads();
     }
+    const int cc = c0 + tx * 8;
+    if (cc < d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + ty * 4 + i;
+            if (t < T) {
+                float4 *o = reinterpret_cast<float4 *>(dx + t * d + cc);
+                o[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                o[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+            }
+        }
 }
 
-constexpr int DW_EG = 16;      // experts per block
 constexpr int DW_TC = 512;     // tokens per chunk (one partial row each)
-constexpr int DW_TS = 32;      // tokens staged in LDS at a time
 
-// part_w[chunk][n][c] = sum over the chunk's tokens t of dz[t, n] x[t, c];
-// column block 0 also writes part_b[chunk][n] = sum_t dz[t, n].
-template <bool BF16>
+// part_w[chunk][n][c] = sum over the chunk's tokens t (in order) of
+// dz[t, n] x[t, c], as a register-tiled product: a block covers EG experts
+// and 8 (1024 / EG) columns; each thread owns 4 experts x 8 columns, so a
+// staged token costs it 16 bytes of dz and 32 bytes of x from LDS for 32
+// FMAs.  Column block 0 also writes part_b[chunk][n] = sum_t dz[t, n].
+template <bool BF16, int EG>
 __global__ __launch_bounds__(256) void router_bwd_dw_kernel(const float *__restrict__ dz,
                                                             const void *__restrict__ x, int64_t T, int d,
                                                             int E, float *__restrict__ part_w,
                                                             float *__restrict__ part_b) {
-    __shared__ __attribute__((aligned(16))) float s_dz[DW_TS][DW_EG];
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    const int n0 = blockIdx.y * DW_EG;
+    constexpr int TY = EG / 4;                       // groups of 4 experts
+    constexpr int TX = 256 / TY;                     // groups of 8 columns
+    constexpr int NC = TX * 8;                       // columns per block
+    constexpr int TS = EG == 64 ? 32 : 16;           // tokens staged at a time
+    __shared__ __attribute__((aligned(16))) float s_dz[TS][EG];
+    __shared__ __attribute__((aligned(16))) float s_x[TS][NC];
+    const int tid = threadIdx.x;
+    const int tx = tid % TX, ty = tid / TX;
+    const int c0 = blockIdx.x * NC;
+    const int n0 = blockIdx.y * EG;
     const int chunk = blockIdx.z;
     const int64_t ta = (int64_t)chunk * DW_TC;
     const int64_t tb = ta + DW_TC < T ? ta + DW_TC : T;
-    float acc[DW_EG];
+    float acc[4][8];
 #pragma unroll
-    for (int i = 0; i < DW_EG; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
     float bacc = 0.f;
-    for (int64_t t0 = ta; t0 < tb; t0 += DW_TS) {
-        for (int i = threadIdx.x; i < DW_TS * DW_EG; i += 256) {
-            const int r = i / DW_EG, q = i - r * DW_EG;
+    for (int64_t t0 = ta; t0 < tb; t0 += TS) {
+        for (int i = tid; i < TS * EG; i += 256) {
+            const int r = i / EG, q = i - r * EG;
             const int64_t t = t0 + r;
             s_dz[r][q] = (t < tb && n0 + q < E) ? dz[t * E + n0 + q] : 0.f;
         }
-        // this column's x for the staged tokens, all loads issued together
-        // (rows past the chunk read as 0, and their dz rows are 0 too)
-        float xv[DW_TS];
+        for (int i = tid; i < TS * (NC / 8); i += 256) {
+            const int r = i / (NC / 8), pc = i - r * (NC / 8);
+            const int64_t t = t0 + r;
+            const int c = c0 + pc * 8;
+            float v[8];
+            if (t < tb && c < d) {
+                load8<BF16>(x, t * d + c, v);
+            } else {
 #pragma unroll
-        for (int r = 0; r < DW_TS; ++r) {
-            const int64_t xi = (t0 + r) * d + c;
-            const bool in = c < d && t0 + r < tb;
-            xv[r] = !in ? 0.f : BF16 ? bf2f(reinterpret_cast<const uint16_t *>(x)[xi])
-                                     : reinterpret_cast<const float *>(x)[xi];
+                for (int h = 0; h < 8; ++h) v[h] = 0.f;
+            }
+            float4 *dst = reinterpret_cast<float4 *>(&s_x[r][pc * 8]);
+            dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+            dst[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
         __syncthreads();
-        const int m = tb - t0 < DW_TS ? (int)(tb - t0) : DW_TS;
-#pragma unroll 4
-        for (int r = 0; r < DW_TS; ++r) {
-            const float4 *z4 = reinterpret_cast<const float4 *>(&s_dz[r][0]);
+        for (int r = 0; r < TS; ++r) {
+            const float4 zv = *reinterpret_cast<const float4 *>(&s_dz[r][ty * 4]);
+            const float4 xa = *reinterpret_cast<const float4 *>(&s_x[r][tx * 8]);
+            const float4 xb = *reinterpret_cast<const float4 *>(&s_x[r][tx * 8 + 4]);
+            const float zs[4] = {zv.x, zv.y, zv.z, zv.w};
+            const float xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-            for (int q = 0; q < DW_EG / 4; ++q) {
-                const float4 v = z4[q];
-                acc[4 * q] = fmaf(v.x, xv[r], acc[4 * q]);
-                acc[4 * q + 1] = fmaf(v.y, xv[r], acc[4 * q + 1]);
-                acc[4 * q + 2] = fmaf(v.z, xv[r], acc[4 * q + 2]);
-                acc[4 * q + 3] = fmaf(v.w, xv[r], acc[4 * q + 3]);
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(zs[i], xs[j], acc[i][j]);
         }
-        if (blockIdx.x == 0 && threadIdx.x < DW_EG)
-            for (int r = 0; r < m; ++r) bacc += s_dz[r][threadIdx.x];
+        if (blockIdx.x == 0 && tid < EG) {
+            const int m = tb - t0 < TS ? (int)(tb - t0) : TS;
+            for (int r = 0; r < m; ++r) bacc += s_dz[r][tid];
+        }
         __syncthreads();
     }
-    if (c < d)
+    const int cc = c0 + tx * 8;
+    if (cc < d)
 #pragma unroll
-        for (int i = 0; i < DW_EG; ++i)
-            if (n0 + i < E) part_w[((int64_t)chunk * E + n0 + i) * d + c] = acc[i];
-    if (blockIdx.x == 0 && threadIdx.x < DW_EG && n0 + threadIdx.x < E)
-        part_b[(int64_t)chunk * E + n0 + threadIdx.x] = bacc;
+        for (int i = 0; i < 4; ++i) {
+            const int n = n0 + ty * 4 + i;
+            if (n < E) {
+                float4 *o = reinterpret_cast<float4 *>(part_w + ((int64_t)chunk * E + n) * d + cc);
+                o[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                o[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+            }
+        }
+    if (blockIdx.x == 0 && tid < EG && n0 + tid < E) part_b[(int64_t)chunk * E + n0 + tid] = bacc;
 }
 
 // dW_r[n][c] = sum over chunks in order of part_w; db_r likewise.
@@ -297,20 +340,28 @@ hipError_t launch_router_backward(const void *x, int dtype_bf16, const float *W_
                                   float z_weight, float *dz, float *dW, float *db, float *dx, float *part_w,
                                   float *part_b, hipStream_t s) {
     const int nchunk = router_bwd_chunks(T);
+    if (nchunk > 65535) return hipErrorInvalidValue;      // the grid's z extent
     if (T > 0) {
         hipLaunchKernelGGL(router_bwd_dz_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits,
                            expert_idx, gate, dgate, route_count, T, E, k, alpha, z_weight, dz);
-        if (dx != nullptr && E <= 256)
-            hipLaunchKernelGGL(router_bwd_dx_kernel<32>, dim3((unsigned)((T + 31) / 32)), dim3(256),
-                               (size_t)32 * E * sizeof(float), s, dz, W_r, T, d, E, dx);
-        else if (dx != nullptr)
-            hipLaunchKernelGGL(router_bwd_dx_kernel<8>, dim3((unsigned)((T + 7) / 8)), dim3(256),
-                               (size_t)8 * E * sizeof(float), s, dz, W_r, T, d, E, dx);
-        const dim3 g((unsigned)((d + 255) / 256), (unsigned)((E + DW_EG - 1) / DW_EG), (unsigned)nchunk);
-        if (dtype_bf16)
-            hipLaunchKernelGGL(router_bwd_dw_kernel<true>, g, dim3(256), 0, s, dz, x, T, d, E, part_w, part_b);
-        else
-            hipLaunchKernelGGL(router_bwd_dw_kernel<false>, g, dim3(256), 0, s, dz, x, T, d, E, part_w, part_b);
+        if (dx != nullptr)
+            hipLaunchKernelGGL(router_bwd_dx_kernel, dim3((unsigned)((T + DX_TT - 1) / DX_TT),
+                                                          (unsigned)((d + DX_NC - 1) / DX_NC)),
+                               dim3(256), 0, s, dz, W_r, T, d, E, dx);
+#define MOE_DW(EGV)                                                                                      \
+    do {                                                                                                 \
+        const dim3 g((unsigned)((d + 8 * (1024 / EGV) - 1) / (8 * (1024 / EGV))),                        \
+                     (unsigned)((E + EGV - 1) / EGV), (unsigned)nchunk);                                 \
+        if (dtype_bf16)                                                                                  \
+            hipLaunchKernelGGL((router_bwd_dw_kernel<true, EGV>), g, dim3(256), 0, s, dz, x, T, d, E,   \
+                               part_w, part_b);                                                          \
+        else                                                                                             \
+            hipLaunchKernelGGL((router_bwd_dw_kernel<false, EGV>), g, dim3(256), 0, s, dz, x, T, d, E,  \
+                               part_w, part_b);                                                          \
+    } while (0)
+        if (E <= 16) MOE_DW(16);
+        else MOE_DW(64);
+#undef MOE_DW
     }
     const int64_t nw = (int64_t)E * d;
     hipLaunchKernelGGL(router_bwd_dw_reduce_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, part_w,

@@ -420,10 +420,11 @@ moe_status moe_router_backward(const void *x, moe_dtype dt, const float *W_r, co
     MOE_CHECK(check_width(d));
     if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
     const bool empty = T == 0;
-    if (!ptr_ok(x, empty) || !ptr4_ok(W_r, false) || !ptr4_ok(logits, empty) || !ptr4_ok(expert_idx, empty) ||
+    if (moe::router_bwd_chunks(T) > 65535) return MOE_ERR_UNSUPPORTED;
+    if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !ptr4_ok(logits, empty) || !ptr4_ok(expert_idx, empty) ||
         !ptr4_ok(gate, empty) || !ptr4_ok(dgate, empty) || !ptr4_ok(route_count, false) ||
         !ptr4_ok(dlogits, empty) || !ptr4_ok(dW_r, false) || !(db_r == nullptr || ptr4_ok(db_r, false)) ||
-        !(dx == nullptr || ptr4_ok(dx, empty)) || !isfinite(alpha) || !isfinite(z_weight))
+        !(dx == nullptr || ptr_ok(dx, empty)) || !isfinite(alpha) || !isfinite(z_weight))
         return MOE_ERR_INVALID_ARGUMENT;
     const size_t nc = (size_t)moe::router_bwd_chunks(T);
     if (ws_bytes < up(nc * E * d * 4) + up(nc * E * 4)) return MOE_ERR_WORKSPACE_TOO_SMALL;
