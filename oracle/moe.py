@@ -278,6 +278,39 @@ def assign_slots_priority(idx: np.ndarray, E: int, C: int, priority: np.ndarray)
     return slot, drop, np.asarray(fill, dtype=np.int64)
 
 
+def assign_slots_reroute(pref: np.ndarray, E: int, C: int, stages: int):
+    """Top-1 capacity slots with multi-stage re-routing of the overflow.
+
+    [CS25-L5] "“No Token Left Behind”为何没有成功": when a token's top-1 expert
+    is full, it is sent to its second choice, then its third, until it gets
+    a slot (the page reports that this did not improve the model).  Stage s
+    visits the tokens still without a slot in token order and offers each
+    its choice of rank s, pref[t, s], filling the experts from where the
+    earlier stages left them; a token still unplaced after `stages` stages
+    is dropped.  Stage 0 alone is assign_slots with k = 1.
+
+    pref [T, R] int: each token's experts in preference order (the router's
+    top-R), stages <= R.  Returns expert [T] (the expert the token landed
+    on, -1 if dropped), slot [T] (-1 if dropped), stage [T] (-1 if dropped)
+    and expert_count [E].
+    """
+    T = pref.shape[0]
+    fill = [0] * E
+    expert = np.full(T, -1, dtype=np.int32)
+    slot = np.full(T, -1, dtype=np.int32)
+    stage = np.full(T, -1, dtype=np.int32)
+    pl = np.asarray(pref).tolist()
+    for s in range(stages):
+        for t in range(T):
+            if stage[t] >= 0:
+                continue
+            e = pl[t][s]
+            if fill[e] < C:
+                expert[t], slot[t], stage[t] = e, fill[e], s
+                fill[e] += 1
+    return expert, slot, stage, np.asarray(fill, dtype=np.int64)
+
+
 # ---------------------------------------------------------------------------
 # O8 experts
 # ---------------------------------------------------------------------------

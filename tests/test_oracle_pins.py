@@ -712,6 +712,59 @@ def test_overloaded_expert_is_pushed_down():
 
 
 # ---------------------------------------------------------------------------
+# "No Token Left Behind" re-routing ([CS25-L5]): overflow tries later choices
+# ---------------------------------------------------------------------------
+
+def _pref(seed, T, E, R):
+    z = np.random.default_rng(seed).standard_normal((T, E))
+    return np.argsort(-z, axis=1, kind="stable")[:, :R].astype(np.int32)
+
+
+def check_reroute_worked_example():
+    """By hand: T = 5, E = 2, C = 2, two stages, preferences
+    [0,1] [0,1] [0,1] [1,0] [0,1].  Stage 0: t0 -> e0 slot 0, t1 -> e0 slot
+    1, t2 finds e0 full, t3 -> e1 slot 0, t4 finds e0 full.  Stage 1: t2 ->
+    e1 slot 1; t4 finds e1 full and is dropped."""
+    pref = np.array([[0, 1], [0, 1], [0, 1], [1, 0], [0, 1]], np.int32)
+    ex, sl, st, cnt = O.assign_slots_reroute(pref, 2, 2, 2)
+    assert ex.tolist() == [0, 0, 1, 1, -1] and sl.tolist() == [0, 1, 1, 0, -1]
+    assert st.tolist() == [0, 0, 1, 0, -1] and cnt.tolist() == [2, 2]
+
+
+def check_reroute_places_everyone():
+    """E stages and E C >= T: nobody is dropped (a dropped token would have
+    found every expert full, so E C tokens would be placed besides it)."""
+    T, E = 300, 6
+    pref = _pref(5, T, E, E)
+    C = O.capacity(T, E, 1, 1.0)
+    ex, sl, st, cnt = O.assign_slots_reroute(pref, E, C, E)
+    assert np.all(ex >= 0) and cnt.sum() == T
+
+
+def test_reroute_one_stage_is_the_plain_rule():
+    pref = _pref(7, 400, 5, 3)
+    C = 60
+    ex, sl, st, cnt = O.assign_slots_reroute(pref, 5, C, 1)
+    rs, rd, rc = O.assign_slots(pref[:, :1].copy(), 5, C)
+    assert np.array_equal(sl, rs[:, 0]) and np.array_equal(ex >= 0, rd[:, 0] == 0)
+    assert np.array_equal(cnt, rc)
+
+
+def test_reroute_no_overflow_stays_in_stage_zero():
+    pref = _pref(8, 200, 4, 3)
+    ex, sl, st, cnt = O.assign_slots_reroute(pref, 4, 200, 3)
+    assert np.all(st == 0) and np.array_equal(ex, pref[:, 0])
+
+
+def test_reroute_worked_example():
+    check_reroute_worked_example()
+
+
+def test_reroute_places_everyone():
+    check_reroute_places_everyone()
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must make at least one pin fail
 # ---------------------------------------------------------------------------
 
@@ -934,3 +987,37 @@ def test_planted_combine_backward_drop_is_caught(monkeypatch):
 
 
 _ORIG_CB = O.combine_backward
+
+
+def _reroute_reverse_later_stages(pref, E, C, stages):
+    """Later stages visit the tokens from the last one back."""
+    T = pref.shape[0]
+    fill = [0] * E
+    ex = np.full(T, -1, np.int32)
+    sl = np.full(T, -1, np.int32)
+    st = np.full(T, -1, np.int32)
+    for s in range(stages):
+        for t in (range(T) if s == 0 else range(T - 1, -1, -1)):
+            if st[t] < 0 and fill[pref[t, s]] < C:
+                e = pref[t, s]
+                ex[t], sl[t], st[t] = e, fill[e], s
+                fill[e] += 1
+    return ex, sl, st, np.array(fill)
+
+
+def _reroute_first_choice_only(pref, E, C, stages):
+    """Every stage offers the first choice again (no re-routing)."""
+    return _ORIG_RR(np.repeat(pref[:, :1], pref.shape[1], axis=1), E, C, stages)
+
+
+_ORIG_RR = O.assign_slots_reroute
+
+
+@pytest.mark.parametrize("repl,check", [
+    (_reroute_reverse_later_stages, check_reroute_worked_example),
+    (_reroute_first_choice_only, check_reroute_places_everyone),
+])
+def test_planted_reroute_mistake_is_caught(monkeypatch, repl, check):
+    monkeypatch.setattr(O, "assign_slots_reroute", repl)
+    with pytest.raises(AssertionError):
+        check()
