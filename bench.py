@@ -193,7 +193,9 @@ def kernel_stage(name: str) -> str:
     if "router" in name:
         return "router"
     if any(t in name for t in ("priority_list", "priority_slot", "permute_slots")):
-        return "priority_dispatch"
+        return "priority_dispatch"          # permute_slots also serves the re-routing dispatch
+    if "reroute_" in name:
+        return "reroute_dispatch"
     if any(t in name for t in ("slot_rank", "slot_scan", "slot_index", "permute_kernel", "tile_map")):
         return "dispatch"
     m = _GEMM_ACT.search(name)
@@ -362,6 +364,8 @@ def main(argv=None):
     ap.add_argument("--backward-calls", type=int, default=20,
                     help="gate-side backward calls (combine + router backward) timed after the steps "
                          "(0 skips them)")
+    ap.add_argument("--reroute-calls", type=int, default=20,
+                    help="re-routing dispatch calls timed after the steps (0 skips them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the "
                          "reference kernel that scales the HBM byte counters), then exit")
@@ -580,6 +584,30 @@ def main(argv=None):
         variants["gate_backward"] = dict(us=round(bw_s * 1e6, 2), bytes=bw["bytes"], flops=bw["flops"],
                                          calls=args.backward_calls, **roofline_of(bw, bw_s))
         del ybuf_b, dyb_b, bws
+    # re-routing of the overflow: the router's top min(4, E) as preferences,
+    # as many stages, the even-split capacity, gates from the logits
+    if args.reroute_calls > 0:
+        R_ = min(4, cfg["E"])
+        idx_r, _, _, _, lg_r = moe.router(x, W_r, k=R_, b_r=b_r, logits=True)
+        C1 = moe.capacity(cfg["T"], cfg["E"], 1, 1.0)
+        rrws = torch.empty(max(L.LIB.moe_dispatch_reroute_workspace_bytes(cfg["T"], cfg["E"]), 256),
+                           dtype=torch.uint8, device=dev)
+        out_r = moe.dispatch_reroute(x, idx_r, cfg["E"], C1, R_, logits=lg_r, workspace=rrws)
+        rr_ev = hip.create(2)
+        hip.record(rr_ev[0], stream.cuda_stream)
+        for _ in range(args.reroute_calls):
+            moe.dispatch_reroute(x, idx_r, cfg["E"], C1, R_, logits=lg_r, workspace=rrws)
+        hip.record(rr_ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        rr_s = hip.elapsed_ms(rr_ev[0], rr_ev[1]) / args.reroute_calls / 1e3
+        hip.destroy(rr_ev)
+        A_r = int(out_r[4].sum().item())
+        s_ = 2 if cfg["dtype"] == "bf16" else 4
+        rw = dict(bytes=2 * A_r * cfg["d"] * s_ + cfg["T"] * (4 * R_ + 4 * cfg["E"] + 13), flops=0,
+                  dtype=cfg["dtype"])
+        variants["reroute_dispatch"] = dict(us=round(rr_s * 1e6, 2), bytes=rw["bytes"], kept=A_r, stages=R_,
+                                            capacity=C1, calls=args.reroute_calls, **roofline_of(rw, rr_s))
+        del rrws, out_r
     stages = {}
     for name in L.STAGES:
         r = roofline_of(work[name], stage_ms[name] / 1e3)

@@ -81,6 +81,7 @@ size_t moe_router_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k);
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
 size_t moe_dispatch_priority_workspace_bytes(int64_t T, int32_t E, int32_t k);
 size_t moe_router_backward_workspace_bytes(int64_t T, int32_t d, int32_t E);
+size_t moe_dispatch_reroute_workspace_bytes(int64_t T, int32_t E);
 size_t moe_expert_ffn_workspace_bytes(int32_t E, int64_t C, int32_t dff, moe_dtype dt);
 size_t moe_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
                            int64_t C, moe_dtype dt, moe_act act);
@@ -199,6 +200,32 @@ moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *exp
                                  const float *priority, int64_t T, int32_t d, int32_t E, int32_t k,
                                  int64_t C, int32_t *slot, uint8_t *drop_mask, int32_t *expert_count,
                                  void *xbuf, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Top-1 dispatch with multi-stage re-routing of the overflow.
+ * [CS25-L5] "“No Token Left Behind”为何没有成功" (a token whose expert is
+ * full is sent to its second, then third choice until it gets a slot; the
+ * page reports that this did not improve the model).  Stage s = 0 ..
+ * stages-1 visits the tokens still without a slot in token order and offers
+ * each its choice pref[t, s]; the experts fill from where the earlier stages
+ * left them, C slots each.  One stage is moe_dispatch with k = 1.
+ *   pref         [T, R]  int32 in, each token's experts in preference order
+ *                        (moe_router's expert_idx with k = R), 1 <= stages <= R
+ *   logits       [T, E]  fp32 in (moe_router's logits output), or NULL
+ *   expert       [T]     int32 out, the expert the token landed on, -1 if dropped
+ *   slot         [T]     int32 out, its slot, -1 if dropped
+ *   drop_mask    [T]     uint8 out
+ *   gate         [T]     fp32 out (NULL exactly when logits is NULL): the
+ *                        full-softmax probability of the landing expert, 0
+ *                        if dropped (the top-1 gate of that expert)
+ *   expert_count [E]     int32 out; xbuf [E, C, d] out as moe_dispatch
+ * expert and slot feed moe_expert_ffn / moe_combine as a k = 1 routing.
+ * ws: moe_dispatch_reroute_workspace_bytes(T, E) bytes.
+ */
+moe_status moe_dispatch_reroute(const void *x, moe_dtype dt, const int32_t *pref, const float *logits, int64_t T,
+                                int32_t d, int32_t E, int32_t R, int32_t stages, int64_t C, int32_t *expert,
+                                int32_t *slot, uint8_t *drop_mask, float *gate, int32_t *expert_count, void *xbuf,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Combine backward: the gradients of moe_combine's y with respect to the

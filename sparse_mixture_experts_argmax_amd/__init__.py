@@ -6,5 +6,5 @@ dispatch, grouped-GEMM expert FFN (ReLU or SwiGLU), gate-scaled combine and
 the auxiliary load-balancing loss.  Entry points mirror include/moe.h.
 """
 from .api import (ForwardPlan, capacity, combine, combine_backward, dispatch, dispatch_priority,  # noqa: F401
-                  expert_ffn, forward, router, router_backward, workspace_bytes)
+                  dispatch_reroute, expert_ffn, forward, router, router_backward, workspace_bytes)
 from ._lib import MoEError, LIB_PATH  # noqa: F401

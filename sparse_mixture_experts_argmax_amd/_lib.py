@@ -43,6 +43,9 @@ SIGNATURES = {
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_dispatch_priority_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_router_backward_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_dispatch_reroute_workspace_bytes": (_sz, [_i64, _i32]),
+    "moe_dispatch_reroute": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _i32, _i64, _p, _p, _p, _p,
+                                       _p, _p, _p, _sz, _p]),
     "moe_combine_backward": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
     "moe_router_backward": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32,
                                       C.c_float, C.c_float, _p, _p, _p, _p, _p, _sz, _p]),

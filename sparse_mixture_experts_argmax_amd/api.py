@@ -153,6 +153,28 @@ def dispatch_priority(x, expert_idx, priority, E: int, C: int, workspace=None):
     return slot, drop, count, xbuf
 
 
+def dispatch_reroute(x, pref, E: int, C: int, stages: int, logits=None, workspace=None):
+    """Top-1 dispatch with re-routing: stage s offers the unplaced tokens their choice pref[:, s].
+    Returns (expert [T], slot [T], drop_mask [T], gate [T] or None, expert_count [E], xbuf)."""
+    T, d = x.shape
+    R = pref.shape[1]
+    dev = x.device
+    expert = torch.empty(T, dtype=torch.int32, device=dev)
+    slot = torch.empty(T, dtype=torch.int32, device=dev)
+    drop = torch.empty(T, dtype=torch.uint8, device=dev)
+    gate = torch.empty(T, dtype=torch.float32, device=dev) if logits is not None else None
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    xbuf = torch.empty((E, C, d), dtype=x.dtype, device=dev)
+    need = L.LIB.moe_dispatch_reroute_workspace_bytes(T, E)
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid dispatch sizes")
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    L.check("moe_dispatch_reroute", L.LIB.moe_dispatch_reroute(
+        _ptr(x), _dtype_code(x), _ptr(pref), _ptr(logits), T, d, E, R, stages, C, _ptr(expert), _ptr(slot),
+        _ptr(drop), _ptr(gate), _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
+    return expert, slot, drop, gate, count, xbuf
+
+
 def combine_backward(dy, ybuf, expert_idx, slot, gate, dybuf=None):
     """Combine backward: returns (dgate [T,k] fp32, dybuf [E,C,d]; kept rows written)."""
     E, C, d = ybuf.shape

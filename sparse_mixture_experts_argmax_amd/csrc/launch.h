@@ -97,6 +97,19 @@ hipError_t launch_router_backward(const void *x, int dtype_bf16, const float *W_
                                   const int32_t *route_count, int64_t T, int d, int E, int k, float alpha,
                                   float z_weight, float *dz, float *dW, float *db, float *dx, float *part_w,
                                   float *part_b, hipStream_t s);
+// xbuf[expert_idx[a], slot[a]] = x[a / k] for every choice a with slot >= 0.
+hipError_t launch_permute_slots(const void *x, int elem_bytes, const int32_t *expert_idx, const int32_t *slot,
+                                int64_t T, int d, int k, int64_t C, void *xbuf, hipStream_t s);
+// Top-1 dispatch with re-routing (reroute.hip): stage s offers the tokens
+// still without a slot their choice pref[t, s] (pref [T, R]), stages <= R;
+// expert [T] and slot [T] (-1 if dropped), drop_mask [T], gate [T] (the
+// full-softmax probability of the landing expert from logits [T, E]; both
+// may be null), expert_count [E] and the kept rows in xbuf.  rank [T], hist
+// [E dispatch_blocks(T)], cand [T], n_e [E] and fill [E] are scratch.
+hipError_t launch_reroute(const void *x, int elem_bytes, const int32_t *pref, const float *logits, int64_t T,
+                          int d, int E, int R, int stages, int64_t C, int32_t *expert, int32_t *slot,
+                          uint8_t *drop_mask, float *gate, int32_t *expert_count, void *xbuf, int32_t *rank,
+                          int32_t *hist, int32_t *cand, int32_t *n_e, int32_t *fill, hipStream_t s);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,

@@ -405,6 +405,53 @@ moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, 
     return MOE_OK;
 }
 
+// rank [T], hist, done (the plain dispatch's scratch for one rank), then
+// cand [T], n_e [E], fill [E].
+struct RerouteWs {
+    DispatchWs d;
+    size_t cand, cnt, fill, total;
+};
+RerouteWs reroute_ws(int64_t T, int E) {
+    RerouteWs w;
+    w.d = dispatch_ws(T, E, 1);
+    w.cand = w.d.total;
+    w.cnt = w.cand + up((size_t)T * 4);
+    w.fill = w.cnt + up((size_t)E * 4);
+    w.total = w.fill + up((size_t)E * 4);
+    return w;
+}
+
+size_t moe_dispatch_reroute_workspace_bytes(int64_t T, int32_t E) {
+    if (check_sizes(T, E, 1) != MOE_OK) return SIZE_MAX;
+    return reroute_ws(T, E).total;
+}
+
+moe_status moe_dispatch_reroute(const void *x, moe_dtype dt, const int32_t *pref, const float *logits, int64_t T,
+                                int32_t d, int32_t E, int32_t R, int32_t stages, int64_t C, int32_t *expert,
+                                int32_t *slot, uint8_t *drop_mask, float *gate, int32_t *expert_count, void *xbuf,
+                                void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, R));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    if (C < 0 || C > T || stages < 1 || stages > R) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr4_ok(pref, empty) || !ptr4_ok(expert, empty) || !ptr4_ok(slot, empty) ||
+        (drop_mask == nullptr && !empty) || !ptr4_ok(expert_count, false) || !ptr_ok(xbuf, C == 0) ||
+        ((logits == nullptr) != (gate == nullptr)) || !(logits == nullptr || ptr4_ok(logits, empty)) ||
+        !(gate == nullptr || ptr4_ok(gate, empty)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const RerouteWs w = reroute_ws(T, E);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    char *base = static_cast<char *>(ws);
+    MOE_HIP(moe::launch_reroute(x, (int)esize(dt), pref, logits, T, d, E, R, stages, C, expert, slot, drop_mask,
+                                gate, expert_count, xbuf, reinterpret_cast<int32_t *>(base + w.d.rank),
+                                reinterpret_cast<int32_t *>(base + w.d.hist),
+                                reinterpret_cast<int32_t *>(base + w.cand), reinterpret_cast<int32_t *>(base + w.cnt),
+                                reinterpret_cast<int32_t *>(base + w.fill), stream));
+    return MOE_OK;
+}
+
 size_t moe_router_backward_workspace_bytes(int64_t T, int32_t d, int32_t E) {
     if (check_sizes(T, E, 1) != MOE_OK || check_width(d) != MOE_OK) return SIZE_MAX;
     const size_t nc = (size_t)moe::router_bwd_chunks(T);

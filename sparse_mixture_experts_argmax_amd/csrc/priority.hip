@@ -216,6 +216,18 @@ __global__ __launch_bounds__(256) void permute_slots_kernel(const uint8_t *__res
 
 }  // namespace
 
+hipError_t launch_permute_slots(const void *x, int elem_bytes, const int32_t *expert_idx, const int32_t *slot,
+                                int64_t T, int d, int k, int64_t C, void *xbuf, hipStream_t s) {
+    const int64_t n = T * k;
+    if (n == 0 || C == 0) return hipSuccess;
+    int64_t blocks = (n + 3) / 4;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(permute_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint8_t *>(x), d * elem_bytes, expert_idx, slot, T, k, C,
+                       reinterpret_cast<uint8_t *>(xbuf));
+    return hipGetLastError();
+}
+
 hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *expert_idx,
                                  const float *priority, const int32_t *rank, const int32_t *base,
                                  const int32_t *n_e, int64_t T, int d, int E, int k, int64_t C,

@@ -119,6 +119,24 @@ def test_router_rejects(case, expect):
 
 @_no_gpu
 @pytest.mark.parametrize("case,expect", [
+    (dict(stages=0), L.MOE_ERR_INVALID_ARGUMENT),
+    (dict(stages=4), L.MOE_ERR_INVALID_ARGUMENT),              # more stages than preferences
+    (dict(lg=None), L.MOE_ERR_INVALID_ARGUMENT),               # gate without logits
+    (dict(R=9), L.MOE_ERR_UNSUPPORTED),
+    (dict(ws_bytes=0), L.MOE_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_reroute_dispatch_rejects(case, expect):
+    a = dict(x=P, dt=L.MOE_BF16, pref=P, lg=P, T=64, d=64, E=16, R=3, stages=3, C=16, ex=P, sl=P, dr=P, g=P,
+             cnt=P, xbuf=P, ws=P, ws_bytes=1 << 30)
+    a.update(case)
+    st = L.LIB.moe_dispatch_reroute(a["x"], a["dt"], a["pref"], a["lg"], a["T"], a["d"], a["E"], a["R"],
+                                    a["stages"], a["C"], a["ex"], a["sl"], a["dr"], a["g"], a["cnt"], a["xbuf"],
+                                    a["ws"], a["ws_bytes"], None)
+    assert st == expect
+
+
+@_no_gpu
+@pytest.mark.parametrize("case,expect", [
     (dict(pr=None), L.MOE_ERR_INVALID_ARGUMENT),               # no scores
     (dict(pr=P + 2), L.MOE_ERR_INVALID_ARGUMENT),              # misaligned scores
     (dict(C=65), L.MOE_ERR_INVALID_ARGUMENT),                  # C > T

@@ -1,0 +1,115 @@
+"""Multi-stage re-routing on the GPU (moe_dispatch_reroute), through the C ABI.
+
+[CS25-L5] "No Token Left Behind": stage s offers the tokens still without a
+slot their choice of rank s, in token order, filling the experts from where
+the earlier stages left them.  Checked bit for bit against the oracle's
+assign_slots_reroute (landing expert, slot, drop flag, counts, and every
+kept row of xbuf); the gate against the full softmax of the logits at the
+landing expert (relative 1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import sparse_mixture_experts_argmax_amd as moe
+from oracle import moe as O
+from gpu_util import check_y, device_inputs, host_bits, host_f64, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x_t, pref, E, C, stages, z=None):
+    gp = torch.from_numpy(np.ascontiguousarray(pref, dtype=np.int32)).cuda()
+    gz = None if z is None else torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).cuda()
+    ex, sl, dr, g, cnt, xbuf = moe.dispatch_reroute(x_t, gp, E, C, stages, logits=gz)
+    torch.cuda.synchronize()
+    rex, rsl, rst, rc = O.assign_slots_reroute(pref, E, C, stages)
+    assert np.array_equal(ex.cpu().numpy(), rex) and np.array_equal(sl.cpu().numpy(), rsl)
+    assert np.array_equal(dr.cpu().numpy(), (rex < 0).astype(np.uint8))
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    T = pref.shape[0]
+    if T and C:
+        kept = rex >= 0
+        assert np.array_equal(host_bits(xbuf)[rex[kept], rsl[kept]], host_bits(x_t)[kept])
+    if z is not None and T:
+        p = O.softmax(z)
+        ref = np.where(rex >= 0, p[np.arange(T), np.maximum(rex, 0)], 0.0)
+        np.testing.assert_allclose(g.cpu().numpy(), ref, rtol=1e-5, atol=1e-7)
+    return ex, sl, g
+
+
+def _x(T, d=64):
+    cfg = datagen.random_case(seed=3, T=max(T, 1), d=d, f=8, E=2, k=1, cf=1.0, dtype="bf16")
+    return dev(cfg["x"][:T], "bf16")
+
+
+@pytest.mark.parametrize("T,E,R,stages,cf,skew", [
+    (1000, 8, 3, 3, 1.0, 2.0),
+    (1000, 8, 4, 2, 0.5, 0.0),
+    (2000, 6, 6, 6, 1.0, 3.0),          # all experts: nobody dropped
+    (700, 300, 2, 2, 1.0, 0.0),
+    (3000, 4, 4, 4, 0.3, 8.0),          # most tokens prefer expert 0
+])
+def test_reroute_matches_oracle(T, E, R, stages, cf, skew):
+    rng = np.random.default_rng(T + E)
+    z = (rng.standard_normal((T, E)) + skew * np.linspace(1, 0, E)[None, :]).astype(np.float32)
+    pref = np.argsort(-z, axis=1, kind="stable")[:, :R].astype(np.int32)
+    C = O.capacity(T, E, 1, cf)
+    print(f"re-routing: T={T} E={E} R={R} stages={stages} C={C}", flush=True)
+    ex, *_ = _check(_x(T), pref, E, C, stages, z)
+    if stages == E and C * E >= T:
+        assert (ex.cpu().numpy() >= 0).all()
+
+
+def test_one_stage_is_the_plain_dispatch():
+    rng = np.random.default_rng(1)
+    T, E = 900, 5
+    pref = np.argsort(-rng.standard_normal((T, E)), axis=1, kind="stable")[:, :2].astype(np.int32)
+    x = _x(T)
+    ex, sl, _ = _check(x, pref, E, 150, 1)
+    slot, drop, cnt, _ = moe.dispatch(x, torch.from_numpy(pref[:, :1].copy()).cuda(), E, 150)
+    torch.cuda.synchronize()
+    assert np.array_equal(sl.cpu().numpy(), slot.cpu().numpy()[:, 0])
+
+
+@pytest.mark.parametrize("T,C", [(0, 0), (1, 1), (64, 0)])
+def test_reroute_degenerate(T, C):
+    pref = np.tile(np.array([[1, 0, 2]], np.int32), (T, 1))
+    print(f"re-routing degenerate: T={T} C={C}", flush=True)
+    _check(_x(T, 32), pref, 3, C, 3)
+
+
+def test_reroute_switch_base():
+    """Full size: the GPU router's top-4 as preferences, its logits for the gates,
+    the even-split capacity, four stages."""
+    cfg = datagen.make("switch_base", seed=0, with_experts=False)
+    t = device_inputs(cfg)
+    idx, gate, ps, rc, lg = moe.router(t["x"], t["W_r"], k=4, logits=True)
+    torch.cuda.synchronize()
+    C = O.capacity(cfg["T"], cfg["E"], 1, 1.0)
+    print(f"re-routing: switch_base C={C}", flush=True)
+    _check(t["x"], idx.cpu().numpy(), cfg["E"], C, 4, lg.cpu().numpy())
+
+
+def test_reroute_layer_end_to_end():
+    """router (top-3 and logits) -> re-routing -> expert FFN -> combine: every
+    token's y against the oracle's experts at its landing expert and gate."""
+    cfg = datagen.random_case(seed=81, T=600, d=48, f=64, E=6, k=1, cf=0.8, dtype="bf16", logit_scale=3.0)
+    t = device_inputs(cfg)
+    idx, gate, ps, rc, lg = moe.router(t["x"], t["W_r"], k=3, logits=True)
+    C = moe.capacity(cfg["T"], cfg["E"], 1, cfg["cf"])
+    ex, sl, dr, g, cnt, xbuf = moe.dispatch_reroute(t["x"], idx, cfg["E"], C, 3, logits=lg)
+    ybuf = moe.expert_ffn(xbuf, cnt, t["W1"], t["W2"], act="relu")
+    y, aux = moe.combine(ybuf, ex.view(-1, 1), sl.view(-1, 1), g.view(-1, 1), ps, rc, cfg["T"])
+    torch.cuda.synchronize()
+    x64 = O.widen(cfg["x"], "bf16")
+    e_np, g_np = ex.cpu().numpy(), g.cpu().numpy().astype(np.float64)
+    ref = np.zeros((cfg["T"], cfg["d"]))
+    for e in range(cfg["E"]):
+        tt = np.nonzero(e_np == e)[0]
+        if tt.size:
+            o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], "bf16"), O.widen(cfg["W2"][e], "bf16"), "relu")
+            ref[tt] = g_np[tt, None] * o
+    assert np.any((e_np >= 0) & (e_np != idx.cpu().numpy()[:, 0]))   # some tokens were re-routed
+    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16")
