@@ -337,6 +337,20 @@ moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const floa
  * NULL array or NULL entries -> MOE_ERR_INVALID_ARGUMENT, nothing enqueued.
  */
 #define MOE_STAGE_EVENTS 6
+/*
+ * moe_forward with the noisy top-k router of moe_router_noisy: the logits
+ * H = W_r x (+ b_r) + noise * softplus(W_noise x) drive the routing, the
+ * gates, the loss and z_loss ([CMU-L16] section 2.3).  W_noise [E, d] fp32
+ * (16-byte aligned), noise [T, E] fp32 standard normal draws; everything
+ * else, the workspace included, as moe_forward.
+ */
+moe_status moe_forward_noisy(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                             const float *W_noise, const float *noise, const void *W1, const void *b1,
+                             const void *W3, const void *W2, const void *b2, moe_act act, int64_t T, int32_t d,
+                             int32_t dff, int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
+                             float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
+                             uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream);
+
 moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                               const void *W1, const void *b1, const void *W3, const void *W2,
                               const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff,

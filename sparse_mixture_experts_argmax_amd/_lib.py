@@ -68,6 +68,9 @@ SIGNATURES = {
     "moe_forward": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _p, C.c_int, _i64, _i32, _i32,
                               _i32, _i32, C.c_double, C.c_float, _p, _p, _p, _p, _p, _p, _p, _sz,
                               _p]),
+    "moe_forward_noisy": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _p, _p, _p, C.c_int, _i64, _i32,
+                                    _i32, _i32, _i32, C.c_double, C.c_float, _p, _p, _p, _p, _p, _p, _p,
+                                    _sz, _p]),
     "moe_forward_staged": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _p, C.c_int, _i64, _i32,
                                      _i32, _i32, _i32, C.c_double, C.c_float, _p, _p, _p, _p, _p, _p,
                                      _p, _sz, _p, _p]),

@@ -275,12 +275,25 @@ class ForwardPlan:
             _ACT[act], lay))
         self.layout = lay
 
-    def __call__(self, x, W_r, W1, W2, *, W3=None, b1=None, b2=None, b_r=None, stream=None):
+    def __call__(self, x, W_r, W1, W2, *, W3=None, b1=None, b2=None, b_r=None, stream=None, W_noise=None,
+                 noise=None):
+        """With W_noise [E, d] and noise [T, E] (fp32) the router is the noisy top-k one."""
         if tuple(x.shape) != (self.T, self.d) or x.dtype != self.dtype:
             raise ValueError("x does not match the plan")
         _same(self.dtype, W1, W2, W3, b1, b2)
-        _same(torch.float32, W_r, b_r)
+        _same(torch.float32, W_r, b_r, W_noise, noise)
         s = stream.cuda_stream if stream is not None else _stream(self.device)
+        if (W_noise is None) != (noise is None):
+            raise ValueError("the noisy router needs both W_noise and noise")
+        if W_noise is not None:
+            if tuple(noise.shape) != (self.T, self.E):
+                raise ValueError("noise must be [T, E]")
+            L.check("moe_forward_noisy", L.LIB.moe_forward_noisy(
+                _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W_noise), _ptr(noise), _ptr(W1), _ptr(b1),
+                _ptr(W3), _ptr(W2), _ptr(b2), _ACT[self.act], self.T, self.d, self.dff, self.E, self.k,
+                self.capacity_factor, self.alpha, _ptr(self.y), _ptr(self.aux), _ptr(self.z_loss),
+                _ptr(self.expert_idx), _ptr(self.gate), _ptr(self.drop_mask), _ptr(self.ws), self.ws.numel(), s))
+            return self.y, self.aux, self.expert_idx, self.gate, self.drop_mask
         L.check("moe_forward", L.LIB.moe_forward(
             _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
             _ptr(b2), _ACT[self.act], self.T, self.d, self.dff, self.E, self.k,

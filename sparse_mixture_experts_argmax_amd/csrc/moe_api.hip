@@ -154,18 +154,24 @@ moe_status check_ffn_args(moe_dtype dt, moe_act act, const void *W1, const void 
 moe_status run_router(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                       int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
                       float *gate, float *prob_sum, int32_t *route_count, float *z_loss, char *ws,
-                      hipStream_t stream, bool reduce = true, float *logits = nullptr) {
+                      hipStream_t stream, bool reduce = true, float *logits = nullptr,
+                      const float *W_noise = nullptr, const float *noise = nullptr) {
     const RouterWs w = router_ws(T, d, E);
     float *part_prob = reinterpret_cast<float *>(ws + w.part_prob);
     int32_t *part_cnt = reinterpret_cast<int32_t *>(ws + w.part_cnt);
     float *part_z = reinterpret_cast<float *>(ws + w.part_z);
     uint16_t *w3 = reinterpret_cast<uint16_t *>(ws + w.w3);
     const int bf16 = dt == MOE_BF16;
-    MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
-                               part_cnt, w3, stream, part_z, logits));
+    if (W_noise != nullptr)
+        MOE_HIP(moe::launch_router_noisy(x, bf16, W_r, b_r, W_noise, noise, T, d, E, k, expert_idx, gate,
+                                         part_prob, part_cnt, part_z, w3, stream));
+    else
+        MOE_HIP(moe::launch_router(x, bf16, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,
+                                   part_cnt, w3, stream, part_z, logits));
+    const int nblk = W_noise != nullptr ? moe::router_noisy_blocks(T, bf16, E) : moe::router_blocks(T, bf16, E);
     if (reduce)
-        MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, moe::router_blocks(T, bf16, E), E,
-                                          prob_sum, route_count, stream, part_z, T, z_loss));
+        MOE_HIP(moe::launch_router_reduce(part_prob, part_cnt, nblk, E, prob_sum, route_count, stream, part_z, T,
+                                          z_loss));
     return MOE_OK;
 }
 
@@ -528,7 +534,8 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
                         const void *b2, moe_act act, int64_t T, int32_t d, int32_t dff, int32_t E,
                         int32_t k, double capacity_factor, float alpha, void *y, float *aux_loss,
                         float *z_loss, int32_t *expert_idx, float *gate, uint8_t *drop_mask,
-                        void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *ev) {
+                        void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *ev,
+                        const float *W_noise = nullptr, const float *noise = nullptr) {
     MOE_CHECK(check_sizes(T, E, k));
     MOE_CHECK(check_width(d));
     MOE_CHECK(check_width(dff));
@@ -539,7 +546,8 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     const bool empty = T == 0;
     if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr_ok(y, empty) ||
         !ptr4_ok(aux_loss, false) || !(z_loss == nullptr || ptr4_ok(z_loss, false)) || !ptr4_ok(expert_idx, empty) ||
-        !ptr4_ok(gate, empty) || (drop_mask == nullptr && !empty))
+        !ptr4_ok(gate, empty) || (drop_mask == nullptr && !empty) ||
+        (W_noise != nullptr && (!ptr_ok(W_noise, false) || !ptr4_ok(noise, empty))))
         return MOE_ERR_INVALID_ARGUMENT;
     if (ev != nullptr) {
         for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
@@ -576,13 +584,14 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     int32_t *row_tok = gather ? reinterpret_cast<int32_t *>(base + w.row_tok) : nullptr;
     float *row_gate = scatter ? reinterpret_cast<float *>(base + w.row_gate) : nullptr;
     MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count,
-                         z_loss, base + w.router, stream, !fuse_reduce));
+                         z_loss, base + w.router, stream, !fuse_reduce, nullptr, W_noise, noise));
+    const int nblk_r = W_noise != nullptr ? moe::router_noisy_blocks(T, bf16, E) : moe::router_blocks(T, bf16, E);
     if (!mark(1)) return MOE_ERR_HIP;
     MOE_CHECK(run_dispatch(x, dt, expert_idx, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
                            base + w.dispatch, stream,
                            fuse_reduce ? reinterpret_cast<const float *>(base + w.router + w.r.part_prob)
                                        : nullptr,
-                           moe::router_blocks(T, bf16, E), prob_sum, route_count,
+                           nblk_r, prob_sum, route_count,
                            T > 0 && C > 0 ? tile_map : nullptr, bm, row_tok, scatter ? y : nullptr,
                            alpha, scatter ? aux_loss : nullptr, gate, row_gate,
                            fuse_reduce ? reinterpret_cast<const float *>(base + w.router + w.r.part_z)
@@ -618,6 +627,18 @@ moe_status moe_forward(const void *x, moe_dtype dt, const float *W_r, const floa
     return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k,
                         capacity_factor, alpha, y, aux_loss, z_loss, expert_idx, gate, drop_mask, ws,
                         ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_noisy(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                             const float *W_noise, const float *noise, const void *W1, const void *b1,
+                             const void *W3, const void *W2, const void *b2, moe_act act, int64_t T, int32_t d,
+                             int32_t dff, int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
+                             float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
+                             uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (W_noise == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k, capacity_factor, alpha, y,
+                        aux_loss, z_loss, expert_idx, gate, drop_mask, ws, ws_bytes, stream, nullptr, W_noise,
+                        noise);
 }
 
 moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, const float *b_r,

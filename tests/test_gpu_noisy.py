@@ -123,3 +123,36 @@ def test_noisy_router_feeds_the_layer():
             o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], "bf16"), O.widen(cfg["W2"][e], "bf16"), cfg["act"])
             ref[tt] += g[tt, jj][:, None] * o
     check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16")
+
+
+@pytest.mark.parametrize("k,dt", [(1, "bf16"), (2, "bf16"), (1, "f32")])
+def test_fused_forward_with_noise(k, dt):
+    """moe_forward_noisy: the fused layer on the noisy logits; routing, totals
+    and z-loss against the oracle's noisy logits, then slots, aux and every
+    token's y against the oracle's experts on the GPU's choices and gates."""
+    cfg = datagen.random_case(seed=91, T=700, d=64, f=96, E=8, k=k, cf=1.0, dtype=dt, logit_scale=2.0)
+    W_n, eps = _noise_inputs(cfg, 19, scale=2.0)
+    t = device_inputs(cfg)
+    print(f"fused forward with noise: k={k} {dt}", flush=True)
+    plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], k, t["x"].dtype, act=cfg["act"],
+                           capacity_factor=cfg["cf"], alpha=cfg["alpha"], device=t["x"].device)
+    y, aux, idx, gate, drop = plan(t["x"], t["W_r"], t["W1"], t["W2"], W_noise=dev(W_n, "f32"),
+                                   noise=dev(eps, "f32"))
+    torch.cuda.synchronize()
+    gi, _ = _checks(cfg, W_n, eps, idx, gate, plan.intermediate("prob_sum"), plan.intermediate("route_count"),
+                    plan.z_loss)
+    C = moe.capacity(cfg["T"], cfg["E"], k, cfg["cf"])
+    rs, rd, _ = O.assign_slots(gi, cfg["E"], C)
+    assert np.array_equal(drop.cpu().numpy(), rd)
+    x64 = O.widen(cfg["x"], dt)
+    H = O.noisy_router_logits(x64, cfg["W_r"], cfg["b_r"], W_n, eps)
+    ref_aux = O.aux_loss(O.softmax(H), gi, cfg["E"], cfg["alpha"])
+    assert abs(float(aux.cpu()[0]) - ref_aux) <= 1e-5 * abs(ref_aux)
+    g = gate.cpu().numpy().astype(np.float64)
+    ref = np.zeros((cfg["T"], cfg["d"]))
+    for e in range(cfg["E"]):
+        tt, jj = np.nonzero((gi == e) & (rd == 0))
+        if tt.size:
+            o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], dt), O.widen(cfg["W2"][e], dt), cfg["act"])
+            ref[tt] += g[tt, jj][:, None] * o
+    check_y(host_f64(y), ref, np.arange(cfg["T"]), dt)
