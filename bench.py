@@ -246,8 +246,9 @@ def summarize(prof_dir: str, workload: str) -> str:
     f_scale = kib / _copy_kib(os.path.join(prof_dir, "copy_fetch"), "FETCH_SIZE")
     w_scale = kib / _copy_kib(os.path.join(prof_dir, "copy_write"), "WRITE_SIZE")
     lines = [f"# Kernel times and HBM traffic, workload {workload}", "",
-             "Made by (REPO = the repository root, on an MI355X):", "", "```"]
-    lines += [c.format(w=workload, o="$REPO/gpurun_out/prof_" + workload) for c in PROFILE_COMMANDS]
+             "Made by (REPO = the repository root, OUT = a directory for the raw rocprofv3 output, "
+             "on an MI355X):", "", "```"]
+    lines += [c.format(w=workload, o="$OUT/prof_" + workload) for c in PROFILE_COMMANDS]
     lines += ["```", "", "## rocprofv3 --kernel-trace --stats", "",
               "| kernel | stage | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
     for r in krows:

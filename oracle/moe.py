@@ -47,7 +47,7 @@ def router_logits(x64: np.ndarray, W_r: np.ndarray, b_r: np.ndarray | None = Non
     [CS25-L5] "稳定训练" (selective precision) and [SW-RES] section 2.1: the
     router is computed in float32.  The dot products are accumulated in
     float64 and rounded once to fp32, so this is the correctly rounded fp32
-    logit.  The optional per-expert bias b_r is this build's reading for the
+    logit.  The optional per-expert bias b_r is the reading taken here for the
     skewed workload (an additive popularity offset inside the fp32 logit).
     """
     z = x64 @ np.asarray(W_r, dtype=np.float64).T
