@@ -107,6 +107,7 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
     uint8_t *__restrict__ drop, int32_t *__restrict__ expert_count) {
     __shared__ __attribute__((aligned(16))) uint64_t s_key[PR_BLOCK];
     __shared__ int s_lo, s_hi;
+    __shared__ int32_t s_off[1024];                  // the list offsets, searched in LDS
     const int tid = threadIdx.x;
     if (blockIdx.x == 0)
         for (int e = tid; e < E; e += PR_BLOCK) {
@@ -116,6 +117,8 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
     const int V = off[E - 1] + n_e[E - 1];           // entries in all lists
     const int p0 = blockIdx.x * PR_BLOCK;
     if (p0 >= V) return;                             // the whole block
+    for (int e = tid; e < E; e += PR_BLOCK) s_off[e] = off[e];
+    __syncthreads();
     const int p = p0 + tid;
     const bool ok = p < V;
     // the expert holding entry p: the largest e with off[e] <= p
@@ -124,12 +127,12 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
         int lo_e = 0, hi_e = E - 1;
         while (lo_e < hi_e) {
             const int mid = (lo_e + hi_e + 1) >> 1;
-            if (off[mid] <= p) lo_e = mid;
+            if (s_off[mid] <= p) lo_e = mid;
             else hi_e = mid - 1;
         }
         e = lo_e;
     }
-    const int oe = ok ? off[e] : 0;
+    const int oe = ok ? s_off[e] : 0;
     const int pl = p - oe;                           // position in the expert's list
     // this entry's rank segment [lo, hi) of the expert's list
     const int32_t *b = base + (int64_t)e * k * nblk;
