@@ -194,7 +194,9 @@ moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx,
  * Other arguments as moe_dispatch; the workspace is
  * moe_dispatch_priority_workspace_bytes(T, E, k) bytes (8 T k + small).
  * E <= 1024.  Cost: about n_e^2 / 2 key compares per expert (n_e its
- * choices before capacity), at most T^2 / 2 when all tokens pick one expert.
+ * choices before capacity), at most (T k)^2 / 2 when all choices go to one
+ * expert; T k is limited to 2^20 (MOE_ERR_UNSUPPORTED above it), which keeps
+ * that worst case well under a second.
  */
 moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *expert_idx,
                                  const float *priority, int64_t T, int32_t d, int32_t E, int32_t k,
@@ -210,7 +212,10 @@ moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *exp
  * each its choice pref[t, s]; the experts fill from where the earlier stages
  * left them, C slots each.  One stage is moe_dispatch with k = 1.
  *   pref         [T, R]  int32 in, each token's experts in preference order
- *                        (moe_router's expert_idx with k = R), 1 <= stages <= R
+ *                        (moe_router's expert_idx with k = R), 1 <= stages <= R;
+ *                        an entry outside [0, E) is no choice: the token stays
+ *                        unplaced at that stage and is offered its next entry
+ *                        at the next one (a shorter list, padded with -1)
  *   logits       [T, E]  fp32 in (moe_router's logits output), or NULL
  *   expert       [T]     int32 out, the expert the token landed on, -1 if dropped
  *   slot         [T]     int32 out, its slot, -1 if dropped

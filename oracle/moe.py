@@ -290,9 +290,12 @@ def assign_slots_reroute(pref: np.ndarray, E: int, C: int, stages: int):
     is dropped.  Stage 0 alone is assign_slots with k = 1.
 
     pref [T, R] int: each token's experts in preference order (the router's
-    top-R), stages <= R.  Returns expert [T] (the expert the token landed
-    on, -1 if dropped), slot [T] (-1 if dropped), stage [T] (-1 if dropped)
-    and expert_count [E].
+    top-R), stages <= R.  The page only speaks of real choices; an entry
+    outside [0, E) is read as no choice at that stage (a list shorter than
+    R, padded): the token stays unplaced there and is offered its next
+    entry at the next stage.  Returns expert [T] (the expert the token
+    landed on, -1 if dropped), slot [T] (-1 if dropped), stage [T] (-1 if
+    dropped) and expert_count [E].
     """
     T = pref.shape[0]
     fill = [0] * E
@@ -305,7 +308,7 @@ def assign_slots_reroute(pref: np.ndarray, E: int, C: int, stages: int):
             if stage[t] >= 0:
                 continue
             e = pl[t][s]
-            if fill[e] < C:
+            if 0 <= e < E and fill[e] < C:
                 expert[t], slot[t], stage[t] = e, fill[e], s
                 fill[e] += 1
     return expert, slot, stage, np.asarray(fill, dtype=np.int64)

@@ -46,6 +46,46 @@ def _same(dtype, *ts):
             raise TypeError(f"expected {dtype}, got {t.dtype}")
 
 
+def _expect(t, name: str, shape: tuple, dtype=None, optional: bool = False):
+    """Checks a tensor argument against its layout before anything reaches the
+    library: the C ABI receives only sizes, so a tensor of the wrong shape or
+    element type would be read past its end or misread."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _tokens(x, name: str = "x"):
+    """x [T, d] in bfloat16 or float32."""
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be [T, d], got {list(x.shape)}")
+    _dtype_code(x)
+    return x.shape
+
+
+def _routing(expert_idx, T: int, name: str = "expert_idx"):
+    """[T, k] int32 routing tensor; returns k."""
+    if expert_idx.dim() != 2 or expert_idx.shape[0] != T:
+        raise ValueError(f"{name} must be [T={T}, k], got {list(expert_idx.shape)}")
+    if expert_idx.dtype != torch.int32:
+        raise TypeError(f"{name} must be torch.int32, got {expert_idx.dtype}")
+    return expert_idx.shape[1]
+
+
+def _experts(E: int, d: int, dff: int, dtype, W1, W2, W3=None, b1=None, b2=None):
+    """Expert weights in the layout [E, dff, d] / [E, d, dff] of the storage dtype."""
+    _expect(W1, "W1", (E, dff, d), dtype)
+    _expect(W2, "W2", (E, d, dff), dtype)
+    _expect(W3, "W3", (E, dff, d), dtype, optional=True)
+    _expect(b1, "b1", (E, dff), dtype, optional=True)
+    _expect(b2, "b2", (E, d), dtype, optional=True)
+
+
 def capacity(T: int, E: int, k: int, capacity_factor: float) -> int:
     """C = ceil(capacity_factor * k * T / E), at most T (host arithmetic in the library)."""
     c = L.LIB.moe_capacity(T, E, k, capacity_factor)
@@ -66,6 +106,15 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
 
 
+def _ws(workspace, nbytes: int, dev) -> torch.Tensor:
+    """The caller's workspace (a uint8 tensor: its numel is its size in bytes) or a new one."""
+    if workspace is None:
+        return _workspace(nbytes, dev)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D torch.uint8 tensor")
+    return workspace
+
+
 def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W_noise=None,
            noise=None, logits: bool = False):
     """Router: returns (expert_idx [T,k] int32, gate [T,k] fp32, prob_sum [E] fp32, route_count [E] int32),
@@ -73,14 +122,19 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W
     log-sum-exp of the logits).  With W_noise [E,d] fp32 and noise [T,E] fp32 (standard normal
     draws) the noisy top-k router: the logits become W_r x + noise * softplus(W_noise x).
     With logits=True (plain router) the fp32 logits [T, E] are returned last."""
-    T, d = x.shape
+    T, d = _tokens(x)
+    if W_r.dim() != 2:
+        raise ValueError(f"W_r must be [E, d], got {list(W_r.shape)}")
     E = W_r.shape[0]
     dev = x.device
-    _same(torch.float32, W_r, b_r, W_noise, noise)
+    _expect(W_r, "W_r", (E, d), torch.float32)
+    _expect(b_r, "b_r", (E,), torch.float32, optional=True)
     if (W_noise is None) != (noise is None):
         raise ValueError("the noisy router needs both W_noise and noise")
-    if noise is not None and tuple(noise.shape) != (T, E):
-        raise ValueError("noise must be [T, E]")
+    _expect(W_noise, "W_noise", (E, d), torch.float32, optional=True)
+    _expect(noise, "noise", (T, E), torch.float32, optional=True)
+    if not 1 <= k <= E:
+        raise ValueError(f"k must be in [1, E={E}], got {k}")
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
@@ -92,7 +146,7 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W
     need = L.LIB.moe_router_workspace_bytes(T, d, E, k)
     if need == L.SIZE_MAX:
         raise ValueError("invalid router sizes")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = _ws(workspace, need, dev)
     if W_noise is None:
         L.check("moe_router", L.LIB.moe_router(
             _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
@@ -112,8 +166,8 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W
 
 def dispatch(x, expert_idx, E: int, C: int, workspace=None):
     """Dispatch: returns (slot [T,k] int32, drop_mask [T,k] uint8, expert_count [E] int32, xbuf [E,C,d])."""
-    T, d = x.shape
-    k = expert_idx.shape[1]
+    T, d = _tokens(x)
+    k = _routing(expert_idx, T)
     dev = x.device
     slot = torch.empty((T, k), dtype=torch.int32, device=dev)
     drop = torch.empty((T, k), dtype=torch.uint8, device=dev)
@@ -122,7 +176,7 @@ def dispatch(x, expert_idx, E: int, C: int, workspace=None):
     need = L.LIB.moe_dispatch_workspace_bytes(T, E, k)
     if need == L.SIZE_MAX:
         raise ValueError("invalid dispatch sizes")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = _ws(workspace, need, dev)
     L.check("moe_dispatch", L.LIB.moe_dispatch(
         _ptr(x), _dtype_code(x), _ptr(expert_idx), T, d, E, k, C, _ptr(slot), _ptr(drop),
         _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
@@ -133,12 +187,10 @@ def dispatch_priority(x, expert_idx, priority, E: int, C: int, workspace=None):
     """Priority dispatch: as dispatch, with the capacity filled in descending
     priority [T] fp32 (ties: lower token index; NaN last), rank-major.
     Returns (slot, drop_mask, expert_count, xbuf)."""
-    T, d = x.shape
-    k = expert_idx.shape[1]
+    T, d = _tokens(x)
+    k = _routing(expert_idx, T)
     dev = x.device
-    _same(torch.float32, priority)
-    if tuple(priority.shape) != (T,):
-        raise ValueError("priority must be [T]")
+    _expect(priority, "priority", (T,), torch.float32)
     slot = torch.empty((T, k), dtype=torch.int32, device=dev)
     drop = torch.empty((T, k), dtype=torch.uint8, device=dev)
     count = torch.empty(E, dtype=torch.int32, device=dev)
@@ -146,7 +198,7 @@ def dispatch_priority(x, expert_idx, priority, E: int, C: int, workspace=None):
     need = L.LIB.moe_dispatch_priority_workspace_bytes(T, E, k)
     if need == L.SIZE_MAX:
         raise ValueError("invalid dispatch sizes")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = _ws(workspace, need, dev)
     L.check("moe_dispatch_priority", L.LIB.moe_dispatch_priority(
         _ptr(x), _dtype_code(x), _ptr(expert_idx), _ptr(priority), T, d, E, k, C, _ptr(slot), _ptr(drop),
         _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
@@ -156,9 +208,12 @@ def dispatch_priority(x, expert_idx, priority, E: int, C: int, workspace=None):
 def dispatch_reroute(x, pref, E: int, C: int, stages: int, logits=None, workspace=None):
     """Top-1 dispatch with re-routing: stage s offers the unplaced tokens their choice pref[:, s].
     Returns (expert [T], slot [T], drop_mask [T], gate [T] or None, expert_count [E], xbuf)."""
-    T, d = x.shape
-    R = pref.shape[1]
+    T, d = _tokens(x)
+    R = _routing(pref, T, "pref")
     dev = x.device
+    if not 1 <= stages <= R:
+        raise ValueError(f"stages must be in [1, R={R}], got {stages}")
+    _expect(logits, "logits", (T, E), torch.float32, optional=True)
     expert = torch.empty(T, dtype=torch.int32, device=dev)
     slot = torch.empty(T, dtype=torch.int32, device=dev)
     drop = torch.empty(T, dtype=torch.uint8, device=dev)
@@ -168,7 +223,7 @@ def dispatch_reroute(x, pref, E: int, C: int, stages: int, logits=None, workspac
     need = L.LIB.moe_dispatch_reroute_workspace_bytes(T, E)
     if need == L.SIZE_MAX:
         raise ValueError("invalid dispatch sizes")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = _ws(workspace, need, dev)
     L.check("moe_dispatch_reroute", L.LIB.moe_dispatch_reroute(
         _ptr(x), _dtype_code(x), _ptr(pref), _ptr(logits), T, d, E, R, stages, C, _ptr(expert), _ptr(slot),
         _ptr(drop), _ptr(gate), _ptr(count), _ptr(xbuf), _ptr(ws), ws.numel(), _stream(dev)))
@@ -177,10 +232,16 @@ def dispatch_reroute(x, pref, E: int, C: int, stages: int, logits=None, workspac
 
 def combine_backward(dy, ybuf, expert_idx, slot, gate, dybuf=None):
     """Combine backward: returns (dgate [T,k] fp32, dybuf [E,C,d]; kept rows written)."""
+    if ybuf.dim() != 3:
+        raise ValueError(f"ybuf must be [E, C, d], got {list(ybuf.shape)}")
     E, C, d = ybuf.shape
-    T, k = expert_idx.shape
+    T = expert_idx.shape[0]
+    k = _routing(expert_idx, T)
     dev = dy.device
-    _same(ybuf.dtype, dy)
+    _expect(dy, "dy", (T, d), ybuf.dtype)
+    _expect(slot, "slot", (T, k), torch.int32)
+    _expect(gate, "gate", (T, k), torch.float32)
+    _expect(dybuf, "dybuf", (E, C, d), ybuf.dtype, optional=True)
     dgate = torch.empty((T, k), dtype=torch.float32, device=dev)
     if dybuf is None:
         dybuf = torch.zeros_like(ybuf)
@@ -193,11 +254,17 @@ def combine_backward(dy, ybuf, expert_idx, slot, gate, dybuf=None):
 def router_backward(x, W_r, logits, expert_idx, gate, dgate, route_count, alpha=1e-2, z_weight=0.0,
                     workspace=None):
     """Router backward: returns (dlogits [T,E], dW_r [E,d], db_r [E], dx [T,d]), all fp32."""
-    T, d = x.shape
+    T, d = _tokens(x)
+    if W_r.dim() != 2:
+        raise ValueError(f"W_r must be [E, d], got {list(W_r.shape)}")
     E = W_r.shape[0]
-    k = expert_idx.shape[1]
+    k = _routing(expert_idx, T)
     dev = x.device
-    _same(torch.float32, W_r, logits, gate, dgate)
+    _expect(W_r, "W_r", (E, d), torch.float32)
+    _expect(logits, "logits", (T, E), torch.float32)
+    _expect(gate, "gate", (T, k), torch.float32)
+    _expect(dgate, "dgate", (T, k), torch.float32)
+    _expect(route_count, "route_count", (E,), torch.int32)
     dz = torch.empty((T, E), dtype=torch.float32, device=dev)
     dW = torch.empty((E, d), dtype=torch.float32, device=dev)
     db = torch.empty(E, dtype=torch.float32, device=dev)
@@ -205,7 +272,7 @@ def router_backward(x, W_r, logits, expert_idx, gate, dgate, route_count, alpha=
     need = L.LIB.moe_router_backward_workspace_bytes(T, d, E)
     if need == L.SIZE_MAX:
         raise ValueError("invalid router sizes")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = _ws(workspace, need, dev)
     L.check("moe_router_backward", L.LIB.moe_router_backward(
         _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(logits), _ptr(expert_idx), _ptr(gate), _ptr(dgate),
         _ptr(route_count), T, d, E, k, alpha, z_weight, _ptr(dz), _ptr(dW), _ptr(db), _ptr(dx), _ptr(ws),
@@ -216,16 +283,23 @@ def router_backward(x, W_r, logits, expert_idx, gate, dgate, route_count, alpha=
 def expert_ffn(xbuf, expert_count, W1, W2, *, W3=None, b1=None, b2=None, act="relu",
                workspace=None, ybuf=None):
     """Grouped expert FFN: returns ybuf [E, C, d] (rows >= expert_count[e] untouched)."""
+    if xbuf.dim() != 3 or W1.dim() != 3:
+        raise ValueError("xbuf must be [E, C, d] and W1 [E, dff, d]")
     E, C, d = xbuf.shape
     dff = W1.shape[1]
     dev = xbuf.device
-    _same(xbuf.dtype, W1, W2, W3, b1, b2)
+    _dtype_code(xbuf)
+    _expect(expert_count, "expert_count", (E,), torch.int32)
+    _experts(E, d, dff, xbuf.dtype, W1, W2, W3, b1, b2)
+    if act == "swiglu" and W3 is None:
+        raise ValueError("the SwiGLU expert needs W3")
+    _expect(ybuf, "ybuf", (E, C, d), xbuf.dtype, optional=True)
     if ybuf is None:
         ybuf = torch.empty_like(xbuf)
     need = L.LIB.moe_expert_ffn_workspace_bytes(E, C, dff, _dtype_code(xbuf))
     if need == L.SIZE_MAX:
         raise ValueError("invalid expert sizes")
-    ws = workspace if workspace is not None else _workspace(need, dev)
+    ws = _ws(workspace, need, dev)
     L.check("moe_expert_ffn", L.LIB.moe_expert_ffn(
         _ptr(xbuf), _dtype_code(xbuf), _ptr(expert_count), E, C, d, dff, _ptr(W1), _ptr(b1),
         _ptr(W3), _ptr(W2), _ptr(b2), _ACT[act], _ptr(ybuf), _ptr(ws), ws.numel(), _stream(dev)))
@@ -234,9 +308,16 @@ def expert_ffn(xbuf, expert_count, W1, W2, *, W3=None, b1=None, b2=None, act="re
 
 def combine(ybuf, expert_idx, slot, gate, prob_sum, route_count, T: int, alpha: float = 1e-2):
     """Combine and aux loss: returns (y [T, d], aux_loss [1] fp32)."""
+    if ybuf.dim() != 3:
+        raise ValueError(f"ybuf must be [E, C, d], got {list(ybuf.shape)}")
     E, C, d = ybuf.shape
-    k = expert_idx.shape[1]
+    k = _routing(expert_idx, T)
     dev = ybuf.device
+    _dtype_code(ybuf)
+    _expect(slot, "slot", (T, k), torch.int32)
+    _expect(gate, "gate", (T, k), torch.float32)
+    _expect(prob_sum, "prob_sum", (E,), torch.float32)
+    _expect(route_count, "route_count", (E,), torch.int32)
     y = torch.empty((T, d), dtype=ybuf.dtype, device=dev)
     aux = torch.empty(1, dtype=torch.float32, device=dev)
     L.check("moe_combine", L.LIB.moe_combine(
@@ -280,14 +361,18 @@ class ForwardPlan:
         """With W_noise [E, d] and noise [T, E] (fp32) the router is the noisy top-k one."""
         if tuple(x.shape) != (self.T, self.d) or x.dtype != self.dtype:
             raise ValueError("x does not match the plan")
-        _same(self.dtype, W1, W2, W3, b1, b2)
-        _same(torch.float32, W_r, b_r, W_noise, noise)
-        s = stream.cuda_stream if stream is not None else _stream(self.device)
+        T, d, E = self.T, self.d, self.E
+        _expect(W_r, "W_r", (E, d), torch.float32)
+        _expect(b_r, "b_r", (E,), torch.float32, optional=True)
+        _experts(E, d, self.dff, self.dtype, W1, W2, W3, b1, b2)
+        if self.act == "swiglu" and W3 is None:
+            raise ValueError("the SwiGLU expert needs W3")
         if (W_noise is None) != (noise is None):
             raise ValueError("the noisy router needs both W_noise and noise")
+        _expect(W_noise, "W_noise", (E, d), torch.float32, optional=True)
+        _expect(noise, "noise", (T, E), torch.float32, optional=True)
+        s = stream.cuda_stream if stream is not None else _stream(self.device)
         if W_noise is not None:
-            if tuple(noise.shape) != (self.T, self.E):
-                raise ValueError("noise must be [T, E]")
             L.check("moe_forward_noisy", L.LIB.moe_forward_noisy(
                 _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W_noise), _ptr(noise), _ptr(W1), _ptr(b1),
                 _ptr(W3), _ptr(W2), _ptr(b2), _ACT[self.act], self.T, self.d, self.dff, self.E, self.k,
@@ -325,7 +410,9 @@ class ForwardPlan:
 def forward(x, W_r, W1, W2, *, W3=None, b1=None, b2=None, b_r=None, k=1, capacity_factor=1.25,
             alpha=1e-2, act="relu"):
     """The whole layer: returns (y, aux_loss, expert_idx, gate, drop_mask)."""
-    T, d = x.shape
+    T, d = _tokens(x)
+    if W_r.dim() != 2 or W1.dim() != 3:
+        raise ValueError("W_r must be [E, d] and W1 [E, dff, d]")
     E = W_r.shape[0]
     dff = W1.shape[1]
     plan = ForwardPlan(T, d, dff, E, k, x.dtype, act=act, capacity_factor=capacity_factor,

@@ -2,8 +2,8 @@
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into sparse_mixture_experts_argmax_amd/libmoe.so.
-Run: python sparse_mixture_experts_argmax_amd/build.py  (by path: importing the package
-loads the library this script builds)
+Run: python sparse_mixture_experts_argmax_amd/build.py [--incremental]  (by path:
+importing the package loads the library this script builds)
 """
 from __future__ import annotations
 
@@ -53,13 +53,25 @@ def _compile(src: str, obj: str) -> None:
             print(line, file=sys.stderr)
 
 
-def build(jobs: int | None = None) -> str:
+def _stale(src: str, obj: str, headers: list) -> bool:
+    """An object older than its source or than any header (sources include several)."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(p) > t for p in [src, *headers])
+
+
+def build(jobs: int | None = None, incremental: bool = False) -> str:
+    """Compile every .hip file and link libmoe.so.  incremental=True recompiles
+    only the objects that are older than their source or any header."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    n = jobs or min(8, len(srcs), os.cpu_count() or 1)
+    headers = sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h")))
+    todo = [(s, o) for s, o in zip(srcs, objs) if not incremental or _stale(s, o, headers)]
+    n = jobs or min(8, max(1, len(todo)), os.cpu_count() or 1)
     with ThreadPoolExecutor(n) as ex:
-        list(ex.map(lambda so: _compile(*so), zip(srcs, objs)))
+        list(ex.map(lambda so: _compile(*so), todo))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -70,4 +82,4 @@ def build(jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(incremental="--incremental" in sys.argv[1:]))

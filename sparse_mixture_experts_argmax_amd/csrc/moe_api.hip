@@ -13,6 +13,7 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 8;
 constexpr int64_t MAX_DIM = 1 << 20;
+constexpr int64_t PRIORITY_MAX_CHOICES = int64_t(1) << 20;   // T k of moe_dispatch_priority
 
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -371,6 +372,8 @@ moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *exp
     MOE_CHECK(check_sizes(T, E, k));
     MOE_CHECK(check_width(d));
     if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    // the per-expert ranking is quadratic in the choices at one expert
+    if (T * (int64_t)k > PRIORITY_MAX_CHOICES) return MOE_ERR_UNSUPPORTED;
     if (C < 0 || C > T) return MOE_ERR_INVALID_ARGUMENT;
     const bool empty = T == 0;
     if (!ptr_ok(x, empty) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(priority, empty) ||

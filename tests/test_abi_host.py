@@ -142,6 +142,7 @@ def test_reroute_dispatch_rejects(case, expect):
     (dict(C=65), L.MOE_ERR_INVALID_ARGUMENT),                  # C > T
     (dict(E=1025), L.MOE_ERR_UNSUPPORTED),
     (dict(ws_bytes=0), L.MOE_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=(1 << 19) + 1, k=2, C=16), L.MOE_ERR_UNSUPPORTED),  # T k above 2^20 (quadratic ranking)
 ])
 def test_priority_dispatch_rejects(case, expect):
     a = dict(x=P, dt=L.MOE_BF16, idx=P, pr=P, T=64, d=64, E=8, k=1, C=16, slot=P, drop=P, cnt=P, xbuf=P,

@@ -21,7 +21,7 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
-from gpu_util import check_routing, check_y, device_inputs, host_f64
+from gpu_util import check_routing, check_y, device_inputs, host_f64, layer_bound
 from test_gpu_parity import _forward_checks
 
 pytestmark = pytest.mark.gpu
@@ -140,4 +140,5 @@ def test_non_finite_tokens():
                                  cfg["act"])
                 ref[i] += float(g[t, j]) * o[0]
     assert np.isfinite(yg[toks]).all()
-    check_y(yg[toks], ref, np.arange(toks.size), "bf16")
+    _, bound = layer_bound(cfg, gi, rs, g, tokens=toks)
+    check_y(yg[toks], ref, np.arange(toks.size), "bf16", bound[toks])

@@ -15,7 +15,7 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
-from gpu_util import Z_RTOL, check_routing, check_y, dev, device_inputs, host_f64
+from gpu_util import Z_RTOL, check_routing, check_y, dev, device_inputs, host_f64, layer_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -122,7 +122,8 @@ def test_noisy_router_feeds_the_layer():
         if tt.size:
             o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], "bf16"), O.widen(cfg["W2"][e], "bf16"), cfg["act"])
             ref[tt] += g[tt, jj][:, None] * o
-    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16")
+    _, bound = layer_bound(cfg, gi, rs, g)
+    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16", bound)
 
 
 @pytest.mark.parametrize("k,dt", [(1, "bf16"), (2, "bf16"), (1, "f32")])
@@ -155,4 +156,5 @@ def test_fused_forward_with_noise(k, dt):
         if tt.size:
             o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], dt), O.widen(cfg["W2"][e], dt), cfg["act"])
             ref[tt] += g[tt, jj][:, None] * o
-    check_y(host_f64(y), ref, np.arange(cfg["T"]), dt)
+    _, bound = layer_bound(cfg, gi, rs, g)
+    check_y(host_f64(y), ref, np.arange(cfg["T"]), dt, bound)

@@ -16,7 +16,7 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
-from gpu_util import check_routing, check_y, dev, device_inputs, host_bits, host_f64
+from gpu_util import check_routing, check_y, dev, device_inputs, host_bits, host_f64, layer_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -139,4 +139,5 @@ def test_priority_layer_end_to_end():
         if tt.size:
             o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], "bf16"), O.widen(cfg["W2"][e], "bf16"), "relu")
             ref[tt] += g[tt, jj].astype(np.float64)[:, None] * o
-    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16")
+    _, bound = layer_bound(cfg, gi, rs, g)
+    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16", bound)

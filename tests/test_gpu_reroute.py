@@ -14,7 +14,7 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
-from gpu_util import check_y, device_inputs, host_bits, host_f64, dev
+from gpu_util import check_y, device_inputs, host_bits, host_f64, dev, layer_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,22 @@ def test_one_stage_is_the_plain_dispatch():
     assert np.array_equal(sl.cpu().numpy(), slot.cpu().numpy()[:, 0])
 
 
+def test_reroute_padded_preferences():
+    """Entries outside [0, E) (-1 padding, or E and above) are no choice at that stage:
+    the token waits for its next entry, as in the oracle."""
+    rng = np.random.default_rng(4)
+    T, E, R = 1500, 7, 4
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    pref = np.argsort(-z, axis=1, kind="stable")[:, :R].astype(np.int32)
+    pad = rng.random((T, R)) < 0.3
+    pref[pad] = np.where(rng.random(int(pad.sum())) < 0.5, -1, E + 3)
+    pref[:5] = -1                                   # no choice at all: always dropped
+    C = O.capacity(T, E, 1, 0.8)
+    print(f"re-routing with padded preferences: T={T} E={E} R={R} C={C}", flush=True)
+    ex, *_ = _check(_x(T), pref, E, C, R, z)
+    assert (ex.cpu().numpy()[:5] == -1).all()
+
+
 @pytest.mark.parametrize("T,C", [(0, 0), (1, 1), (64, 0)])
 def test_reroute_degenerate(T, C):
     pref = np.tile(np.array([[1, 0, 2]], np.int32), (T, 1))
@@ -112,4 +128,5 @@ def test_reroute_layer_end_to_end():
             o = O.expert_ffn(x64[tt], O.widen(cfg["W1"][e], "bf16"), O.widen(cfg["W2"][e], "bf16"), "relu")
             ref[tt] = g_np[tt, None] * o
     assert np.any((e_np >= 0) & (e_np != idx.cpu().numpy()[:, 0]))   # some tokens were re-routed
-    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16")
+    _, bound = layer_bound(cfg, e_np[:, None], sl.cpu().numpy()[:, None], g_np[:, None])
+    check_y(host_f64(y), ref, np.arange(cfg["T"]), "bf16", bound)

@@ -756,8 +756,24 @@ def test_reroute_no_overflow_stays_in_stage_zero():
     assert np.all(st == 0) and np.array_equal(ex, pref[:, 0])
 
 
+def check_reroute_padded_preferences():
+    """By hand: an entry outside [0, E) is no choice at that stage.  T = 4,
+    E = 2, C = 1, three stages, preferences [-1,0,1] [0,5,1] [-1,-1,-1]
+    [0,1,0].  Stage 0: t0 has no choice, t1 -> e0 slot 0, t2 has none, t3
+    finds e0 full.  Stage 1: t0 finds e0 full, t2 has none, t3 -> e1 slot
+    0.  Stage 2: t0 finds e1 full, t2 has none: both are dropped."""
+    pref = np.array([[-1, 0, 1], [0, 5, 1], [-1, -1, -1], [0, 1, 0]], np.int32)
+    ex, sl, st, cnt = O.assign_slots_reroute(pref, 2, 1, 3)
+    assert ex.tolist() == [-1, 0, -1, 1] and sl.tolist() == [-1, 0, -1, 0]
+    assert st.tolist() == [-1, 0, -1, 1] and cnt.tolist() == [1, 1]
+
+
 def test_reroute_worked_example():
     check_reroute_worked_example()
+
+
+def test_reroute_padded_preferences():
+    check_reroute_padded_preferences()
 
 
 def test_reroute_places_everyone():
@@ -1021,3 +1037,68 @@ def test_planted_reroute_mistake_is_caught(monkeypatch, repl, check):
     monkeypatch.setattr(O, "assign_slots_reroute", repl)
     with pytest.raises(AssertionError):
         check()
+
+
+# ---------------------------------------------------------------------------
+# the near-tie exemption of the parity rule
+# ---------------------------------------------------------------------------
+
+def check_near_tie_table():
+    """Hand-worked flags on logits whose gaps are exact binary fractions."""
+    g = golden("near_tie.json")
+    for case in g["cases"]:
+        z = np.array([case["z"]], dtype=np.float32)
+        got = bool(O.near_tie_tokens(z, case["k"], g["gap"])[0])
+        assert got == case["tie"], case["what"]
+
+
+def check_near_tie_batch_is_rowwise():
+    """A batch gives each row's own flag (no mixing across tokens)."""
+    g = golden("near_tie.json")
+    for k in (1, 2):
+        rows = [c for c in g["cases"] if c["k"] == k and len(c["z"]) == 4]
+        z = np.array([c["z"] for c in rows], dtype=np.float32)
+        assert O.near_tie_tokens(z, k, g["gap"]).tolist() == [c["tie"] for c in rows]
+
+
+def test_near_tie_table():
+    check_near_tie_table()
+    check_near_tie_batch_is_rowwise()
+
+
+def _near_tie_top2_gap_only(z, k, gap=1e-5):
+    """Only the top-1/top-2 gap, whatever k."""
+    s = -np.sort(-np.asarray(z, np.float64), axis=1)
+    if s.shape[1] < 2:
+        return np.zeros(s.shape[0], bool)
+    return (s[:, 0] - s[:, 1]) < gap
+
+
+def _near_tie_one_too_many(z, k, gap=1e-5):
+    """Gaps among the k+2 largest instead of the k+1 largest."""
+    return _ORIG_NT(z, k + 1, gap)
+
+
+def _near_tie_index_order(z, k, gap=1e-5):
+    """Adjacent gaps in expert-index order instead of sorted order."""
+    a = np.asarray(z, np.float64)
+    if a.shape[1] < 2:
+        return np.zeros(a.shape[0], bool)
+    return np.any(np.abs(a[:, 1:] - a[:, :-1]) < gap, axis=1)
+
+
+def _near_tie_probabilities(z, k, gap=1e-5):
+    """Gaps between softmax probabilities instead of fp32 logits."""
+    p = O.softmax(np.asarray(z, np.float64))
+    return _ORIG_NT(p, k, gap)
+
+
+_ORIG_NT = O.near_tie_tokens
+
+
+@pytest.mark.parametrize("repl", [_near_tie_top2_gap_only, _near_tie_one_too_many,
+                                  _near_tie_index_order, _near_tie_probabilities])
+def test_planted_near_tie_mistake_is_caught(monkeypatch, repl):
+    monkeypatch.setattr(O, "near_tie_tokens", repl)
+    with pytest.raises(AssertionError):
+        check_near_tie_table()
