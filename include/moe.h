@@ -15,7 +15,9 @@
  *     CUDA tensor) unless stated otherwise.  All arrays are dense, row-major,
  *     16-byte aligned.  The library never allocates, frees or synchronises;
  *     every buffer is owned by the caller.  It keeps no global mutable state
- *     and is safe to call from several threads on distinct streams.
+ *     and is safe to call from several threads on distinct streams; the one
+ *     exception is moe_router_noalloc, whose scratch is a static array per
+ *     GPU (see there).
  *   - dtype: MOE_F32 or MOE_BF16 names the storage type of x, W1, W3, W2,
  *     b1, b2, the dispatch buffer, the expert outputs and y.  The router
  *     weight W_r, its bias and the gates are always fp32 ([CS25-L5]
@@ -137,6 +139,31 @@ moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float
                       int64_t T, int32_t d, int32_t E, int32_t k,
                       int32_t *expert_idx, float *gate, float *prob_sum, int32_t *route_count,
                       float *z_loss, float *logits, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_router for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, outputs and kernels, with no workspace argument.  Its
+ * scratch (the router's per-block partial rows and the three-part split of
+ * W_r) lives in a static device array of moe_router_noalloc_scratch_bytes()
+ * = 32 MiB that the library holds on each GPU it runs on until the process
+ * ends.  The call allocates nothing: on its first call on a GPU it looks up
+ * that GPU's copy of the array (hipGetSymbolAddress, with the GPU current)
+ * and keeps the address.  Sizes whose router workspace,
+ * moe_router_workspace_bytes(T, d, E, k), exceeds the array return
+ * MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the five
+ * workloads of this library need at most 10 MiB).  `stream` must belong to
+ * the current device.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (two streams, or two threads) race
+ * and give wrong results; calls in order on one stream are safe.  Each call
+ * writes every scratch byte it reads, so nothing carries over between calls.
+ * MOE_ERR_HIP if the array's address cannot be found.
+ */
+size_t moe_router_noalloc_scratch_bytes(void);
+moe_status moe_router_noalloc(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                              int64_t T, int32_t d, int32_t E, int32_t k,
+                              int32_t *expert_idx, float *gate, float *prob_sum, int32_t *route_count,
+                              float *z_loss, float *logits, hipStream_t stream);
 
 /*
  * Noisy top-k router: moe_router on the logits

@@ -164,6 +164,36 @@ def router(x, W_r, k: int = 1, b_r=None, workspace=None, z_loss: bool = False, W
     return out
 
 
+def router_noalloc(x, W_r, k: int = 1, b_r=None, z_loss: bool = False, logits: bool = False):
+    """router() through moe_router_noalloc: the library's static per-GPU scratch instead of a
+    workspace (for callers that cannot allocate; the outputs are still the caller's).  Returns
+    what router() returns for the same flags."""
+    T, d = _tokens(x)
+    if W_r.dim() != 2:
+        raise ValueError(f"W_r must be [E, d], got {list(W_r.shape)}")
+    E = W_r.shape[0]
+    dev = x.device
+    _expect(W_r, "W_r", (E, d), torch.float32)
+    _expect(b_r, "b_r", (E,), torch.float32, optional=True)
+    if not 1 <= k <= E:
+        raise ValueError(f"k must be in [1, E={E}], got {k}")
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    prob_sum = torch.empty(E, dtype=torch.float32, device=dev)
+    route_count = torch.empty(E, dtype=torch.int32, device=dev)
+    zl = torch.empty(1, dtype=torch.float32, device=dev) if z_loss else None
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if logits else None
+    L.check("moe_router_noalloc", L.LIB.moe_router_noalloc(
+        _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), T, d, E, k, _ptr(idx), _ptr(gate),
+        _ptr(prob_sum), _ptr(route_count), _ptr(zl), _ptr(lg), _stream(dev)))
+    out = (idx, gate, prob_sum, route_count)
+    if z_loss:
+        out += (zl,)
+    if logits:
+        out += (lg,)
+    return out
+
+
 def dispatch(x, expert_idx, E: int, C: int, workspace=None):
     """Dispatch: returns (slot [T,k] int32, drop_mask [T,k] uint8, expert_count [E] int32, xbuf [E,C,d])."""
     T, d = _tokens(x)

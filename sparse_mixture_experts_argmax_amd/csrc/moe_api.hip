@@ -5,7 +5,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
+
+// Scratch of moe_router_noalloc: one copy per GPU, held for the life of the
+// process.  Host code never uses this name as an address (on the host it is
+// a stand-in); noalloc_scratch() returns the device address of the current
+// GPU's copy.
+#define MOE_NOALLOC_SCRATCH_BYTES (size_t(32) << 20)
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -309,6 +318,54 @@ moe_status moe_router(const void *x, moe_dtype dt, const float *W_r, const float
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
     return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count, z_loss,
                       static_cast<char *>(ws), stream, true, logits);
+}
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::once_flag g_scratch_once[NOALLOC_MAX_DEVICES];
+void *g_scratch_ptr[NOALLOC_MAX_DEVICES];
+hipError_t g_scratch_err[NOALLOC_MAX_DEVICES];
+
+// The device address of the current GPU's scratch array, looked up once per
+// device (with that device current) and kept.
+moe_status noalloc_scratch(char **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return MOE_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return MOE_ERR_HIP;
+    *out = static_cast<char *>(g_scratch_ptr[dev]);
+    return MOE_OK;
+}
+
+}  // namespace
+
+size_t moe_router_noalloc_scratch_bytes(void) { return MOE_NOALLOC_SCRATCH_BYTES; }
+
+moe_status moe_router_noalloc(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
+                              int64_t T, int32_t d, int32_t E, int32_t k, int32_t *expert_idx,
+                              float *gate, float *prob_sum, int32_t *route_count, float *z_loss,
+                              float *logits, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr4_ok(expert_idx, empty) ||
+        !ptr4_ok(gate, empty) || !ptr4_ok(prob_sum, false) || !ptr4_ok(route_count, false) ||
+        !(z_loss == nullptr || ptr4_ok(z_loss, false)) || !(logits == nullptr || ptr4_ok(logits, empty)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (router_ws(T, d, E).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    char *ws = nullptr;
+    MOE_CHECK(noalloc_scratch(&ws));
+    // every scratch byte the router reads (per-block partial rows, the
+    // three-part split of W_r) is written earlier in the same call, so the
+    // previous call's contents need no clearing
+    return run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count, z_loss, ws,
+                      stream, true, logits);
 }
 
 moe_status moe_router_noisy(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
