@@ -1,24 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the Switch MoE layer forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload switch_base]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
 
 A step is one whole layer forward (router, dispatch, expert FFN, combine
 and loss) over one batch of seeded synthetic inputs already resident in
-HBM.  First the GPU settles: untimed forwards run for --settle-seconds
-(0.3 s), since the chip leaves its idle clocks only under load and the
-first ~100 forwards after even 0.2 s of idle run up to 25 % slower.  Then W
-untimed warm-up steps, then exactly K timed steps bracketed by device
-synchronisation; value = tokens per second over the K steps.
+HBM.  The headline workload is the Mixtral-shaped layer (8192 tokens,
+d_model 4096, d_ff 14336, 8 SwiGLU experts, top-2), the largest of the five.
+First the GPU settles: untimed forwards run for --settle-seconds (0.3 s),
+since the chip leaves its idle clocks only under load.  Then W untimed
+warm-up steps, then exactly K timed steps bracketed by device
+synchronisation; each step starts with the 256 MB last-level cache flushed
+(512 MB of scratch written before it, outside its HIP-event interval), and
+value = T K / the summed step time.  warm_tokens_per_s gives the same K
+steps back to back.
 
-After the timed steps the same K steps run again through
-moe_forward_staged, which records HIP events at the stage boundaries on the
-stream the kernels run on, giving each stage's average duration (the
-events cost time of their own, so the timed steps run without them); the
-roofline object reports the stage that takes the longest, with its
-algorithmic bytes / flops per launch (see `stage_work`).  step_ms gives the
-spread of single forwards, warm and with a cold last-level cache.  The CPU
-baseline times the CPU oracle on the same workload, on this host.
+The same K steps then run through moe_forward_staged, which records HIP
+events at the stage boundaries on the stream the kernels run on, giving each
+stage's average duration; the roofline object reports the stage that takes
+the longest, with its algorithmic bytes / flops per launch (`stage_work`).
+The other four workloads follow (their tokens/s and dominant-kernel roofline
+under "workloads"), then the CPU baseline: the CPU oracle on the headline
+workload, on this host.
 
 Prints one JSON line.
 """
@@ -73,12 +76,16 @@ def stage_work(cfg: dict, A: int) -> dict:
       dispatch T k (4 + 4 + 1) (indices read, slots and drop flags written)
                + 2 A d s (x rows read, xbuf rows written), or, fused,
                + 4 A (row index written) [+ (T - A) d s, dropped rows of y cleared]
-      gemm1    W1 (+W3) [E,f,d] + A d s read + A f s written;
+      gemm1    W1 (+W3) [E,f,d] + A d s read (the kept token rows);
                flops 2 A d f (x2 for SwiGLU)
-      gemm2    W2 [E,d,f] + A f s read + A d s written; flops 2 A f d
-               [fused: + 8 A, the row's token and gate]
+      gemm2    W2 [E,d,f] read + A d s written (the expert output rows);
+               flops 2 A f d [fused: + 8 A, the row's token and gate]
       combine  A d s read + T d s written + T k 12 (indices, slots, gates);
                nothing when the second GEMM wrote y
+    The FFN's minimum bytes are the weights once plus its input and output
+    rows; the hidden activations H [A, f] written by the first GEMM and read
+    by the second are not part of them (a fused FFN would keep H on chip),
+    so their round trip shows up only in the measured traffic.
     """
     T, d, f, E, k = cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"]
     s = 2 if cfg["dtype"] == "bf16" else 4
@@ -91,9 +98,9 @@ def stage_work(cfg: dict, A: int) -> dict:
                        flops=(3 if mfma_router else 1) * 2 * T * d * E,
                        dtype="bf16" if mfma_router else "f32"),
         "dispatch": dict(bytes=disp, flops=0, dtype=cfg["dtype"]),
-        "expert_gemm1": dict(bytes=m * E * f * d * s + A * d * s + A * f * s, flops=2 * m * A * d * f,
+        "expert_gemm1": dict(bytes=m * E * f * d * s + A * d * s, flops=2 * m * A * d * f,
                              dtype=cfg["dtype"]),
-        "expert_gemm2": dict(bytes=E * d * f * s + A * f * s + A * d * s + 8 * A * scatter,
+        "expert_gemm2": dict(bytes=E * d * f * s + A * d * s + 8 * A * scatter,
                              flops=2 * A * f * d, dtype=cfg["dtype"]),
         "combine": dict(bytes=0 if scatter else A * d * s + T * d * s + T * k * 12, flops=0,
                         dtype=cfg["dtype"]),
@@ -348,14 +355,233 @@ def cpu_baseline(cfg: dict, min_seconds: float) -> dict:
                        f"{el:.1f} s; NumPy oracle, fp64 experts")
 
 
+class Workload:
+    """One seeded workload resident on the GPU, with its forward plan."""
+
+    def __init__(self, name: str, torch, moe, dev):
+        self.cfg = cfg = datagen.make(name, seed=0)
+        self.name = name
+        self.dev = dev
+        bf = cfg["dtype"] == "bf16"
+
+        def todev(a, bf16=False):
+            if a is None:
+                return None
+            t = torch.from_numpy(a.view("int16") if bf16 else a)
+            return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+        self.todev = todev
+        self.x = todev(cfg["x"], bf)
+        self.W_r = todev(cfg["W_r"])
+        self.b_r = todev(cfg["b_r"])
+        self.W1, self.W3, self.W2 = todev(cfg["W1"], bf), todev(cfg["W3"], bf), todev(cfg["W2"], bf)
+        self.b1, self.b2 = todev(cfg["b1"], bf), todev(cfg["b2"], bf)
+        dt = torch.bfloat16 if bf else torch.float32
+        self.plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"], dt, act=cfg["act"],
+                                    capacity_factor=cfg["cf"], alpha=cfg["alpha"], device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def step(self):
+        return self.plan(self.x, self.W_r, self.W1, self.W2, W3=self.W3, b1=self.b1, b2=self.b2, b_r=self.b_r)
+
+    def staged_step(self, L, events):
+        from sparse_mixture_experts_argmax_amd.api import _ACT, _dtype_code, _ptr
+        p, cfg = self.plan, self.cfg
+        arr = (ctypes.c_void_p * len(events))(*events)
+        L.check("moe_forward_staged", L.LIB.moe_forward_staged(
+            _ptr(self.x), _dtype_code(self.x), _ptr(self.W_r), _ptr(self.b_r), _ptr(self.W1), _ptr(self.b1),
+            _ptr(self.W3), _ptr(self.W2), _ptr(self.b2), _ACT[cfg["act"]], cfg["T"], cfg["d"], cfg["f"],
+            cfg["E"], cfg["k"], p.capacity_factor, p.alpha, _ptr(p.y), _ptr(p.aux), _ptr(p.z_loss),
+            _ptr(p.expert_idx), _ptr(p.gate), _ptr(p.drop_mask), _ptr(p.ws), p.ws.numel(),
+            self.stream.cuda_stream, arr))
+
+
+def _spread(v, T):
+    q = np.percentile(np.asarray(v, dtype=np.float64), [50, 10, 90])
+    return dict(median=round(float(q[0]), 4), p10=round(float(q[1]), 4), p90=round(float(q[2]), 4),
+                n=len(v), tokens_per_s=round(T / (float(q[0]) / 1e3), 1))
+
+
+def measure(W: Workload, torch, L, hip, steps: int, warmup: int, settle_seconds: float, flush) -> dict:
+    """Settle, warm up, then the timed steps (each after a last-level-cache flush), the
+    same steps through moe_forward_staged for the stage times, and warm back-to-back steps."""
+    T = W.cfg["T"]
+    sid = W.stream.cuda_stream
+    # settle: untimed forwards in rounds of 10 until settle_seconds have passed
+    n_settle, t_s = 0, time.perf_counter()
+    while n_settle == 0 or time.perf_counter() - t_s < settle_seconds:
+        for _ in range(10):
+            W.step()
+        n_settle += 10
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_s
+    for _ in range(warmup):
+        W.step()
+    torch.cuda.synchronize()
+    # the timed steps: each forward starts with the 256 MB last-level cache
+    # holding none of its data (512 MB of scratch written just before it,
+    # outside its event interval)
+    ev = hip.create(2 * steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        hip.record(ev[2 * i], sid)
+        W.step()
+        hip.record(ev[2 * i + 1], sid)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cold_ms = [hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)]
+    hip.destroy(ev)
+    # stage times: the same cold steps with an event at every stage boundary
+    nev = L.MOE_STAGE_EVENTS
+    sev = hip.create(nev * steps)
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        W.staged_step(L, sev[i * nev:(i + 1) * nev])
+    torch.cuda.synchronize()
+    stage_ms = {name: 0.0 for name in L.STAGES}
+    for i in range(steps):
+        e = sev[i * nev:(i + 1) * nev]
+        for j, name in enumerate(L.STAGES):
+            stage_ms[name] += hip.elapsed_ms(e[j], e[j + 1]) / steps
+    hip.destroy(sev)
+    # warm: back-to-back forwards, caches holding whatever the last one left
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        W.step()
+    torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t1
+    A = int(W.plan.intermediate("expert_count").sum().item())
+    drops = int(W.plan.drop_mask.sum().item())
+    return dict(cold_ms=cold_ms, wall_s=wall, stage_ms=stage_ms, warm_s=warm_s, steps=steps, A=A, drops=drops,
+                settle=dict(seconds=round(settle_s, 3), forwards=n_settle),
+                value=T * steps / (sum(cold_ms) / 1e3), warm_value=T * steps / warm_s)
+
+
+def stage_report(W: Workload, m: dict, L) -> tuple[dict, dict]:
+    """Per-stage rooflines and the roofline object of the dominant (longest) kernel."""
+    work = stage_work(W.cfg, m["A"])
+    stages = {}
+    for name in L.STAGES:
+        r = roofline_of(work[name], m["stage_ms"][name] / 1e3)
+        stages[name] = dict(us=round(m["stage_ms"][name] * 1e3, 2), bytes=work[name]["bytes"],
+                            flops=work[name]["flops"], **r)
+    dominant = max(L.STAGES, key=lambda n: m["stage_ms"][n])
+    dom = stages[dominant]
+    traffic, traffic_src = committed_traffic(W.name, dominant)
+    roofline = dict(bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"], unit=dom["unit"],
+                    frac=dom["frac"], traffic=traffic, traffic_unit="bytes/launch",
+                    traffic_source=traffic_src, kernel=dominant,
+                    algorithmic_bytes=work[dominant]["bytes"], algorithmic_flops=work[dominant]["flops"],
+                    avg_us=dom["us"])
+    return stages, roofline
+
+
+def ffn_mfma_pct(W: Workload, m: dict) -> float:
+    work = stage_work(W.cfg, m["A"])
+    ffn_s = (m["stage_ms"]["expert_gemm1"] + m["stage_ms"]["expert_gemm2"]) / 1e3
+    ffn_flops = work["expert_gemm1"]["flops"] + work["expert_gemm2"]["flops"]
+    return round(100.0 * ffn_flops / ffn_s / 1e12 / PEAK_TFLOPS[W.cfg["dtype"]], 2)
+
+
+def time_calls(hip, stream_id, torch, fn, calls: int) -> float:
+    """Seconds per call of fn over `calls` calls after one untimed call (HIP events)."""
+    fn()
+    ev = hip.create(2)
+    hip.record(ev[0], stream_id)
+    for _ in range(calls):
+        fn()
+    hip.record(ev[1], stream_id)
+    torch.cuda.synchronize()
+    s = hip.elapsed_ms(ev[0], ev[1]) / calls / 1e3
+    hip.destroy(ev)
+    return s
+
+
+def measure_variants(W: Workload, torch, moe, L, hip, args) -> dict:
+    """The router and dispatch variants and the gate-side backward, each timed on its own."""
+    cfg, plan, x, dev, sid = W.cfg, W.plan, W.x, W.dev, W.stream.cuda_stream
+    T_, d_, E_, k_ = cfg["T"], cfg["d"], cfg["E"], cfg["k"]
+    s_ = 2 if cfg["dtype"] == "bf16" else 4
+    variants = {}
+    # the noisy top-k router: the same tokens and W_r, seeded W_noise and standard normal draws
+    if args.noisy_calls > 0:
+        rng = np.random.default_rng(1)
+        W_n = W.todev((rng.standard_normal((E_, d_)) * np.sqrt(0.1 / d_)).astype(np.float32))
+        eps = W.todev(rng.standard_normal((T_, E_)).astype(np.float32))
+        rws = torch.empty(L.LIB.moe_router_workspace_bytes(T_, d_, E_, k_), dtype=torch.uint8, device=dev)
+        sec = time_calls(hip, sid, torch, lambda: moe.router(x, W.W_r, k=k_, b_r=W.b_r, workspace=rws, z_loss=True,
+                                                             W_noise=W_n, noise=eps), args.noisy_calls)
+        nw = noisy_router_work(cfg)
+        variants["noisy_router"] = dict(us=round(sec * 1e6, 2), bytes=nw["bytes"], flops=nw["flops"],
+                                        calls=args.noisy_calls, **roofline_of(nw, sec))
+        del W_n, eps, rws
+    # priority routing: the capacity filled in descending first-gate order
+    if args.priority_calls > 0:
+        pr = plan.gate[:, 0].contiguous()
+        pws = torch.empty(L.LIB.moe_dispatch_priority_workspace_bytes(T_, E_, k_), dtype=torch.uint8, device=dev)
+        sec = time_calls(hip, sid, torch, lambda: moe.dispatch_priority(x, plan.expert_idx, pr, E_, plan.C,
+                                                                        workspace=pws), args.priority_calls)
+        A_pr = int(moe.dispatch_priority(x, plan.expert_idx, pr, E_, plan.C, workspace=pws)[2].sum().item())
+        pw = dict(bytes=2 * A_pr * d_ * s_ + T_ * k_ * 9 + T_ * 4, flops=0, dtype=cfg["dtype"])
+        variants["priority_dispatch"] = dict(us=round(sec * 1e6, 2), bytes=pw["bytes"], kept=A_pr,
+                                             calls=args.priority_calls, **roofline_of(pw, sec))
+        del pws
+    # the gate-side backward (combine backward, then router backward through
+    # the gates, the balance loss and the z-loss) on the split API's buffers
+    if args.backward_calls > 0:
+        idx_b, gate_b, _, rc_b, lg_b = moe.router(x, W.W_r, k=k_, b_r=W.b_r, logits=True)
+        slot_b, _, cnt_b, xbuf_b = moe.dispatch(x, idx_b, E_, plan.C)
+        ybuf_b = moe.expert_ffn(xbuf_b, cnt_b, W.W1, W.W2, W3=W.W3, b1=W.b1, b2=W.b2, act=cfg["act"])
+        del xbuf_b
+        dy_b = torch.randn((T_, d_), device=dev).to(x.dtype)
+        dyb_b = torch.zeros_like(ybuf_b)
+        bws = torch.empty(max(L.LIB.moe_router_backward_workspace_bytes(T_, d_, E_), 256), dtype=torch.uint8,
+                          device=dev)
+
+        def gate_backward():
+            dg, _ = moe.combine_backward(dy_b, ybuf_b, idx_b, slot_b, gate_b, dybuf=dyb_b)
+            moe.router_backward(x, W.W_r, lg_b, idx_b, gate_b, dg, rc_b, alpha=cfg["alpha"], z_weight=1e-3,
+                                workspace=bws)
+        sec = time_calls(hip, sid, torch, gate_backward, args.backward_calls)
+        A_b = int(cnt_b.sum().item())
+        bw = dict(bytes=3 * A_b * d_ * s_ + 16 * T_ * k_ + 8 * T_ * E_ + T_ * d_ * (s_ + 4) + 8 * E_ * d_
+                  + 12 * T_ * k_, flops=4 * T_ * E_ * d_, dtype="f32")
+        variants["gate_backward"] = dict(us=round(sec * 1e6, 2), bytes=bw["bytes"], flops=bw["flops"],
+                                         calls=args.backward_calls, **roofline_of(bw, sec))
+        del ybuf_b, dyb_b, bws
+    # re-routing of the overflow: the router's top min(4, E) as preferences,
+    # as many stages, the even-split capacity, gates from the logits
+    if args.reroute_calls > 0:
+        R_ = min(4, E_)
+        idx_r, _, _, _, lg_r = moe.router(x, W.W_r, k=R_, b_r=W.b_r, logits=True)
+        C1 = moe.capacity(T_, E_, 1, 1.0)
+        rrws = torch.empty(max(L.LIB.moe_dispatch_reroute_workspace_bytes(T_, E_), 256), dtype=torch.uint8,
+                           device=dev)
+        sec = time_calls(hip, sid, torch, lambda: moe.dispatch_reroute(x, idx_r, E_, C1, R_, logits=lg_r,
+                                                                       workspace=rrws), args.reroute_calls)
+        A_r = int(moe.dispatch_reroute(x, idx_r, E_, C1, R_, logits=lg_r, workspace=rrws)[4].sum().item())
+        rw = dict(bytes=2 * A_r * d_ * s_ + T_ * (4 * R_ + 4 * E_ + 13), flops=0, dtype=cfg["dtype"])
+        variants["reroute_dispatch"] = dict(us=round(sec * 1e6, 2), bytes=rw["bytes"], kept=A_r, stages=R_,
+                                            capacity=C1, calls=args.reroute_calls, **roofline_of(rw, sec))
+        del rrws
+    return variants
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-seconds", type=float, default=0.3,
                     help="untimed forwards before the warm-up steps, to bring the GPU to its load clocks")
-    ap.add_argument("--workload", default="switch_base", choices=datagen.CONFIG_ORDER)
+    ap.add_argument("--workload", default="mixtral", choices=datagen.CONFIG_ORDER,
+                    help="the workload of the headline line (default: the Mixtral-shaped layer, the largest)")
+    ap.add_argument("--others", type=int, default=1,
+                    help="also measure the other four workloads (tokens/s and dominant-kernel roofline "
+                         "of each under 'workloads'); 0 skips them")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--noisy-calls", type=int, default=20,
@@ -395,245 +621,32 @@ def main(argv=None):
     import torch
     import sparse_mixture_experts_argmax_amd as moe
     from sparse_mixture_experts_argmax_amd import _lib as L
-    from sparse_mixture_experts_argmax_amd.api import _dtype_code, _ptr, _ACT
 
-    cfg = datagen.make(args.workload, seed=0)
     dev = torch.device("cuda:0")
-    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
-
-    def todev(a, bf=False):
-        if a is None:
-            return None
-        t = torch.from_numpy(a.view("int16") if bf else a)
-        return (t.view(torch.bfloat16) if bf else t).to(dev)
-
-    bf = cfg["dtype"] == "bf16"
-    x = todev(cfg["x"], bf)
-    W_r = todev(cfg["W_r"])
-    b_r = todev(cfg["b_r"])
-    W1, W3, W2 = todev(cfg["W1"], bf), todev(cfg["W3"], bf), todev(cfg["W2"], bf)
-    b1, b2 = todev(cfg["b1"], bf), todev(cfg["b2"], bf)
-    plan = moe.ForwardPlan(cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"], dt, act=cfg["act"],
-                           capacity_factor=cfg["cf"], alpha=cfg["alpha"], device=dev)
-    stream = torch.cuda.current_stream(dev)
     hip = HipEvents()
-    nev = L.MOE_STAGE_EVENTS
-    events = hip.create(nev * args.steps)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    def step(i=None):
-        if i is None:
-            return plan(x, W_r, W1, W2, W3=W3, b1=b1, b2=b2, b_r=b_r)
-        arr = (ctypes.c_void_p * nev)(*events[i * nev:(i + 1) * nev])
-        L.check("moe_forward_staged", L.LIB.moe_forward_staged(
-            _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
-            _ptr(b2), _ACT[cfg["act"]], cfg["T"], cfg["d"], cfg["f"], cfg["E"], cfg["k"],
-            plan.capacity_factor, plan.alpha, _ptr(plan.y), _ptr(plan.aux), _ptr(plan.z_loss),
-            _ptr(plan.expert_idx),
-            _ptr(plan.gate), _ptr(plan.drop_mask), _ptr(plan.ws), plan.ws.numel(),
-            stream.cuda_stream, arr))
-
-    # settle: untimed forwards in rounds of 10 until settle_seconds have passed
-    n_settle, t_s = 0, time.perf_counter()
-    while n_settle == 0 or time.perf_counter() - t_s < args.settle_seconds:
-        for _ in range(10):
-            step()
-        n_settle += 10
-        torch.cuda.synchronize()
-    settle_s = time.perf_counter() - t_s
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # the stage breakdown: the same steps again through moe_forward_staged,
-    # which records a HIP event at every stage boundary (the events cost
-    # time of their own, so the timed steps above run without them)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-
-    stage_ms = {name: 0.0 for name in L.STAGES}
-    for i in range(args.steps):
-        ev = events[i * nev:(i + 1) * nev]
-        for j, name in enumerate(L.STAGES):
-            stage_ms[name] += hip.elapsed_ms(ev[j], ev[j + 1]) / args.steps
-    hip.destroy(events)
-
-    # per-step spread (warm): one HIP event between consecutive forwards, so
-    # each interval holds one forward and one event record (~4.5 us)
-    step_ev = hip.create(args.steps + 1)
-    hip.record(step_ev[0], stream.cuda_stream)
-    for i in range(args.steps):
-        step()
-        hip.record(step_ev[i + 1], stream.cuda_stream)
-    torch.cuda.synchronize()
-    warm_ms = [hip.elapsed_ms(step_ev[i], step_ev[i + 1]) for i in range(args.steps)]
-    hip.destroy(step_ev)
-    # cold last-level cache: 512 MB of scratch written before each timed forward
-    n_cold = min(args.steps, 10)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold_ev = hip.create(2 * n_cold)
-    for i in range(n_cold):
-        scratch.fill_(i & 0xFF)
-        hip.record(cold_ev[2 * i], stream.cuda_stream)
-        step()
-        hip.record(cold_ev[2 * i + 1], stream.cuda_stream)
-    torch.cuda.synchronize()
-    cold_ms = [hip.elapsed_ms(cold_ev[2 * i], cold_ev[2 * i + 1]) for i in range(n_cold)]
-    hip.destroy(cold_ev)
-    del scratch
-
-    def spread(v):
-        q = np.percentile(np.asarray(v, dtype=np.float64), [50, 10, 90])
-        return dict(median=round(float(q[0]), 4), p10=round(float(q[1]), 4), p90=round(float(q[2]), 4),
-                    n=len(v), tokens_per_s=round(cfg["T"] / (float(q[0]) / 1e3), 1))
-
-    A = int(plan.intermediate("expert_count").sum().item())
-    drops = int(plan.drop_mask.sum().item())
-    work = stage_work(cfg, A)
+    W = Workload(args.workload, torch, moe, dev)
+    cfg = W.cfg
+    print(f"[bench] {cfg['name']}: {args.steps} cold-cache steps", file=sys.stderr, flush=True)
+    m = measure(W, torch, L, hip, args.steps, args.warmup, args.settle_seconds, flush)
+    stages, roofline = stage_report(W, m, L)
     # the standalone dispatch (slots + permutation into xbuf), timed on its
-    # own outside the steps: the forward itself gathers rows inside the first
-    # GEMM when it can, so it has no permutation to time
-    n_disp = 10
-    disp_ev = hip.create(2)
-    moe.dispatch(x, plan.expert_idx, cfg["E"], plan.C)
-    hip.record(disp_ev[0], stream.cuda_stream)
-    for _ in range(n_disp):
-        moe.dispatch(x, plan.expert_idx, cfg["E"], plan.C)
-    hip.record(disp_ev[1], stream.cuda_stream)
-    torch.cuda.synchronize()
-    disp_s = hip.elapsed_ms(disp_ev[0], disp_ev[1]) / n_disp / 1e3
-    hip.destroy(disp_ev)
-    disp_bytes = 2 * A * cfg["d"] * (2 if cfg["dtype"] == "bf16" else 4) + cfg["T"] * cfg["k"] * 9
-    # the noisy top-k router variant, timed on its own outside the steps:
-    # the same tokens and W_r, seeded W_noise and standard normal draws
-    variants = {}
-    if args.noisy_calls > 0:
-        rng = np.random.default_rng(1)
-        W_n = todev((rng.standard_normal((cfg["E"], cfg["d"])) * np.sqrt(0.1 / cfg["d"])).astype(np.float32))
-        eps = todev(rng.standard_normal((cfg["T"], cfg["E"])).astype(np.float32))
-        rws = torch.empty(L.LIB.moe_router_workspace_bytes(cfg["T"], cfg["d"], cfg["E"], cfg["k"]), dtype=torch.uint8,
-                          device=dev)
-        moe.router(x, W_r, k=cfg["k"], b_r=b_r, workspace=rws, z_loss=True, W_noise=W_n, noise=eps)
-        nz_ev = hip.create(2)
-        hip.record(nz_ev[0], stream.cuda_stream)
-        for _ in range(args.noisy_calls):
-            moe.router(x, W_r, k=cfg["k"], b_r=b_r, workspace=rws, z_loss=True, W_noise=W_n, noise=eps)
-        hip.record(nz_ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        nz_s = hip.elapsed_ms(nz_ev[0], nz_ev[1]) / args.noisy_calls / 1e3
-        hip.destroy(nz_ev)
-        nw = noisy_router_work(cfg)
-        variants["noisy_router"] = dict(us=round(nz_s * 1e6, 2), bytes=nw["bytes"], flops=nw["flops"],
-                                        calls=args.noisy_calls, **roofline_of(nw, nz_s))
-        del W_n, eps, rws
-    # priority routing: the plain dispatch's work with the capacity filled in
-    # descending first-gate order, timed on its own like the dispatch above
-    if args.priority_calls > 0:
-        pr = plan.gate[:, 0].contiguous()
-        pws = torch.empty(L.LIB.moe_dispatch_priority_workspace_bytes(cfg["T"], cfg["E"], cfg["k"]),
-                          dtype=torch.uint8, device=dev)
-        moe.dispatch_priority(x, plan.expert_idx, pr, cfg["E"], plan.C, workspace=pws)
-        pr_ev = hip.create(2)
-        hip.record(pr_ev[0], stream.cuda_stream)
-        for _ in range(args.priority_calls):
-            moe.dispatch_priority(x, plan.expert_idx, pr, cfg["E"], plan.C, workspace=pws)
-        hip.record(pr_ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        pr_s = hip.elapsed_ms(pr_ev[0], pr_ev[1]) / args.priority_calls / 1e3
-        hip.destroy(pr_ev)
-        A_pr = int(moe.dispatch_priority(x, plan.expert_idx, pr, cfg["E"], plan.C, workspace=pws)[2].sum().item())
-        pw = dict(bytes=2 * A_pr * cfg["d"] * (2 if cfg["dtype"] == "bf16" else 4) + cfg["T"] * cfg["k"] * 9
-                  + cfg["T"] * 4, flops=0, dtype=cfg["dtype"])
-        variants["priority_dispatch"] = dict(us=round(pr_s * 1e6, 2), bytes=pw["bytes"], kept=A_pr,
-                                             calls=args.priority_calls, **roofline_of(pw, pr_s))
-        del pws
-    # the gate-side backward (combine backward, then router backward through
-    # the gates, the balance loss and the z-loss), on the split API's forward
-    # buffers, timed on its own
-    if args.backward_calls > 0:
-        idx_b, gate_b, _, rc_b, lg_b = moe.router(x, W_r, k=cfg["k"], b_r=b_r, logits=True)
-        slot_b, _, cnt_b, xbuf_b = moe.dispatch(x, idx_b, cfg["E"], plan.C)
-        ybuf_b = moe.expert_ffn(xbuf_b, cnt_b, W1, W2, W3=W3, b1=b1, b2=b2, act=cfg["act"])
-        del xbuf_b
-        dy_b = torch.randn((cfg["T"], cfg["d"]), device=dev).to(x.dtype)
-        dyb_b = torch.zeros_like(ybuf_b)
-        bws = torch.empty(max(L.LIB.moe_router_backward_workspace_bytes(cfg["T"], cfg["d"], cfg["E"]), 256),
-                          dtype=torch.uint8, device=dev)
-
-        def gate_backward():
-            dg, _ = moe.combine_backward(dy_b, ybuf_b, idx_b, slot_b, gate_b, dybuf=dyb_b)
-            moe.router_backward(x, W_r, lg_b, idx_b, gate_b, dg, rc_b, alpha=cfg["alpha"], z_weight=1e-3,
-                                workspace=bws)
-        gate_backward()
-        bw_ev = hip.create(2)
-        hip.record(bw_ev[0], stream.cuda_stream)
-        for _ in range(args.backward_calls):
-            gate_backward()
-        hip.record(bw_ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        bw_s = hip.elapsed_ms(bw_ev[0], bw_ev[1]) / args.backward_calls / 1e3
-        hip.destroy(bw_ev)
-        A_b = int(cnt_b.sum().item())
-        T_, d_, E_, k_ = cfg["T"], cfg["d"], cfg["E"], cfg["k"]
-        s_ = 2 if cfg["dtype"] == "bf16" else 4
-        bw = dict(bytes=3 * A_b * d_ * s_ + 16 * T_ * k_ + 8 * T_ * E_ + T_ * d_ * (s_ + 4) + 8 * E_ * d_
-                  + 12 * T_ * k_, flops=4 * T_ * E_ * d_, dtype="f32")
-        variants["gate_backward"] = dict(us=round(bw_s * 1e6, 2), bytes=bw["bytes"], flops=bw["flops"],
-                                         calls=args.backward_calls, **roofline_of(bw, bw_s))
-        del ybuf_b, dyb_b, bws
-    # re-routing of the overflow: the router's top min(4, E) as preferences,
-    # as many stages, the even-split capacity, gates from the logits
-    if args.reroute_calls > 0:
-        R_ = min(4, cfg["E"])
-        idx_r, _, _, _, lg_r = moe.router(x, W_r, k=R_, b_r=b_r, logits=True)
-        C1 = moe.capacity(cfg["T"], cfg["E"], 1, 1.0)
-        rrws = torch.empty(max(L.LIB.moe_dispatch_reroute_workspace_bytes(cfg["T"], cfg["E"]), 256),
-                           dtype=torch.uint8, device=dev)
-        out_r = moe.dispatch_reroute(x, idx_r, cfg["E"], C1, R_, logits=lg_r, workspace=rrws)
-        rr_ev = hip.create(2)
-        hip.record(rr_ev[0], stream.cuda_stream)
-        for _ in range(args.reroute_calls):
-            moe.dispatch_reroute(x, idx_r, cfg["E"], C1, R_, logits=lg_r, workspace=rrws)
-        hip.record(rr_ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        rr_s = hip.elapsed_ms(rr_ev[0], rr_ev[1]) / args.reroute_calls / 1e3
-        hip.destroy(rr_ev)
-        A_r = int(out_r[4].sum().item())
-        s_ = 2 if cfg["dtype"] == "bf16" else 4
-        rw = dict(bytes=2 * A_r * cfg["d"] * s_ + cfg["T"] * (4 * R_ + 4 * cfg["E"] + 13), flops=0,
-                  dtype=cfg["dtype"])
-        variants["reroute_dispatch"] = dict(us=round(rr_s * 1e6, 2), bytes=rw["bytes"], kept=A_r, stages=R_,
-                                            capacity=C1, calls=args.reroute_calls, **roofline_of(rw, rr_s))
-        del rrws, out_r
-    stages = {}
-    for name in L.STAGES:
-        r = roofline_of(work[name], stage_ms[name] / 1e3)
-        stages[name] = dict(us=round(stage_ms[name] * 1e3, 2), bytes=work[name]["bytes"],
-                            flops=work[name]["flops"], **r)
-    dominant = max(L.STAGES, key=lambda n: stage_ms[n])
-    dom = dict(stages[dominant])
-    traffic, traffic_src = committed_traffic(cfg["name"], dominant)
-    roofline = dict(bound=dom["bound"], achieved=dom["achieved"], peak=dom["peak"], unit=dom["unit"],
-                    frac=dom["frac"], traffic=traffic, traffic_unit="bytes/launch",
-                    traffic_source=traffic_src, kernel=dominant,
-                    algorithmic_bytes=work[dominant]["bytes"], algorithmic_flops=work[dominant]["flops"],
-                    avg_us=dom["us"])
-    ffn_s = (stage_ms["expert_gemm1"] + stage_ms["expert_gemm2"]) / 1e3
-    ffn_flops = work["expert_gemm1"]["flops"] + work["expert_gemm2"]["flops"]
-    peak = PEAK_TFLOPS[cfg["dtype"]]
-    ms_per_step = elapsed / args.steps * 1e3
+    # own: the fused forward gathers rows inside the first GEMM when it can,
+    # so it has no permutation to time
+    disp_s = time_calls(hip, W.stream.cuda_stream, torch,
+                        lambda: moe.dispatch(W.x, W.plan.expert_idx, cfg["E"], W.plan.C), 10)
+    disp_bytes = 2 * m["A"] * cfg["d"] * (2 if cfg["dtype"] == "bf16" else 4) + cfg["T"] * cfg["k"] * 9
+    variants = measure_variants(W, torch, moe, L, hip, args)
+    mean_ms = float(np.mean(m["cold_ms"]))
     out = {
         "metric": METRIC,
-        "value": round(cfg["T"] * args.steps / elapsed, 1),
+        "value": round(m["value"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(mean_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -641,19 +654,46 @@ def main(argv=None):
         "data": "synthetic (seeded, LayerNorm(N(0,1)) tokens, truncated-normal sigma=sqrt(0.1/fan_in) weights)",
         "config": {"workload": cfg["name"], "T": cfg["T"], "d_model": cfg["d"], "d_ff": cfg["f"],
                    "experts": cfg["E"], "k": cfg["k"], "capacity_factor": cfg["cf"],
-                   "capacity": plan.C, "act": cfg["act"], "router": "fp32",
-                   "kept_assignments": A, "dropped": drops},
-        "grouped_gemm_mfma_pct": round(100.0 * ffn_flops / ffn_s / 1e12 / peak, 2),
+                   "capacity": W.plan.C, "act": cfg["act"], "router": "fp32",
+                   "kept_assignments": m["A"], "dropped": m["drops"]},
+        "timing": "value = T x steps / the summed HIP-event time of the steps; each step is one whole "
+                  "forward on inputs resident in HBM, started with the 256 MB last-level cache flushed "
+                  "(512 MB of scratch written before it, outside its interval)",
+        "warm_tokens_per_s": round(m["warm_value"], 1),
+        "timed_wall_s": round(m["wall_s"], 4),
+        "grouped_gemm_mfma_pct": ffn_mfma_pct(W, m),
         "permute_GBps": round(disp_bytes / disp_s / 1e9, 1),
         "permute_us": round(disp_s * 1e6, 2),
         "stages": stages,
         "variants": variants,
-        "settle": {"seconds": round(settle_s, 3), "forwards": n_settle},
-        "step_ms": {"warm": spread(warm_ms), "cold_mall": spread(cold_ms),
-                    "note": "per-forward HIP event intervals (each holds one event record, "
-                            "about 4.5 us); cold_mall writes 512 MB of scratch before each forward"},
+        "settle": m["settle"],
+        "step_ms": {"cold_mall": _spread(m["cold_ms"], cfg["T"])},
         "roofline": roofline,
     }
+    # the other workloads: tokens/s and the dominant kernel's roofline of each
+    if args.others:
+        table = {cfg["name"]: dict(tokens_per_s=out["value"], warm_tokens_per_s=out["warm_tokens_per_s"],
+                                   ms_per_step=out["ms_per_step"], roofline=roofline,
+                                   grouped_gemm_mfma_pct=out["grouped_gemm_mfma_pct"],
+                                   stages_us={k_: v["us"] for k_, v in stages.items()})}
+        host_cfg = cfg
+        del W
+        torch.cuda.empty_cache()
+        for name in datagen.CONFIG_ORDER:
+            if name in table:
+                continue
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            Wo = Workload(name, torch, moe, dev)
+            mo = measure(Wo, torch, L, hip, min(args.steps, 20), 3, args.settle_seconds, flush)
+            st_o, rf_o = stage_report(Wo, mo, L)
+            table[name] = dict(tokens_per_s=round(mo["value"], 1), warm_tokens_per_s=round(mo["warm_value"], 1),
+                               ms_per_step=round(float(np.mean(mo["cold_ms"])), 4), roofline=rf_o,
+                               grouped_gemm_mfma_pct=ffn_mfma_pct(Wo, mo),
+                               stages_us={k_: v["us"] for k_, v in st_o.items()})
+            del Wo
+            torch.cuda.empty_cache()
+        out["workloads"] = {n: table[n] for n in datagen.CONFIG_ORDER if n in table}
+        cfg = host_cfg
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     else:
