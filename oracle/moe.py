@@ -27,9 +27,12 @@ import numpy as np
 # ---------------------------------------------------------------------------
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage values as float64 (bf16 patterns are the top 16 bits of fp32)."""
+    """Storage values as float64 (bf16 patterns are the top 16 bits of fp32;
+    "f64" takes float64 inputs as they are, for the finite-difference pins)."""
     if a is None:
         return None
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     if dtype == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
@@ -474,6 +477,118 @@ def router_backward(x64: np.ndarray, W_r: np.ndarray, z: np.ndarray, idx: np.nda
     db = dz.sum(axis=0)
     dx = dz @ np.asarray(W_r, dtype=np.float64)
     return dz, dW, db, dx
+
+
+# ---------------------------------------------------------------------------
+# O12 backward of the expert side: the expert FFN and the dispatch
+# ---------------------------------------------------------------------------
+
+def silu_grad(a):
+    """d/da of a sigmoid(a): sigmoid(a) (1 + a (1 - sigmoid(a)))."""
+    sg = 1.0 / (1.0 + np.exp(-a))
+    return sg * (1.0 + a * (1.0 - sg))
+
+
+def expert_ffn_backward(u: np.ndarray, W1: np.ndarray, W2: np.ndarray, act: str, dout: np.ndarray,
+                        b1: np.ndarray | None = None, W3: np.ndarray | None = None):
+    """Gradients of one expert applied to the rows u, given dL/d(output) `dout`.
+
+    The expert is expert_ffn: ReLU y = W_2 relu(W_1 x + b) + c, or SwiGLU
+    y = W_2 (silu(W x) * (V x)) ([SW-GLaM] "Dense Scaling 与 MoE 的核心差异";
+    [CMU-L16] sections 2.1 and 2.3).  [CMU-L16] exercise 2 and section 5:
+    each expert is an ordinary FFN on the rows routed to it, so its backward
+    is the chain rule through the two matrix products and the activation,
+    with the hidden pre-activations recomputed from u:
+      dH = dout W2;  dW2 = dout^T H;  db2 = sum over rows of dout;
+      ReLU:   dA = dH * 1[A > 0];  dW1 = dA^T u;  db1 = sum of dA;  du = dA W1
+      SwiGLU: dA = dH * G * silu'(A), dG = dH * silu(A);
+              dW1 = dA^T u, dW3 = dG^T u;  du = dA W1 + dG W3
+    (A = W1 u + b1, G = W3 u; at A = 0 the ReLU derivative is taken as 0).
+    All in float64.  Returns a dict with du [rows, d], dW1 [f, d], dW2 [d, f],
+    dW3 [f, d] or None, db1 [f] and db2 [d] (zero when the expert has no bias).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    W1 = np.asarray(W1, dtype=np.float64)
+    W2 = np.asarray(W2, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    a = u @ W1.T
+    if b1 is not None:
+        a = a + np.asarray(b1, dtype=np.float64)[None, :]
+    dH = dout @ W2
+    out = dict(dW3=None, db2=dout.sum(axis=0))
+    if act == "relu":
+        h = relu(a)
+        dA = dH * (a > 0)
+        out["du"] = dA @ W1
+    elif act == "swiglu":
+        W3 = np.asarray(W3, dtype=np.float64)
+        g = u @ W3.T
+        h = silu(a) * g
+        dA = dH * g * silu_grad(a)
+        dG = dH * silu(a)
+        out["dW3"] = dG.T @ u
+        out["du"] = dA @ W1 + dG @ W3
+    else:
+        raise ValueError(act)
+    out["dW2"] = dout.T @ h
+    out["dW1"] = dA.T @ u
+    out["db1"] = dA.sum(axis=0)
+    return out
+
+
+def experts_backward(x64, idx, slot, E, C, W1, W2, act, dybuf, b1=None, W3=None, dtype="f32"):
+    """expert_ffn_backward for every expert over its kept rows in slot order.
+
+    dybuf [E, C, d]: dL/d(expert output) of every kept (expert, slot) row
+    (moe_combine_backward's output: gate times dL/dy of the row's token).
+    Returns dxbuf [E, C, d] (rows at or beyond an expert's count are zero),
+    dW1, dW2, dW3 (or None), db1 [E, f], db2 [E, d], all float64.
+    """
+    T, k = idx.shape
+    d = x64.shape[1]
+    f = np.asarray(W1).shape[1]
+    dxbuf = np.zeros((E, C, d))
+    g = dict(dW1=np.zeros((E, f, d)), dW2=np.zeros((E, d, f)),
+             dW3=None if W3 is None else np.zeros((E, f, d)), db1=np.zeros((E, f)), db2=np.zeros((E, d)))
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & (slot >= 0))
+        if tt.size == 0:
+            continue
+        order = np.argsort(slot[tt, jj], kind="stable")
+        tt, jj = tt[order], jj[order]
+        sl = slot[tt, jj]
+        r = expert_ffn_backward(x64[tt], widen(W1[e], dtype), widen(W2[e], dtype), act,
+                                np.asarray(dybuf[e, sl], dtype=np.float64),
+                                None if b1 is None else widen(b1[e], dtype),
+                                None if W3 is None else widen(W3[e], dtype))
+        dxbuf[e, sl] = r["du"]
+        for name in ("dW1", "dW2", "db1", "db2"):
+            g[name][e] = r[name]
+        if W3 is not None:
+            g["dW3"][e] = r["dW3"]
+    g["dxbuf"] = dxbuf
+    return g
+
+
+def dispatch_backward(dxbuf: np.ndarray, idx: np.ndarray, slot: np.ndarray, dx_add=None) -> np.ndarray:
+    """The adjoint of the dispatch: dx_t = sum over kept choices (t, j) of
+    dxbuf[e_tj, slot_tj] (+ dx_add_t), float64.
+
+    The dispatch copies x_t to row slot_tj of expert e_tj for each kept
+    choice ([SW-GLaM] "All-to-All": tokens travel to their experts and the
+    results travel back); its transpose gathers those rows back and adds them
+    per token.  A dropped choice received no copy and returns nothing (the
+    token's residual path carries it, [CS25-L5] "Capacity Factor").
+    dx_add is the router's share of dx (router_backward), added here.
+    """
+    T, k = idx.shape
+    d = dxbuf.shape[2]
+    dx = np.zeros((T, d)) if dx_add is None else np.array(dx_add, dtype=np.float64)
+    for j in range(k):
+        keep = slot[:, j] >= 0
+        tt = np.nonzero(keep)[0]
+        dx[tt] += dxbuf[idx[tt, j], slot[tt, j]]
+    return dx
 
 
 # ---------------------------------------------------------------------------

@@ -1102,3 +1102,243 @@ def test_planted_near_tie_mistake_is_caught(monkeypatch, repl):
     monkeypatch.setattr(O, "near_tie_tokens", repl)
     with pytest.raises(AssertionError):
         check_near_tie_table()
+
+
+# ---------------------------------------------------------------------------
+# expert-side backward: the expert FFN and the dispatch ([CMU-L16] exercise 2,
+# section 5: each expert is an ordinary FFN on its routed rows)
+# ---------------------------------------------------------------------------
+
+def _expert_case(act, bias, seed=3, rows=5, d=6, f=7):
+    rng = np.random.default_rng(seed)
+    c = dict(u=rng.normal(size=(rows, d)), W1=rng.normal(size=(f, d)) * 0.5, W2=rng.normal(size=(d, f)) * 0.5,
+             W3=rng.normal(size=(f, d)) * 0.5 if act == "swiglu" else None,
+             b1=rng.normal(size=f) * 0.3 if bias else None, b2=rng.normal(size=d) * 0.3 if bias else None,
+             dout=rng.normal(size=(rows, d)))
+    return c
+
+
+def check_expert_backward_finite_differences(act, bias):
+    """Central differences of the oracle's own expert forward (float64, h = 1e-6)
+    for every entry of u, W1, W2, W3, b1 and b2."""
+    c = _expert_case(act, bias)
+
+    def loss(**over):
+        a = dict(c)
+        a.update(over)
+        o = O.expert_ffn(a["u"], a["W1"], a["W2"], act, b1=a["b1"], b2=a["b2"], W3=a["W3"])
+        return float(np.sum(o * c["dout"]))
+
+    # keep every pre-activation away from the ReLU kink, where no derivative exists
+    a0 = c["u"] @ c["W1"].T + (0 if c["b1"] is None else c["b1"])
+    assert np.min(np.abs(a0)) > 1e-3
+    g = O.expert_ffn_backward(c["u"], c["W1"], c["W2"], act, c["dout"], b1=c["b1"], W3=c["W3"])
+    want = dict(u="du", W1="dW1", W2="dW2", W3="dW3", b1="db1", b2="db2")
+    h = 1e-6
+    for name, gname in want.items():
+        if c[name] is None:
+            continue
+        base = c[name]
+        num = np.zeros_like(base)
+        for i in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[i] += h
+            m[i] -= h
+            num[i] = (loss(**{name: p}) - loss(**{name: m})) / (2 * h)
+        assert np.allclose(g[gname], num, rtol=1e-6, atol=1e-7), (name, np.max(np.abs(g[gname] - num)))
+
+
+@pytest.mark.parametrize("act,bias", [("relu", True), ("relu", False), ("swiglu", False)])
+def test_expert_backward_finite_differences(act, bias):
+    check_expert_backward_finite_differences(act, bias)
+
+
+@pytest.mark.parametrize("act,bias", [("relu", True), ("swiglu", False)])
+def test_expert_backward_matches_autograd(act, bias):
+    """torch.autograd in float64 on the same FFN (a library's differentiation, independent
+    of the hand-derived chain rule), on a wider case."""
+    import torch
+    c = _expert_case(act, bias, seed=9, rows=40, d=24, f=56)
+    t = {k: (None if v is None else torch.tensor(v, dtype=torch.float64, requires_grad=True))
+         for k, v in c.items() if k != "dout"}
+    a = t["u"] @ t["W1"].T + (t["b1"] if t["b1"] is not None else 0)
+    if act == "relu":
+        h = torch.relu(a)
+    else:
+        h = torch.nn.functional.silu(a) * (t["u"] @ t["W3"].T)
+    o = h @ t["W2"].T + (t["b2"] if t["b2"] is not None else 0)
+    names = [k for k in ("u", "W1", "W2", "W3", "b1", "b2") if t[k] is not None]
+    grads = torch.autograd.grad(o, [t[k] for k in names], grad_outputs=torch.tensor(c["dout"]))
+    g = O.expert_ffn_backward(c["u"], c["W1"], c["W2"], act, c["dout"], b1=c["b1"], W3=c["W3"])
+    for k, ref in zip(names, grads):
+        gname = {"u": "du"}.get(k, "d" + k)
+        np.testing.assert_allclose(g[gname], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _routing_case(seed=4, T=60, E=5, k=2, C=9):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    slot, drop, cnt = O.assign_slots(idx, E, C)
+    return rng, idx, slot, drop, cnt
+
+
+def check_dispatch_adjoint():
+    """<dispatch(x), dxbuf> = <x, dispatch_backward(dxbuf)> on the kept rows, with drops."""
+    rng, idx, slot, drop, cnt = _routing_case()
+    T, k = idx.shape
+    E, C, d = 5, 9, 3
+    assert drop.any() and (drop == 0).any()
+    x = rng.normal(size=(T, d))
+    dxbuf = rng.normal(size=(E, C, d))
+    xbuf = np.zeros((E, C, d))
+    for t in range(T):
+        for j in range(k):
+            if slot[t, j] >= 0:
+                xbuf[idx[t, j], slot[t, j]] = x[t]
+    # rows at or beyond an expert's count are never written by the dispatch and never read back
+    live = np.arange(C)[None, :] < cnt[:, None]
+    lhs = np.sum(xbuf * dxbuf * live[:, :, None])
+    rhs = np.sum(x * O.dispatch_backward(dxbuf, idx, slot))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (lhs, rhs)
+
+
+def check_dispatch_backward_brute():
+    """Token by token: dx_t = dx_add_t + the rows of its kept choices."""
+    rng, idx, slot, drop, cnt = _routing_case(seed=6, T=40, E=4, k=3, C=20)
+    dxbuf = rng.normal(size=(4, 20, 2))
+    add = rng.normal(size=(40, 2))
+    got = O.dispatch_backward(dxbuf, idx, slot, dx_add=add)
+    for t in range(40):
+        want = add[t].copy()
+        for j in range(3):
+            if drop[t, j] == 0:
+                want += dxbuf[idx[t, j], slot[t, j]]
+        assert np.allclose(got[t], want, rtol=0, atol=1e-15)
+
+
+def test_dispatch_adjoint():
+    check_dispatch_adjoint()
+
+
+def test_dispatch_backward_brute():
+    check_dispatch_backward_brute()
+
+
+_ORIG_EFB = O.expert_ffn_backward
+_ORIG_DB = O.dispatch_backward
+
+
+def _efb_mask_from_dH(u, W1, W2, act, dout, b1=None, W3=None):
+    """ReLU derivative gated by dH > 0 instead of A > 0."""
+    g = _ORIG_EFB(u, W1, W2, act, dout, b1=b1, W3=W3)
+    a = u @ W1.T + (0 if b1 is None else b1)
+    dH = dout @ W2
+    dA = dH * (dH > 0)
+    g.update(du=dA @ W1, dW1=dA.T @ u, db1=dA.sum(0))
+    return g
+
+
+def _efb_sigmoid_for_silu_grad(u, W1, W2, act, dout, b1=None, W3=None):
+    """SwiGLU with sigmoid(a) taken as the derivative of silu(a)."""
+    g = _ORIG_EFB(u, W1, W2, act, dout, b1=b1, W3=W3)
+    a = u @ W1.T
+    gg = u @ W3.T
+    dH = dout @ W2
+    dA = dH * gg / (1 + np.exp(-a))
+    dG = dH * O.silu(a)
+    g.update(du=dA @ W1 + dG @ W3, dW1=dA.T @ u)
+    return g
+
+
+def _efb_dW2_from_preactivation(u, W1, W2, act, dout, b1=None, W3=None):
+    """dW2 from the pre-activation A instead of the hidden activation H."""
+    g = _ORIG_EFB(u, W1, W2, act, dout, b1=b1, W3=W3)
+    g["dW2"] = dout.T @ (u @ W1.T + (0 if b1 is None else b1))
+    return g
+
+
+def _efb_no_dG_in_du(u, W1, W2, act, dout, b1=None, W3=None):
+    """SwiGLU du without the gate partner's path dG W3."""
+    g = _ORIG_EFB(u, W1, W2, act, dout, b1=b1, W3=W3)
+    a = u @ W1.T
+    dA = (dout @ W2) * (u @ W3.T) * O.silu_grad(a)
+    g["du"] = dA @ W1
+    return g
+
+
+def _db_keeps_dropped(dxbuf, idx, slot, dx_add=None):
+    """Dropped choices read row 0 of their expert instead of nothing."""
+    return _ORIG_DB(dxbuf, idx, np.maximum(slot, 0), dx_add)
+
+
+@pytest.mark.parametrize("repl,check", [
+    (_efb_mask_from_dH, lambda: check_expert_backward_finite_differences("relu", True)),
+    (_efb_sigmoid_for_silu_grad, lambda: check_expert_backward_finite_differences("swiglu", False)),
+    (_efb_dW2_from_preactivation, lambda: check_expert_backward_finite_differences("relu", False)),
+    (_efb_no_dG_in_du, lambda: check_expert_backward_finite_differences("swiglu", False)),
+])
+def test_planted_expert_backward_mistake_is_caught(monkeypatch, repl, check):
+    monkeypatch.setattr(O, "expert_ffn_backward", repl)
+    with pytest.raises(AssertionError):
+        check()
+
+
+def test_planted_dispatch_backward_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "dispatch_backward", _db_keeps_dropped)
+    with pytest.raises(AssertionError):
+        check_dispatch_adjoint()
+
+
+def check_layer_backward_finite_differences(act):
+    """The whole layer with the routing held fixed: L = <dy, y>, y = combine of the gated
+    expert outputs.  combine_backward -> experts_backward -> dispatch_backward must give the
+    central differences of L with respect to x, W1, W2 (and W3, b1, b2), drops included."""
+    rng = np.random.default_rng(12)
+    T, d, f, E, k, C = 14, 4, 5, 3, 2, 7
+    x = rng.normal(size=(T, d))
+    W1, W2 = rng.normal(size=(E, f, d)) * 0.5, rng.normal(size=(E, d, f)) * 0.5
+    W3 = rng.normal(size=(E, f, d)) * 0.5 if act == "swiglu" else None
+    b1 = rng.normal(size=(E, f)) * 0.3 if act == "relu" else None
+    b2 = rng.normal(size=(E, d)) * 0.3 if act == "relu" else None
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    slot, drop, _ = O.assign_slots(idx, E, C)
+    assert drop.any()
+    gate = rng.uniform(0.2, 0.8, size=(T, k))
+    dy = rng.normal(size=(T, d))
+
+    def loss(x_=x, W1_=W1, W2_=W2, W3_=W3, b1_=b1, b2_=b2):
+        _, out = O.experts_by_slot(x_, idx, slot, E, C, W1_, W2_, act, b1_, b2_, W3_, dtype="f64")
+        return float(np.sum(dy * O.combine(gate, drop, out)))
+
+    _, out = O.experts_by_slot(x, idx, slot, E, C, W1, W2, act, b1, b2, W3, dtype="f64")
+    _, dout = O.combine_backward(dy, gate, drop, out)
+    dybuf = np.zeros((E, C, d))
+    for t in range(T):
+        for j in range(k):
+            if slot[t, j] >= 0:
+                dybuf[idx[t, j], slot[t, j]] = dout[t, j]
+    g = O.experts_backward(x, idx, slot, E, C, W1, W2, act, dybuf, b1=b1, W3=W3, dtype="f64")
+    g["dx"] = O.dispatch_backward(g["dxbuf"], idx, slot)
+    h = 1e-6
+    for name, arr, gname in [("x_", x, "dx"), ("W1_", W1, "dW1"), ("W2_", W2, "dW2"), ("W3_", W3, "dW3"),
+                             ("b1_", b1, "db1"), ("b2_", b2, "db2")]:
+        if arr is None:
+            continue
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[i] += h
+            m[i] -= h
+            num[i] = (loss(**{name: p}) - loss(**{name: m})) / (2 * h)
+        assert np.allclose(g[gname], num, rtol=1e-6, atol=1e-7), (gname, np.max(np.abs(g[gname] - num)))
+
+
+@pytest.mark.parametrize("act", ["relu", "swiglu"])
+def test_layer_backward_finite_differences(act):
+    check_layer_backward_finite_differences(act)
+
+
+def test_planted_layer_backward_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "dispatch_backward", _db_keeps_dropped)
+    with pytest.raises(AssertionError):
+        check_layer_backward_finite_differences("relu")
