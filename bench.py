@@ -151,11 +151,14 @@ COPY_PROBE_BYTES = 1 << 30
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d {o}/ktrace -o k -- "
-    "python3 $REPO/bench.py --workload {w} --steps 10 --warmup 3 --cpu-seconds 0",
+    "python3 $REPO/bench.py --workload {w} --steps 10 --warmup 3 --cpu-seconds 0 --others 0 "
+    "--expert-backward-calls 0",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/fetch -o f -- "
-    "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0",
+    "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --others 0 "
+    "--expert-backward-calls 0",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/write -o w -- "
-    "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0",
+    "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --others 0 "
+    "--expert-backward-calls 0",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/copy_fetch -o c -- "
     "python3 $REPO/bench.py --copy-probe %d" % COPY_PROBE_BYTES,
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/copy_write -o c -- "
@@ -195,6 +198,9 @@ def kernel_stage(name: str) -> str:
     dispatch scan), so they form a stage of their own."""
     if "combine_backward" in name or "router_bwd" in name:
         return "gate_backward"
+    if any(t in name for t in ("transpose_kernel", "act_backward", "rowsum_kernel", "fill_i32", "zero16",
+                               "dispatch_backward")):
+        return "expert_backward"
     if _NOISY.search(name):
         return "noisy_router"
     if "router" in name:
@@ -552,6 +558,38 @@ def measure_variants(W: Workload, torch, moe, L, hip, args) -> dict:
         variants["gate_backward"] = dict(us=round(sec * 1e6, 2), bytes=bw["bytes"], flops=bw["flops"],
                                          calls=args.backward_calls, **roofline_of(bw, sec))
         del ybuf_b, dyb_b, bws
+    # the expert side of the backward: expert FFN backward (pre-activations
+    # recomputed, dgrad and wgrad) then the un-permute onto the router's dx
+    if args.expert_backward_calls > 0:
+        idx_e, gate_e, _, rc_e, lg_e = moe.router(x, W.W_r, k=k_, b_r=W.b_r, logits=True)
+        slot_e, _, cnt_e, xbuf_e = moe.dispatch(x, idx_e, E_, plan.C)
+        ybuf_e = moe.expert_ffn(xbuf_e, cnt_e, W.W1, W.W2, W3=W.W3, b1=W.b1, b2=W.b2, act=cfg["act"])
+        dy_e = (torch.randn((T_, d_), device=dev) * 0.02).to(x.dtype)
+        _, dyb_e = moe.combine_backward(dy_e, ybuf_e, idx_e, slot_e, gate_e)
+        del ybuf_e
+        f_ = cfg["f"]
+        ews = torch.empty(L.LIB.moe_expert_ffn_backward_workspace_bytes(E_, plan.C, d_, f_, 1 if s_ == 2 else 0,
+                                                                        1 if cfg["act"] == "swiglu" else 0),
+                          dtype=torch.uint8, device=dev)
+        dx_r = torch.zeros((T_, d_), dtype=torch.float32, device=dev)
+        dx_o = torch.empty_like(dx_r)
+
+        def expert_backward():
+            outs = moe.expert_ffn_backward(xbuf_e, cnt_e, W.W1, W.W2, dyb_e, W3=W.W3, b1=W.b1, act=cfg["act"],
+                                           bias_grads=W.b1 is not None, workspace=ews)
+            moe.dispatch_backward(outs[0], idx_e, slot_e, T_, dx_add=dx_r, dx=dx_o)
+        sec = time_calls(hip, sid, torch, expert_backward, args.expert_backward_calls)
+        A_e = int(cnt_e.sum().item())
+        m_ = 2 if cfg["act"] == "swiglu" else 1
+        # dgrad (dH, then dX through each first-layer weight) and wgrad (dW2,
+        # each first-layer weight): twice the forward's products; the
+        # recomputed pre-activations are extra work on top
+        ew = dict(bytes=2 * (m_ + 1) * E_ * d_ * f_ * s_ + 3 * A_e * d_ * s_ + 8 * T_ * d_,
+                  flops=2 * (2 * m_ + 2) * A_e * d_ * f_, dtype=cfg["dtype"])
+        variants["expert_backward"] = dict(us=round(sec * 1e6, 2), bytes=ew["bytes"], flops=ew["flops"],
+                                           recompute_flops=2 * m_ * A_e * d_ * f_, calls=args.expert_backward_calls,
+                                           **roofline_of(ew, sec))
+        del ews, xbuf_e, dyb_e, dx_r, dx_o
     # re-routing of the overflow: the router's top min(4, E) as preferences,
     # as many stages, the even-split capacity, gates from the logits
     if args.reroute_calls > 0:
@@ -591,6 +629,9 @@ def main(argv=None):
     ap.add_argument("--backward-calls", type=int, default=20,
                     help="gate-side backward calls (combine + router backward) timed after the steps "
                          "(0 skips them)")
+    ap.add_argument("--expert-backward-calls", type=int, default=5,
+                    help="expert-side backward calls (expert FFN backward + un-permute) timed after the "
+                         "steps (0 skips them)")
     ap.add_argument("--reroute-calls", type=int, default=20,
                     help="re-routing dispatch calls timed after the steps (0 skips them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",

@@ -303,6 +303,53 @@ moe_status moe_router_backward(const void *x, moe_dtype dt, const float *W_r, co
                                float *dx, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Expert FFN backward: the gradients of moe_expert_ffn given
+ * dybuf = dL/d(expert output) (moe_combine_backward's dybuf).  [CMU-L16]
+ * exercise 2 and section 5: each expert is an ordinary FFN on its routed
+ * rows, so the backward is the chain rule through both products and the
+ * activation, with the pre-activations A = W1 x + b1 (and G = W3 x)
+ * recomputed from xbuf:
+ *   dH = dY W2;  dW2 = dY^T H;  db2 = column sums of dY
+ *   ReLU:   dA = dH * 1[A > 0]                (the derivative at A = 0 is 0)
+ *   SwiGLU: dA = dH * G * silu'(A), dG = dH * silu(A)
+ *   dX = dA W1 (+ dG W3);  dW1 = dA^T X;  dW3 = dG^T X;  db1 = column sums of dA
+ *   xbuf, expert_count, W1, b1, W3, W2, act as moe_expert_ffn (the forward's
+ *     inputs; b2 does not enter the backward)
+ *   dybuf [E, C, d] in, rows < expert_count[e] read
+ *   dxbuf [E, C, d] out, rows < expert_count[e] written (dL/d(expert input))
+ *   dW1, dW3 [E, dff, d], dW2 [E, d, dff] out (dW3 exactly when W3 is given)
+ *   db1 [E, dff], db2 [E, d] out or NULL (ReLU only)
+ * Outputs in the storage dtype; sums in fp32; A, G, H, dH, dA and dG are
+ * rounded to the storage dtype in between, as the forward rounds H.
+ * ws: moe_expert_ffn_backward_workspace_bytes(E, C, d, dff, dt, act) bytes
+ * (the transposed weights, the recomputed activations and their transposes).
+ */
+size_t moe_expert_ffn_backward_workspace_bytes(int32_t E, int64_t C, int32_t d, int32_t dff, moe_dtype dt,
+                                              moe_act act);
+moe_status moe_expert_ffn_backward(const void *xbuf, moe_dtype dt, const int32_t *expert_count, int32_t E,
+                                   int64_t C, int32_t d, int32_t dff, const void *W1, const void *b1,
+                                   const void *W3, const void *W2, moe_act act, const void *dybuf, void *dxbuf,
+                                   void *dW1, void *dW3, void *dW2, void *db1, void *db2, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch backward (the un-permute of the gradients): the adjoint of
+ * moe_dispatch's copy.  The dispatch sent x_t to row slot[t, j] of expert
+ * expert_idx[t, j] for every kept choice ([SW-GLaM] "All-to-All"); its
+ * transpose gathers those rows back and adds them per token:
+ *   dx_t = dx_add_t + sum over kept j (rank order) of dxbuf[e_tj, slot_tj]
+ * in fp32; a dropped choice adds nothing (the token's residual path carries
+ * its gradient).
+ *   dxbuf [E, C, d] in (storage dtype; moe_expert_ffn_backward's dxbuf)
+ *   expert_idx, slot [T, k] as moe_combine
+ *   dx_add [T, d] fp32 in or NULL (moe_router_backward's dx, the router's share)
+ *   dx [T, d] fp32 out (may be dx_add itself)
+ */
+moe_status moe_dispatch_backward(const void *dxbuf, moe_dtype dt, const int32_t *expert_idx, const int32_t *slot,
+                                 int64_t T, int32_t d, int32_t E, int32_t k, int64_t C, const float *dx_add,
+                                 float *dx, hipStream_t stream);
+
+/*
  * Experts: every expert's FFN on its kept rows, as grouped GEMMs.
  * ReLU expert y = W_2 relu(W_1 x + b_1) + b_2 ([SW-GLaM] FFN equation;
  * [CMU-L16] section 2.1); SwiGLU expert y = W_2 (silu(W_1 x) * (W_3 x))

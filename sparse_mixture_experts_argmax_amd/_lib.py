@@ -55,6 +55,10 @@ SIGNATURES = {
                                                C.c_int, C.POINTER(WsLayout)]),
     "moe_router": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p,
                              _p, _p, _p, _sz, _p]),
+    "moe_expert_ffn_backward_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, C.c_int, C.c_int]),
+    "moe_expert_ffn_backward": (C.c_int, [_p, C.c_int, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p, C.c_int,
+                                          _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_dispatch_backward": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
     "moe_router_noalloc": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p,
                                      _p, _p, _p]),
     "moe_router_noalloc_scratch_bytes": (_sz, []),

@@ -336,6 +336,60 @@ def expert_ffn(xbuf, expert_count, W1, W2, *, W3=None, b1=None, b2=None, act="re
     return ybuf
 
 
+def expert_ffn_backward(xbuf, expert_count, W1, W2, dybuf, *, W3=None, b1=None, act="relu", bias_grads=False,
+                        workspace=None):
+    """Expert FFN backward: returns (dxbuf [E, C, d], dW1, dW3 or None, dW2, db1, db2), the weight
+    gradients in the weights' layouts and dtype; db1 [E, dff] and db2 [E, d] only with
+    bias_grads=True (ReLU), else None.  dxbuf rows >= expert_count[e] are left unwritten."""
+    if xbuf.dim() != 3 or W1.dim() != 3:
+        raise ValueError("xbuf must be [E, C, d] and W1 [E, dff, d]")
+    E, C, d = xbuf.shape
+    dff = W1.shape[1]
+    dev = xbuf.device
+    _dtype_code(xbuf)
+    _expect(expert_count, "expert_count", (E,), torch.int32)
+    _experts(E, d, dff, xbuf.dtype, W1, W2, W3, b1)
+    _expect(dybuf, "dybuf", (E, C, d), xbuf.dtype)
+    if act == "swiglu" and W3 is None:
+        raise ValueError("the SwiGLU expert needs W3")
+    if act == "swiglu" and bias_grads:
+        raise ValueError("the SwiGLU expert has no biases")
+    dxbuf = torch.empty_like(xbuf)
+    dW1 = torch.empty_like(W1)
+    dW2 = torch.empty_like(W2)
+    dW3 = torch.empty_like(W3) if W3 is not None else None
+    db1 = torch.empty((E, dff), dtype=xbuf.dtype, device=dev) if bias_grads else None
+    db2 = torch.empty((E, d), dtype=xbuf.dtype, device=dev) if bias_grads else None
+    need = L.LIB.moe_expert_ffn_backward_workspace_bytes(E, C, d, dff, _dtype_code(xbuf), _ACT[act])
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid expert sizes")
+    ws = _ws(workspace, need, dev)
+    L.check("moe_expert_ffn_backward", L.LIB.moe_expert_ffn_backward(
+        _ptr(xbuf), _dtype_code(xbuf), _ptr(expert_count), E, C, d, dff, _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2),
+        _ACT[act], _ptr(dybuf), _ptr(dxbuf), _ptr(dW1), _ptr(dW3), _ptr(dW2), _ptr(db1), _ptr(db2), _ptr(ws),
+        ws.numel(), _stream(dev)))
+    return dxbuf, dW1, dW3, dW2, db1, db2
+
+
+def dispatch_backward(dxbuf, expert_idx, slot, T: int, dx_add=None, dx=None):
+    """Dispatch backward (un-permute): dx [T, d] fp32 = dx_add + the kept rows of dxbuf per token."""
+    if dxbuf.dim() != 3:
+        raise ValueError(f"dxbuf must be [E, C, d], got {list(dxbuf.shape)}")
+    E, C, d = dxbuf.shape
+    k = _routing(expert_idx, T)
+    dev = dxbuf.device
+    _dtype_code(dxbuf)
+    _expect(slot, "slot", (T, k), torch.int32)
+    _expect(dx_add, "dx_add", (T, d), torch.float32, optional=True)
+    _expect(dx, "dx", (T, d), torch.float32, optional=True)
+    if dx is None:
+        dx = torch.empty((T, d), dtype=torch.float32, device=dev)
+    L.check("moe_dispatch_backward", L.LIB.moe_dispatch_backward(
+        _ptr(dxbuf), _dtype_code(dxbuf), _ptr(expert_idx), _ptr(slot), T, d, E, k, C, _ptr(dx_add), _ptr(dx),
+        _stream(dev)))
+    return dx
+
+
 def combine(ybuf, expert_idx, slot, gate, prob_sum, route_count, T: int, alpha: float = 1e-2):
     """Combine and aux loss: returns (y [T, d], aux_loss [1] fp32)."""
     if ybuf.dim() != 3:

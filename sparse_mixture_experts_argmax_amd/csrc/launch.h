@@ -137,6 +137,29 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
                                const int32_t *row_tok = nullptr, int64_t T = 0,
                                const float *row_gate = nullptr);
 
+// ---- expert-side backward (expert_backward.hip) ----------------------------
+// Byte offsets of the backward's scratch inside one workspace: tile maps and
+// constant row counts, the recomputed pre-activations A (and G), dH, [dA | dG],
+// the transposed weights W2t [E, f, d] and W13t [E, d, f (+ f)], and the
+// transposed activations dYt, Xt [E, d, Cp], Ht, dAt (, dGt) [E, f, Cp],
+// Cp = C rounded up to 64.
+struct ExpertBwdWs {
+    size_t tmap_r, tmap_d, tmap_f, cnt_d, cnt_f, a, g, dh, dag, w2t, w13t, dyt, xt, ht, dat, dgt, total;
+};
+ExpertBwdWs expert_backward_ws(int E, int64_t C, int d, int f, int dtype_bf16, int act);
+// The gradients of the grouped expert FFN (act 1 ReLU, 2 SwiGLU) given dybuf
+// = dL/d(expert output) [E, C, d]: dxbuf [E, C, d] (kept rows), dW1, dW3
+// (SwiGLU), dW2 in the weights' layouts, db1 [E, f] and db2 [E, d] (may be
+// null), all in the storage dtype.  ws holds expert_backward_ws(...).total bytes.
+hipError_t launch_expert_backward(const void *xbuf, int dtype_bf16, const int32_t *expert_count, int E, int64_t C,
+                                  int d, int f, const void *W1, const void *b1, const void *W3, const void *W2,
+                                  int act, const void *dybuf, void *dxbuf, void *dW1, void *dW3, void *dW2,
+                                  void *db1, void *db2, char *ws, hipStream_t s);
+// dx [T, d] fp32 = dx_add (may be null) + the kept rows of dxbuf, per token.
+hipError_t launch_dispatch_backward(const void *dxbuf, int dtype_bf16, const int32_t *expert_idx, const int32_t *slot,
+                                    int64_t T, int d, int E, int k, int64_t C, const float *dx_add, float *dx,
+                                    hipStream_t s);
+
 // ---- combine ----------------------------------------------------------
 hipError_t launch_combine(const void *ybuf, int dtype_bf16, const int32_t *expert_idx,
                           const int32_t *slot, const float *gate, const float *prob_sum,

@@ -567,6 +567,57 @@ moe_status moe_expert_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_
                    (int64_t)E * C, static_cast<char *>(ws), stream);
 }
 
+size_t moe_expert_ffn_backward_workspace_bytes(int32_t E, int64_t C, int32_t d, int32_t dff, moe_dtype dt,
+                                              moe_act act) {
+    if (E < 1 || E > MAX_E || C < 0 || check_width(d) != MOE_OK || check_width(dff) != MOE_OK ||
+        !dtype_ok(dt) || !act_ok(act))
+        return SIZE_MAX;
+    return moe::expert_backward_ws(E, C, d, dff, dt == MOE_BF16, act == MOE_ACT_SWIGLU ? 2 : 1).total;
+}
+
+moe_status moe_expert_ffn_backward(const void *xbuf, moe_dtype dt, const int32_t *expert_count, int32_t E,
+                                   int64_t C, int32_t d, int32_t dff, const void *W1, const void *b1,
+                                   const void *W3, const void *W2, moe_act act, const void *dybuf, void *dxbuf,
+                                   void *dW1, void *dW3, void *dW2, void *db1, void *db2, void *ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    if (E < 1 || C < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (E > MAX_E) return MOE_ERR_UNSUPPORTED;
+    MOE_CHECK(check_width(d));
+    MOE_CHECK(check_width(dff));
+    // the forward's weight arguments, and their gradients alike
+    MOE_CHECK(check_ffn_args(dt, act, W1, b1, W3, W2, nullptr));
+    if ((dW3 == nullptr) != (W3 == nullptr) || !ptr_ok(dW1, false) || !ptr_ok(dW2, false) || !opt_ok(dW3) ||
+        !opt_ok(db1) || !opt_ok(db2))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (act == MOE_ACT_SWIGLU && (db1 != nullptr || db2 != nullptr)) return MOE_ERR_UNSUPPORTED;
+    if (!ptr_ok(xbuf, C == 0) || !ptr4_ok(expert_count, false) || !ptr_ok(dybuf, C == 0) ||
+        !ptr_ok(dxbuf, C == 0))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = moe::expert_backward_ws(E, C, d, dff, dt == MOE_BF16, act == MOE_ACT_SWIGLU ? 2 : 1).total;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_HIP(moe::launch_expert_backward(xbuf, dt == MOE_BF16, expert_count, E, C, d, dff, W1, b1, W3, W2,
+                                        act == MOE_ACT_SWIGLU ? 2 : 1, dybuf, dxbuf, dW1, dW3, dW2, db1, db2,
+                                        static_cast<char *>(ws), stream));
+    return MOE_OK;
+}
+
+moe_status moe_dispatch_backward(const void *dxbuf, moe_dtype dt, const int32_t *expert_idx, const int32_t *slot,
+                                 int64_t T, int32_t d, int32_t E, int32_t k, int64_t C, const float *dx_add,
+                                 float *dx, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+    if (C < 0 || C > T) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(dxbuf, empty || C == 0) || !ptr4_ok(expert_idx, empty) || !ptr4_ok(slot, empty) ||
+        !opt_ok(dx_add) || !ptr_ok(dx, empty))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_HIP(moe::launch_dispatch_backward(dxbuf, dt == MOE_BF16, expert_idx, slot, T, d, E, k, C, dx_add, dx,
+                                          stream));
+    return MOE_OK;
+}
+
 moe_status moe_combine(const void *ybuf, moe_dtype dt, const int32_t *expert_idx,
                        const int32_t *slot, const float *gate, const float *prob_sum,
                        const int32_t *route_count, int64_t T, int32_t d, int32_t E, int32_t k,

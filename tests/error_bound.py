@@ -165,3 +165,94 @@ def check_elementwise(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, rows=
                              f"{i}: |err| {err[i]:.3e} > bound {bound[i]:.3e}")
     fin = np.isfinite(bound) & (bound > 0)
     return float(np.max(err[fin] / bound[fin])) if fin.any() else 0.0
+
+
+SILU_GRAD_SLOPE = 0.55      # max |d^2 silu / da^2| is 0.5 (at a = 0)
+
+
+def expert_backward_bound(u, W1, W2, act: str, dY, b1=None, W3=None, store: str = "bf16", rows_pad=None):
+    """Bounds of the GPU's expert-FFN backward for one expert's rows, from the
+    same rounding model as the forward: the recomputed A', G', dH' and the
+    activation outputs H', dA', dG' are stored (ub), every product sum is an
+    fp32 sum (ACC), and the bf16 inputs u, dY and the weights are exact.
+
+      ReLU:   mask' = 1[A' > 0] equals 1[A > 0] wherever |A| > EA; elsewhere
+              dA' may be dH' or 0, so the bound there is |dH| + EdH.
+      SwiGLU: |silu'(A') - silu'(A)| <= 0.55 |A' - A| (|silu''| <= 0.5) plus
+              the hardware exp2 / rcp error es on sigma and a sigma (1 - sigma).
+
+    rows_pad: the contraction length of the weight-gradient sums (rows of the
+    expert rounded up to the GPU's K tile); defaults to the row count.
+    Returns a dict name -> (exact fp32 evaluation, bound) for du, dW1, dW2,
+    dW3 (SwiGLU), db1 and db2, float64 arrays."""
+    ub = unit_roundoff(store)
+    u, W1, W2, W3, b1, dY = (_f32(v) for v in (u, W1, W2, W3, b1, dY))
+    n, d = u.shape
+    f = W1.shape[0]
+    npad = n if rows_pad is None else rows_pad
+    sw = act == "swiglu"
+    u2, dY2 = u * u, dY * dY
+    aW1, aW2 = np.abs(W1), np.abs(W2)
+    a = u @ W1.T
+    sa = u2 @ (W1 * W1).T
+    if b1 is not None:
+        a = a + b1[None, :]
+        sa = sa + (b1 * b1)[None, :]
+    ea = acc_factor(d + 1) * np.sqrt(sa)
+    EA = ea + ub * (np.abs(a) + ea)
+    dH = dY @ W2
+    edh = acc_factor(d) * np.sqrt(dY2 @ (W2 * W2))
+    EdH = edh + ub * (np.abs(dH) + edh)
+    out = {}
+    if not sw:
+        H = np.maximum(a, 0.0)
+        EH = EA
+        dA = dH * (a > 0)
+        sure = np.abs(a) > EA
+        EdA = np.where(sure, (a > 0) * EdH + ub * (np.abs(dA) + EdH), (np.abs(dH) + EdH) * (1 + ub))
+        dG = EdG = None
+    else:
+        g = u @ W3.T
+        eg = acc_factor(d) * np.sqrt(u2 @ (W3 * W3).T)
+        EG = eg + ub * (np.abs(g) + eg)
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-a))
+        s = a * sg
+        s1 = sg * (1.0 + a * (1.0 - sg))
+        ds = SILU_SLOPE * EA + ES * (np.abs(s) + SILU_SLOPE * EA)
+        ds1 = SILU_GRAD_SLOPE * EA + ES * (1.0 + np.abs(a) + EA)
+        H = s * g
+        DH = ds * (np.abs(g) + EG) + np.abs(s) * EG
+        EH = DH + (U + ub) * (np.abs(H) + DH)
+        dG = dH * s
+        DdG = EdH * (np.abs(s) + ds) + np.abs(dH) * ds
+        EdG = DdG + (U + ub) * (np.abs(dG) + DdG)
+        dA = dH * g * s1
+        DdA = (EdH * (np.abs(g) + EG) * (np.abs(s1) + ds1) + np.abs(dH) * EG * (np.abs(s1) + ds1)
+               + np.abs(dH) * np.abs(g) * ds1)
+        EdA = DdA + (2 * U + ub) * (np.abs(dA) + DdA)
+
+    def fin(v, pre):
+        """Bound of a stored result: the propagated and summation error `pre`, then one rounding."""
+        v64 = v.astype(np.float64)
+        pre = pre.astype(np.float64)
+        return v64, (pre + ub * (np.abs(v64) + pre)) * SLACK
+
+    # dX = dA W1 (+ dG W3)
+    du = dA @ W1
+    pre = EdA @ aW1
+    sq = (dA * dA) @ (W1 * W1)
+    if sw:
+        du = du + dG @ W3
+        pre = pre + EdG @ np.abs(W3)
+        sq = sq + (dG * dG) @ (W3 * W3)
+    out["du"] = fin(du, pre + acc_factor(f * (2 if sw else 1)) * np.sqrt(sq))
+    # dW2 = dY^T H', dW1 = dA'^T u, dW3 = dG'^T u (sums over the rows)
+    accn = acc_factor(npad)
+    out["dW2"] = fin(dY.T @ H, np.abs(dY).T @ EH + accn * np.sqrt(dY2.T @ (H * H)))
+    out["dW1"] = fin(dA.T @ u, EdA.T @ np.abs(u) + accn * np.sqrt((dA * dA).T @ u2))
+    if sw:
+        out["dW3"] = fin(dG.T @ u, EdG.T @ np.abs(u) + accn * np.sqrt((dG * dG).T @ u2))
+    out["db2"] = fin(dY.sum(axis=0), accn * np.sqrt(dY2.sum(axis=0)))
+    out["db1"] = fin(dA.sum(axis=0), EdA.sum(axis=0) + accn * np.sqrt((dA * dA).sum(axis=0)))
+    return out

@@ -143,3 +143,68 @@ def test_dropped_tokens_have_a_zero_bound():
     gone = np.all(ref["drop_mask"] == 1, axis=1)
     assert gone.any()
     assert (Ey[gone] == 0).all() and (y_sim[gone] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# the expert backward's bound
+# ---------------------------------------------------------------------------
+
+def _simulate_expert_backward(u, W1, W2, act, dY, b1=None, W3=None, store="bf16"):
+    """The backward kernels' rounding steps in NumPy: fp32 products, A', G', dH', H', dA', dG'
+    and the outputs rounded to the storage type."""
+    rnd = _bf16 if store == "bf16" else (lambda v: np.asarray(v, dtype=np.float32))
+    f32 = lambda a: None if a is None else np.asarray(a, dtype=np.float32)   # noqa: E731
+    u, W1, W2, W3, b1, dY = (f32(v) for v in (u, W1, W2, W3, b1, dY))
+    a = rnd(u @ W1.T + (0 if b1 is None else b1[None, :]))
+    dH = rnd(dY @ W2)
+    out = {}
+    if act == "relu":
+        H = rnd(np.maximum(a, 0))
+        dA = rnd(dH * (a > 0))
+        du = rnd(dA @ W1)
+    else:
+        g = rnd(u @ W3.T)
+        sg = 1 / (1 + np.exp(-a))
+        s = a * sg
+        H = rnd(s * g)
+        dA = rnd(dH * g * (sg * (1 + a * (1 - sg))))
+        dG = rnd(dH * s)
+        du = rnd(dA @ W1 + dG @ W3)
+        out["dW3"] = rnd(dG.T @ u)
+    out.update(du=du, dW2=rnd(dY.T @ H), dW1=rnd(dA.T @ u), db2=rnd(dY.sum(0)), db1=rnd(dA.sum(0)))
+    return {k: v.astype(np.float64) for k, v in out.items()}
+
+
+def _bwd_case(act, store="bf16", seed=2, n=300, d=64, f=96):
+    rng = np.random.default_rng(seed)
+    cast = (lambda a: _bf16(a).astype(np.float64)) if store == "bf16" else (lambda a: a.astype(np.float32).astype(np.float64))
+    c = dict(u=cast(rng.normal(size=(n, d))), W1=cast(rng.normal(size=(f, d)) * 0.04),
+             W2=cast(rng.normal(size=(d, f)) * 0.03), dY=cast(rng.normal(size=(n, d)) * 0.01),
+             W3=cast(rng.normal(size=(f, d)) * 0.04) if act == "swiglu" else None,
+             b1=cast(rng.normal(size=f) * 0.04) if act == "relu" else None)
+    return c
+
+
+@pytest.mark.parametrize("act,store", [("relu", "bf16"), ("swiglu", "bf16"), ("relu", "f32"), ("swiglu", "f32")])
+def test_simulated_backward_is_inside_the_bound(act, store):
+    from error_bound import expert_backward_bound
+    c = _bwd_case(act, store)
+    ref = O.expert_ffn_backward(c["u"], c["W1"], c["W2"], act, c["dY"], b1=c["b1"], W3=c["W3"])
+    sim = _simulate_expert_backward(c["u"], c["W1"], c["W2"], act, c["dY"], b1=c["b1"], W3=c["W3"], store=store)
+    bnd = expert_backward_bound(c["u"], c["W1"], c["W2"], act, c["dY"], b1=c["b1"], W3=c["W3"], store=store)
+    for name, (_, E) in bnd.items():
+        w = check_elementwise(sim[name], ref[name], E, what=name)
+        assert w <= 1.0
+
+
+@pytest.mark.parametrize("name,how", [("dW1", "transposed"), ("dW2", "zero"), ("du", "rows_shifted"),
+                                      ("dW3", "next_column_tile")])
+def test_corrupted_backward_block_fails_the_bound(name, how):
+    from error_bound import expert_backward_bound
+    c = _bwd_case("swiglu")
+    ref = O.expert_ffn_backward(c["u"], c["W1"], c["W2"], "swiglu", c["dY"], W3=c["W3"])
+    sim = _simulate_expert_backward(c["u"], c["W1"], c["W2"], "swiglu", c["dY"], W3=c["W3"])
+    bnd = expert_backward_bound(c["u"], c["W1"], c["W2"], "swiglu", c["dY"], W3=c["W3"])
+    bad = _corrupt(sim[name], 32, 0, how)
+    with pytest.raises(AssertionError):
+        check_elementwise(bad, ref[name], bnd[name][1], what=name)
