@@ -59,8 +59,21 @@ typedef enum {
     MOE_ERR_HIP = 4                 /* a HIP launch reported an error */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
-typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+/* The *_RANGE_ entries are not valid arguments: they make every 32-bit int a
+ * value of the type, so that an unknown code passed by a C caller reaches the
+ * argument checks (MOE_ERR_UNSUPPORTED) as a defined value in C++ as well. */
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_DTYPE_RANGE_LO_ = -0x7fffffff - 1,
+    MOE_DTYPE_RANGE_HI_ = 0x7fffffff
+} moe_dtype;
+typedef enum {
+    MOE_ACT_RELU = 0,
+    MOE_ACT_SWIGLU = 1,
+    MOE_ACT_RANGE_LO_ = -0x7fffffff - 1,
+    MOE_ACT_RANGE_HI_ = 0x7fffffff
+} moe_act;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *moe_status_string(int status);
