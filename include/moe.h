@@ -75,6 +75,14 @@ typedef enum {
     MOE_ACT_RANGE_HI_ = 0x7fffffff
 } moe_act;
 
+/* Overflow policy of moe_forward_policy (range markers as above). */
+typedef enum {
+    MOE_POLICY_PRIORITY = 1,
+    MOE_POLICY_REROUTE = 2,
+    MOE_POLICY_RANGE_LO_ = -0x7fffffff - 1,
+    MOE_POLICY_RANGE_HI_ = 0x7fffffff
+} moe_policy;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *moe_status_string(int status);
 
@@ -442,6 +450,38 @@ moe_status moe_forward_noisy(const void *x, moe_dtype dt, const float *W_r, cons
                              int32_t dff, int32_t E, int32_t k, double capacity_factor, float alpha, void *y,
                              float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
                              uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The fused layer with an overflow policy in place of the plain capacity rule
+ * (the same router, expert FFN, combine and losses as moe_forward, and the
+ * dispatch of moe_dispatch_priority or moe_dispatch_reroute):
+ *   MOE_POLICY_PRIORITY  [CS25-L5], the V-MoE part: the capacity
+ *       C = moe_capacity(T, E, k, capacity_factor) is filled in descending
+ *       priority[t] (NULL: each token's first gate, gate[t, 0]); any k.
+ *       expert_idx, gate, drop_mask [T, k] as moe_forward.
+ *   MOE_POLICY_REROUTE   [CS25-L5] "“No Token Left Behind”为何没有成功":
+ *       k = 1; the router's top-`stages` choices are each token's
+ *       preferences (1 <= stages <= min(E, 8)) and stage s offers the tokens
+ *       still without a slot their choice s, C = moe_capacity(T, E, 1,
+ *       capacity_factor) slots per expert.  expert_idx [T, 1] is the expert
+ *       the token landed on (-1 if dropped), gate [T, 1] the full-softmax
+ *       probability of that expert (0 if dropped), drop_mask [T, 1].  The
+ *       loss counts each token's first choice (f_i over the top-1 choices,
+ *       before capacity).  priority must be NULL.
+ * aux_loss and z_loss as moe_forward (the z-loss over all logits).
+ * ws: moe_forward_policy_workspace_bytes(...) bytes (it also holds xbuf and
+ * the expert outputs: this path runs the split kernels, not the fused
+ * gather / scatter of moe_forward).
+ */
+size_t moe_forward_policy_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
+                                          double capacity_factor, moe_dtype dt, moe_act act, moe_policy policy,
+                                          int32_t stages);
+moe_status moe_forward_policy(const void *x, moe_dtype dt, const float *W_r, const float *b_r, const void *W1,
+                              const void *b1, const void *W3, const void *W2, const void *b2, moe_act act,
+                              int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k, double capacity_factor,
+                              float alpha, moe_policy policy, const float *priority, int32_t stages, void *y,
+                              float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
+                              uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream);
 
 moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, const float *b_r,
                               const void *W1, const void *b1, const void *W3, const void *W2,

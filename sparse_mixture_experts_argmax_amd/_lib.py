@@ -21,6 +21,8 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_ACT_RELU = 0
 MOE_ACT_SWIGLU = 1
+MOE_POLICY_PRIORITY = 1
+MOE_POLICY_REROUTE = 2
 
 SIZE_MAX = (1 << 64) - 1
 
@@ -59,6 +61,10 @@ SIGNATURES = {
     "moe_expert_ffn_backward": (C.c_int, [_p, C.c_int, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p, C.c_int,
                                           _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_dispatch_backward": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "moe_forward_policy_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, C.c_double, C.c_int, C.c_int,
+                                                 C.c_int, _i32]),
+    "moe_forward_policy": (C.c_int, [_p, C.c_int, _p, _p, _p, _p, _p, _p, _p, C.c_int, _i64, _i32, _i32, _i32, _i32,
+                                     C.c_double, C.c_float, C.c_int, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_router_noalloc": (C.c_int, [_p, C.c_int, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p,
                                      _p, _p, _p]),
     "moe_router_noalloc_scratch_bytes": (_sz, []),

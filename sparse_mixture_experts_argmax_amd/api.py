@@ -491,6 +491,46 @@ class ForwardPlan:
         return self.ws[off:off + n * sz].view(dt).view(shape)
 
 
+def forward_policy(x, W_r, W1, W2, *, policy, W3=None, b1=None, b2=None, b_r=None, k=1, capacity_factor=1.25,
+                   alpha=1e-2, act="relu", priority=None, stages=2, workspace=None):
+    """The whole layer with an overflow policy: policy="priority" (capacity spent on the highest
+    priority [T] fp32 first, default each token's first gate) or "reroute" (k = 1; the router's
+    top-`stages` choices offered in stages).  Returns (y, aux_loss, z_loss, expert_idx, gate,
+    drop_mask); with "reroute" expert_idx [T, 1] is the landing expert (-1 if dropped)."""
+    T, d = _tokens(x)
+    if W_r.dim() != 2 or W1.dim() != 3:
+        raise ValueError("W_r must be [E, d] and W1 [E, dff, d]")
+    E = W_r.shape[0]
+    dff = W1.shape[1]
+    dev = x.device
+    pol = {"priority": L.MOE_POLICY_PRIORITY, "reroute": L.MOE_POLICY_REROUTE}.get(policy)
+    if pol is None:
+        raise ValueError(f"policy must be 'priority' or 'reroute', got {policy!r}")
+    _expect(W_r, "W_r", (E, d), torch.float32)
+    _expect(b_r, "b_r", (E,), torch.float32, optional=True)
+    _experts(E, d, dff, x.dtype, W1, W2, W3, b1, b2)
+    _expect(priority, "priority", (T,), torch.float32, optional=True)
+    if pol == L.MOE_POLICY_REROUTE and (k != 1 or priority is not None):
+        raise ValueError("re-routing is a top-1 policy (k = 1) and takes no priority")
+    kk = k
+    need = L.LIB.moe_forward_policy_workspace_bytes(T, d, dff, E, kk, capacity_factor, _dtype_code(x), _ACT[act],
+                                                    pol, stages)
+    if need == L.SIZE_MAX:
+        raise ValueError("invalid sizes or policy arguments")
+    ws = _ws(workspace, need, dev)
+    y = torch.empty((T, d), dtype=x.dtype, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    zl = torch.empty(1, dtype=torch.float32, device=dev)
+    idx = torch.empty((T, kk), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, kk), dtype=torch.float32, device=dev)
+    drop = torch.empty((T, kk), dtype=torch.uint8, device=dev)
+    L.check("moe_forward_policy", L.LIB.moe_forward_policy(
+        _ptr(x), _dtype_code(x), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2), _ACT[act],
+        T, d, dff, E, kk, capacity_factor, alpha, pol, _ptr(priority), stages, _ptr(y), _ptr(aux), _ptr(zl),
+        _ptr(idx), _ptr(gate), _ptr(drop), _ptr(ws), ws.numel(), _stream(dev)))
+    return y, aux, zl, idx, gate, drop
+
+
 def forward(x, W_r, W1, W2, *, W3=None, b1=None, b2=None, b_r=None, k=1, capacity_factor=1.25,
             alpha=1e-2, act="relu"):
     """The whole layer: returns (y, aux_loss, expert_idx, gate, drop_mask)."""

@@ -110,6 +110,11 @@ hipError_t launch_reroute(const void *x, int elem_bytes, const int32_t *pref, co
                           int d, int E, int R, int stages, int64_t C, int32_t *expert, int32_t *slot,
                           uint8_t *drop_mask, float *gate, int32_t *expert_count, void *xbuf, int32_t *rank,
                           int32_t *hist, int32_t *cand, int32_t *n_e, int32_t *fill, hipStream_t s);
+// counts [E] = how many tokens have e as their first preference pref[t, 0]
+// (pref [T, R]); the fused re-routing forward's choice counts for the loss.
+hipError_t launch_first_choice_count(const int32_t *pref, int64_t T, int R, int E, int32_t *counts, hipStream_t s);
+// out [T] = gate[t, 0] of gate [T, k]: the default priority score.
+hipError_t launch_first_gate(const float *gate, int64_t T, int k, float *out, hipStream_t s);
 hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_idx,
                           const int32_t *rank, const int32_t *base, int64_t T, int d, int E,
                           int k, int64_t C, int32_t *slot, uint8_t *drop_mask, void *xbuf,

@@ -417,6 +417,27 @@ moe_status moe_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, 
                         static_cast<char *>(ws), stream);
 }
 
+namespace {
+moe_status run_priority_dispatch(const void *x, moe_dtype dt, const int32_t *expert_idx, const float *priority,
+                                 int64_t T, int32_t d, int32_t E, int32_t k, int64_t C, int32_t *slot,
+                                 uint8_t *drop_mask, int32_t *expert_count, void *xbuf, char *base,
+                                 hipStream_t stream) {
+    const PriorityWs w = priority_ws(T, E, k);
+    int32_t *rank = reinterpret_cast<int32_t *>(base + w.d.rank);
+    int32_t *hist = reinterpret_cast<int32_t *>(base + w.d.hist);
+    int32_t *n_e = reinterpret_cast<int32_t *>(base + w.cnt);
+    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, nullptr, stream));
+    // an unbounded capacity: the scan's counts are the experts' choice counts
+    MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, T * k + 1, n_e, nullptr, 0, nullptr,
+                                  nullptr, nullptr, 0, nullptr, stream));
+    MOE_HIP(moe::launch_priority_slots(x, (int)esize(dt), expert_idx, priority, rank, hist, n_e, T, d, E, k,
+                                       C, reinterpret_cast<uint64_t *>(base + w.list),
+                                       reinterpret_cast<int32_t *>(base + w.off), slot, drop_mask,
+                                       expert_count, xbuf, stream));
+    return MOE_OK;
+}
+}  // namespace
+
 size_t moe_dispatch_priority_workspace_bytes(int64_t T, int32_t E, int32_t k) {
     if (check_sizes(T, E, k) != MOE_OK) return SIZE_MAX;
     return priority_ws(T, E, k).total;
@@ -437,22 +458,10 @@ moe_status moe_dispatch_priority(const void *x, moe_dtype dt, const int32_t *exp
         !ptr4_ok(slot, empty) || (drop_mask == nullptr && !empty) || !ptr4_ok(expert_count, false) ||
         !ptr_ok(xbuf, C == 0))
         return MOE_ERR_INVALID_ARGUMENT;
-    const PriorityWs w = priority_ws(T, E, k);
-    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < priority_ws(T, E, k).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
-    char *base = static_cast<char *>(ws);
-    int32_t *rank = reinterpret_cast<int32_t *>(base + w.d.rank);
-    int32_t *hist = reinterpret_cast<int32_t *>(base + w.d.hist);
-    int32_t *n_e = reinterpret_cast<int32_t *>(base + w.cnt);
-    MOE_HIP(moe::launch_slot_rank(expert_idx, T, E, k, rank, hist, nullptr, stream));
-    // an unbounded capacity: the scan's counts are the experts' choice counts
-    MOE_HIP(moe::launch_slot_scan(hist, moe::dispatch_blocks(T), E, k, T * k + 1, n_e, nullptr, 0, nullptr,
-                                  nullptr, nullptr, 0, nullptr, stream));
-    MOE_HIP(moe::launch_priority_slots(x, (int)esize(dt), expert_idx, priority, rank, hist, n_e, T, d, E, k,
-                                       C, reinterpret_cast<uint64_t *>(base + w.list),
-                                       reinterpret_cast<int32_t *>(base + w.off), slot, drop_mask,
-                                       expert_count, xbuf, stream));
-    return MOE_OK;
+    return run_priority_dispatch(x, dt, expert_idx, priority, T, d, E, k, C, slot, drop_mask, expert_count, xbuf,
+                                 static_cast<char *>(ws), stream);
 }
 
 moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, const int32_t *expert_idx,
@@ -763,6 +772,142 @@ moe_status moe_forward_staged(const void *x, moe_dtype dt, const float *W_r, con
     return forward_impl(x, dt, W_r, b_r, W1, b1, W3, W2, b2, act, T, d, dff, E, k,
                         capacity_factor, alpha, y, aux_loss, z_loss, expert_idx, gate, drop_mask, ws,
                         ws_bytes, stream, stage_events);
+}
+
+// ---- the fused forward with an overflow policy -------------------------------
+
+namespace {
+
+// Workspace of moe_forward_policy: the router's scratch and totals, the
+// policy's inputs (priority: the first-rank gates as scores; re-routing: the
+// router's top-`stages` preferences, their gates and the logits), the
+// policy dispatch's scratch, then slot, expert_count, xbuf, the FFN scratch
+// and ybuf.
+struct PolicyWs {
+    RouterWs r;
+    size_t router, prob_sum, route_count, count1, score, pref, pgate, logits, pdisp, slot, expert_count, xbuf, ffn,
+        ybuf, total;
+};
+PolicyWs policy_ws(int64_t T, int d, int dff, int E, int k, int64_t C, moe_dtype dt, int policy, int stages) {
+    PolicyWs w{};
+    w.r = router_ws(T, d, E);
+    const bool rr = policy == MOE_POLICY_REROUTE;
+    const int kr = rr ? stages : k;                      // the router's choices per token
+    size_t o = 0;
+    w.router = o;       o += w.r.total;
+    w.prob_sum = o;     o += up((size_t)E * 4);
+    w.route_count = o;  o += up((size_t)E * 4);
+    w.count1 = o;       o += up((size_t)E * 4);
+    w.score = o;        o += rr ? 0 : up((size_t)T * 4);
+    w.pref = o;         o += rr ? up((size_t)T * kr * 4) : 0;
+    w.pgate = o;        o += rr ? up((size_t)T * kr * 4) : 0;
+    w.logits = o;       o += rr ? up((size_t)T * E * 4) : 0;
+    w.pdisp = o;        o += rr ? reroute_ws(T, E).total : priority_ws(T, E, k).total;
+    w.slot = o;         o += up((size_t)T * (rr ? 1 : k) * 4);
+    w.expert_count = o; o += up((size_t)E * 4);
+    w.xbuf = o;         o += up((size_t)E * C * d * esize(dt));
+    w.ffn = o;          o += ffn_ws(E, C, dff, dt).total;
+    w.ybuf = o;         o += up((size_t)E * C * d * esize(dt));
+    w.total = o;
+    return w;
+}
+
+bool policy_ok(int policy, int k, int32_t stages, int E) {
+    if (policy == MOE_POLICY_PRIORITY) return true;
+    if (policy == MOE_POLICY_REROUTE) return k == 1 && stages >= 1 && stages <= E && stages <= MAX_K;
+    return false;
+}
+
+}  // namespace
+
+size_t moe_forward_policy_workspace_bytes(int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k,
+                                          double capacity_factor, moe_dtype dt, moe_act act, moe_policy policy,
+                                          int32_t stages) {
+    if (check_sizes(T, E, k) != MOE_OK || check_width(d) != MOE_OK || check_width(dff) != MOE_OK ||
+        !dtype_ok(dt) || !act_ok(act) || !policy_ok(policy, k, stages, E))
+        return SIZE_MAX;
+    if (policy == MOE_POLICY_PRIORITY && T * (int64_t)k > PRIORITY_MAX_CHOICES) return SIZE_MAX;
+    if (policy == MOE_POLICY_REROUTE && check_sizes(T, E, stages) != MOE_OK) return SIZE_MAX;
+    const int64_t C = moe_capacity(T, E, k, capacity_factor);
+    if (C < 0) return SIZE_MAX;
+    return policy_ws(T, d, dff, E, k, C, dt, policy, stages).total;
+}
+
+moe_status moe_forward_policy(const void *x, moe_dtype dt, const float *W_r, const float *b_r, const void *W1,
+                              const void *b1, const void *W3, const void *W2, const void *b2, moe_act act,
+                              int64_t T, int32_t d, int32_t dff, int32_t E, int32_t k, double capacity_factor,
+                              float alpha, moe_policy policy, const float *priority, int32_t stages, void *y,
+                              float *aux_loss, float *z_loss, int32_t *expert_idx, float *gate,
+                              uint8_t *drop_mask, void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_sizes(T, E, k));
+    MOE_CHECK(check_width(d));
+    MOE_CHECK(check_width(dff));
+    MOE_CHECK(check_ffn_args(dt, act, W1, b1, W3, W2, b2));
+    if (policy != MOE_POLICY_PRIORITY && policy != MOE_POLICY_REROUTE) return MOE_ERR_UNSUPPORTED;
+    if (!policy_ok(policy, k, stages, E)) return MOE_ERR_INVALID_ARGUMENT;
+    if (policy == MOE_POLICY_PRIORITY && T * (int64_t)k > PRIORITY_MAX_CHOICES) return MOE_ERR_UNSUPPORTED;
+    if (policy == MOE_POLICY_REROUTE && priority != nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!isfinite(alpha)) return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t C = moe_capacity(T, E, k, capacity_factor);
+    if (C < 0) return MOE_ERR_INVALID_ARGUMENT;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !opt_ok(b_r) || !ptr_ok(y, empty) ||
+        !ptr4_ok(aux_loss, false) || !(z_loss == nullptr || ptr4_ok(z_loss, false)) ||
+        !ptr4_ok(expert_idx, empty) || !ptr4_ok(gate, empty) || (drop_mask == nullptr && !empty) ||
+        !(priority == nullptr || ptr4_ok(priority, empty)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const PolicyWs w = policy_ws(T, d, dff, E, k, C, dt, policy, stages);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
+    char *base = static_cast<char *>(ws);
+    float *prob_sum = reinterpret_cast<float *>(base + w.prob_sum);
+    int32_t *route_count = reinterpret_cast<int32_t *>(base + w.route_count);
+    int32_t *count1 = reinterpret_cast<int32_t *>(base + w.count1);
+    int32_t *slot = reinterpret_cast<int32_t *>(base + w.slot);
+    int32_t *expert_count = reinterpret_cast<int32_t *>(base + w.expert_count);
+    void *xbuf = base + w.xbuf;
+    void *ybuf = base + w.ybuf;
+    const int bf16 = dt == MOE_BF16;
+    const int32_t *loss_count = route_count;
+    if (policy == MOE_POLICY_PRIORITY) {
+        // [CS25-L5], the V-MoE part: the router's top-k, then the capacity
+        // spent on the highest scores first (the caller's, or each token's
+        // first gate)
+        MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, k, expert_idx, gate, prob_sum, route_count, z_loss,
+                             base + w.router, stream, true));
+        const float *score = priority;
+        if (score == nullptr) {
+            float *sc = reinterpret_cast<float *>(base + w.score);
+            MOE_HIP(moe::launch_first_gate(gate, T, k, sc, stream));
+            score = sc;
+        }
+        MOE_CHECK(run_priority_dispatch(x, dt, expert_idx, score, T, d, E, k, C, slot, drop_mask, expert_count,
+                                        xbuf, base + w.pdisp, stream));
+    } else {
+        // [CS25-L5] "No Token Left Behind": the router's top-`stages` choices
+        // are the preferences; stage s offers the unplaced tokens their
+        // choice s.  The loss counts each token's first choice (k = 1).
+        int32_t *pref = reinterpret_cast<int32_t *>(base + w.pref);
+        float *pgate = reinterpret_cast<float *>(base + w.pgate);
+        float *logits = reinterpret_cast<float *>(base + w.logits);
+        MOE_CHECK(run_router(x, dt, W_r, b_r, T, d, E, stages, pref, pgate, prob_sum, route_count, z_loss,
+                             base + w.router, stream, true, logits));
+        MOE_HIP(moe::launch_first_choice_count(pref, T, stages, E, count1, stream));
+        loss_count = count1;
+        const RerouteWs rw = reroute_ws(T, E);
+        char *rb = base + w.pdisp;
+        MOE_HIP(moe::launch_reroute(x, (int)esize(dt), pref, logits, T, d, E, stages, stages, C, expert_idx, slot,
+                                    drop_mask, gate, expert_count, xbuf, reinterpret_cast<int32_t *>(rb + rw.d.rank),
+                                    reinterpret_cast<int32_t *>(rb + rw.d.hist),
+                                    reinterpret_cast<int32_t *>(rb + rw.cand), reinterpret_cast<int32_t *>(rb + rw.cnt),
+                                    reinterpret_cast<int32_t *>(rb + rw.fill), stream));
+    }
+    const int kc = policy == MOE_POLICY_REROUTE ? 1 : k;
+    MOE_CHECK(run_ffn(xbuf, dt, expert_count, E, C, d, dff, W1, b1, W3, W2, b2, act, ybuf, T * (int64_t)kc,
+                      base + w.ffn, stream));
+    MOE_HIP(moe::launch_combine(ybuf, bf16, expert_idx, slot, gate, prob_sum, loss_count, T, d, E, kc, C, alpha, y,
+                                aux_loss, stream));
+    return MOE_OK;
 }
 
 }  // extern "C"

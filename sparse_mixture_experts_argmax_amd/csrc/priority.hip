@@ -258,4 +258,22 @@ hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *e
     return hipGetLastError();
 }
 
+namespace {
+
+// out[t] = gate[t k], the gate of each token's first choice (the default
+// priority score of the fused forward)
+__global__ __launch_bounds__(256) void first_gate_kernel(const float *__restrict__ gate, int64_t T, int k,
+                                                          float *__restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < T) out[t] = gate[t * k];
+}
+
+}  // namespace
+
+hipError_t launch_first_gate(const float *gate, int64_t T, int k, float *out, hipStream_t s) {
+    if (T > 0)
+        hipLaunchKernelGGL(first_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, gate, T, k, out);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -121,4 +121,40 @@ hipError_t launch_reroute(const void *x, int elem_bytes, const int32_t *pref, co
     return launch_permute_slots(x, elem_bytes, expert, slot, T, d, 1, C, xbuf, s);
 }
 
+namespace {
+
+// counts[e] = number of tokens whose first preference is e (entries outside
+// [0, E) count nowhere); an LDS histogram per block, added to counts, which
+// the launcher clears first.  Integer sums: the same counts in any order.
+__global__ __launch_bounds__(256) void first_choice_count_kernel(const int32_t *__restrict__ pref, int64_t T, int R,
+                                                                  int E, int32_t *__restrict__ counts) {
+    __shared__ int h[1024];
+    for (int i = threadIdx.x; i < E; i += 256) h[i] = 0;
+    __syncthreads();
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < T; t += (int64_t)gridDim.x * 256) {
+        const int e = pref[t * R];
+        if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += 256)
+        if (h[i]) atomicAdd(&counts[i], h[i]);
+}
+
+__global__ __launch_bounds__(256) void clear_i32_kernel(int32_t *__restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_first_choice_count(const int32_t *pref, int64_t T, int R, int E, int32_t *counts, hipStream_t s) {
+    hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, counts, E);
+    if (T > 0) {
+        int64_t b = (T + 255) / 256;
+        if (b > 1024) b = 1024;
+        hipLaunchKernelGGL(first_choice_count_kernel, dim3((unsigned)b), dim3(256), 0, s, pref, T, R, E, counts);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -109,6 +109,19 @@ int main() {
     EXPECT(moe_forward_noisy(P, MOE_BF16, (float *)P, nullptr, nullptr, (float *)P, P, nullptr, nullptr, P, nullptr,
                              MOE_ACT_RELU, 64, 64, 128, 8, 1, 1.25, 0.01f, P, (float *)P, nullptr, (int32_t *)P,
                              (float *)P, (uint8_t *)P, P, BIG, nullptr), MOE_ERR_INVALID_ARGUMENT);
+    EXPECT(moe_forward_policy(P, MOE_BF16, (float *)P, nullptr, P, nullptr, nullptr, P, nullptr, MOE_ACT_RELU, 64,
+                              64, 128, 8, 2, 1.25, 0.01f, MOE_POLICY_REROUTE, nullptr, 2, P, (float *)P, nullptr,
+                              (int32_t *)P, (float *)P, (uint8_t *)P, P, BIG, nullptr), MOE_ERR_INVALID_ARGUMENT);
+    EXPECT(moe_forward_policy(P, MOE_BF16, (float *)P, nullptr, P, nullptr, nullptr, P, nullptr, MOE_ACT_RELU, 64,
+                              64, 128, 8, 1, 1.25, 0.01f, (moe_policy)7, nullptr, 2, P, (float *)P, nullptr,
+                              (int32_t *)P, (float *)P, (uint8_t *)P, P, BIG, nullptr), MOE_ERR_UNSUPPORTED);
+    EXPECT(moe_forward_policy(P, MOE_BF16, (float *)P, nullptr, P, nullptr, nullptr, P, nullptr, MOE_ACT_RELU, 64,
+                              64, 128, 8, 1, 1.25, 0.01f, MOE_POLICY_PRIORITY, nullptr, 0, P, (float *)P, nullptr,
+                              (int32_t *)P, (float *)P, (uint8_t *)P, P, 16, nullptr), MOE_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(moe_forward_policy_workspace_bytes(64, 64, 128, 8, 1, 1.0, MOE_BF16, MOE_ACT_RELU, MOE_POLICY_REROUTE, 9),
+           SIZE_MAX);
+    EXPECT(moe_forward_policy_workspace_bytes(64, 64, 128, 8, 1, 1.0, MOE_BF16, MOE_ACT_RELU, MOE_POLICY_REROUTE, 4) >
+           0, 1);
     if (failures) return 1;
     printf("abi checks passed\n");
     return 0;

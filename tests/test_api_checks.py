@@ -156,3 +156,14 @@ def test_forward_plan_rejects(what, over, exc, msg):
 def test_workspace_must_be_bytes():
     with pytest.raises(TypeError, match="workspace"):
         api._ws(torch.zeros(16, dtype=f32), 64, "cpu")
+
+
+def test_forward_policy_rejects():
+    a = dict(W_r=torch.zeros((E, d), dtype=f32), **_w())
+    with pytest.raises(ValueError, match="policy"):
+        moe.forward_policy(_x(), a["W_r"], a["W1"], a["W2"], policy="bogus")
+    with pytest.raises(ValueError, match="top-1"):
+        moe.forward_policy(_x(), a["W_r"], a["W1"], a["W2"], policy="reroute", k=2)
+    with pytest.raises(ValueError, match="priority"):
+        moe.forward_policy(_x(), a["W_r"], a["W1"], a["W2"], policy="priority", k=2,
+                           priority=torch.zeros(T + 1, dtype=f32))
