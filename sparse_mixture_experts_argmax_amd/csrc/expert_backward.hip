@@ -83,6 +83,56 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ sr
     }
 }
 
+// The bf16 transpose with 16-byte accesses on both sides: a thread loads 8
+// consecutive columns of one source row, and stores 8 consecutive source
+// rows of one column as one 16-byte piece of its destination row (read from
+// the LDS tile one element at a time).  Needs Cc, R_pad, src_ld, dst_ld and
+// dst_col0 to be multiples of 8 (every use here: widths and the padded row
+// count are); same result as transpose_kernel.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__restrict__ src, int64_t src_es,
+                                                          int src_ld, int R, int Cc,
+                                                          const int32_t *__restrict__ rcount,
+                                                          uint16_t *__restrict__ dst, int64_t dst_es, int dst_ld,
+                                                          int dst_col0, int R_pad) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[TT][TT + 8];
+    const int e = blockIdx.z;
+    const int c0 = blockIdx.x * TT;
+    const int r0 = blockIdx.y * TT;
+    int rc = R;
+    if (rcount != nullptr) {
+        rc = rcount[e];
+        rc = rc < 0 ? 0 : (rc > R ? R : rc);
+    }
+    const uint16_t *s = src + (int64_t)e * src_es;
+    uint16_t *d = dst + (int64_t)e * dst_es;
+    const int t = threadIdx.x;
+    // load: 64 rows x 8 pieces, two per thread
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = t + 256 * h;
+        const int i = q >> 3, pc = (q & 7) * 8;
+        const int r = r0 + i, c = c0 + pc;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < rc && c < Cc) v = ld16(s + (int64_t)r * src_ld + c);
+        *reinterpret_cast<u32x4 *>(&tile[i][pc]) = v;
+    }
+    __syncthreads();
+    // store: 64 destination rows (source columns) x 8 pieces of 8 source rows
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = t + 256 * h;
+        const int j = q >> 3, pr = (q & 7) * 8;
+        const int c = c0 + j, r = r0 + pr;
+        if (c < Cc && r < R_pad) {
+            u32x4 v;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = (uint32_t)tile[pr + 2 * u][j] | ((uint32_t)tile[pr + 2 * u + 1][j] << 16);
+            st16(d + (int64_t)c * dst_ld + dst_col0 + r, v);
+        }
+    }
+}
+
 // The activation backward of one 64-row x 64-column tile of one expert, from
 // the recomputed pre-activations A (and G) and dH = dY W2:
 //   ReLU:   H = max(A, 0), dA = dH * 1[A > 0]
@@ -247,8 +297,14 @@ hipError_t transpose(const void *src, int64_t src_es, int src_ld, int R, int Cc,
                      int64_t dst_es, int dst_ld, int dst_col0, int R_pad, int E, hipStream_t s) {
     if (R_pad <= 0 || Cc <= 0 || E <= 0) return hipSuccess;
     const dim3 grid((unsigned)((Cc + TT - 1) / TT), (unsigned)((R_pad + TT - 1) / TT), (unsigned)E);
-    hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, (const T *)src, src_es, src_ld, R, Cc, rcount,
-                       (T *)dst, dst_es, dst_ld, dst_col0, R_pad);
+    const bool vec16 = sizeof(T) == 2 && Cc % 8 == 0 && R_pad % 8 == 0 && src_ld % 8 == 0 && dst_ld % 8 == 0 &&
+                       dst_col0 % 8 == 0;
+    if (vec16)
+        hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, s, (const uint16_t *)src, src_es, src_ld, R, Cc,
+                           rcount, (uint16_t *)dst, dst_es, dst_ld, dst_col0, R_pad);
+    else
+        hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, (const T *)src, src_es, src_ld, R, Cc, rcount,
+                           (T *)dst, dst_es, dst_ld, dst_col0, R_pad);
     return hipGetLastError();
 }
 
@@ -367,13 +423,15 @@ hipError_t launch_expert_backward(const void *xbuf, int dtype_bf16, const int32_
     MOE_TRY(launch_grouped_gemm(dAG, W13t, nullptr, nullptr, dtype_bf16, 0, expert_count, tmap_r, bm_r, E, C, d, nf,
                                 rows, dxbuf, s));
     // the weight gradients, contracting over the (padded) rows of each expert
+    // (bf16: each expert's sum stops after its own rows, in whole K tiles)
+    const int32_t *kc = dtype_bf16 ? expert_count : nullptr;
     MOE_TRY(launch_grouped_gemm(dYt, Ht, nullptr, nullptr, dtype_bf16, 0, cnt_d, tmap_d, bm_d, E, d, f, Cp,
-                                (int64_t)E * d, dW2, s));
+                                (int64_t)E * d, dW2, s, nullptr, 0, nullptr, kc));
     MOE_TRY(launch_grouped_gemm(dAt, Xt, nullptr, nullptr, dtype_bf16, 0, cnt_f, tmap_f, bm_f, E, f, d, Cp,
-                                (int64_t)E * f, dW1, s));
+                                (int64_t)E * f, dW1, s, nullptr, 0, nullptr, kc));
     if (sw)
         MOE_TRY(launch_grouped_gemm(dGt, Xt, nullptr, nullptr, dtype_bf16, 0, cnt_f, tmap_f, bm_f, E, f, d, Cp,
-                                    (int64_t)E * f, dW3, s));
+                                    (int64_t)E * f, dW3, s, nullptr, 0, nullptr, kc));
     // the bias gradients: row sums of the transposed dA and dY
     if (db1 != nullptr && E * (int64_t)f > 0) {
         const unsigned g = (unsigned)(((int64_t)E * f + 3) / 4);

@@ -158,14 +158,15 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
                                int dtype_bf16, int act, const int32_t *expert_count,
                                const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
                                int64_t rows_bound, void *out, hipStream_t s, const int32_t *row_tok,
-                               int64_t T, const float *gate) {
+                               int64_t T, const float *gate, const int32_t *kcount) {
     if (C == 0 || rows_bound == 0) return hipSuccess;
     if (row_tok != nullptr && (!dtype_bf16 || T < 1 || (act == 0 && gate == nullptr)))
         return hipErrorInvalidValue;
+    if (kcount != nullptr && (K % 64 != 0 || row_tok != nullptr)) return hipErrorInvalidValue;
     if (dtype_bf16) {
         // fused forward: the first GEMM gathers token rows, the second
         // scatters gated rows to y (out is then y)
-        FuseArgs fz{row_tok, T, gate, (uint16_t *)out, row_tok == nullptr ? 0 : (act == 0 ? 2 : 1)};
+        FuseArgs fz{row_tok, T, gate, (uint16_t *)out, row_tok == nullptr ? 0 : (act == 0 ? 2 : 1), kcount};
         // the gated tiles exist for 128 and 256 rows only
         if ((bm != 128 && bm != 192 && bm != 256 && bm != 320) || (act == 2 && bm != 128 && bm != 256))
             return hipErrorInvalidValue;

@@ -16,12 +16,17 @@ namespace moe {
 // expert e straight from x (row m of the expert is token row_tok[e C + m]);
 // mode 2 scales output row m by row_gate[e C + m] (its token's gate) and
 // writes it to row row_tok[e C + m] of y (one expert choice per token).
+// kcount (null = off; K a multiple of 64): expert e's K loop covers only its
+// first kcount[e] columns of K, rounded up to the 64-wide K tile (at least
+// one tile), the rest being zeros it need not read (the weight-gradient
+// products contract over an expert's rows, padded to the capacity).
 struct FuseArgs {
     const int32_t *row_tok;
     int64_t T;
     const float *gate;                                   // row_gate [E, C]
     uint16_t *y;
     int mode;
+    const int32_t *kcount;
 };
 
 // One grouped-GEMM launch (the arguments of launch_grouped_gemm, resolved):
@@ -743,6 +748,12 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     c.st0 = st0; c.st1 = st1; c.st2 = st2; c.st3 = st3; c.st4 = st4;
     // wave-uniform wave index (DMA base)
     c.set_lanes(threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), K);
+    if (fz.kcount != nullptr) {
+        // this expert's rows of K only, in whole K tiles (K % 64 == 0: no tail)
+        const int kc = fz.kcount[e];
+        const int nke = (kc + TL::BK - 1) / TL::BK;
+        c.nk = nke < 1 ? 1 : (nke < c.nk ? nke : c.nk);
+    }
     c.m0 = mt * BM;
     c.b3off = X::DUAL ? (int64_t)(B3 - B) : 0;
     c.gather = fz.mode == 1;

@@ -140,7 +140,7 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
                                const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
                                int64_t rows_bound, void *out, hipStream_t s,
                                const int32_t *row_tok = nullptr, int64_t T = 0,
-                               const float *row_gate = nullptr);
+                               const float *row_gate = nullptr, const int32_t *kcount = nullptr);
 
 // ---- expert-side backward (expert_backward.hip) ----------------------------
 // Byte offsets of the backward's scratch inside one workspace: tile maps and
