@@ -16,6 +16,13 @@ namespace moe {
 
 namespace {
 
+constexpr int CMB_MAXK = 8;
+
+// One wave per token.  The token's choices (row offset of its expert row,
+// or -1, and gate) are read once into registers, then each lane walks its
+// 16-byte pieces of d two at a time, so the row loads of both pieces and of
+// every choice are in flight together instead of each waiting on the index
+// loads of its own iteration.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint8_t *__restrict__ ybuf, const int32_t *__restrict__ expert_idx,
@@ -36,28 +43,32 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int64_t row_bytes = (int64_t)d * ES;
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < T; t += nwaves) {
-        for (int p = lane; p < pieces; p += 64) {
-            float acc[EPP];
+        // the kept choices of token t, in rank order
+        int64_t roff[CMB_MAXK];
+        float g[CMB_MAXK];
+        int nk = 0;
+        for (int j = 0; j < k; ++j) {
+            const int64_t a = t * k + j;
+            const int s = slot[a];
+            const int e = expert_idx[a];
+            const bool kept = !(s < 0 || s >= C || e < 0 || e >= E);
+            roff[j] = kept ? ((int64_t)e * C + s) * row_bytes : -1;
+            g[j] = gate[a];
+            nk = j + 1;
+        }
+        auto accum = [&](float (&acc)[EPP], const u32x4 &v, float gj) {
+            if (BF16) {
 #pragma unroll
-            for (int q = 0; q < EPP; ++q) acc[q] = 0.f;
-            for (int j = 0; j < k; ++j) {
-                const int64_t a = t * k + j;
-                const int s = slot[a];
-                const int e = expert_idx[a];
-                if (s < 0 || s >= C || e < 0 || e >= E) continue;
-                const float g = gate[a];
-                const u32x4 v = ld16(ybuf + ((int64_t)e * C + s) * row_bytes + p * 16);
-                if (BF16) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[2 * q] = fmaf(g, bf2f((uint16_t)(v[q] & 0xFFFFu)), acc[2 * q]);
-                        acc[2 * q + 1] = fmaf(g, bf2f((uint16_t)(v[q] >> 16)), acc[2 * q + 1]);
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(v[q]), acc[q]);
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = fmaf(gj, bf2f((uint16_t)(v[q] & 0xFFFFu)), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(gj, bf2f((uint16_t)(v[q] >> 16)), acc[2 * q + 1]);
                 }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(gj, __uint_as_float(v[q]), acc[q]);
             }
+        };
+        auto out = [&](const float (&acc)[EPP], int p) {
             u32x4 o;
             if (BF16) {
 #pragma unroll
@@ -67,6 +78,36 @@ __global__ __launch_bounds__(256) void combine_kernel(
                 for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
             }
             st16(y + t * row_bytes + p * 16, o);
+        };
+        int p = lane;
+        for (; p + 64 < pieces; p += 128) {
+            float a0[EPP], a1[EPP];
+#pragma unroll
+            for (int q = 0; q < EPP; ++q) a0[q] = a1[q] = 0.f;
+            u32x4 v0[CMB_MAXK], v1[CMB_MAXK];
+#pragma unroll
+            for (int j = 0; j < CMB_MAXK; ++j)
+                if (j < nk && roff[j] >= 0) {
+                    v0[j] = ld16(ybuf + roff[j] + p * 16);
+                    v1[j] = ld16(ybuf + roff[j] + (p + 64) * 16);
+                }
+#pragma unroll
+            for (int j = 0; j < CMB_MAXK; ++j)
+                if (j < nk && roff[j] >= 0) {
+                    accum(a0, v0[j], g[j]);
+                    accum(a1, v1[j], g[j]);
+                }
+            out(a0, p);
+            out(a1, p + 64);
+        }
+        if (p < pieces) {
+            float a0[EPP];
+#pragma unroll
+            for (int q = 0; q < EPP; ++q) a0[q] = 0.f;
+#pragma unroll
+            for (int j = 0; j < CMB_MAXK; ++j)
+                if (j < nk && roff[j] >= 0) accum(a0, ld16(ybuf + roff[j] + p * 16), g[j]);
+            out(a0, p);
         }
     }
 }
