@@ -84,6 +84,8 @@ template <bool COHERENT>
 __device__ void tile_map_block(const int32_t *expert_count, int E, int bm, int32_t *tile_map, int *s_wsum) {
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
+    if (t < TAIL_SPLIT_SLOTS) tile_map[E + 1 + t] = 0;    // the split last wave's counters
+    static_assert(TAIL_SPLIT_SLOTS <= 256, "one counter per thread");
     int c[4];
     int local = 0;
 #pragma unroll

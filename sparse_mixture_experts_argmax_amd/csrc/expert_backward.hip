@@ -317,9 +317,9 @@ ExpertBwdWs expert_backward_ws(int E, int64_t C, int d, int f, int dtype_bf16, i
     const size_t Cp = (size_t)((C + 63) / 64 * 64);
     ExpertBwdWs w;
     size_t o = 0;
-    w.tmap_r = o;  o += up256((size_t)(E + 1) * 4);
-    w.tmap_d = o;  o += up256((size_t)(E + 1) * 4);
-    w.tmap_f = o;  o += up256((size_t)(E + 1) * 4);
+    w.tmap_r = o;  o += up256((size_t)tile_map_ints(E) * 4);
+    w.tmap_d = o;  o += up256((size_t)tile_map_ints(E) * 4);
+    w.tmap_f = o;  o += up256((size_t)tile_map_ints(E) * 4);
     w.cnt_d = o;   o += up256((size_t)E * 4);
     w.cnt_f = o;   o += up256((size_t)E * 4);
     w.a = o;       o += up256((size_t)E * C * f * es);
@@ -333,6 +333,7 @@ ExpertBwdWs expert_backward_ws(int E, int64_t C, int d, int f, int dtype_bf16, i
     w.ht = o;      o += up256((size_t)E * f * Cp * es);
     w.dat = o;     o += up256((size_t)E * f * Cp * es);
     w.dgt = o;     o += sw ? up256((size_t)E * f * Cp * es) : 0;
+    w.part = o;    o += up256(tail_split_bytes(dtype_bf16, C));   // the products over the experts' rows
     w.total = o;
     return w;
 }
@@ -379,11 +380,12 @@ hipError_t launch_expert_backward(const void *xbuf, int dtype_bf16, const int32_
     MOE_TRY(launch_tile_map(cnt_f, E, bm_f, tmap_f, s));
     const int64_t rows = (int64_t)E * C;
     // the pre-activations, recomputed: A = X W1^T (+ b1), G = X W3^T
+    float *part = w.part < w.total ? reinterpret_cast<float *>(ws + w.part) : nullptr;
     MOE_TRY(launch_grouped_gemm(xbuf, W1, nullptr, b1, dtype_bf16, 0, expert_count, tmap_r, bm_r, E, C, f, d, rows,
-                                Aa, s));
+                                Aa, s, nullptr, 0, nullptr, nullptr, part));
     if (sw)
         MOE_TRY(launch_grouped_gemm(xbuf, W3, nullptr, nullptr, dtype_bf16, 0, expert_count, tmap_r, bm_r, E, C, f,
-                                    d, rows, Ga, s));
+                                    d, rows, Ga, s, nullptr, 0, nullptr, nullptr, part));
     // the K-contiguous operands: W2t, W13t, dYt, Xt
     if (dtype_bf16) {
         MOE_TRY(transpose<uint16_t>(W2, (int64_t)d * f, f, d, f, nullptr, W2t, (int64_t)f * d, d, 0, d, E, s));
@@ -402,7 +404,7 @@ hipError_t launch_expert_backward(const void *xbuf, int dtype_bf16, const int32_
     }
     // dH = dY W2
     MOE_TRY(launch_grouped_gemm(dybuf, W2t, nullptr, nullptr, dtype_bf16, 0, expert_count, tmap_r, bm_r, E, C, f, d,
-                                rows, dH, s));
+                                rows, dH, s, nullptr, 0, nullptr, nullptr, part));
     // the activation backward: dA (and dG) row-major, H, dA (and dG) transposed
     {
         const dim3 grid((unsigned)((f + TT - 1) / TT), (unsigned)(Cp / TT), (unsigned)E);
@@ -421,7 +423,7 @@ hipError_t launch_expert_backward(const void *xbuf, int dtype_bf16, const int32_
     }
     // dX = [dA | dG] [W1; W3]
     MOE_TRY(launch_grouped_gemm(dAG, W13t, nullptr, nullptr, dtype_bf16, 0, expert_count, tmap_r, bm_r, E, C, d, nf,
-                                rows, dxbuf, s));
+                                rows, dxbuf, s, nullptr, 0, nullptr, nullptr, part));
     // the weight gradients, contracting over the (padded) rows of each expert
     // (bf16: each expert's sum stops after its own rows, in whole K tiles)
     const int32_t *kc = dtype_bf16 ? expert_count : nullptr;

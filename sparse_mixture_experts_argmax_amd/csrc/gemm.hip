@@ -36,6 +36,8 @@
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 x 16 tiles).
 #include "gemm_kernel.h"
 
+#include <atomic>
+
 namespace moe {
 
 namespace {
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     __shared__ int s_map[MAX_E_LDS + 1];
 
     int e, mt, nt;
-    if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt)) return;
+    SplitPart sp;
+    if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt, sp)) return;
     const int cnt = count[e];
     const int m0 = mt * FBM;
     const int n0 = nt * FBN;
@@ -113,11 +116,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     }
 }
 
-// tile_map[0] = 0, tile_map[e+1] = sum_{e' <= e} ceil(count[e'] / bm); one block
+// tile_map[0] = 0, tile_map[e+1] = sum_{e' <= e} ceil(count[e'] / bm); one block.
+// The split last wave's counters after it are cleared.
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t *__restrict__ count, int E, int bm,
                                                         int32_t *__restrict__ tile_map) {
     __shared__ int s[1024];
     const int t = threadIdx.x;
+    if (t < TAIL_SPLIT_SLOTS) tile_map[E + 1 + t] = 0;
     s[t] = (t < E) ? (count[t] + bm - 1) / bm : 0;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -148,6 +153,29 @@ int gemm_bm(int dtype_bf16, int64_t C, int act) {
     return 128;
 }
 
+size_t tail_split_bytes(int dtype_bf16, int64_t C) {
+    // a bf16 launch takes the tile map (and may split its last wave) when
+    // the capacity exceeds the row tile, which is at least 128 rows
+    if (!dtype_bf16 || C <= 128) return 0;
+    return (size_t)TAIL_SPLIT_SLOTS * TAIL_SPLIT_PART_FLOATS * sizeof(float);
+}
+
+// Compute units of the current device, read once per device; at most
+// TAIL_SPLIT_SLOTS (the split last wave's counters and partial slots).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+        v = n < TAIL_SPLIT_SLOTS ? n : TAIL_SPLIT_SLOTS;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s) {
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, expert_count, E, bm, tile_map);
@@ -158,7 +186,7 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
                                int dtype_bf16, int act, const int32_t *expert_count,
                                const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
                                int64_t rows_bound, void *out, hipStream_t s, const int32_t *row_tok,
-                               int64_t T, const float *gate, const int32_t *kcount) {
+                               int64_t T, const float *gate, const int32_t *kcount, float *split_part) {
     if (C == 0 || rows_bound == 0) return hipSuccess;
     if (row_tok != nullptr && (!dtype_bf16 || T < 1 || (act == 0 && gate == nullptr)))
         return hipErrorInvalidValue;
@@ -166,7 +194,17 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
     if (dtype_bf16) {
         // fused forward: the first GEMM gathers token rows, the second
         // scatters gated rows to y (out is then y)
-        FuseArgs fz{row_tok, T, gate, (uint16_t *)out, row_tok == nullptr ? 0 : (act == 0 ? 2 : 1), kcount};
+        FuseArgs fz{row_tok, T, gate, (uint16_t *)out, row_tok == nullptr ? 0 : (act == 0 ? 2 : 1), kcount,
+                    nullptr, nullptr, 0};
+        if (split_part != nullptr && C > bm) {
+            // the split last wave (tile-map launches): partial sums in
+            // split_part, counters after the tile map
+            fz.ncu = device_cus();
+            if (fz.ncu >= 8) {
+                fz.part = split_part;
+                fz.flags = const_cast<int32_t *>(tile_map) + E + 1;
+            }
+        }
         // the gated tiles exist for 128 and 256 rows only
         if ((bm != 128 && bm != 192 && bm != 256 && bm != 320) || (act == 2 && bm != 128 && bm != 256))
             return hipErrorInvalidValue;
@@ -174,8 +212,11 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
                        *bi = (const uint16_t *)bias;
         uint16_t *o = (uint16_t *)out;
         // row tiles an expert-parallel launch can expect (for the column-tile
-        // choice): one per expert when a tile holds the whole capacity
-        const int64_t mt_est = C <= bm ? (rows_bound < E ? rows_bound : E) : (rows_bound + bm - 1) / bm;
+        // choice): one per expert when a tile holds the whole capacity; with
+        // the tile map, E ceil(C / bm) whatever rows_bound, so that the fused
+        // forward and the split expert FFN pick the same column tiles and so
+        // split the same last wave (the same sums, bit for bit)
+        const int64_t mt_est = C <= bm ? (rows_bound < E ? rows_bound : E) : (int64_t)E * ((C + bm - 1) / bm);
         // a tile that holds the whole capacity goes by (expert, column tile)
         // without the tile map
         const bool expert = C <= bm;

@@ -20,6 +20,8 @@ namespace moe {
 // first kcount[e] columns of K, rounded up to the 64-wide K tile (at least
 // one tile), the rest being zeros it need not read (the weight-gradient
 // products contract over an expert's rows, padded to the capacity).
+// part (null = off): the split last wave's partial sums (tile-map launches
+// only; ncu = the device's compute units, at most TAIL_SPLIT_SLOTS).
 struct FuseArgs {
     const int32_t *row_tok;
     int64_t T;
@@ -27,6 +29,9 @@ struct FuseArgs {
     uint16_t *y;
     int mode;
     const int32_t *kcount;
+    float *part;
+    int32_t *flags;                                      // the counters after the tile map
+    int ncu;
 };
 
 // One grouped-GEMM launch (the arguments of launch_grouped_gemm, resolved):
@@ -50,20 +55,64 @@ namespace {
 
 constexpr int MAX_E_LDS = 1024;
 
+// A block's share of a split tile: part p of ns along K, in partial-sum slot
+// `slot` (ns = 1: the whole tile, no split).
+struct SplitPart {
+    int ns, p, slot;
+};
+
+// The split of the last wave.  With W < 8 full waves of ncu tiles and R
+// tiles left over, 0 < 2 R <= ncu, the R tiles of the last wave are each
+// split into ns = min(ncu / R, nk / 8, 8) parts along K (at least 8 K tiles
+// per part), so that the last wave keeps the whole chip busy for 1 / ns of a
+// tile's time instead of R / ncu of it for a whole tile's.  Measured on the
+// Mixtral-shaped layer: its second GEMM (4 waves + 80 tiles of 224 K tiles)
+// 1960 -> 1715 us; its first (30 waves + 48 tiles of 64) was 2 % slower
+// split, as tiles of unequal height already stagger the end of a long launch.
+__device__ __forceinline__ int split_count(int total, int ncu, int nk) {
+    if (ncu < 8 || total <= 0 || total >= 8 * ncu) return 1;
+    const int R = total % ncu;
+    if (R == 0 || 2 * R > ncu) return 1;
+    int ns = ncu / R;
+    ns = ns < nk / 8 ? ns : nk / 8;
+    ns = ns < 8 ? ns : 8;
+    return ns < 2 ? 1 : ns;
+}
+
 // Which tile this block computes (tile_map staged in LDS).  Returns false if none.
 // Order: expert-major, then column tile, then row tile; block b of XCD b % 8
-// takes the (b / 8)-th tile of that XCD's contiguous share.
+// takes the (b / 8)-th tile of that XCD's contiguous share.  With a split
+// last wave (split_count > 1) the first W ncu blocks take the first W ncu
+// tiles that way and the blocks after them take the parts of the rest,
+// tile by tile; the hardware hands out blocks in index order, so those run
+// last.
 __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ tile_map, int E, int tiles_n,
-                                         int *s_map, int &e, int &mt, int &nt) {
+                                         int *s_map, int &e, int &mt, int &nt, SplitPart &sp, int ncu = 0,
+                                         int nk = 0) {
     for (int i = threadIdx.x; i <= E; i += blockDim.x) s_map[i] = tile_map[i];
     __syncthreads();
     const int total = s_map[E] * tiles_n;
-    const int per_xcd = (total + 7) >> 3;
+    const int ns = split_count(total, ncu, nk);
+    const int ndp = ns > 1 ? total - total % ncu : total;       // tiles of the whole waves
     const int b = blockIdx.x;
-    const int slot = b >> 3;
-    if (slot >= per_xcd) return false;
-    const int L = (b & 7) * per_xcd + slot;
-    if (L >= total) return false;
+    int L;
+    sp.ns = 1;
+    sp.p = 0;
+    sp.slot = 0;
+    if (b < ((ndp + 7) & ~7)) {
+        const int per_xcd = (ndp + 7) >> 3;
+        const int slot = b >> 3;
+        L = (b & 7) * per_xcd + slot;
+        if (L >= ndp) return false;
+    } else {
+        const int q = b - ((ndp + 7) & ~7);
+        if (ns == 1 || q >= (total - ndp) * ns) return false;
+        const int st = q / ns;
+        sp.ns = ns;
+        sp.p = q - st * ns;
+        sp.slot = q;
+        L = ndp + st;
+    }
     int lo = 0, hi = E - 1;           // largest e with s_map[e] * tiles_n <= L
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -188,6 +237,14 @@ struct TileCtx {
     // of the 8-row group: 4 i + wave for A, wave BI + j for B, BI even)
     int K, m0, lane, wave, lr, lcA, lcB[2], nk;
     bool tailA, tailB[2];                                          // piece past K in the last K tile
+    // split last wave: this block's K range starts kofs elements in (the DMA
+    // sources are offset once, so the K loop is the same for every block);
+    // sp says which part of the tile it holds
+    int kofs;
+    SplitPart sp;
+    float *part;
+    int32_t *flags;
+    int *sflag;                                                    // LDS: this part is the last
 
     __device__ __forceinline__ void set_lanes(int lane_, int wave_, int K_) {
         lane = lane_;
@@ -220,7 +277,7 @@ struct TileCtx {
         for (int i = 0; i < NA; ++i) {
             int am = m0 + (4 * i + wave) * RPI + lr;
             am = am < last ? am : last;
-            asrc[i] = Ae + (int64_t)am * K + lcA * 8;
+            asrc[i] = Ae + (int64_t)am * K + lcA * 8 + kofs;
         }
     }
     // gathering: the tokens of the rows the A instructions cover (rows past
@@ -237,11 +294,13 @@ struct TileCtx {
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
             const int64_t t = (uint32_t)tok[i];
-            asrc[i] = Ae + (t < arows ? t : arows - 1) * K + lcA * 8;
+            asrc[i] = Ae + (t < arows ? t : arows - 1) * K + lcA * 8 + kofs;
         }
     }
-    // K offset (elements) of K tile kt for A and for B group j: the pieces
-    // past K of the last K tile read column 0 instead
+    // K offset (elements, from the block's first K tile) of K tile kt for A
+    // and for B group j: the pieces past K of the last K tile read the
+    // block's first column instead (in bounds; a part other than the last of
+    // a split tile has no tail: its tail flags are cleared)
     template <bool KTAIL>
     __device__ __forceinline__ int ka(int kt) const {
         return (KTAIL && kt == nk - 1 && tailA) ? -lcA * 8 : kt * BK;
@@ -255,8 +314,8 @@ struct TileCtx {
 // DMA of K tile kt into one stage: NA instructions of A, then those of B (and
 // B3).  Lane l lands at byte 16 l of its 1 KB group = row l / PIECES,
 // position l % PIECES, which holds logical piece (l % PIECES) ^ swz(row).  The
-// pieces past K (K % BK != 0) of the last K tile are read from column 0 and
-// cleared in LDS once they have landed.
+// pieces past K (K % BK != 0) of the last K tile are read from the block's
+// first column and cleared in LDS once they have landed.
 // PARTS: 1 = the A instructions (K tile kta into abase), 2 = the weight
 // instructions (K tile ktb into bbase), 3 = both (the waits count the
 // instructions issued after a stage's own, so the order matters).
@@ -589,6 +648,72 @@ __device__ __forceinline__ void tile_body(X &c, const uint16_t *__restrict__ bia
 #undef MOE_TAILS
 #undef MOE_TAIL
 
+    // ---- split last wave: every part stores its fp32 sums (lane-major, so
+    // the stores and loads are 16-byte and coalesced); the last part to finish
+    // adds all of them in part order, so the result does not depend on which
+    // part finishes last, and goes on to the epilogue
+    if (c.sp.ns > 1) {
+        constexpr int PF4 = TAIL_SPLIT_PART_FLOATS / 4;
+        static_assert(FV * FN * NBT * 16 * 256 <= TAIL_SPLIT_PART_FLOATS, "partial-sum slot");
+        const int tid = threadIdx.x;
+        f32x4 *own = reinterpret_cast<f32x4 *>(c.part) + (size_t)c.sp.slot * PF4;
+#pragma unroll
+        for (int i = 0; i < FV; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    own[(((i * FN + j) * 4 + v) << 8) + tid] =
+                        f32x4{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+                    if (DUAL)
+                        own[((((FV + i) * FN + j) * 4 + v) << 8) + tid] =
+                            f32x4{acc3[DUAL ? i : 0][DUAL ? j : 0][4 * v], acc3[DUAL ? i : 0][DUAL ? j : 0][4 * v + 1],
+                                  acc3[DUAL ? i : 0][DUAL ? j : 0][4 * v + 2], acc3[DUAL ? i : 0][DUAL ? j : 0][4 * v + 3]};
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        const int tile_slot = c.sp.slot / c.sp.ns;
+        // every wave's stores have reached L2; one device-scope release fence
+        // (it writes back the whole L2, so once per block) makes them visible
+        // before the count, and the last part's acquire fence (it invalidates
+        // this CU's L1 and the L2) comes before any wave reads the others'
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            __threadfence();
+            *c.sflag = atomicAdd(c.flags + tile_slot, 1) == c.sp.ns - 1;
+            if (*c.sflag) __threadfence();
+        }
+        __syncthreads();
+        if (!*c.sflag) return;
+        const f32x4 *first = reinterpret_cast<const f32x4 *>(c.part) + (size_t)(c.sp.slot - c.sp.p) * PF4 + tid;
+        const int ns = c.sp.ns;
+        // one 16-byte piece at a time through the parts (few live registers:
+        // the accumulators fill the register file)
+        auto total = [&](int f, int v) -> f32x4 {
+            const f32x4 *src = first + (((f * 4 + v)) << 8);
+            f32x4 t = src[0];
+            for (int q = 1; q < ns; ++q) t += src[(size_t)q * PF4];
+            return t;
+        };
+#pragma unroll
+        for (int i = 0; i < FV; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const f32x4 t = total(i * FN + j, v);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[i][j][4 * v + u] = t[u];
+                    if (DUAL) {
+                        const f32x4 t3 = total((FV + i) * FN + j, v);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) acc3[DUAL ? i : 0][DUAL ? j : 0][4 * v + u] = t3[u];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        if (tid == 0) c.flags[tile_slot] = 0;            // cleared for the next launch
+    }
+
     // ---- epilogue: bias, activation, bf16.  With STAGED_OUT the rows of wave
     // row wm go to stage buffer wm (16-byte pieces swizzled by row), so that
     // rows leave as coalesced 16-byte stores; otherwise each lane stores its
@@ -727,8 +852,10 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     __shared__ int s_map[EXPERT ? 1 : MAX_E_LDS + 1];
     __shared__ int s_tok[BM];                            // scattering: token and gate of each row
     __shared__ float s_g[BM];
+    __shared__ int s_last;
 
     int e, mt, nt;
+    SplitPart sp{1, 0, 0};
     if (EXPERT) {
         // expert-major, then column tile; block b of XCD b % 8 takes the
         // (b / 8)-th tile of that XCD's contiguous share
@@ -741,7 +868,10 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
         nt = L - e * tiles_n;
         mt = 0;
     } else {
-        if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt)) return;
+        // the split last wave needs whole K loops (no per-expert K) and the
+        // partial-sum buffer
+        const int ncu = (fz.part != nullptr && fz.kcount == nullptr) ? fz.ncu : 0;
+        if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt, sp, ncu, (K + TL::BK - 1) / TL::BK)) return;
     }
 
     X c;
@@ -753,6 +883,25 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
         const int kc = fz.kcount[e];
         const int nke = (kc + TL::BK - 1) / TL::BK;
         c.nk = nke < 1 ? 1 : (nke < c.nk ? nke : c.nk);
+    }
+    c.kofs = 0;
+    c.sp = SplitPart{1, 0, 0};
+    c.part = fz.part;
+    c.flags = fz.flags;
+    c.sflag = &s_last;
+    if constexpr (!EXPERT) {
+        // wave-uniform (scalar registers: the vector ones are all taken)
+        c.sp.ns = __builtin_amdgcn_readfirstlane(sp.ns);
+        c.sp.p = __builtin_amdgcn_readfirstlane(sp.p);
+        c.sp.slot = __builtin_amdgcn_readfirstlane(sp.slot);
+    }
+    if (c.sp.ns > 1) {
+        // K tiles [p nk / ns, (p + 1) nk / ns): at least 8 each; only the
+        // last part holds the K tail
+        const int k0 = c.sp.p * c.nk / c.sp.ns, k1 = (c.sp.p + 1) * c.nk / c.sp.ns;
+        c.kofs = __builtin_amdgcn_readfirstlane(k0) * TL::BK;
+        c.nk = __builtin_amdgcn_readfirstlane(k1 - k0);
+        if (c.sp.p != c.sp.ns - 1) c.tailA = c.tailB[0] = c.tailB[1] = false;
     }
     c.m0 = mt * BM;
     c.b3off = X::DUAL ? (int64_t)(B3 - B) : 0;
@@ -771,7 +920,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
         for (int j = 0; j < TL::BI; ++j) {
             int bn = n0 + (c.wave * TL::BI + j) * X::RPI + c.lr;
             bn = bn < N ? bn : N - 1;
-            c.bsrc[j] = Be + (int64_t)bn * K + c.lcB[j & 1] * 8;
+            c.bsrc[j] = Be + (int64_t)bn * K + c.lcB[j & 1] * 8 + c.kofs;
         }
     }
     // prologue: K tiles 0 .. S - 2 with every A row (clamped to the last row
@@ -865,8 +1014,10 @@ using TileG128 = Tile<128, 128, 3, 64, 1, 0>;
 template <class TL, int ACT, bool BIAS>
 hipError_t launch_bf16_tile(const GemmArgs &g) {
     const int tiles_n = (g.N + TL::BN - 1) / TL::BN;
+    // tile-map launches: up to ncu more blocks for the parts of a split last wave
+    const int64_t extra = (!g.expert && g.fz.part != nullptr && g.fz.kcount == nullptr) ? g.fz.ncu : 0;
     const dim3 grid((unsigned)(g.expert ? (((int64_t)g.E * tiles_n + 7) / 8) * 8
-                                        : grid_for(g.C, g.E, TL::BM, tiles_n, g.rows_bound)));
+                                        : grid_for(g.C, g.E, TL::BM, tiles_n, g.rows_bound) + extra));
 #define MOE_GEMM_L(KT, EXP, NT)                                                                   \
     hipLaunchKernelGGL((gemm_bf16_kernel<TL, ACT, BIAS, KT, EXP, NT>), grid, dim3(256), 0, g.s, g.a, \
                        g.b, g.b3, g.bias, g.count, g.tile_map, g.E, g.C, g.N, g.K, tiles_n, g.out, g.fz)

@@ -123,8 +123,21 @@ hipError_t launch_permute(const void *x, int elem_bytes, const int32_t *expert_i
 // ---- experts ----------------------------------------------------------
 // Row-tile height of the grouped GEMM (act: 0 none, 1 relu, 2 swiglu, the
 // activation of the first GEMM; both GEMMs use the same height); tile_map
-// holds E+1 prefix sums of ceil(expert_count / gemm_bm(dtype, C, act)).
+// holds E+1 prefix sums of ceil(expert_count / gemm_bm(dtype, C, act)),
+// followed by TAIL_SPLIT_SLOTS completion counters of the split last wave
+// (below), which every builder of the map clears.
 int gemm_bm(int dtype_bf16, int64_t C, int act);
+constexpr int TAIL_SPLIT_SLOTS = 256;
+inline int64_t tile_map_ints(int E) { return (int64_t)E + 1 + TAIL_SPLIT_SLOTS; }
+// The split last wave: a tile-map launch whose tiles leave a last wave at most
+// half full splits each of those tiles' K loop over up to 8 blocks; each
+// block stores its fp32 partial sums (TAIL_SPLIT_PART_FLOATS per block, at
+// most TAIL_SPLIT_SLOTS blocks) and the last to finish adds them in part
+// order and runs the epilogue.  Bytes of that partial buffer for a bf16
+// launch over experts of capacity C (0 when none is needed: one tile per
+// expert, or fp32).
+constexpr int TAIL_SPLIT_PART_FLOATS = 256 * 256;
+size_t tail_split_bytes(int dtype_bf16, int64_t C);
 hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *tile_map,
                            hipStream_t s);
 // out[e, m, :] = act(A[e, m, :] . B[e]^T (+ bias[e]))  for m < count[e]
@@ -135,12 +148,15 @@ hipError_t launch_tile_map(const int32_t *expert_count, int E, int bm, int32_t *
 // row_tok[e C + m].  With act != 0, A is x [T, K] and the expert rows are
 // gathered from it; with act == 0, out is y [T, N] and each output row goes
 // to its token's row scaled by row_gate[e C + m] (one choice per token).
+// split_part: tail_split_bytes(dtype, C) bytes for the split last wave, or
+// null (no split); the counters follow the tile map.
 hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, const void *bias,
                                int dtype_bf16, int act, const int32_t *expert_count,
                                const int32_t *tile_map, int bm, int E, int64_t C, int N, int K,
                                int64_t rows_bound, void *out, hipStream_t s,
                                const int32_t *row_tok = nullptr, int64_t T = 0,
-                               const float *row_gate = nullptr, const int32_t *kcount = nullptr);
+                               const float *row_gate = nullptr, const int32_t *kcount = nullptr,
+                               float *split_part = nullptr);
 
 // ---- expert-side backward (expert_backward.hip) ----------------------------
 // Byte offsets of the backward's scratch inside one workspace: tile maps and
@@ -149,7 +165,7 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
 // transposed activations dYt, Xt [E, d, Cp], Ht, dAt (, dGt) [E, f, Cp],
 // Cp = C rounded up to 64.
 struct ExpertBwdWs {
-    size_t tmap_r, tmap_d, tmap_f, cnt_d, cnt_f, a, g, dh, dag, w2t, w13t, dyt, xt, ht, dat, dgt, total;
+    size_t tmap_r, tmap_d, tmap_f, cnt_d, cnt_f, a, g, dh, dag, w2t, w13t, dyt, xt, ht, dat, dgt, part, total;
 };
 ExpertBwdWs expert_backward_ws(int E, int64_t C, int d, int f, int dtype_bf16, int act);
 // The gradients of the grouped expert FFN (act 1 ReLU, 2 SwiGLU) given dybuf

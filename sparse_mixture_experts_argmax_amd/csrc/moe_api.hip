@@ -76,14 +76,18 @@ PriorityWs priority_ws(int64_t T, int E, int k) {
     return w;
 }
 
+// The expert FFN's scratch: the tile map (with the split last wave's
+// counters after it), the hidden activations H, and the split last wave's
+// partial sums.
 struct FfnWs {
-    size_t tile_map, h, total;
+    size_t tile_map, h, part, total;
 };
 FfnWs ffn_ws(int E, int64_t C, int dff, moe_dtype dt) {
     FfnWs w;
     w.tile_map = 0;
-    w.h = up((size_t)(E + 1) * 4);
-    w.total = w.h + up((size_t)E * C * dff * esize(dt));
+    w.h = up((size_t)moe::tile_map_ints(E) * 4);
+    w.part = w.h + up((size_t)E * C * dff * esize(dt));
+    w.total = w.part + up(moe::tail_split_bytes(dt == MOE_BF16, C));
     return w;
 }
 
@@ -227,14 +231,15 @@ moe_status run_ffn(const void *xbuf, moe_dtype dt, const int32_t *expert_count, 
     const FfnWs w = ffn_ws(E, C, dff, dt);
     int32_t *tile_map = reinterpret_cast<int32_t *>(ws + w.tile_map);
     void *H = ws + w.h;
+    float *part = w.part < w.total ? reinterpret_cast<float *>(ws + w.part) : nullptr;
     const int bf16 = dt == MOE_BF16;
     const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
     const int bm = moe::gemm_bm(bf16, C, act1);
     MOE_HIP(moe::launch_tile_map(expert_count, E, bm, tile_map, stream));
     MOE_HIP(moe::launch_grouped_gemm(xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map, bm, E, C,
-                                     dff, d, rows_bound, H, stream));
+                                     dff, d, rows_bound, H, stream, nullptr, 0, nullptr, nullptr, part));
     MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, bm, E, C,
-                                     d, dff, rows_bound, ybuf, stream));
+                                     d, dff, rows_bound, ybuf, stream, nullptr, 0, nullptr, nullptr, part));
     return MOE_OK;
 }
 
@@ -686,6 +691,7 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     const int bf16 = dt == MOE_BF16;
     int32_t *tile_map = reinterpret_cast<int32_t *>(base + w.ffn + w.f.tile_map);
     void *H = base + w.ffn + w.f.h;
+    float *part = w.f.part < w.f.total ? reinterpret_cast<float *>(base + w.ffn + w.f.part) : nullptr;
     const int64_t rows = T * (int64_t)k;
     const int act1 = (act == MOE_ACT_SWIGLU) ? 2 : 1;
     const int bm = moe::gemm_bm(bf16, C, act1);
@@ -720,12 +726,12 @@ moe_status forward_impl(const void *x, moe_dtype dt, const float *W_r, const flo
     if (!mark(2)) return MOE_ERR_HIP;
     if (C > 0)
         MOE_HIP(moe::launch_grouped_gemm(gather ? x : xbuf, W1, W3, b1, bf16, act1, expert_count, tile_map,
-                                         bm, E, C, dff, d, rows, H, stream, row_tok, T));
+                                         bm, E, C, dff, d, rows, H, stream, row_tok, T, nullptr, nullptr, part));
     if (!mark(3)) return MOE_ERR_HIP;
     if (C > 0)
         MOE_HIP(moe::launch_grouped_gemm(H, W2, nullptr, b2, bf16, 0, expert_count, tile_map, bm, E, C, d,
                                          dff, rows, scatter ? y : ybuf, stream, scatter ? row_tok : nullptr,
-                                         T, row_gate));
+                                         T, row_gate, nullptr, part));
     if (!mark(4)) return MOE_ERR_HIP;
     if (!scatter)
         MOE_HIP(moe::launch_combine(ybuf, bf16, expert_idx, slot, gate, prob_sum, route_count, T, d, E,

@@ -99,3 +99,42 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, rows: np.ndarray, dtype: str, 
     ratio = err.sum() / denom if denom > 0 else err.sum()
     assert ratio <= l1, f"mean relative error {ratio:.3e}"
     return float(err.max()), float(ratio), worst
+
+
+# ---------------------------------------------------------------------------
+# Which bf16 grouped-GEMM launches split their last wave of tiles along K.
+# A restatement of the library's launch rules (row tile, column tile, the
+# split count), used only to check that a test case reaches that path.
+# ---------------------------------------------------------------------------
+
+def gemm_row_tile(C: int, act: str) -> int:
+    if C >= 512:
+        return 256
+    if act != "swiglu" and 256 < C <= 320:
+        return 320
+    if act != "swiglu" and 128 < C <= 192:
+        return 192
+    return 128
+
+
+def tail_split_parts(counts, C: int, E: int, act: str, N: int, K: int, gated: bool = False,
+                     ncu: int = 256) -> int:
+    """Parts per tile of the last wave (1 = no split) of one launch over
+    `counts` rows per expert; `act` is the first GEMM's activation (it sets the
+    row tile of both), `gated` marks the SwiGLU first GEMM."""
+    bm = gemm_row_tile(C, act)
+    if C <= bm:
+        return 1
+    row_tiles = int(sum((int(c) + bm - 1) // bm for c in counts))
+    if gated:
+        bn = 128
+    else:
+        mt_est = E * ((C + bm - 1) // bm)
+        bn = 256 if mt_est * ((N + 255) // 256) >= 256 else 128
+    total = row_tiles * ((N + bn - 1) // bn)
+    nk = (K + 63) // 64
+    R = total % ncu
+    if total == 0 or total >= 8 * ncu or R == 0 or 2 * R > ncu:
+        return 1
+    ns = min(ncu // R, nk // 8, 8)
+    return ns if ns >= 2 else 1

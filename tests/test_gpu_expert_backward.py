@@ -18,7 +18,7 @@ import torch
 import datagen
 import sparse_mixture_experts_argmax_amd as moe
 from error_bound import U, check_elementwise, expert_backward_bound
-from gpu_util import dev, device_inputs, host_bits, host_f64
+from gpu_util import dev, device_inputs, host_bits, host_f64, tail_split_parts
 from oracle import moe as O
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +68,10 @@ SMALL = {
     "tiles_320": (19200, 72, 136, 64, 1, 1.0, "bf16", "relu", False),
     "f32_relu_bias": (300, 24, 40, 4, 1, 1.25, "f32", "relu", True),
     "f32_swiglu": (200, 16, 24, 3, 2, 1.5, "f32", "swiglu", False),
+    # long K and a last wave of tiles under half the chip: the products over
+    # the experts' rows split that wave along K
+    "split_swiglu": (1200, 1024, 1536, 4, 2, 1.25, "bf16", "swiglu", False),
+    "split_relu": (1200, 1024, 1536, 4, 1, 1.25, "bf16", "relu", True),
 }
 
 
@@ -202,3 +206,16 @@ def test_expert_backward_no_rows():
     torch.cuda.synchronize()
     for o in (outs[1], outs[3], outs[4], outs[5]):
         assert (o.float() == 0).all()
+
+
+@pytest.mark.parametrize("name", ["split_swiglu", "split_relu"])
+def test_split_cases_reach_the_split(name):
+    """Precondition of the split cases: the recomputed pre-activations, dH or dX split
+    their last wave of tiles (the products over the experts' rows; act none)."""
+    cfg, C, _, count, _ = _small_inputs(name)
+    cnt = count.cpu().numpy()
+    d, f, E = cfg["d"], cfg["f"], cfg["E"]
+    nf = 2 * f if cfg["act"] == "swiglu" else f
+    parts = [tail_split_parts(cnt, C, E, "none", f, d), tail_split_parts(cnt, C, E, "none", d, nf)]
+    print(f"{name}: counts {cnt.tolist()}, parts per split tile: A/dH {parts[0]}, dX {parts[1]}", flush=True)
+    assert max(parts) > 1

@@ -15,7 +15,7 @@ import sparse_mixture_experts_argmax_amd as moe
 from oracle import moe as O
 from error_bound import check_elementwise, expert_bound
 from gpu_util import (AUX_RTOL, Y_TOL, Z_RTOL, check_routing, check_y, device_inputs, host_bits,
-                      host_f64, layer_bound)
+                      host_f64, layer_bound, tail_split_parts)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,14 @@ SMALL = {
     # capacity 240: row tiles of 128 from the tile map, in the wide column
     # tiles (first GEMM), with K and N tails
     "tiles_128": (12288, 72, 776, 64, 1, 1.25, "bf16", "relu", True, False, 1.0),
+    # a last wave of tiles under half the chip, long K: each of those tiles
+    # is split along K over several blocks (fused gather and scatter with
+    # k = 1, the K tail with d = 1000, ybuf and the combine with k = 2)
+    "split_relu": (1200, 1536, 2048, 2, 1, 1.0, "bf16", "relu", True, False, 1.0),
+    "split_swiglu": (1100, 1000, 1536, 2, 1, 1.0, "bf16", "swiglu", False, False, 1.0),
+    "split_top2": (1000, 1024, 1024, 4, 2, 1.25, "bf16", "relu", False, True, 2.0),
 }
+SPLIT = ["split_relu", "split_swiglu", "split_top2"]
 
 
 def _small(name, seed=0):
@@ -193,9 +200,11 @@ def test_forward_small(name):
     _forward_checks(_small(name))
 
 
-def test_split_api_equals_forward():
-    """router -> dispatch -> expert_ffn -> combine gives the fused call's outputs bitwise."""
-    cfg = _small("top2_swiglu", seed=3)
+@pytest.mark.parametrize("name", ["top2_swiglu"] + SPLIT)
+def test_split_api_equals_forward(name):
+    """router -> dispatch -> expert_ffn -> combine gives the fused call's outputs bitwise
+    (also when the GEMMs split their last wave of tiles)."""
+    cfg = _small(name, seed=3)
     t = device_inputs(cfg)
     C = moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
     idx, gate, ps, rc, zl = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"], z_loss=True)
@@ -277,7 +286,7 @@ def _ffn_rows(cfg, per_block=None, seed=7):
 
 @pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "tiles_320",
                                   "tiles_192", "tiles_128", "ragged_f32", "switch_base", "zipf_skew",
-                                  "mixtral", "many_expert"])
+                                  "mixtral", "many_expert"] + SPLIT)
 def test_expert_ffn_elementwise(name):
     """Each GEMM tile shape against the oracle's expert FFN, every element of the checked rows
     within its rounding bound; the L1 ratio of the layer's tolerance on top."""
@@ -289,3 +298,20 @@ def test_expert_ffn_elementwise(name):
     print(f"expert FFN parity: {name}, {n} rows, max-abs {err.max():.3e}, L1 ratio {ratio:.3e}, "
           f"largest error/bound {worst:.3f}", flush=True)
     assert ratio <= Y_TOL[cfg["dtype"]][1]
+
+
+@pytest.mark.parametrize("name", SPLIT)
+def test_split_cases_reach_the_split(name):
+    """Precondition of the split cases: on the GPU's own expert counts, at least one
+    of their two GEMMs splits its last wave (else they would test nothing new)."""
+    cfg = _small(name)
+    t = device_inputs(cfg)
+    C = moe.capacity(cfg["T"], cfg["E"], cfg["k"], cfg["cf"])
+    idx, _, _, _ = moe.router(t["x"], t["W_r"], k=cfg["k"], b_r=t["b_r"])
+    _, _, count, _ = moe.dispatch(t["x"], idx, cfg["E"], C)
+    cnt = count.cpu().numpy()
+    d, f, E = cfg["d"], cfg["f"], cfg["E"]
+    g1 = tail_split_parts(cnt, C, E, cfg["act"], f, d, gated=cfg["act"] == "swiglu")
+    g2 = tail_split_parts(cnt, C, E, cfg["act"], d, f)
+    print(f"{name}: counts {cnt.tolist()}, parts per split tile: first GEMM {g1}, second {g2}", flush=True)
+    assert max(g1, g2) > 1
