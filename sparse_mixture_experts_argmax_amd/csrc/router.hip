@@ -105,7 +105,9 @@ struct RGeo {
     static constexpr int PERW = STAGE / 4096;            // 1 KB DMA instructions per wave per stage
     static constexpr int RPI = 1024 / ROWB;              // rows per DMA instruction
     static_assert(S >= 2 && STAGE % 4096 == 0, "router stage ring");
-    static __device__ __forceinline__ int swz(int r) { return KC == 64 ? (r & 7) : ((r >> 1) & 3); }
+    static __device__ __forceinline__ int swz(int r) {
+        return KC == 128 ? (r & 15) : KC == 64 ? (r & 7) : ((r >> 1) & 3);
+    }
 };
 
 template <int NB, int KC>
@@ -117,6 +119,12 @@ constexpr bool rgeo_ok() { return RM_LDS / ((3 * NB * 16 + RM_TOK_BLOCK) * KC * 
 // products are exact in fp32, so three v_mfma_f32_16x16x32_bf16 per 16
 // experts and 32 columns give the fp32 dot products.
 //
+// NB = 1 (E <= 16; KC = 128): one group of 16 experts would leave three waves
+// without work, so instead wave w takes the w-th 32 columns of every stage
+// for all 64 tokens, and the four partial logits are added in wave order
+// before the epilogue.  With 16 rather than 64 weight rows a stage holds
+// twice the token bytes of the wider kernels, and the ring keeps that much
+// more of x in flight.
 // NZ (noisy top-k, W3 from router_split_noisy_kernel):
 //  0  the plain router;
 //  1  W3 is the stacked weight with NB / 2 groups of 16 rows per half; lane
@@ -158,13 +166,17 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // part's EW rows repeat its last one), the rest the block's tokens (past
     // T: row T - 1)
     const int lr = lane / PIECES;
-    const int lc = (lane % PIECES) ^ G::swz(lr);
     const int EW = NZ == 1 ? EP : NZ == 2 ? 2 * EP : E;
     const int64_t nW = (int64_t)EW * d;
     const uint16_t *src[PERW];
+    // the logical piece this lane fetches for instruction i (its row's swizzle;
+    // with 64- and 32-wide stages that depends on lr alone)
+    int lcs[PERW];
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
         const int row = (wave * PERW + i) * RPI + lr;
+        const int lc = (lane % PIECES) ^ G::swz(row);
+        lcs[i] = lc;
         if (row < 3 * EP) {
             const int p = row / EP;
             int n = row - p * EP;
@@ -177,31 +189,32 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         }
     }
     const int nk = (d + KC - 1) / KC;
-    const bool tail_piece = KTAIL && ((nk - 1) * KC + lc * 8 >= d);
+    auto tail_piece = [&](int i) { return KTAIL && ((nk - 1) * KC + lcs[i] * 8 >= d); };
     auto issue = [&](uint8_t *base, int kt) {
-        const int k0 = (KTAIL && kt == nk - 1 && tail_piece) ? -lc * 8 : kt * KC;
 #pragma unroll
-        for (int i = 0; i < PERW; ++i)
+        for (int i = 0; i < PERW; ++i) {
+            const int k0 = (KTAIL && kt == nk - 1 && tail_piece(i)) ? -lcs[i] * 8 : kt * KC;
             __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(src[i] + k0),
                                              (MOE_LDS_AS void *)(base + (wave * PERW + i) * 1024),
                                              16, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
     // the pieces past d were loaded from column 0: clear them (products with a
     // zero operand on either side are zero)
     auto clear_tail = [&](uint8_t *base) {
-        if (tail_piece) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < PERW; ++i) *reinterpret_cast<u32x4 *>(base + (wave * PERW + i) * 1024 + lane * 16) = z;
-        }
+        for (int i = 0; i < PERW; ++i)
+            if (tail_piece(i)) *reinterpret_cast<u32x4 *>(base + (wave * PERW + i) * 1024 + lane * 16) = z;
     };
 
     // wave w computes the logits of all 64 tokens (4 row blocks of 16) for its
     // NBW groups of 16 experts, g = w NBW .. w NBW + NBW - 1: every weight
     // fragment read from LDS feeds 4 MFMAs
-    constexpr int NBW = NB / RM_WAVES;
-    static_assert(NB % RM_WAVES == 0, "expert groups per wave");
+    constexpr bool KSPLIT = NB < RM_WAVES;
+    constexpr int NBW = KSPLIT ? 1 : NB / RM_WAVES;
+    static_assert(KSPLIT ? (NB == 1 && KC == 128 && NZ == 0) : NB % RM_WAVES == 0, "expert groups per wave");
     f32x4 acc[4][NBW];
 #pragma unroll
     for (int ab = 0; ab < 4; ++ab)
@@ -211,11 +224,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // row bases are multiples of 16, so swz(row) = swz(col)
     const int fs = G::swz(col);
     const int arow = (3 * EP + col) * ROWB;
-    const int brow = (wave * NBW * 16 + col) * ROWB;
+    const int brow = ((KSPLIT ? 0 : wave * NBW * 16) + col) * ROWB;
     auto compute = [&](const uint8_t *sb) {
 #pragma unroll
-        for (int sub = 0; sub < KC / 32; ++sub) {
-            const int po = ((sub * 4 + kg) ^ fs) << 4;
+        for (int sub = 0; sub < (KSPLIT ? 1 : KC / 32); ++sub) {
+            const int po = (((KSPLIT ? wave : sub) * 4 + kg) ^ fs) << 4;
             bf16x8 a[4];
 #pragma unroll
             for (int ab = 0; ab < 4; ++ab)
@@ -328,7 +341,16 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // drained), then each wave takes 16 tokens across all experts
     constexpr int ZS = EP + 4;                           // fp32 row stride
     static_assert(32 * ZS * 4 <= STAGE, "logit rows fit a stage buffer");
+    static_assert(!KSPLIT || (S == 4 && 64 * ZS * 4 <= STAGE), "one stage buffer per wave's partial logits");
     lds_barrier();
+    if constexpr (KSPLIT) {
+        // wave w's partial sums (its columns of every stage) for all 64 tokens
+        float *zw = reinterpret_cast<float *>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zw[(ab * 16 + 4 * kg + i) * ZS + col] = acc[ab][0][i];
+    } else {
 #pragma unroll
     for (int ab = 0; ab < 4; ++ab)
 #pragma unroll
@@ -352,6 +374,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                     zr[n] = acc[ab][g][i];
                 }
             }
+    }
     lds_barrier();
 
     // ---- epilogue: lane holds logits of tokens tw + 4*kg + i, experts nb*16 + col
@@ -378,7 +401,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
         for (int nb = 0; nb < NE; ++nb) {
             const int n = nb * 16 + col;
-            float z = zr[n] + bias[nb];
+            // K split: the four waves' partial sums, in wave order
+            float z = KSPLIT ? ((reinterpret_cast<const float *>(st0)[tok * ZS + n] +
+                                 reinterpret_cast<const float *>(st1)[tok * ZS + n]) +
+                                reinterpret_cast<const float *>(st2)[tok * ZS + n]) +
+                                   reinterpret_cast<const float *>(st3)[tok * ZS + n] + bias[nb]
+                             : zr[n] + bias[nb];
             if (NZ == 1) {
                 // H = z + eps softplus(zn); softplus without overflow:
                 // max(a, 0) + log(1 + exp(-|a|))
@@ -718,6 +746,7 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
         else MOE_ROUTER_K(NBV, KCV, true);                                                     \
         return hipGetLastError();                                                              \
     }
+        MOE_ROUTER_CASE(1, 128)
         MOE_ROUTER_CASE(4, 64)
         MOE_ROUTER_CASE(8, 64)
         MOE_ROUTER_CASE(16, 32)
