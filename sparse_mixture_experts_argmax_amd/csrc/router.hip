@@ -13,8 +13,9 @@
 //    round-to-nearest bf16 of what the previous parts left, so the sum
 //    reproduces all 24 significand bits).  bf16 x bf16 products are exact
 //    in fp32, so three bf16 MFMAs with fp32 accumulation give an fp32 dot
-//    product without any fp32 vector FMA.  router_split makes the three
-//    parts once per call; a block of 64 tokens streams them and its token
+//    product without any fp32 vector FMA.  A block of 64 tokens streams W_r
+//    (fp32, split into its three parts in registers as each fragment is
+//    read; with 256 experts the parts, made once per call) and its token
 //    rows through a ring of LDS stages filled by 16-byte DMA, and each of
 //    its four waves computes the logits of all 64 tokens for a quarter of
 //    the experts.  The logits go through LDS to one wave per 16 tokens,
@@ -58,7 +59,9 @@ __device__ __forceinline__ void split3(float w, uint16_t &h, uint16_t &m, uint16
     l = f2bf(r2);
 }
 
-// W3[p][n][:] = part p of W_r[n][:] (p = 0 hi, 1 mid, 2 lo), once per call.
+// W3[p][n][:] = part p of W_r[n][:] (p = 0 hi, 1 mid, 2 lo), once per call
+// (the widest router, 256 experts, reads the parts; the narrower ones split
+// W_r in registers).
 __global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ Wr, int64_t n,
                                                            uint16_t *__restrict__ W3) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
@@ -91,15 +94,16 @@ __global__ __launch_bounds__(256) void router_split_noisy_kernel(const float *__
 }
 
 // Stage geometry of the MFMA router: a stage holds KC columns of the three
-// weight parts (3 x EP rows) and of the block's 64 token rows, in LDS rows of
+// weights (WR x EP rows: the three bf16 parts, or fp32 W_r with each row's
+// KC values in two LDS rows) and of the block's 64 token rows, in LDS rows of
 // KC bf16.  Piece c (16 bytes) of row r is stored at c ^ swz(r), as in the
 // expert GEMM: conflict-free 16-byte fragment reads and DMA writes.
-template <int NB, int KC>
+template <int NB, int KC, int WR = 3>
 struct RGeo {
     static constexpr int EP = NB * 16;
     static constexpr int ROWB = KC * 2;
     static constexpr int PIECES = KC / 8;
-    static constexpr int ROWS = 3 * EP + RM_TOK_BLOCK;
+    static constexpr int ROWS = WR * EP + RM_TOK_BLOCK;
     static constexpr int STAGE = ROWS * ROWB;
     static constexpr int S = RM_LDS / STAGE > 4 ? 4 : RM_LDS / STAGE;
     static constexpr int PERW = STAGE / 4096;            // 1 KB DMA instructions per wave per stage
@@ -110,14 +114,20 @@ struct RGeo {
     }
 };
 
-template <int NB, int KC>
-constexpr bool rgeo_ok() { return RM_LDS / ((3 * NB * 16 + RM_TOK_BLOCK) * KC * 2) >= 2; }
+template <int NB, int KC, int WR = 3>
+constexpr bool rgeo_ok() { return RM_LDS / ((WR * NB * 16 + RM_TOK_BLOCK) * KC * 2) >= 2; }
 
-// One block = 64 tokens (4 waves x 16) and every expert.  The three bf16
-// parts of W_r (exact split, see router_split_kernel) and the token rows flow
-// through an S-deep ring of LDS stages filled by 16-byte DMA; bf16 x bf16
-// products are exact in fp32, so three v_mfma_f32_16x16x32_bf16 per 16
-// experts and 32 columns give the fp32 dot products.
+// One block = 64 tokens (4 waves x 16) and every expert.  The weights and the
+// token rows flow through an S-deep ring of LDS stages filled by 16-byte DMA;
+// bf16 x bf16 products are exact in fp32, so three v_mfma_f32_16x16x32_bf16
+// per 16 experts and 32 columns, one per exact bf16 part of the weight, give
+// the fp32 dot products.  The plain router with up to 128 experts stages W_r
+// itself in fp32 and splits each fragment into its three parts in registers
+// as it reads it (split3: no launch of its own, and two thirds of the weight
+// bytes of the three parts: 7-12 % faster on 8 to 128 experts); with 256
+// experts the splitting takes more vector ALU time than it saves (3 % slower
+// on many_expert), so that form, like the noisy ones, reads the parts that
+// router_split_kernel (router_split_noisy_kernel) made.
 //
 // NB = 1 (E <= 16; KC = 128): one group of 16 experts would leave three waves
 // without work, so instead wave w takes the w-th 32 columns of every stage
@@ -136,11 +146,14 @@ constexpr bool rgeo_ok() { return RM_LDS / ((3 * NB * 16 + RM_TOK_BLOCK) * KC * 
 //     (token, expert) entries before they go to LDS.
 template <int NB, int KC, bool KTAIL, int KSEL, int NZ>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ br,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ Wf,
+    const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
     float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z,
     const float *__restrict__ eps, float *__restrict__ logits) {
-    using G = RGeo<NB, KC>;
+    constexpr bool WF32 = NZ == 0 && NB <= 8;           // fp32 W_r, split in registers
+    constexpr int WR = WF32 ? 2 : 3;                     // LDS rows of weights per expert row
+    using G = RGeo<NB, KC, WR>;
     constexpr int EP = G::EP, ROWB = G::ROWB, PIECES = G::PIECES, S = G::S, PERW = G::PERW;
     constexpr int STAGE = G::STAGE, RPI = G::RPI;
     constexpr int NEWER = (S - 2) * PERW;
@@ -169,31 +182,46 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     const int EW = NZ == 1 ? EP : NZ == 2 ? 2 * EP : E;
     const int64_t nW = (int64_t)EW * d;
     const uint16_t *src[PERW];
-    // the logical piece this lane fetches for instruction i (its row's swizzle;
-    // with 64- and 32-wide stages that depends on lr alone)
-    int lcs[PERW];
+    // instruction i of this lane: the K column of its piece within a chunk
+    // (its row's swizzle decides which piece) and the source's 16-bit units
+    // per K column (2 for fp32 weight rows)
+    int coff[PERW], kmul[PERW];
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
         const int row = (wave * PERW + i) * RPI + lr;
         const int lc = (lane % PIECES) ^ G::swz(row);
-        lcs[i] = lc;
-        if (row < 3 * EP) {
-            const int p = row / EP;
-            int n = row - p * EP;
-            n = n < EW ? n : EW - 1;
-            src[i] = W3 + p * nW + (int64_t)n * d + lc * 8;
+        if (row < WR * EP) {
+            if constexpr (WF32) {
+                // fp32 row n: columns [0, KC / 2) of the chunk in LDS row 2n,
+                // the rest in 2n + 1; a 16-byte piece holds 4 of them
+                const int h = row & 1;
+                int n = row >> 1;
+                n = n < E ? n : E - 1;
+                coff[i] = h * (KC / 2) + lc * 4;
+                kmul[i] = 2;
+                src[i] = reinterpret_cast<const uint16_t *>(Wf + (int64_t)n * d + coff[i]);
+            } else {
+                const int p = row / EP;
+                int n = row - p * EP;
+                n = n < EW ? n : EW - 1;
+                coff[i] = lc * 8;
+                kmul[i] = 1;
+                src[i] = W3 + p * nW + (int64_t)n * d + coff[i];
+            }
         } else {
-            int64_t t = t0 + (row - 3 * EP);
+            int64_t t = t0 + (row - WR * EP);
             t = t < T ? t : T - 1;
-            src[i] = x + t * d + lc * 8;
+            coff[i] = lc * 8;
+            kmul[i] = 1;
+            src[i] = x + t * d + coff[i];
         }
     }
     const int nk = (d + KC - 1) / KC;
-    auto tail_piece = [&](int i) { return KTAIL && ((nk - 1) * KC + lcs[i] * 8 >= d); };
+    auto tail_piece = [&](int i) { return KTAIL && ((nk - 1) * KC + coff[i] >= d); };
     auto issue = [&](uint8_t *base, int kt) {
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
-            const int k0 = (KTAIL && kt == nk - 1 && tail_piece(i)) ? -lcs[i] * 8 : kt * KC;
+            const int k0 = ((KTAIL && kt == nk - 1 && tail_piece(i)) ? -coff[i] : kt * KC) * kmul[i];
             __builtin_amdgcn_global_load_lds((const MOE_GLB_AS void *)(src[i] + k0),
                                              (MOE_LDS_AS void *)(base + (wave * PERW + i) * 1024),
                                              16, 0, 0);
@@ -223,8 +251,33 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // fragment rows: A = token row ab 16 + col, B = weight row p EP + g 16 + col;
     // row bases are multiples of 16, so swz(row) = swz(col)
     const int fs = G::swz(col);
-    const int arow = (3 * EP + col) * ROWB;
+    const int arow = (WR * EP + col) * ROWB;
     const int brow = ((KSPLIT ? 0 : wave * NBW * 16) + col) * ROWB;
+    // fp32 weights: expert row n = g 16 + col (+ the wave's groups) sits in LDS
+    // rows 2n and 2n + 1; a lane's 8 columns k0 .. k0 + 7 (k0 = 32 sub + 8 kg)
+    // are two pieces of row 2n + k0 / (KC / 2)
+    auto wf_frag = [&](const uint8_t *sb, int g, int ksub, bf16x8 (&b)[3]) {
+        const int k0 = ksub * 32 + kg * 8;
+        const int R = 2 * ((KSPLIT ? 0 : wave * NBW * 16) + g * 16 + col) + k0 / (KC / 2);
+        const int pc = (k0 % (KC / 2)) / 4;
+        const int sw = G::swz(R);
+        const u32x4 w0 = *reinterpret_cast<const u32x4 *>(sb + R * ROWB + ((pc ^ sw) << 4));
+        const u32x4 w1 = *reinterpret_cast<const u32x4 *>(sb + R * ROWB + (((pc + 1) ^ sw) << 4));
+        u32x4 ph, pm, pl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 &w = q < 2 ? w0 : w1;
+            uint16_t h0, m0, l0, h1, m1, l1;
+            split3(__uint_as_float(w[(2 * q) & 3]), h0, m0, l0);
+            split3(__uint_as_float(w[(2 * q + 1) & 3]), h1, m1, l1);
+            ph[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            pm[q] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+            pl[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        b[0] = as_bf16x8(ph);
+        b[1] = as_bf16x8(pm);
+        b[2] = as_bf16x8(pl);
+    };
     auto compute = [&](const uint8_t *sb) {
 #pragma unroll
         for (int sub = 0; sub < (KSPLIT ? 1 : KC / 32); ++sub) {
@@ -236,12 +289,19 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
             for (int g = 0; g < NBW; ++g) {
                 const int o = brow + g * 16 * ROWB + po;
+                bf16x8 bp[3];
+                if constexpr (WF32) {
+                    wf_frag(sb, g, KSPLIT ? wave : sub, bp);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        bp[p] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + p * EP * ROWB + o));
+                }
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
-                    const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + p * EP * ROWB + o));
 #pragma unroll
                     for (int ab = 0; ab < 4; ++ab)
-                        acc[ab][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab], b, acc[ab][g], 0, 0, 0);
+                        acc[ab][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab], bp[p], acc[ab][g], 0, 0, 0);
                 }
             }
         }
@@ -271,7 +331,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
                 }
 #pragma unroll
             for (int i = 0; i < PERW; ++i)
-                if ((wave * PERW + i) * RPI + lr < 3 * EP) src[i] += (int64_t)EP * d;
+                if ((wave * PERW + i) * RPI + lr < WR * EP) src[i] += (int64_t)EP * d;
             lds_barrier();                               // every wave is done with the last stage
         }
         issue(st0, 0);
@@ -724,15 +784,19 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
     const int nblk = router_blocks(T, dtype_bf16, E);
     if (nblk == 0) return hipSuccess;
     if (use_mfma(dtype_bf16, E)) {
-        const int64_t n = (int64_t)E * d;
-        const int sg = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-        hipLaunchKernelGGL(router_split_kernel, dim3(sg), dim3(256), 0, s, W_r, n, w3);
-        const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
+        // up to 128 experts W_r is staged in fp32 and split into its bf16 parts
+        // in registers; beyond, the kernel reads the parts from w3
         const int nb = (E + 15) / 16;
+        if (nb > 8) {
+            const int64_t n = (int64_t)E * d;
+            const int sg = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+            hipLaunchKernelGGL(router_split_kernel, dim3(sg), dim3(256), 0, s, W_r, n, w3);
+        }
+        const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
 #define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
     hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
-                       0, s, xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt,     \
-                       part_z, nullptr, logits)
+                       0, s, xb, w3, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,          \
+                       part_cnt, part_z, nullptr, logits)
 #define MOE_ROUTER_K(NBV, KCV, TAILV)                                                          \
     do {                                                                                       \
         if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, 0);                                  \
@@ -741,7 +805,7 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
     } while (0)
 #define MOE_ROUTER_CASE(NBV, KCV)                                                              \
     if (nb <= NBV) {                                                                           \
-        static_assert(rgeo_ok<NBV, KCV>(), "router ring");                                     \
+        static_assert(rgeo_ok<NBV, KCV, NBV <= 8 ? 2 : 3>(), "router ring");                   \
         if (d % KCV == 0) MOE_ROUTER_K(NBV, KCV, false);                                       \
         else MOE_ROUTER_K(NBV, KCV, true);                                                     \
         return hipGetLastError();                                                              \
@@ -789,8 +853,8 @@ hipError_t launch_router_noisy(const void *x, int dtype_bf16, const float *W_r, 
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
 #define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
     hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
-                       0, s, xb, w3, b_r, T, d, E, k, expert_idx, gate, part_prob, part_cnt,     \
-                       part_z, eps, nullptr)
+                       0, s, xb, w3, nullptr, b_r, T, d, E, k, expert_idx, gate, part_prob,      \
+                       part_cnt, part_z, eps, nullptr)
 #define MOE_ROUTER_K(NBV, KCV, TAILV, NZV)                                                     \
     do {                                                                                       \
         if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, NZV);                                \
