@@ -151,8 +151,9 @@ moe_status moe_forward_workspace_layout(int64_t T, int32_t d, int32_t dff, int32
  *   logits      [T, E]  fp32 out, or NULL: the logits W_r x + b_r as the
  *                       softmax sees them (what moe_router_backward takes)
  *   ws          moe_router_workspace_bytes(T, d, E, k) bytes of device scratch
- *               (per-block partial sums, and for bf16 x with E <= 256 the
- *               exact three-part bf16 split of W_r that the MFMA path reads)
+ *               (per-block partial sums, and for bf16 x with E <= 256 room
+ *               for the exact three-part bf16 split of W_r, which the MFMA
+ *               path makes there for E > 128)
  * Logits are fp32 ([SW-RES] section 2.1); non-finite inputs do not fault
  * and still give indices in [0, E).
  */
@@ -309,8 +310,9 @@ moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, 
  *   [T, k] fp32 (from moe_combine_backward), alpha and z_weight the loss
  *   weights (0 leaves a term out).
  *   dlogits [T, E] fp32 out, dL/dz
- *   dW_r    [E, d] fp32 out, dlogits^T x (fp32, fixed order: 512-token
- *           partial sums, then their sum in order)
+ *   dW_r    [E, d] fp32 out, dlogits^T x (fp32, fixed order: partial sums
+ *           over chunks of 128, 256 or 512 tokens, the size fixed by T, d
+ *           and E, then their sum in chunk order)
  *   db_r    [E] fp32 out or NULL, sum_t dlogits_t
  *   dx      [T, d] fp32 out or NULL, the router's part of dL/dx, dlogits W_r
  *   ws      moe_router_backward_workspace_bytes(T, d, E) bytes of scratch

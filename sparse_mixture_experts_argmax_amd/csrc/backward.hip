@@ -210,7 +210,20 @@ __global__ __launch_bounds__(256) void router_bwd_dx_kernel(const float *__restr
         }
 }
 
-constexpr int DW_TC = 512;     // tokens per chunk (one partial row each)
+// Tokens per chunk (one partial row each): 512, halved down to 128 while the
+// grid has fewer than 1024 blocks.  Few experts and a narrow d leave few
+// blocks otherwise (Mixtral-shaped: 128 at 512 tokens), and each block
+// stages its tokens in turn; at 128 the gate-side backward ran 291 -> 201 us
+// there and 176 -> 137 us on switch_base.  With 256 experts the grid is
+// large already and smaller chunks only grow the partial sums (+12 %).
+int dw_expert_group(int E) { return E <= 16 ? 16 : 64; }
+int dw_chunk_tokens(int64_t T, int d, int E) {
+    const int eg = dw_expert_group(E);
+    const int64_t blocks = (int64_t)((d + 8 * (1024 / eg) - 1) / (8 * (1024 / eg))) * ((E + eg - 1) / eg);
+    int tc = 512;
+    while (tc > 128 && blocks * ((T + tc - 1) / tc) < 1024) tc /= 2;
+    return tc;
+}
 
 // part_w[chunk][n][c] = sum over the chunk's tokens t (in order) of
 // dz[t, n] x[t, c], as a register-tiled product: a block covers EG experts
@@ -220,7 +233,7 @@ constexpr int DW_TC = 512;     // tokens per chunk (one partial row each)
 template <bool BF16, int EG>
 __global__ __launch_bounds__(256) void router_bwd_dw_kernel(const float *__restrict__ dz,
                                                             const void *__restrict__ x, int64_t T, int d,
-                                                            int E, float *__restrict__ part_w,
+                                                            int E, int tc, float *__restrict__ part_w,
                                                             float *__restrict__ part_b) {
     constexpr int TY = EG / 4;                       // groups of 4 experts
     constexpr int TX = 256 / TY;                     // groups of 8 columns
@@ -233,8 +246,8 @@ __global__ __launch_bounds__(256) void router_bwd_dw_kernel(const float *__restr
     const int c0 = blockIdx.x * NC;
     const int n0 = blockIdx.y * EG;
     const int chunk = blockIdx.z;
-    const int64_t ta = (int64_t)chunk * DW_TC;
-    const int64_t tb = ta + DW_TC < T ? ta + DW_TC : T;
+    const int64_t ta = (int64_t)chunk * tc;
+    const int64_t tb = ta + tc < T ? ta + tc : T;
     float acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -316,7 +329,10 @@ __global__ __launch_bounds__(256) void router_bwd_dw_reduce_kernel(const float *
 
 }  // namespace
 
-int router_bwd_chunks(int64_t T) { return (int)((T + DW_TC - 1) / DW_TC); }
+int router_bwd_chunks(int64_t T, int d, int E) {
+    const int tc = dw_chunk_tokens(T, d, E);
+    return (int)((T + tc - 1) / tc);
+}
 
 hipError_t launch_combine_backward(const void *dy, int dtype_bf16, const void *ybuf, const int32_t *expert_idx,
                                    const int32_t *slot, const float *gate, int64_t T, int d, int E, int k,
@@ -339,7 +355,8 @@ hipError_t launch_router_backward(const void *x, int dtype_bf16, const float *W_
                                   const int32_t *route_count, int64_t T, int d, int E, int k, float alpha,
                                   float z_weight, float *dz, float *dW, float *db, float *dx, float *part_w,
                                   float *part_b, hipStream_t s) {
-    const int nchunk = router_bwd_chunks(T);
+    const int nchunk = router_bwd_chunks(T, d, E);
+    const int tc = dw_chunk_tokens(T, d, E);
     if (nchunk > 65535) return hipErrorInvalidValue;      // the grid's z extent
     if (T > 0) {
         hipLaunchKernelGGL(router_bwd_dz_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits,
@@ -354,12 +371,12 @@ hipError_t launch_router_backward(const void *x, int dtype_bf16, const float *W_
                      (unsigned)((E + EGV - 1) / EGV), (unsigned)nchunk);                                 \
         if (dtype_bf16)                                                                                  \
             hipLaunchKernelGGL((router_bwd_dw_kernel<true, EGV>), g, dim3(256), 0, s, dz, x, T, d, E,   \
-                               part_w, part_b);                                                          \
+                               tc, part_w, part_b);                                                      \
         else                                                                                             \
             hipLaunchKernelGGL((router_bwd_dw_kernel<false, EGV>), g, dim3(256), 0, s, dz, x, T, d, E,  \
-                               part_w, part_b);                                                          \
+                               tc, part_w, part_b);                                                      \
     } while (0)
-        if (E <= 16) MOE_DW(16);
+        if (dw_expert_group(E) == 16) MOE_DW(16);
         else MOE_DW(64);
 #undef MOE_DW
     }

@@ -86,9 +86,9 @@ hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *e
 // Backward of the gate side (backward.hip).  Combine: dgate [T, k] fp32 and
 // the kept rows of dybuf [E, C, d] (g dy, storage dtype).  Router: dz [T, E]
 // from the logits, gates and dgate; dW [E, d], db [E] (may be null) and dx
-// [T, d] (may be null), fp32; part_w [router_bwd_chunks(T)][E][d] and part_b
-// [router_bwd_chunks(T)][E] are scratch.
-int router_bwd_chunks(int64_t T);
+// [T, d] (may be null), fp32; part_w [router_bwd_chunks(T, d, E)][E][d] and
+// part_b [router_bwd_chunks(T, d, E)][E] are scratch.
+int router_bwd_chunks(int64_t T, int d, int E);
 hipError_t launch_combine_backward(const void *dy, int dtype_bf16, const void *ybuf, const int32_t *expert_idx,
                                    const int32_t *slot, const float *gate, int64_t T, int d, int E, int k,
                                    int64_t C, float *dgate, void *dybuf, hipStream_t s);

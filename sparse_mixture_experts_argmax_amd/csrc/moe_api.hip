@@ -534,7 +534,7 @@ moe_status moe_dispatch_reroute(const void *x, moe_dtype dt, const int32_t *pref
 
 size_t moe_router_backward_workspace_bytes(int64_t T, int32_t d, int32_t E) {
     if (check_sizes(T, E, 1) != MOE_OK || check_width(d) != MOE_OK) return SIZE_MAX;
-    const size_t nc = (size_t)moe::router_bwd_chunks(T);
+    const size_t nc = (size_t)moe::router_bwd_chunks(T, d, E);
     return up(nc * E * d * 4) + up(nc * E * 4);
 }
 
@@ -547,13 +547,13 @@ moe_status moe_router_backward(const void *x, moe_dtype dt, const float *W_r, co
     MOE_CHECK(check_width(d));
     if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
     const bool empty = T == 0;
-    if (moe::router_bwd_chunks(T) > 65535) return MOE_ERR_UNSUPPORTED;
+    if (moe::router_bwd_chunks(T, d, E) > 65535) return MOE_ERR_UNSUPPORTED;
     if (!ptr_ok(x, empty) || !ptr_ok(W_r, false) || !ptr4_ok(logits, empty) || !ptr4_ok(expert_idx, empty) ||
         !ptr4_ok(gate, empty) || !ptr4_ok(dgate, empty) || !ptr4_ok(route_count, false) ||
         !ptr4_ok(dlogits, empty) || !ptr4_ok(dW_r, false) || !(db_r == nullptr || ptr4_ok(db_r, false)) ||
         !(dx == nullptr || ptr_ok(dx, empty)) || !isfinite(alpha) || !isfinite(z_weight))
         return MOE_ERR_INVALID_ARGUMENT;
-    const size_t nc = (size_t)moe::router_bwd_chunks(T);
+    const size_t nc = (size_t)moe::router_bwd_chunks(T, d, E);
     if (ws_bytes < up(nc * E * d * 4) + up(nc * E * 4)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!ptr_ok(ws, false)) return MOE_ERR_INVALID_ARGUMENT;
     float *part_w = static_cast<float *>(ws);
