@@ -194,8 +194,16 @@ hipError_t launch_grouped_gemm(const void *A, const void *B, const void *B3, con
     if (dtype_bf16) {
         // fused forward: the first GEMM gathers token rows, the second
         // scatters gated rows to y (out is then y)
+        // tile order: consecutive blocks (the same XCD) share the panel of the
+        // operand that is re-read more cheaply.  Column tile major shares the
+        // weight panel across an expert's row tiles (the expert GEMMs: C rows
+        // against N >= C columns); when an expert's rows outnumber the
+        // columns (the weight gradients dW1, dW3: f rows against d columns)
+        // the A panels are the large operand, and row tile major streams
+        // each once while the small B panels are re-read from the caches.
+        // Measured on the Mixtral-shaped expert backward: 17.6 -> 16.5 ms.
         FuseArgs fz{row_tok, T, gate, (uint16_t *)out, row_tok == nullptr ? 0 : (act == 0 ? 2 : 1), kcount,
-                    nullptr, nullptr, 0};
+                    nullptr, nullptr, 0, C > N ? 1 : 0};
         if (split_part != nullptr && C > bm) {
             // the split last wave (tile-map launches): partial sums in
             // split_part, counters after the tile map

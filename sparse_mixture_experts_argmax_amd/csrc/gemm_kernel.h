@@ -32,6 +32,9 @@ struct FuseArgs {
     float *part;
     int32_t *flags;                                      // the counters after the tile map
     int ncu;
+    // tile order within an expert: row tile major (consecutive blocks share
+    // the A panel and sweep the column tiles) instead of column tile major
+    int row_major;
 };
 
 // One grouped-GEMM launch (the arguments of launch_grouped_gemm, resolved):
@@ -80,15 +83,16 @@ __device__ __forceinline__ int split_count(int total, int ncu, int nk) {
 }
 
 // Which tile this block computes (tile_map staged in LDS).  Returns false if none.
-// Order: expert-major, then column tile, then row tile; block b of XCD b % 8
-// takes the (b / 8)-th tile of that XCD's contiguous share.  With a split
+// Order: expert-major, then column tile, then row tile (row_major: row tile,
+// then column tile); block b of XCD b % 8 takes the (b / 8)-th tile of that
+// XCD's contiguous share.  With a split
 // last wave (split_count > 1) the first W ncu blocks take the first W ncu
 // tiles that way and the blocks after them take the parts of the rest,
 // tile by tile; the hardware hands out blocks in index order, so those run
 // last.
 __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ tile_map, int E, int tiles_n,
                                          int *s_map, int &e, int &mt, int &nt, SplitPart &sp, int ncu = 0,
-                                         int nk = 0) {
+                                         int nk = 0, bool row_major = false) {
     for (int i = threadIdx.x; i <= E; i += blockDim.x) s_map[i] = tile_map[i];
     __syncthreads();
     const int total = s_map[E] * tiles_n;
@@ -120,9 +124,14 @@ __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ tile_map, i
     }
     e = lo;
     const int r = L - s_map[e] * tiles_n;
-    const int mtiles = s_map[e + 1] - s_map[e];
-    nt = r / mtiles;
-    mt = r - nt * mtiles;
+    if (row_major) {
+        mt = r / tiles_n;
+        nt = r - mt * tiles_n;
+    } else {
+        const int mtiles = s_map[e + 1] - s_map[e];
+        nt = r / mtiles;
+        mt = r - nt * mtiles;
+    }
     return true;
 }
 
@@ -871,7 +880,9 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
         // the split last wave needs whole K loops (no per-expert K) and the
         // partial-sum buffer
         const int ncu = (fz.part != nullptr && fz.kcount == nullptr) ? fz.ncu : 0;
-        if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt, sp, ncu, (K + TL::BK - 1) / TL::BK)) return;
+        if (!map_tile(tile_map, E, tiles_n, s_map, e, mt, nt, sp, ncu, (K + TL::BK - 1) / TL::BK,
+                      fz.row_major != 0))
+            return;
     }
 
     X c;
