@@ -64,21 +64,24 @@ struct SplitPart {
     int ns, p, slot;
 };
 
-// The split of the last wave.  With W < 8 full waves of ncu tiles and R
-// tiles left over, 0 < 2 R <= ncu, the R tiles of the last wave are each
-// split into ns = min(ncu / R, nk / 8, 8) parts along K (at least 8 K tiles
-// per part), so that the last wave keeps the whole chip busy for 1 / ns of a
-// tile's time instead of R / ncu of it for a whole tile's.  Measured on the
-// Mixtral-shaped layer: its second GEMM (4 waves + 80 tiles of 224 K tiles)
-// 1960 -> 1715 us; its first (30 waves + 48 tiles of 64) was 2 % slower
-// split, as tiles of unequal height already stagger the end of a long launch.
+// The split of the last wave.  With W full waves of ncu tiles and R tiles
+// left over, 0 < 2 R <= ncu, the R tiles of the last wave are each split
+// into ns = min(ncu / R, nk / 8, cap) parts along K (at least 8 K tiles per
+// part), so that the last wave keeps the whole chip busy for 1 / ns of a
+// tile's time instead of R / ncu of it for a whole tile's.  cap = 8 for
+// W < 8; 2 for 8 <= W < 32, where tiles of unequal height already stagger
+// the end of the launch and each part's own prologue, partial sums and
+// fence weigh more; none beyond.  Measured on the Mixtral-shaped layer: its
+// second GEMM (4 waves + 80 tiles of 224 K tiles) 1960 -> 1715 us; its first
+// (30 waves + 48 tiles of 64) 2 % slower with cap 8, 0.6 % faster with 2.
 __device__ __forceinline__ int split_count(int total, int ncu, int nk) {
-    if (ncu < 8 || total <= 0 || total >= 8 * ncu) return 1;
+    if (ncu < 8 || total <= 0 || total >= 32 * ncu) return 1;
     const int R = total % ncu;
     if (R == 0 || 2 * R > ncu) return 1;
+    const int cap = total >= 8 * ncu ? 2 : 8;
     int ns = ncu / R;
     ns = ns < nk / 8 ? ns : nk / 8;
-    ns = ns < 8 ? ns : 8;
+    ns = ns < cap ? ns : cap;
     return ns < 2 ? 1 : ns;
 }
 

@@ -134,7 +134,7 @@ def tail_split_parts(counts, C: int, E: int, act: str, N: int, K: int, gated: bo
     total = row_tiles * ((N + bn - 1) // bn)
     nk = (K + 63) // 64
     R = total % ncu
-    if total == 0 or total >= 8 * ncu or R == 0 or 2 * R > ncu:
+    if total == 0 or total >= 32 * ncu or R == 0 or 2 * R > ncu:
         return 1
-    ns = min(ncu // R, nk // 8, 8)
+    ns = min(ncu // R, nk // 8, 2 if total >= 8 * ncu else 8)
     return ns if ns >= 2 else 1
