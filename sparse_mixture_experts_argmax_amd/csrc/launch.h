@@ -76,13 +76,14 @@ hipError_t launch_slot_index(const int32_t *expert_idx, const int32_t *rank, con
 // launch_slot_scan with an unbounded capacity (n_e = each expert's choice
 // count), the slots of the capacity rule with tokens visited in descending
 // priority[t] (ties: lower index; NaN last), rank-major; also drop_mask,
-// expert_count = min(n_e, C) and the kept rows in xbuf.  list [T k] uint64
-// and off [E] are scratch.  E <= 1024.
+// expert_count = min(n_e, C) and the kept rows in xbuf.  list [T k] uint64,
+// off [E] and pcnt [T k] int32 (may be null: no split count) are scratch.
+// E <= 1024.
 hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *expert_idx,
                                  const float *priority, const int32_t *rank, const int32_t *base,
                                  const int32_t *n_e, int64_t T, int d, int E, int k, int64_t C,
                                  uint64_t *list, int32_t *off, int32_t *slot, uint8_t *drop_mask,
-                                 int32_t *expert_count, void *xbuf, hipStream_t s);
+                                 int32_t *expert_count, void *xbuf, hipStream_t s, int32_t *pcnt);
 // Backward of the gate side (backward.hip).  Combine: dgate [T, k] fp32 and
 // the kept rows of dybuf [E, C, d] (g dy, storage dtype).  Router: dz [T, E]
 // from the logits, gates and dgate; dW [E, d], db [E] (may be null) and dx

@@ -64,7 +64,7 @@ DispatchWs dispatch_ws(int64_t T, int E, int k) {
 // per-expert order-key lists, the choice counts and the list offsets.
 struct PriorityWs {
     DispatchWs d;
-    size_t list, cnt, off, total;
+    size_t list, cnt, off, pcnt, total;
 };
 PriorityWs priority_ws(int64_t T, int E, int k) {
     PriorityWs w;
@@ -72,7 +72,8 @@ PriorityWs priority_ws(int64_t T, int E, int k) {
     w.list = w.d.total;
     w.cnt = w.list + up((size_t)T * k * 8);
     w.off = w.cnt + up((size_t)E * 4);
-    w.total = w.off + up((size_t)E * 4);
+    w.pcnt = w.off + up((size_t)E * 4);
+    w.total = w.pcnt + up((size_t)T * k * 4);
     return w;
 }
 
@@ -438,7 +439,7 @@ moe_status run_priority_dispatch(const void *x, moe_dtype dt, const int32_t *exp
     MOE_HIP(moe::launch_priority_slots(x, (int)esize(dt), expert_idx, priority, rank, hist, n_e, T, d, E, k,
                                        C, reinterpret_cast<uint64_t *>(base + w.list),
                                        reinterpret_cast<int32_t *>(base + w.off), slot, drop_mask,
-                                       expert_count, xbuf, stream));
+                                       expert_count, xbuf, stream, reinterpret_cast<int32_t *>(base + w.pcnt)));
     return MOE_OK;
 }
 }  // namespace

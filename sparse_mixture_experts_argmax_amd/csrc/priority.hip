@@ -15,7 +15,9 @@
 //  * priority_slot_kernel: one block per 256 entries of the lists laid end
 //    to end; an entry's slot is the start of its rank's segment plus the
 //    number of keys in that segment below its own (keys are distinct),
-//    found by streaming the segment through LDS;
+//    found by streaming the segment through LDS (with few experts split
+//    over several blocks per entry block, whose counts a second pass of the
+//    same kernel gathers);
 //  * permute_slots_kernel: the rows of the kept choices into xbuf.
 // Work is sum over experts of n_e^2 / 2 compares (rank segments bound it
 // further): 4 M for 16384 tokens over 64 experts, and at most T^2 / 2 when
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_list_kernel(
     const int32_t *__restrict__ rank, const int32_t *__restrict__ base,
     const int32_t *__restrict__ n_e, int64_t T, int E, int k, int nblk,
     uint64_t *__restrict__ list, int32_t *__restrict__ off_out, int32_t *__restrict__ slot,
-    uint8_t *__restrict__ drop) {
+    uint8_t *__restrict__ drop, int32_t *__restrict__ pcnt) {
     __shared__ int32_t s_off[1024];
     block_offsets(n_e, E, s_off);
     if (blockIdx.x == 0)
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_list_kernel(
     const int blk = (int)(t / DISPATCH_TOK_BLOCK);
     const int64_t pos = (int64_t)base[(int64_t)e * k * nblk + (int64_t)j * nblk + blk] + rank[(int64_t)j * T + t];
     list[s_off[e] + pos] = ((uint64_t)desc_key(priority[t]) << 32) | (uint64_t)(uint32_t)t;
+    if (pcnt != nullptr) pcnt[s_off[e] + pos] = 0;    // the split count's sums start at zero
 }
 
 // Block b takes entries [256 b, 256 b + 256) of the experts' lists laid end
@@ -100,16 +103,22 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_list_kernel(
 // a binary search over off.  The block streams the union of its entries'
 // rank segments through LDS; an entry counts the keys of its own segment
 // (global positions [off[e] + lo, off[e] + hi), disjoint across experts)
-// below its key.
+// below its key.  With few experts (long segments) the stream is split over
+// gridDim.y blocks: block (b, y) takes the y-th of every gridDim.y tiles of
+// 256 keys and adds its counts to pcnt (integer sums: the same total in any
+// order), and priority_final_kernel turns them into slots; with gridDim.y =
+// 1 the block writes the slots itself.
 __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
     const uint64_t *__restrict__ list, const int32_t *__restrict__ off, const int32_t *__restrict__ n_e,
     const int32_t *__restrict__ base, int E, int k, int nblk, int64_t C, int32_t *__restrict__ slot,
-    uint8_t *__restrict__ drop, int32_t *__restrict__ expert_count) {
+    uint8_t *__restrict__ drop, int32_t *__restrict__ expert_count, int32_t *__restrict__ pcnt,
+    int final_pass) {
     __shared__ __attribute__((aligned(16))) uint64_t s_key[PR_BLOCK];
     __shared__ int s_lo, s_hi;
     __shared__ int32_t s_off[1024];                  // the list offsets, searched in LDS
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0)
+    const int ny = gridDim.y, y = blockIdx.y;
+    if (blockIdx.x == 0 && y == 0 && !final_pass)
         for (int e = tid; e < E; e += PR_BLOCK) {
             const int n = n_e[e];
             expert_count[e] = (int32_t)((int64_t)n < C ? (int64_t)n : C);
@@ -146,6 +155,17 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
         hi = j + 1 < k ? b[(int64_t)(j + 1) * nblk] : n_e[e];
         my = list[p];
     }
+    if (final_pass) {
+        // the split count's sums, gathered (one entry per thread)
+        if (ok) {
+            const int64_t s = (int64_t)lo + pcnt[p];
+            const int64_t t = (int64_t)(uint32_t)(my & 0xFFFFFFFFull);
+            const int64_t a = t * k + j;
+            slot[a] = s < C ? (int32_t)s : -1;
+            drop[a] = s < C ? 0 : 1;
+        }
+        return;
+    }
     if (tid == 0) {
         s_lo = 0x7fffffff;
         s_hi = 0;
@@ -163,7 +183,7 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
     const uint32_t span = (uint32_t)(hi - lo);
     const int glo = oe + lo;
     int cnt = 0;
-    for (int q0 = blo; q0 < bhi; q0 += PR_BLOCK) {
+    for (int q0 = blo + y * PR_BLOCK; q0 < bhi; q0 += ny * PR_BLOCK) {
         const int q = q0 + tid;
         s_key[tid] = q < bhi ? list[q] : ~0ull;
         __syncthreads();
@@ -189,7 +209,9 @@ __global__ __launch_bounds__(PR_BLOCK) void priority_slot_kernel(
         }
         __syncthreads();
     }
-    if (ok) {
+    if (ok && ny > 1) {
+        if (cnt > 0) atomicAdd(&pcnt[p], cnt);
+    } else if (ok) {
         const int64_t s = (int64_t)lo + cnt;
         const int64_t t = (int64_t)(uint32_t)(my & 0xFFFFFFFFull);
         const int64_t a = t * k + j;
@@ -235,20 +257,29 @@ hipError_t launch_priority_slots(const void *x, int elem_bytes, const int32_t *e
                                  const float *priority, const int32_t *rank, const int32_t *base,
                                  const int32_t *n_e, int64_t T, int d, int E, int k, int64_t C,
                                  uint64_t *list, int32_t *off, int32_t *slot, uint8_t *drop_mask,
-                                 int32_t *expert_count, void *xbuf, hipStream_t s) {
+                                 int32_t *expert_count, void *xbuf, hipStream_t s, int32_t *pcnt) {
     if (E > 1024) return hipErrorInvalidValue;
     const int64_t n = T * k;
     const int nblk = dispatch_blocks(T);
     const unsigned lb = (unsigned)((n + PR_BLOCK - 1) / PR_BLOCK);
+    // split the key stream when the average segment is long (few experts):
+    // about 512 keys of it per block, at most 8 blocks per entry block
+    int64_t ny = n / E / 512;
+    ny = ny < 1 ? 1 : ny > 8 ? 8 : ny;
+    if (pcnt == nullptr) ny = 1;
+    int32_t *pc = ny > 1 ? pcnt : nullptr;
     if (n > 0)
         hipLaunchKernelGGL(priority_list_kernel, dim3(lb), dim3(PR_BLOCK), 0, s, expert_idx, priority, rank,
-                           base, n_e, T, E, k, nblk, list, off, slot, drop_mask);
+                           base, n_e, T, E, k, nblk, list, off, slot, drop_mask, pc);
     else
         hipLaunchKernelGGL(priority_list_kernel, dim3(1), dim3(PR_BLOCK), 0, s, expert_idx, priority, rank,
-                           base, n_e, T, E, k, nblk, list, off, slot, drop_mask);
+                           base, n_e, T, E, k, nblk, list, off, slot, drop_mask, pc);
     // the lists hold at most T k entries
-    hipLaunchKernelGGL(priority_slot_kernel, dim3(lb > 0 ? lb : 1), dim3(PR_BLOCK), 0, s, list, off, n_e,
-                       base, E, k, nblk, C, slot, drop_mask, expert_count);
+    hipLaunchKernelGGL(priority_slot_kernel, dim3(lb > 0 ? lb : 1, (unsigned)ny), dim3(PR_BLOCK), 0, s, list, off,
+                       n_e, base, E, k, nblk, C, slot, drop_mask, expert_count, pc, 0);
+    if (ny > 1)
+        hipLaunchKernelGGL(priority_slot_kernel, dim3(lb > 0 ? lb : 1), dim3(PR_BLOCK), 0, s, list, off, n_e, base,
+                           E, k, nblk, C, slot, drop_mask, expert_count, pc, 1);
     if (n == 0 || C == 0) return hipGetLastError();
     int64_t blocks = (n + 3) / 4;
     if (blocks > 65536) blocks = 65536;

@@ -60,6 +60,9 @@ def _idx(rng, T, E, k, skew=0.0):
     (3000, 3, 1, 1.0, 8.0, "rand"),          # most tokens at expert 0: many chunks and tiles
     (500, 5, 2, 1.0, 0.0, "special"),        # NaN, +-inf, +-0 scores
     (300, 7, 2, 1.0, 0.0, "same"),           # one score: the plain token order
+    # long segments: the key stream is split over 7 and 8 blocks per entry block
+    (12000, 3, 1, 0.8, 8.0, "rand"),
+    (20000, 2, 2, 1.0, 0.0, "round"),
 ])
 def test_priority_dispatch_matches_oracle(T, E, k, cf, skew, scores):
     rng = np.random.default_rng(T + E + k)
