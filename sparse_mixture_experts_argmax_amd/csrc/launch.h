@@ -106,11 +106,13 @@ hipError_t launch_permute_slots(const void *x, int elem_bytes, const int32_t *ex
 // expert [T] and slot [T] (-1 if dropped), drop_mask [T], gate [T] (the
 // full-softmax probability of the landing expert from logits [T, E]; both
 // may be null), expert_count [E] and the kept rows in xbuf.  rank [T], hist
-// [E dispatch_blocks(T)], cand [T], n_e [E] and fill [E] are scratch.
+// [E dispatch_blocks(T)], cand [T] and n_e [REROUTE_MAX_STAGES E] are
+// scratch.  stages <= REROUTE_MAX_STAGES.
+constexpr int REROUTE_MAX_STAGES = 8;
 hipError_t launch_reroute(const void *x, int elem_bytes, const int32_t *pref, const float *logits, int64_t T,
                           int d, int E, int R, int stages, int64_t C, int32_t *expert, int32_t *slot,
                           uint8_t *drop_mask, float *gate, int32_t *expert_count, void *xbuf, int32_t *rank,
-                          int32_t *hist, int32_t *cand, int32_t *n_e, int32_t *fill, hipStream_t s);
+                          int32_t *hist, int32_t *cand, int32_t *n_e, hipStream_t s);
 // counts [E] = how many tokens have e as their first preference pref[t, 0]
 // (pref [T, R]); the fused re-routing forward's choice counts for the loss.
 hipError_t launch_first_choice_count(const int32_t *pref, int64_t T, int R, int E, int32_t *counts, hipStream_t s);

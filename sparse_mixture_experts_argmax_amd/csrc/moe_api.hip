@@ -488,17 +488,18 @@ moe_status moe_combine_backward(const void *dy, moe_dtype dt, const void *ybuf, 
 
 // rank [T], hist, done (the plain dispatch's scratch for one rank), then
 // cand [T], n_e [E], fill [E].
+// Re-routing: the plain dispatch's rank and scan scratch, the candidates and
+// every stage's per-expert candidate counts.
 struct RerouteWs {
     DispatchWs d;
-    size_t cand, cnt, fill, total;
+    size_t cand, cnt, total;
 };
 RerouteWs reroute_ws(int64_t T, int E) {
     RerouteWs w;
     w.d = dispatch_ws(T, E, 1);
     w.cand = w.d.total;
     w.cnt = w.cand + up((size_t)T * 4);
-    w.fill = w.cnt + up((size_t)E * 4);
-    w.total = w.fill + up((size_t)E * 4);
+    w.total = w.cnt + up((size_t)moe::REROUTE_MAX_STAGES * E * 4);
     return w;
 }
 
@@ -529,7 +530,7 @@ moe_status moe_dispatch_reroute(const void *x, moe_dtype dt, const int32_t *pref
                                 gate, expert_count, xbuf, reinterpret_cast<int32_t *>(base + w.d.rank),
                                 reinterpret_cast<int32_t *>(base + w.d.hist),
                                 reinterpret_cast<int32_t *>(base + w.cand), reinterpret_cast<int32_t *>(base + w.cnt),
-                                reinterpret_cast<int32_t *>(base + w.fill), stream));
+                                stream));
     return MOE_OK;
 }
 
@@ -907,7 +908,7 @@ moe_status moe_forward_policy(const void *x, moe_dtype dt, const float *W_r, con
                                     drop_mask, gate, expert_count, xbuf, reinterpret_cast<int32_t *>(rb + rw.d.rank),
                                     reinterpret_cast<int32_t *>(rb + rw.d.hist),
                                     reinterpret_cast<int32_t *>(rb + rw.cand), reinterpret_cast<int32_t *>(rb + rw.cnt),
-                                    reinterpret_cast<int32_t *>(rb + rw.fill), stream));
+                                    stream));
     }
     const int kc = policy == MOE_POLICY_REROUTE ? 1 : k;
     MOE_CHECK(run_ffn(xbuf, dt, expert_count, E, C, d, dff, W1, b1, W3, W2, b2, act, ybuf, T * (int64_t)kc,

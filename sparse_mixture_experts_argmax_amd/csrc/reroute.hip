@@ -11,9 +11,11 @@
 // unbounded capacity) over a candidate array that holds the stage's choice
 // of the unplaced tokens and -1 for the rest, then a placement pass
 // (slot = fill[e] + position among the stage's candidates of e, kept while
-// below C) and a pass that advances fill[e] = min(fill[e] + n_e, C).  A
-// final pass writes the drop flags, the expert counts and each token's gate,
-// the full-softmax probability of the expert it landed on.
+// below C, with fill[e] folded from the earlier stages' counts as
+// min(fill + n_e, C)), which also writes the next stage's candidates: three
+// launches per stage.  A final pass writes the drop flags, the expert counts
+// and each token's gate, the full-softmax probability of the expert it
+// landed on.
 #include "common.h"
 #include "launch.h"
 
@@ -36,46 +38,73 @@ __global__ __launch_bounds__(256) void reroute_cand_kernel(const int32_t *__rest
     cand[t] = e;
 }
 
-__global__ __launch_bounds__(256) void reroute_place_kernel(const int32_t *__restrict__ cand,
+// Stage s's placement: slot = (the expert's fill after the earlier stages) +
+// the candidate's position among this stage's candidates of its expert, kept
+// while below C.  The fill after stage q is min(fill after q - 1 + n_q, C),
+// folded here from the per-stage counts n_e [stages][E] (no pass of its own).
+// Unless this is the last stage, each thread then writes its token's next
+// candidate in place: the next preference (or -1 past [0, E)) while the
+// token has no slot, -1 once it has one.
+__global__ __launch_bounds__(256) void reroute_place_kernel(int32_t *__restrict__ cand,
                                                             const int32_t *__restrict__ rank,
                                                             const int32_t *__restrict__ base,
-                                                            const int32_t *__restrict__ fill, int64_t T, int nblk,
-                                                            int64_t C, int s, int32_t *__restrict__ expert,
+                                                            const int32_t *__restrict__ n_hist, int64_t T, int nblk,
+                                                            int64_t C, int s, int E, const int32_t *__restrict__ pref,
+                                                            int R, bool last, int32_t *__restrict__ expert,
                                                             int32_t *__restrict__ slot) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= T) return;
     const int e = cand[t];
     int64_t sl = -1;
     if (e >= 0) {
+        int64_t f = 0;
+        for (int q = 0; q < s; ++q) {
+            f += n_hist[(int64_t)q * E + e];
+            f = f < C ? f : C;
+        }
         const int blk = (int)(t / DISPATCH_TOK_BLOCK);
-        sl = (int64_t)(s == 0 ? 0 : fill[e]) + base[(int64_t)e * nblk + blk] + rank[t];
+        sl = f + base[(int64_t)e * nblk + blk] + rank[t];
         if (sl >= C) sl = -1;
     }
+    int landed;
     if (sl >= 0) {
         expert[t] = e;
         slot[t] = (int32_t)sl;
+        landed = e;
     } else if (s == 0) {
         expert[t] = -1;
         slot[t] = -1;
+        landed = -1;
+    } else {
+        landed = expert[t];                          // placed at an earlier stage, or not yet
+    }
+    if (!last) {
+        int nx = -1;
+        if (landed < 0) {
+            nx = pref[t * R + s + 1];
+            if (nx < 0 || nx >= E) nx = -1;
+        }
+        cand[t] = nx;
     }
 }
 
-__global__ __launch_bounds__(256) void reroute_fill_kernel(const int32_t *__restrict__ n_e,
-                                                           int32_t *__restrict__ fill, int E, int64_t C, int s) {
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= E) return;
-    const int64_t f = (int64_t)(s == 0 ? 0 : fill[e]) + n_e[e];
-    fill[e] = (int32_t)(f < C ? f : C);
-}
-
-// One wave per token: drop flag and gate; block 0 also copies the counts.
+// One wave per token: drop flag and gate; block 0 also writes the counts
+// (each expert's fill after the last stage, folded from the stage counts).
 __global__ __launch_bounds__(256) void reroute_final_kernel(const float *__restrict__ logits,
                                                             const int32_t *__restrict__ expert,
-                                                            const int32_t *__restrict__ fill, int64_t T, int E,
+                                                            const int32_t *__restrict__ n_hist, int stages,
+                                                            int64_t C, int64_t T, int E,
                                                             uint8_t *__restrict__ drop, float *__restrict__ gate,
                                                             int32_t *__restrict__ expert_count) {
     if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e < E; e += 256) expert_count[e] = fill[e];
+        for (int e = threadIdx.x; e < E; e += 256) {
+            int64_t f = 0;
+            for (int q = 0; q < stages; ++q) {
+                f += n_hist[(int64_t)q * E + e];
+                f = f < C ? f : C;
+            }
+            expert_count[e] = (int32_t)f;
+        }
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -97,25 +126,26 @@ __global__ __launch_bounds__(256) void reroute_final_kernel(const float *__restr
 hipError_t launch_reroute(const void *x, int elem_bytes, const int32_t *pref, const float *logits, int64_t T,
                           int d, int E, int R, int stages, int64_t C, int32_t *expert, int32_t *slot,
                           uint8_t *drop_mask, float *gate, int32_t *expert_count, void *xbuf, int32_t *rank,
-                          int32_t *hist, int32_t *cand, int32_t *n_e, int32_t *fill, hipStream_t s) {
-    if (stages < 1 || stages > R) return hipErrorInvalidValue;
+                          int32_t *hist, int32_t *cand, int32_t *n_e, hipStream_t s) {
+    if (stages < 1 || stages > R || stages > REROUTE_MAX_STAGES) return hipErrorInvalidValue;
     const int nblk = dispatch_blocks(T);
     const unsigned tb = (unsigned)((T + 255) / 256);
-    const unsigned eb = (unsigned)((E + 255) / 256);
+    // stage 0's candidates; each placement pass writes the next stage's
+    if (T > 0) hipLaunchKernelGGL(reroute_cand_kernel, dim3(tb), dim3(256), 0, s, pref, R, 0, T, E, expert, cand);
     for (int st = 0; st < stages; ++st) {
-        if (T > 0) hipLaunchKernelGGL(reroute_cand_kernel, dim3(tb), dim3(256), 0, s, pref, R, st, T, E, expert, cand);
         hipError_t err = launch_slot_rank(cand, T, E, 1, rank, hist, nullptr, s);
         if (err != hipSuccess) return err;
-        err = launch_slot_scan(hist, nblk, E, 1, T + 1, n_e, nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr, s);
+        // an unbounded capacity: n_e[st] = this stage's candidates per expert
+        err = launch_slot_scan(hist, nblk, E, 1, T + 1, n_e + (int64_t)st * E, nullptr, 0, nullptr, nullptr,
+                               nullptr, 0, nullptr, s);
         if (err != hipSuccess) return err;
         if (T > 0)
-            hipLaunchKernelGGL(reroute_place_kernel, dim3(tb), dim3(256), 0, s, cand, rank, hist, fill, T, nblk, C,
-                               st, expert, slot);
-        hipLaunchKernelGGL(reroute_fill_kernel, dim3(eb), dim3(256), 0, s, n_e, fill, E, C, st);
+            hipLaunchKernelGGL(reroute_place_kernel, dim3(tb), dim3(256), 0, s, cand, rank, hist, n_e, T, nblk, C,
+                               st, E, pref, R, st == stages - 1, expert, slot);
     }
     const unsigned fb = (unsigned)((T + 3) / 4);
-    hipLaunchKernelGGL(reroute_final_kernel, dim3(fb > 0 ? fb : 1), dim3(256), 0, s, logits, expert, fill, T, E,
-                       drop_mask, gate, expert_count);
+    hipLaunchKernelGGL(reroute_final_kernel, dim3(fb > 0 ? fb : 1), dim3(256), 0, s, logits, expert, n_e, stages, C,
+                       T, E, drop_mask, gate, expert_count);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     return launch_permute_slots(x, elem_bytes, expert, slot, T, d, 1, C, xbuf, s);
