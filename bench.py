@@ -152,13 +152,13 @@ PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d {o}/ktrace -o k -- "
     "python3 $REPO/bench.py --workload {w} --steps 10 --warmup 3 --cpu-seconds 0 --others 0 "
-    "--expert-backward-calls 0",
+    "--expert-backward-calls 2",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/fetch -o f -- "
     "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --others 0 "
-    "--expert-backward-calls 0",
+    "--expert-backward-calls 1",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/write -o w -- "
     "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --others 0 "
-    "--expert-backward-calls 0",
+    "--expert-backward-calls 1",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/copy_fetch -o c -- "
     "python3 $REPO/bench.py --copy-probe %d" % COPY_PROBE_BYTES,
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/copy_write -o c -- "
@@ -227,14 +227,33 @@ def _counter_rows(d: str):
         return list(csv.DictReader(fh))
 
 
+def stages_by_dispatch(rows) -> dict:
+    """Stage of every dispatch (rows with Dispatch_Id and Kernel_Name), in
+    dispatch order.  The launches of an expert-side backward call, from its
+    first kernel (fill_i32_kernel) to its un-permute (dispatch_backward_kernel),
+    belong to the expert backward whatever their name: its products run on
+    the forward's GEMM kernel."""
+    names = {}
+    for r in rows:
+        names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    stage, inside = {}, False
+    for did in sorted(names):
+        nm = names[did]
+        if "fill_i32_kernel" in nm:
+            inside = True
+        stage[did] = "expert_backward" if inside else kernel_stage(nm)
+        if "dispatch_backward_kernel" in nm:
+            inside = False
+    return stage
+
+
 def _per_stage_kib(d: str, counter: str) -> dict:
     """Mean counter value (KiB) per launch of each stage's kernels."""
+    rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
+    stage = stages_by_dispatch(rows)
     acc = {}
-    for r in _counter_rows(d):
-        if r["Counter_Name"] != counter:
-            continue
-        st = kernel_stage(r["Kernel_Name"])
-        acc.setdefault(st, []).append(float(r["Counter_Value"]))
+    for r in rows:
+        acc.setdefault(stage[int(r["Dispatch_Id"])], []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
@@ -248,11 +267,26 @@ def _copy_kib(d: str, counter: str) -> float:
 
 def summarize(prof_dir: str, workload: str) -> str:
     """Markdown summary of one profile set: kernel times and HBM traffic per launch."""
-    stats = glob.glob(os.path.join(prof_dir, "ktrace", "*kernel_stats.csv"))
-    if not stats:
-        raise SystemExit(f"no kernel_stats.csv under {prof_dir}/ktrace")
-    with open(stats[0]) as fh:
-        krows = list(csv.DictReader(fh))
+    trace = glob.glob(os.path.join(prof_dir, "ktrace", "*kernel_trace.csv"))
+    if not trace:
+        raise SystemExit(f"no kernel_trace.csv under {prof_dir}/ktrace")
+    with open(trace[0]) as fh:
+        trows = list(csv.DictReader(fh))
+    # per (kernel, stage): calls, mean / min / max duration, share of the time
+    tstage = stages_by_dispatch(trows)
+    agg = {}
+    for r in trows:
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        key = (r["Kernel_Name"], tstage[int(r["Dispatch_Id"])])
+        a = agg.setdefault(key, [0, 0, None, 0])
+        a[0] += 1
+        a[1] += dur
+        a[2] = dur if a[2] is None else min(a[2], dur)
+        a[3] = max(a[3], dur)
+    total_ns = sum(a[1] for a in agg.values()) or 1
+    krows = [dict(Name=nm, Stage=st, Calls=a[0], AverageNs=a[1] / a[0], MinNs=a[2], MaxNs=a[3],
+                  Percentage=100.0 * a[1] / total_ns)
+             for (nm, st), a in sorted(agg.items(), key=lambda kv: -kv[1][1])]
     fetch = _per_stage_kib(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
     write = _per_stage_kib(os.path.join(prof_dir, "write"), "WRITE_SIZE")
     kib = COPY_PROBE_BYTES / 1024
@@ -268,7 +302,7 @@ def summarize(prof_dir: str, workload: str) -> str:
         nm = r["Name"]
         short = re.sub(r"\(.*$", "", nm.replace("moe::(anonymous namespace)::", ""))
         short = short.replace("void ", "")
-        lines.append(f"| `{short}` | {kernel_stage(nm)} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} "
+        lines.append(f"| `{short}` | {r['Stage']} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} "
                      f"| {float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.1f} |")
     lines += ["", "## HBM traffic per launch (rocprofv3 --pmc, scaled by the copy probe)", "",
               f"Copy probe: {COPY_PROBE_BYTES} bytes copied device to device; FETCH_SIZE scale "
@@ -283,7 +317,9 @@ def summarize(prof_dir: str, workload: str) -> str:
         lines.append(f"| {st} | {fetch.get(st, 0):.1f} | {write.get(st, 0):.1f} | {fb:.0f} | {wb:.0f} "
                      f"| {fb + wb:.0f} |")
     lines += ["", "Per launch means the mean over that stage's kernel launches in the profiled steps; "
-              "the dispatch and noisy_router stages are several kernels, each counted as one launch.", "",
+              "the dispatch, noisy_router and expert_backward stages are several kernels, each counted as "
+              "one launch (the expert backward's launches are those from an expert-backward call's first "
+              "kernel to its un-permute, its GEMMs included).", "",
               TRAFFIC_TAG + json.dumps(dict(workload=workload, source_digest=source_digest(),
                                              fetch_scale=round(f_scale, 5), write_scale=round(w_scale, 5),
                                              stages=traffic)), ""]
