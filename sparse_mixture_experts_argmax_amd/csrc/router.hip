@@ -13,12 +13,12 @@
 //    round-to-nearest bf16 of what the previous parts left, so the sum
 //    reproduces all 24 significand bits).  bf16 x bf16 products are exact
 //    in fp32, so three bf16 MFMAs with fp32 accumulation give an fp32 dot
-//    product without any fp32 vector FMA.  A block of 64 tokens streams W_r
-//    (fp32, split into its three parts in registers as each fragment is
-//    read; with 256 experts the parts, made once per call) and its token
-//    rows through a ring of LDS stages filled by 16-byte DMA, and each of
-//    its four waves computes the logits of all 64 tokens for a quarter of
-//    the experts.  The logits go through LDS to one wave per 16 tokens,
+//    product without any fp32 vector FMA.  A block of 64 tokens (128 with
+//    more than 128 experts) streams W_r (fp32, split into its three parts
+//    in registers as each fragment is read) and its token rows through a
+//    ring of LDS stages filled by 16-byte DMA, and each of its four waves
+//    computes the logits of all the block's tokens for a quarter of the
+//    experts.  The logits go through LDS to one wave per 16 tokens,
 //    where row softmax and top-k use 16-lane DPP row reductions.
 //  * router_generic (fp32 x, or E > 256): fp32 FMA dot products into LDS,
 //    then one wave per token row.
@@ -59,20 +59,6 @@ __device__ __forceinline__ void split3(float w, uint16_t &h, uint16_t &m, uint16
     l = f2bf(r2);
 }
 
-// W3[p][n][:] = part p of W_r[n][:] (p = 0 hi, 1 mid, 2 lo), once per call
-// (the widest router, 256 experts, reads the parts; the narrower ones split
-// W_r in registers).
-__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ Wr, int64_t n,
-                                                           uint16_t *__restrict__ W3) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        uint16_t h, m, l;
-        split3(Wr[i], h, m, l);
-        W3[i] = h;
-        W3[n + i] = m;
-        W3[2 * n + i] = l;
-    }
-}
-
 // The stacked noisy weight: rows [0, EH) are W_r, rows [EH, 2 EH) W_noise,
 // rows past E in either half zero; the same three-part split into W3.
 __global__ __launch_bounds__(256) void router_split_noisy_kernel(const float *__restrict__ Wr,
@@ -98,12 +84,12 @@ __global__ __launch_bounds__(256) void router_split_noisy_kernel(const float *__
 // KC values in two LDS rows) and of the block's 64 token rows, in LDS rows of
 // KC bf16.  Piece c (16 bytes) of row r is stored at c ^ swz(r), as in the
 // expert GEMM: conflict-free 16-byte fragment reads and DMA writes.
-template <int NB, int KC, int WR = 3>
+template <int NB, int KC, int WR = 3, int TB = RM_TOK_BLOCK>
 struct RGeo {
     static constexpr int EP = NB * 16;
     static constexpr int ROWB = KC * 2;
     static constexpr int PIECES = KC / 8;
-    static constexpr int ROWS = WR * EP + RM_TOK_BLOCK;
+    static constexpr int ROWS = WR * EP + TB;
     static constexpr int STAGE = ROWS * ROWB;
     static constexpr int S = RM_LDS / STAGE > 4 ? 4 : RM_LDS / STAGE;
     static constexpr int PERW = STAGE / 4096;            // 1 KB DMA instructions per wave per stage
@@ -114,20 +100,20 @@ struct RGeo {
     }
 };
 
-template <int NB, int KC, int WR = 3>
-constexpr bool rgeo_ok() { return RM_LDS / ((WR * NB * 16 + RM_TOK_BLOCK) * KC * 2) >= 2; }
+template <int NB, int KC, int WR = 3, int TB = RM_TOK_BLOCK>
+constexpr bool rgeo_ok() { return RM_LDS / ((WR * NB * 16 + TB) * KC * 2) >= 2; }
 
 // One block = 64 tokens (4 waves x 16) and every expert.  The weights and the
 // token rows flow through an S-deep ring of LDS stages filled by 16-byte DMA;
 // bf16 x bf16 products are exact in fp32, so three v_mfma_f32_16x16x32_bf16
 // per 16 experts and 32 columns, one per exact bf16 part of the weight, give
-// the fp32 dot products.  The plain router with up to 128 experts stages W_r
-// itself in fp32 and splits each fragment into its three parts in registers
-// as it reads it (split3: no launch of its own, and two thirds of the weight
-// bytes of the three parts: 7-12 % faster on 8 to 128 experts); with 256
-// experts the splitting takes more vector ALU time than it saves (3 % slower
-// on many_expert), so that form, like the noisy ones, reads the parts that
-// router_split_kernel (router_split_noisy_kernel) made.
+// the fp32 dot products.  The plain router stages W_r itself in fp32 and
+// splits each fragment into its three parts in registers as it reads it
+// (split3: no launch of its own, and two thirds of the weight bytes of the
+// three parts: 7-12 % faster on 8 to 128 experts); with more than 128
+// experts it takes 128 tokens a block, so that each staged weight fragment
+// (and its split) serves twice the tokens.  The noisy forms read the parts
+// that router_split_noisy_kernel made.
 //
 // NB = 1 (E <= 16; KC = 128): one group of 16 experts would leave three waves
 // without work, so instead wave w takes the w-th 32 columns of every stage
@@ -144,16 +130,20 @@ constexpr bool rgeo_ok() { return RM_LDS / ((WR * NB * 16 + RM_TOK_BLOCK) * KC *
 //     twice (the token rows are re-read, mostly from L2) and the first
 //     pass's logits stay in registers, so each lane forms H for its own
 //     (token, expert) entries before they go to LDS.
-template <int NB, int KC, bool KTAIL, int KSEL, int NZ>
+// TB: tokens per block, 64 or (the plain router with 256 experts) 128, which
+// halves the weight bytes streamed per token (the epilogue then runs twice).
+template <int NB, int KC, bool KTAIL, int KSEL, int NZ, int TB = RM_TOK_BLOCK>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W3, const float *__restrict__ Wf,
     const float *__restrict__ br,
     int64_t T, int d, int E, int k, int32_t *__restrict__ out_idx, float *__restrict__ out_gate,
     float *__restrict__ part_prob, int32_t *__restrict__ part_cnt, float *__restrict__ part_z,
     const float *__restrict__ eps, float *__restrict__ logits) {
-    constexpr bool WF32 = NZ == 0 && NB <= 8;           // fp32 W_r, split in registers
+    constexpr bool WF32 = NZ == 0 && (NB <= 8 || TB == 128);   // fp32 W_r, split in registers
     constexpr int WR = WF32 ? 2 : 3;                     // LDS rows of weights per expert row
-    using G = RGeo<NB, KC, WR>;
+    constexpr int AB = TB / 16;                          // 16-token row blocks
+    static_assert(TB == RM_TOK_BLOCK || (TB == 128 && NZ == 0 && NB >= RM_WAVES), "tokens per block");
+    using G = RGeo<NB, KC, WR, TB>;
     constexpr int EP = G::EP, ROWB = G::ROWB, PIECES = G::PIECES, S = G::S, PERW = G::PERW;
     constexpr int STAGE = G::STAGE, RPI = G::RPI;
     constexpr int NEWER = (S - 2) * PERW;
@@ -163,15 +153,14 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
     __shared__ float sProb[RM_WAVES][EP];
     __shared__ int sCnt[EP];
-    __shared__ float sLz[RM_TOK_BLOCK];                 // each token's log-sum-exp, squared
+    __shared__ float sLz[TB];                           // each token's log-sum-exp, squared
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;      // expert column within a 16-block / token row of A
     const int kg = lane >> 4;       // k group (A/B operands) or row group (D)
-    const int64_t t0 = (int64_t)blockIdx.x * RM_TOK_BLOCK;
-    const int64_t tw = t0 + wave * RM_TOK_WAVE;
+    const int64_t t0 = (int64_t)blockIdx.x * TB;
     for (int i = tid; i < EP; i += 256) sCnt[i] = 0;
 
     // DMA sources: block instruction q = wave * PERW + i fills rows
@@ -243,9 +232,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     constexpr bool KSPLIT = NB < RM_WAVES;
     constexpr int NBW = KSPLIT ? 1 : NB / RM_WAVES;
     static_assert(KSPLIT ? (NB == 1 && KC == 128 && NZ == 0) : NB % RM_WAVES == 0, "expert groups per wave");
-    f32x4 acc[4][NBW];
+    f32x4 acc[AB][NBW];
 #pragma unroll
-    for (int ab = 0; ab < 4; ++ab)
+    for (int ab = 0; ab < AB; ++ab)
 #pragma unroll
         for (int g = 0; g < NBW; ++g) acc[ab][g] = f32x4{0.f, 0.f, 0.f, 0.f};
     // fragment rows: A = token row ab 16 + col, B = weight row p EP + g 16 + col;
@@ -282,9 +271,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
         for (int sub = 0; sub < (KSPLIT ? 1 : KC / 32); ++sub) {
             const int po = (((KSPLIT ? wave : sub) * 4 + kg) ^ fs) << 4;
-            bf16x8 a[4];
+            bf16x8 a[AB];
 #pragma unroll
-            for (int ab = 0; ab < 4; ++ab)
+            for (int ab = 0; ab < AB; ++ab)
                 a[ab] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + arow + ab * 16 * ROWB + po));
 #pragma unroll
             for (int g = 0; g < NBW; ++g) {
@@ -300,7 +289,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
 #pragma unroll
-                    for (int ab = 0; ab < 4; ++ab)
+                    for (int ab = 0; ab < AB; ++ab)
                         acc[ab][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab], bp[p], acc[ab][g], 0, 0, 0);
                 }
             }
@@ -317,7 +306,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     // fragment read.
     constexpr int NPASS = NZ == 2 ? 2 : 1;
     int kt = 0;
-    f32x4 acc0[4][NBW];                                  // NZ 2: the first pass's logits
+    f32x4 acc0[4][NBW];                                  // NZ 2 (TB 64): the first pass's logits
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         if (pass == 1) {
@@ -397,47 +386,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #undef MOE_RSTEP
     }
 
-    // ---- logits to LDS (token rows 0..31 in st0, 32..63 in st1; the ring is
-    // drained), then each wave takes 16 tokens across all experts
-    constexpr int ZS = EP + 4;                           // fp32 row stride
-    static_assert(32 * ZS * 4 <= STAGE, "logit rows fit a stage buffer");
-    static_assert(!KSPLIT || (S == 4 && 64 * ZS * 4 <= STAGE), "one stage buffer per wave's partial logits");
-    lds_barrier();
-    if constexpr (KSPLIT) {
-        // wave w's partial sums (its columns of every stage) for all 64 tokens
-        float *zw = reinterpret_cast<float *>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
-#pragma unroll
-        for (int ab = 0; ab < 4; ++ab)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) zw[(ab * 16 + 4 * kg + i) * ZS + col] = acc[ab][0][i];
-    } else {
-#pragma unroll
-    for (int ab = 0; ab < 4; ++ab)
-#pragma unroll
-        for (int g = 0; g < NBW; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = ab * 16 + 4 * kg + i;
-                const int n = (wave * NBW + g) * 16 + col;
-                float *zr = reinterpret_cast<float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
-                if constexpr (NZ == 2) {
-                    // H = (W_r x + b) + eps softplus(W_noise x), softplus as
-                    // max(a, 0) + log(1 + exp(-|a|)) (no overflow)
-                    const int64_t t = t0 + tok;
-                    const bool ok = t < T && n < E;
-                    const float zn = acc[ab][g][i];
-                    const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
-                    const float b = (br != nullptr && n < E) ? br[n] : 0.f;
-                    const float e = ok ? eps[t * E + n] : 0.f;
-                    zr[n] = fmaf(e, sp, acc0[ab][g][i] + b);
-                } else {
-                    zr[n] = acc[ab][g][i];
-                }
-            }
-    }
-    lds_barrier();
-
-    // ---- epilogue: lane holds logits of tokens tw + 4*kg + i, experts nb*16 + col
+    // ---- epilogue: lane holds logits of tokens t0 + 64 h + 16 wave + 4 kg + i,
+    // experts nb 16 + col
     constexpr int NE = NZ == 1 ? NB / 2 : NB;            // expert groups
     static_assert(NZ != 1 || NB % 2 == 0, "noisy halves");
     float bias[NE];                                      // (NZ 2: already in the logits)
@@ -450,121 +400,169 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
     for (int nb = 0; nb < NE; ++nb) psum[nb] = 0.f;
 
+    // passes of 64 tokens (TB = 128: two)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t t = tw + 4 * kg + i;
-        const bool tok_ok = t < T;
-        float v[NE];
-        float mx = -INFINITY;
-        const int tok = wave * RM_TOK_WAVE + 4 * kg + i;
-        const float *zr = reinterpret_cast<const float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
+    for (int h = 0; h < TB / 64; ++h) {
+        // ---- logits to LDS, 64 tokens at a time (token rows 0..31 of the pass in
+        // st0, 32..63 in st1; the ring is drained), then each wave takes 16 of
+        // them across all experts
+        constexpr int ZS = EP + 4;                           // fp32 row stride
+        static_assert(32 * ZS * 4 <= STAGE, "logit rows fit a stage buffer");
+        static_assert(!KSPLIT || (S == 4 && 64 * ZS * 4 <= STAGE), "one stage buffer per wave's partial logits");
+        lds_barrier();
+        if constexpr (KSPLIT) {
+            // wave w's partial sums (its columns of every stage) for all 64 tokens
+            float *zw = reinterpret_cast<float *>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
 #pragma unroll
-        for (int nb = 0; nb < NE; ++nb) {
-            const int n = nb * 16 + col;
-            // K split: the four waves' partial sums, in wave order
-            float z = KSPLIT ? ((reinterpret_cast<const float *>(st0)[tok * ZS + n] +
-                                 reinterpret_cast<const float *>(st1)[tok * ZS + n]) +
-                                reinterpret_cast<const float *>(st2)[tok * ZS + n]) +
-                                   reinterpret_cast<const float *>(st3)[tok * ZS + n] + bias[nb]
-                             : zr[n] + bias[nb];
-            if (NZ == 1) {
-                // H = z + eps softplus(zn); softplus without overflow:
-                // max(a, 0) + log(1 + exp(-|a|))
-                const float zn = zr[NE * 16 + n];
-                const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
-                const float e = (tok_ok && n < E) ? eps[t * E + n] : 0.f;
-                z = fmaf(e, sp, z);
-            }
-            if (logits != nullptr && tok_ok && n < E) logits[t * E + n] = z;
-            if (z != z) z = -INFINITY;          // NaN ranks as -inf: indices stay in range
-            v[nb] = z;
-            if (n < E) mx = fmaxf(mx, z);
-        }
-        mx = row16_max(mx);
-        // exp through the hardware exp2 (about 1 ulp): these terms only feed
-        // the sum s and the per-expert probability sums, whose bounds are far
-        // looser; the gate of the chosen expert is 1 / s with s from them
-        const float mxl = mx * 1.44269504088896341f;
-        float ex[NE];
-        float s = 0.f;
+            for (int ab = 0; ab < 4; ++ab)
 #pragma unroll
-        for (int nb = 0; nb < NE; ++nb) {
-            const int n = nb * 16 + col;
-            ex[nb] = (n < E) ? __builtin_amdgcn_exp2f(fmaf(v[nb], 1.44269504088896341f, -mxl)) : 0.f;
-            s += ex[nb];
-        }
-        s = row16_sum(s);
-        if (tok_ok) {
-            const float inv = 1.0f / s;
+                for (int i = 0; i < 4; ++i) zw[(ab * 16 + 4 * kg + i) * ZS + col] = acc[ab][0][i];
+        } else {
 #pragma unroll
-            for (int nb = 0; nb < NE; ++nb) psum[nb] = fmaf(ex[nb], inv, psum[nb]);
+        for (int abl = 0; abl < 4; ++abl)
+#pragma unroll
+            for (int g = 0; g < NBW; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ab = 4 * h + abl;
+                    const int tok = abl * 16 + 4 * kg + i;
+                    const int n = (wave * NBW + g) * 16 + col;
+                    float *zr = reinterpret_cast<float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
+                    if constexpr (NZ == 2) {
+                        // H = (W_r x + b) + eps softplus(W_noise x), softplus as
+                        // max(a, 0) + log(1 + exp(-|a|)) (no overflow)
+                        const int64_t t = t0 + 64 * h + tok;
+                        const bool ok = t < T && n < E;
+                        const float zn = acc[ab][g][i];
+                        const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
+                        const float b = (br != nullptr && n < E) ? br[n] : 0.f;
+                        const float e = ok ? eps[t * E + n] : 0.f;
+                        zr[n] = fmaf(e, sp, acc0[ab][g][i] + b);
+                    } else {
+                        zr[n] = acc[ab][g][i];
+                    }
+                }
         }
-        if (col == 0) {
-            // z-loss term: log sum_i exp z_i = max + log sum_i exp(z_i - max)
-            const float l = mx + logf(s);
-            sLz[tok] = tok_ok ? l * l : 0.f;
-        }
+        lds_barrier();
 
-        // top-k by k rounds over the not-yet-chosen experts: the round's
-        // largest logit (a 16-lane max), then the lowest expert index holding
-        // it (a 16-lane min), so ties go to the lower index.  Round 0 reuses
-        // the softmax max.  (KSEL = k when it is 1 or 2, so that the common
-        // cases stay small code; 0 = any k up to MAXK.)
-        constexpr int KMAX = KSEL ? KSEL : MAXK;
-        const int kk = KSEL ? KSEL : k;
-        uint32_t excl = 0u;                      // bit nb: this lane's expert nb*16+col is taken
-        static_assert(NE <= 32, "exclusion mask");
-        float vsel[KMAX];
-        int isel[KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            vsel[j] = -INFINITY;
-            isel[j] = 0;
-            if (j < kk) {
-                float m = mx;
-                if (j > 0) {
-                    m = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + 64 * h + wave * RM_TOK_WAVE + 4 * kg + i;
+            const bool tok_ok = t < T;
+            float v[NE];
+            float mx = -INFINITY;
+            const int tok = wave * RM_TOK_WAVE + 4 * kg + i;
+            const float *zr = reinterpret_cast<const float *>(tok < 32 ? st0 : st1) + (tok & 31) * ZS;
 #pragma unroll
-                    for (int nb = 0; nb < NE; ++nb)
-                        if (nb * 16 + col < E && !((excl >> nb) & 1u)) m = fmaxf(m, v[nb]);
-                    m = row16_max(m);
+            for (int nb = 0; nb < NE; ++nb) {
+                const int n = nb * 16 + col;
+                // K split: the four waves' partial sums, in wave order
+                float z = KSPLIT ? ((reinterpret_cast<const float *>(st0)[tok * ZS + n] +
+                                     reinterpret_cast<const float *>(st1)[tok * ZS + n]) +
+                                    reinterpret_cast<const float *>(st2)[tok * ZS + n]) +
+                                       reinterpret_cast<const float *>(st3)[tok * ZS + n] + bias[nb]
+                                 : zr[n] + bias[nb];
+                if (NZ == 1) {
+                    // H = z + eps softplus(zn); softplus without overflow:
+                    // max(a, 0) + log(1 + exp(-|a|))
+                    const float zn = zr[NE * 16 + n];
+                    const float sp = fmaxf(zn, 0.f) + log1pf(expf(-fabsf(zn)));
+                    const float e = (tok_ok && n < E) ? eps[t * E + n] : 0.f;
+                    z = fmaf(e, sp, z);
                 }
-                int best = 0x7fffffff;
-#pragma unroll
-                for (int nb = 0; nb < NE; ++nb) {
-                    const int n = nb * 16 + col;
-                    const bool cand = n < E && !((excl >> nb) & 1u) && v[nb] == m;
-                    best = cand ? min(best, n) : best;
-                }
-                best = row16_min(best);
-                if ((best & 15) == col) excl |= 1u << (best >> 4);
-                vsel[j] = m;
-                isel[j] = best;
+                if (logits != nullptr && tok_ok && n < E) logits[t * E + n] = z;
+                if (z != z) z = -INFINITY;          // NaN ranks as -inf: indices stay in range
+                v[nb] = z;
+                if (n < E) mx = fmaxf(mx, z);
             }
-        }
-        if (tok_ok && col == 0) {
-            if (kk == 1) {
-                out_idx[t] = isel[0];
-                out_gate[t] = 1.0f / s;        // p_{i*} = exp(0) / sum
-                atomicAdd(&sCnt[isel[0]], 1);
-            } else {
-                float ek[KMAX];
-                float sk = 0.f;
+            mx = row16_max(mx);
+            // exp through the hardware exp2 (about 1 ulp): these terms only feed
+            // the sum s and the per-expert probability sums, whose bounds are far
+            // looser; the gate of the chosen expert is 1 / s with s from them
+            const float mxl = mx * 1.44269504088896341f;
+            float ex[NE];
+            float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < KMAX; ++j) {
-                    ek[j] = (j < kk) ? expf(vsel[j] - vsel[0]) : 0.f;
-                    sk += ek[j];
+            for (int nb = 0; nb < NE; ++nb) {
+                const int n = nb * 16 + col;
+                ex[nb] = (n < E) ? __builtin_amdgcn_exp2f(fmaf(v[nb], 1.44269504088896341f, -mxl)) : 0.f;
+                s += ex[nb];
+            }
+            s = row16_sum(s);
+            if (tok_ok) {
+                const float inv = 1.0f / s;
+#pragma unroll
+                for (int nb = 0; nb < NE; ++nb) psum[nb] = fmaf(ex[nb], inv, psum[nb]);
+            }
+            if (col == 0) {
+                // z-loss term: log sum_i exp z_i = max + log sum_i exp(z_i - max)
+                const float l = mx + logf(s);
+                sLz[64 * h + tok] = tok_ok ? l * l : 0.f;
+            }
+
+            // top-k by k rounds over the not-yet-chosen experts: the round's
+            // largest logit (a 16-lane max), then the lowest expert index holding
+            // it (a 16-lane min), so ties go to the lower index.  Round 0 reuses
+            // the softmax max.  (KSEL = k when it is 1 or 2, so that the common
+            // cases stay small code; 0 = any k up to MAXK.)
+            constexpr int KMAX = KSEL ? KSEL : MAXK;
+            const int kk = KSEL ? KSEL : k;
+            uint32_t excl = 0u;                      // bit nb: this lane's expert nb*16+col is taken
+            static_assert(NE <= 32, "exclusion mask");
+            float vsel[KMAX];
+            int isel[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                vsel[j] = -INFINITY;
+                isel[j] = 0;
+                if (j < kk) {
+                    float m = mx;
+                    if (j > 0) {
+                        m = -INFINITY;
+#pragma unroll
+                        for (int nb = 0; nb < NE; ++nb)
+                            if (nb * 16 + col < E && !((excl >> nb) & 1u)) m = fmaxf(m, v[nb]);
+                        m = row16_max(m);
+                    }
+                    int best = 0x7fffffff;
+#pragma unroll
+                    for (int nb = 0; nb < NE; ++nb) {
+                        const int n = nb * 16 + col;
+                        const bool cand = n < E && !((excl >> nb) & 1u) && v[nb] == m;
+                        best = cand ? min(best, n) : best;
+                    }
+                    best = row16_min(best);
+                    if ((best & 15) == col) excl |= 1u << (best >> 4);
+                    vsel[j] = m;
+                    isel[j] = best;
                 }
+            }
+            if (tok_ok && col == 0) {
+                if (kk == 1) {
+                    out_idx[t] = isel[0];
+                    out_gate[t] = 1.0f / s;        // p_{i*} = exp(0) / sum
+                    atomicAdd(&sCnt[isel[0]], 1);
+                } else {
+                    float ek[KMAX];
+                    float sk = 0.f;
 #pragma unroll
-                for (int j = 0; j < KMAX; ++j) {
-                    if (j < kk) {
-                        out_idx[t * k + j] = isel[j];
-                        out_gate[t * k + j] = ek[j] / sk;
-                        atomicAdd(&sCnt[isel[j]], 1);
+                    for (int j = 0; j < KMAX; ++j) {
+                        ek[j] = (j < kk) ? expf(vsel[j] - vsel[0]) : 0.f;
+                        sk += ek[j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < KMAX; ++j) {
+                        if (j < kk) {
+                            out_idx[t * k + j] = isel[j];
+                            out_gate[t * k + j] = ek[j] / sk;
+                            atomicAdd(&sCnt[isel[j]], 1);
+                        }
                     }
                 }
             }
         }
+
+        lds_barrier();                                   // the pass's logits are read
     }
 
     // ---- block partials: probability sums and choice counts per expert
@@ -584,9 +582,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
         part_cnt[(int64_t)blockIdx.x * E + n] = sCnt[n];
     }
     // the block's z-loss partial, summed in a fixed order
-    if (tid < RM_TOK_BLOCK) {
-        static_assert(RM_TOK_BLOCK == 64, "one wave sums the block's tokens");
+    if (tid < 64) {
+        static_assert(TB % 64 == 0, "one wave sums the block's tokens");
         float v = sLz[tid];
+#pragma unroll
+        for (int h = 1; h < TB / 64; ++h) v += sLz[64 * h + tid];
         for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
         if (tid == 0) part_z[blockIdx.x] = v;
     }
@@ -772,8 +772,11 @@ int noisy_half_rows(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128
 
 }  // namespace
 
+// tokens per block of the plain MFMA router: 128 with more than 128 experts
+static int router_tok_block(int E) { return E > 128 ? 128 : RM_TOK_BLOCK; }
+
 int router_blocks(int64_t T, int dtype_bf16, int E) {
-    const int per = use_mfma(dtype_bf16, E) ? RM_TOK_BLOCK : RG_TOK;
+    const int per = use_mfma(dtype_bf16, E) ? router_tok_block(E) : RG_TOK;
     return (int)((T + per - 1) / per);
 }
 
@@ -784,36 +787,32 @@ hipError_t launch_router(const void *x, int dtype_bf16, const float *W_r, const 
     const int nblk = router_blocks(T, dtype_bf16, E);
     if (nblk == 0) return hipSuccess;
     if (use_mfma(dtype_bf16, E)) {
-        // up to 128 experts W_r is staged in fp32 and split into its bf16 parts
-        // in registers; beyond, the kernel reads the parts from w3
-        const int nb = (E + 15) / 16;
-        if (nb > 8) {
-            const int64_t n = (int64_t)E * d;
-            const int sg = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-            hipLaunchKernelGGL(router_split_kernel, dim3(sg), dim3(256), 0, s, W_r, n, w3);
-        }
+        // W_r is staged in fp32 and split into its bf16 parts in registers
+        // (w3 is left unused); more than 128 experts take 128 tokens a block
+        (void)w3;
         const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
-#define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, NZV)                                           \
-    hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, NZV>), dim3(nblk), dim3(256),   \
-                       0, s, xb, w3, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,          \
+        const int nb = (E + 15) / 16;
+#define MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, KSV, TBV)                                           \
+    hipLaunchKernelGGL((router_mfma_kernel<NBV, KCV, TAILV, KSV, 0, TBV>), dim3(nblk), dim3(256), \
+                       0, s, xb, nullptr, W_r, b_r, T, d, E, k, expert_idx, gate, part_prob,     \
                        part_cnt, part_z, nullptr, logits)
-#define MOE_ROUTER_K(NBV, KCV, TAILV)                                                          \
+#define MOE_ROUTER_K(NBV, KCV, TAILV, TBV)                                                     \
     do {                                                                                       \
-        if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, 0);                                  \
-        else if (k == 2) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 2, 0);                             \
-        else MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 0, 0);                                         \
+        if (k == 1) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 1, TBV);                                \
+        else if (k == 2) MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 2, TBV);                           \
+        else MOE_ROUTER_LAUNCH(NBV, KCV, TAILV, 0, TBV);                                       \
     } while (0)
-#define MOE_ROUTER_CASE(NBV, KCV)                                                              \
+#define MOE_ROUTER_CASE(NBV, KCV, TBV)                                                         \
     if (nb <= NBV) {                                                                           \
-        static_assert(rgeo_ok<NBV, KCV, NBV <= 8 ? 2 : 3>(), "router ring");                   \
-        if (d % KCV == 0) MOE_ROUTER_K(NBV, KCV, false);                                       \
-        else MOE_ROUTER_K(NBV, KCV, true);                                                     \
+        static_assert(rgeo_ok<NBV, KCV, 2, TBV>(), "router ring");                             \
+        if (d % KCV == 0) MOE_ROUTER_K(NBV, KCV, false, TBV);                                  \
+        else MOE_ROUTER_K(NBV, KCV, true, TBV);                                                \
         return hipGetLastError();                                                              \
     }
-        MOE_ROUTER_CASE(1, 128)
-        MOE_ROUTER_CASE(4, 64)
-        MOE_ROUTER_CASE(8, 64)
-        MOE_ROUTER_CASE(16, 32)
+        MOE_ROUTER_CASE(1, 128, 64)
+        MOE_ROUTER_CASE(4, 64, 64)
+        MOE_ROUTER_CASE(8, 64, 64)
+        MOE_ROUTER_CASE(16, 32, 128)
 #undef MOE_ROUTER_CASE
 #undef MOE_ROUTER_K
 #undef MOE_ROUTER_LAUNCH

@@ -28,6 +28,9 @@ SMALL = {
     "top2_swiglu": (777, 64, 136, 10, 2, 1.0, "bf16", "swiglu", False, False, 6.0),
     "top3_relu": (517, 32, 96, 7, 3, 0.8, "bf16", "relu", False, False, 5.0),
     "e300_generic": (400, 32, 64, 300, 2, 2.0, "bf16", "relu", False, False, 2.0),
+    # 128 < E <= 256: the MFMA router with 128 tokens a block (a ragged last
+    # block, a K tail of 8 columns)
+    "e200_mfma": (1000, 136, 72, 200, 2, 2.0, "bf16", "relu", False, True, 2.0),
     "f32_swiglu": (150, 16, 24, 6, 2, 1.5, "f32", "swiglu", False, True, 4.0),
     "tiles": (4096, 256, 384, 16, 1, 1.25, "bf16", "relu", True, False, 1.0),
     # experts of at least 512 rows: the 256-row GEMM tiles, with K and N tails
