@@ -31,7 +31,6 @@ import argparse
 import csv
 import ctypes
 import glob
-import hashlib
 import json
 import os
 import re
@@ -167,26 +166,18 @@ PROFILE_COMMANDS = [
 ]
 
 
-_COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
-
-
 def source_digest() -> str:
-    """sha256 over the kernel sources with comments and blank space removed:
-    counters taken on other code are stale, a reworded comment changes nothing."""
-    h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if path.endswith((".hip", ".h")):
-            h.update(os.path.basename(path).encode())
-            with open(path, encoding="utf-8") as fh:
-                code = _COMMENT.sub(" ", fh.read())
-            h.update(" ".join(code.split()).encode())
-    return h.hexdigest()[:16]
+    """The kernel sources' digest (comments and blank space removed): counters
+    taken on other code are stale, a reworded comment changes nothing."""
+    from sparse_mixture_experts_argmax_amd.source_digest import source_digest as digest
+    return digest(CSRC)
 
 
 _GEMM_ACT = re.compile(r"gemm_(?:bf16|f32)_kernel<(?:[^<>]*<[^<>]*>, )?(\d+),")
 
 
-_NOISY = re.compile(r"router_generic_kernel<\w+, true>|router_mfma_kernel<\d+, \d+, \w+, \d+, [12]>"
+# the noisy router kernels: NZ (the fifth argument) 1 or 2, tokens per block after it
+_NOISY = re.compile(r"router_generic_kernel<\w+, true>|router_mfma_kernel<\d+, \d+, \w+, \d+, [12](?:, \d+)?>"
                     r"|router_split_noisy_kernel|router_reduce_kernel")
 
 

@@ -87,6 +87,15 @@ typedef enum {
 const char *moe_status_string(int status);
 
 /*
+ * The digest of the kernel sources this library was built from (16 hex
+ * digits of a sha256 over the csrc/ files with comments and blank space
+ * removed; static string, never NULL).  A caller that holds the sources can
+ * compare it with their digest to tell a stale build; the Python binding
+ * refuses to load a library whose digest differs from its tree's.
+ */
+const char *moe_source_digest(void);
+
+/*
  * Expert capacity C = ceil(capacity_factor * k * T / E - 1e-9), clamped to
  * [0, T].  Host function, no GPU work.
  * [SW-GLaM] "Expert Capacity 与 Token Dropping": C = (T/N) x capacity factor;

@@ -8,6 +8,8 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+from .source_digest import source_digest
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
@@ -40,6 +42,7 @@ class WsLayout(C.Structure):
 # name -> (restype, argtypes); mirrors include/moe.h
 SIGNATURES = {
     "moe_status_string": (C.c_char_p, [C.c_int]),
+    "moe_source_digest": (C.c_char_p, []),
     "moe_capacity": (_i64, [_i64, _i32, _i32, C.c_double]),
     "moe_router_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i32, _i32]),
@@ -109,6 +112,14 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    # a library built from other kernel sources than the tree's would run
+    # code that no test in this tree has seen
+    built = lib.moe_source_digest().decode()
+    here = source_digest()
+    if built != here:
+        raise RuntimeError(
+            f"{path} was built from other sources (digest {built}, the tree's csrc/ is {here}): rebuild it "
+            "with `python sparse_mixture_experts_argmax_amd/build.py`")
     return lib
 
 

@@ -61,6 +61,24 @@ def _stale(src: str, obj: str, headers: list) -> bool:
     return any(os.path.getmtime(p) > t for p in [src, *headers])
 
 
+def _digest_object() -> str:
+    """moe_source_digest(): the digest of the sources being built, in an object
+    of its own (source_digest.py by path, like this script)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_moe_digest", os.path.join(PKG, "source_digest.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    src = os.path.join(BUILD_DIR, "source_digest.cpp")
+    obj = os.path.join(BUILD_DIR, "source_digest.o")
+    with open(src, "w") as fh:
+        fh.write("// written by build.py: the digest of the sources this library is built from\n"
+                 f'extern "C" const char *moe_source_digest(void) {{ return "{mod.source_digest(CSRC)}"; }}\n')
+    r = subprocess.run(["g++", "-O2", "-fPIC", "-c", src, "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed on {src}:\n{r.stderr}")
+    return obj
+
+
 def build(jobs: int | None = None, incremental: bool = False) -> str:
     """Compile every .hip file and link libmoe.so.  incremental=True recompiles
     only the objects that are older than their source or any header."""
@@ -72,6 +90,7 @@ def build(jobs: int | None = None, incremental: bool = False) -> str:
     n = jobs or min(8, max(1, len(todo)), os.cpu_count() or 1)
     with ThreadPoolExecutor(n) as ex:
         list(ex.map(lambda so: _compile(*so), todo))
+    objs = objs + [_digest_object()]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
