@@ -33,7 +33,8 @@
 //   * The epilogue adds the bias, applies the activation and rounds to bf16;
 //     the tile goes out through LDS as coalesced 16-byte row stores when it
 //     fits a stage buffer, else straight from registers.
-// fp32 path: a plain LDS-tiled FMA kernel (64 x 64 x 16 tiles).
+// fp32 path: a plain LDS-tiled FMA kernel (64 x 64 x 32 tiles, the next K
+// tile's loads in flight during the current one's FMAs).
 #include "gemm_kernel.h"
 
 #include <atomic>
@@ -45,8 +46,13 @@ namespace {
 // ---------------------------------------------------------------------------
 // fp32 path
 // ---------------------------------------------------------------------------
-constexpr int FBM = 64, FBN = 64, FBK = 16;
+constexpr int FBM = 64, FBN = 64, FBK = 32;
+constexpr int FLQ = FBM * FBK / 256;                 // values of each operand a thread stages per K tile
 
+// The K loop keeps the next K tile's loads in flight (in registers) while the
+// current tile is multiplied out of LDS, so that a step costs its FMAs rather
+// than a global-memory round trip; each output still sums its K terms in
+// ascending k, one fma at a time.
 template <int ACT, bool BIAS>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float *__restrict__ A, const float *__restrict__ B, const float *__restrict__ B3,
@@ -72,21 +78,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float *Be = B + (int64_t)e * N * K;
     const float *B3e = DUAL ? B3 + (int64_t)e * N * K : nullptr;
 
-    float acc[4][4] = {};
-    float acc3[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += FBK) {
-        for (int q = tid; q < FBM * FBK; q += 256) {
+    // staged value l of this thread: tile row r = q / FBK, column c = q % FBK
+    // (q = tid + 256 l), so 32 consecutive threads read 128 contiguous bytes
+    // of one row; rows past the count or past N repeat the last one
+    float ra[FLQ], rb[FLQ], rb3[DUAL ? FLQ : 1];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int l = 0; l < FLQ; ++l) {
+            const int q = tid + 256 * l;
             const int r = q / FBK, c = q % FBK;
             int am = m0 + r;
             if (am > cnt - 1) am = cnt - 1;
             int bn = n0 + r;
             if (bn > N - 1) bn = N - 1;
             const bool in = k0 + c < K;
-            sA[c][r] = in ? Ae[(int64_t)am * K + k0 + c] : 0.f;
-            sB[c][r] = in ? Be[(int64_t)bn * K + k0 + c] : 0.f;
-            if (DUAL) sB3[c][r] = in ? B3e[(int64_t)bn * K + k0 + c] : 0.f;
+            ra[l] = in ? Ae[(int64_t)am * K + k0 + c] : 0.f;
+            rb[l] = in ? Be[(int64_t)bn * K + k0 + c] : 0.f;
+            if (DUAL) rb3[DUAL ? l : 0] = in ? B3e[(int64_t)bn * K + k0 + c] : 0.f;
         }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int l = 0; l < FLQ; ++l) {
+            const int q = tid + 256 * l;
+            const int r = q / FBK, c = q % FBK;
+            sA[c][r] = ra[l];
+            sB[c][r] = rb[l];
+            if (DUAL) sB3[DUAL ? c : 0][r] = rb3[DUAL ? l : 0];
+        }
+    };
+
+    float acc[4][4] = {};
+    float acc3[4][4] = {};
+    load(0);
+    for (int k0 = 0; k0 < K; k0 += FBK) {
+        store();
         __syncthreads();
+        if (k0 + FBK < K) load(k0 + FBK);
+#pragma unroll 8
         for (int kk = 0; kk < FBK; ++kk) {
             float a[4], b[4], b3[4];
             for (int i = 0; i < 4; ++i) a[i] = sA[kk][tm + i];
