@@ -861,10 +861,33 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t st2[SPLIT ? SBW : (S > 2 ? STAGE : 16)];
     __shared__ __attribute__((aligned(1024))) uint8_t st3[SPLIT ? SBW : (S > 3 ? STAGE : 16)];
     __shared__ __attribute__((aligned(1024))) uint8_t st4[SPLIT ? SBW : 16];
-    __shared__ int s_map[EXPERT ? 1 : MAX_E_LDS + 1];
-    __shared__ int s_tok[BM];                            // scattering: token and gate of each row
-    __shared__ float s_g[BM];
-    __shared__ int s_last;
+    // the tile map (read before the ring starts), the scattered rows' tokens
+    // and gates and the split flag (both used after the ring has drained):
+    // when the ring takes the whole LDS they live in the last weight stage,
+    // which the ring first fills in its first step (after a barrier every
+    // wave reaches past its tile-map reads) and which the epilogue's row
+    // staging (chunks of 64 rows in the first four stages) leaves alone
+    constexpr int NMAP = EXPERT ? 1 : MAX_E_LDS + 1;
+    constexpr int SMALL = (NMAP + 2 * BM + 1) * 4;
+    constexpr bool ALIAS = SPLIT && 2 * SA + 3 * SBW + SMALL > 160 * 1024;
+    static_assert(!ALIAS || (SMALL <= SBW && FM <= 4 && 64 * BN * 2 <= SA), "small arrays in the last weight stage");
+    int *s_map, *s_tok, *s_last;                         // s_tok, s_g: scattering, token and gate of each row
+    float *s_g;
+    if constexpr (ALIAS) {
+        s_map = reinterpret_cast<int *>(st4);
+        s_tok = s_map + NMAP;
+        s_g = reinterpret_cast<float *>(s_tok + BM);
+        s_last = reinterpret_cast<int *>(s_g + BM);
+    } else {
+        __shared__ int s_map_[NMAP];
+        __shared__ int s_tok_[BM];
+        __shared__ float s_g_[BM];
+        __shared__ int s_last_;
+        s_map = s_map_;
+        s_tok = s_tok_;
+        s_g = s_g_;
+        s_last = &s_last_;
+    }
 
     int e, mt, nt;
     SplitPart sp{1, 0, 0};
@@ -902,7 +925,7 @@ __global__ __launch_bounds__(256, TL::MINB) void gemm_bf16_kernel(
     c.sp = SplitPart{1, 0, 0};
     c.part = fz.part;
     c.flags = fz.flags;
-    c.sflag = &s_last;
+    c.sflag = s_last;
     if constexpr (!EXPERT) {
         // wave-uniform (scalar registers: the vector ones are all taken)
         c.sp.ns = __builtin_amdgcn_readfirstlane(sp.ns);
@@ -1003,21 +1026,24 @@ inline int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_boun
 
 // bf16 tile shapes: W = wide (192 or 256 output columns), N = 128 columns,
 // G = gated (128 columns of each weight); the suffix is BM.  64-wide K
-// stages, one block per CU and 112-152 KB rings (one or two stages ahead of
+// stages, one block per CU and 112-160 KB rings (one or two stages ahead of
 // the MFMAs), except the narrow 128-row shape, which runs two blocks per CU
 // on 32-wide K stages.  The 256- and 320-row tiles spread each stage's DMA
 // over the MFMAs of the first two k steps (measured faster there; neutral to
 // slower on the 128-row ones).  The wide 320- and 192-row tiles (one tile per
-// expert, weights streamed once) use the split ring, which keeps the weights
-// two K tiles ahead: 3 % off both many-expert GEMMs for the 192-row one,
-// where the two-stage ring left the weight stream waiting on HBM latency;
-// the wide 128-row tile measured 6 % slower with it and keeps three uniform
-// stages.
+// expert, weights streamed once) and the 256-row wide and gated tiles use the
+// split ring, which keeps the weights two K tiles ahead: 3 % off both
+// many-expert GEMMs for the 192-row one, where the two-stage ring left the
+// weight stream waiting on HBM latency; on the Mixtral-shaped layer 1 % off
+// the first GEMM and 2 % off the second (alternating runs on one device; the
+// ring then fills all 160 KB of LDS, and the kernel's small arrays move into
+// its last weight stage); the wide 128-row tile measured 6 % slower with it
+// and keeps three uniform stages.
 using TileW320 = Tile<320, 192, 2, 64, 1, 2, 3>;
 using TileN320 = Tile<320, 128, 2, 64, 1, 2>;
-using TileW256 = Tile<256, 256, 2, 64, 1, 2>;
+using TileW256 = Tile<256, 256, 2, 64, 1, 2, 3>;
 using TileN256 = Tile<256, 128, 3, 64, 1, 2>;
-using TileG256 = Tile<256, 128, 2, 64, 1, 2>;
+using TileG256 = Tile<256, 128, 2, 64, 1, 2, 3>;
 using TileW192 = Tile<192, 256, 2, 64, 1, 2, 3, 2>;
 using TileN192 = Tile<192, 128, 3, 64, 1, 0>;
 using TileW128 = Tile<128, 256, 3, 64, 1, 0>;
