@@ -1041,9 +1041,9 @@ inline int64_t grid_for(int64_t C, int E, int bm, int tiles_n, int64_t rows_boun
 // and keeps three uniform stages.
 using TileW320 = Tile<320, 192, 2, 64, 1, 2, 3>;
 using TileN320 = Tile<320, 128, 2, 64, 1, 2>;
-using TileW256 = Tile<256, 256, 2, 64, 1, 2, 3>;
+using TileW256 = Tile<256, 256, 2, 64, 1, 2, 3, 2>;
 using TileN256 = Tile<256, 128, 3, 64, 1, 2>;
-using TileG256 = Tile<256, 128, 2, 64, 1, 2, 3>;
+using TileG256 = Tile<256, 128, 2, 64, 1, 2, 3, 2>;
 using TileW192 = Tile<192, 256, 2, 64, 1, 2, 3, 2>;
 using TileN192 = Tile<192, 128, 3, 64, 1, 0>;
 using TileW128 = Tile<128, 256, 3, 64, 1, 0>;
