@@ -158,6 +158,9 @@ PROFILE_COMMANDS = [
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/write -o w -- "
     "python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --others 0 "
     "--expert-backward-calls 1",
+    "timeout -s KILL 120 rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv "
+    "-d {o}/mfma -o m -- python3 $REPO/bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --others 0 "
+    "--expert-backward-calls 1",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {o}/copy_fetch -o c -- "
     "python3 $REPO/bench.py --copy-probe %d" % COPY_PROBE_BYTES,
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {o}/copy_write -o c -- "
@@ -248,6 +251,50 @@ def _per_stage_kib(d: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def _num_xcc(d: str) -> int:
+    """XCDs of the profiled GPU (GRBM_GUI_ACTIVE adds up one count per XCD)."""
+    for path in glob.glob(os.path.join(d, "*agent_info.csv")):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Agent_Type") == "GPU" and r.get("Num_Xcc"):
+                    return int(r["Num_Xcc"])
+    raise SystemExit(f"no GPU agent under {d}")
+
+
+def mfma_by_stage(d: str, peak: float = PEAK_TFLOPS["bf16"] * 1e12) -> dict:
+    """Per stage, over the launches that ran bf16 MFMAs: the MFMA flops the
+    counters saw (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), MfmaUtil (MFMA busy
+    cycles over active cycles x SIMDs, duration-weighted), the effective
+    clock (GRBM_GUI_ACTIVE per XCD over the launch's duration) and the flop
+    rate as a fraction of the nominal bf16 peak (under the counters)."""
+    rows = _counter_rows(d)
+    stage = stages_by_dispatch(rows)
+    per = {}
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        rec = per.setdefault(did, dict(dur=int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        rec[r["Counter_Name"]] = float(r["Counter_Value"])
+    xcc = _num_xcc(d)
+    acc = {}
+    for did, rec in per.items():
+        mops = rec.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        if mops <= 0 or rec["dur"] <= 0:
+            continue
+        a = acc.setdefault(stage[did], dict(n=0, dur=0, mops=0.0, util_dur=0.0, cycles=0.0))
+        a["n"] += 1
+        a["dur"] += rec["dur"]
+        a["mops"] += mops
+        a["util_dur"] += rec.get("MfmaUtil", 0.0) * rec["dur"]
+        a["cycles"] += rec.get("GRBM_GUI_ACTIVE", 0.0) / xcc
+    out = {}
+    for st, a in acc.items():
+        flops = a["mops"] * 512
+        out[st] = dict(launches=a["n"], flops_per_launch=flops / a["n"], avg_us=a["dur"] / a["n"] / 1e3,
+                       mfma_util_pct=a["util_dur"] / a["dur"], clock_ghz=a["cycles"] / a["dur"],
+                       frac_of_peak=flops / (a["dur"] * 1e-9) / peak)
+    return out
+
+
 def _copy_kib(d: str, counter: str) -> float:
     vals = [float(r["Counter_Value"]) for r in _counter_rows(d)
             if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
@@ -307,6 +354,23 @@ def summarize(prof_dir: str, workload: str) -> str:
         traffic[st] = dict(fetch_bytes=round(fb), write_bytes=round(wb), traffic_bytes=round(fb + wb))
         lines.append(f"| {st} | {fetch.get(st, 0):.1f} | {write.get(st, 0):.1f} | {fb:.0f} | {wb:.0f} "
                      f"| {fb + wb:.0f} |")
+    mdir = os.path.join(prof_dir, "mfma")
+    if os.path.isdir(mdir):
+        mf = mfma_by_stage(mdir)
+        lines += ["", "## MFMA utilisation (rocprofv3 --pmc MfmaUtil GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
+                  "MfmaUtil: MFMA busy cycles over active cycles x SIMDs (at the clock the chip ran); clock: "
+                  "GRBM_GUI_ACTIVE per XCD over the launch's duration (the counter's window is a few us wider "
+                  "than the kernel's, so on launches shorter than about 0.5 ms it reads high, even above the "
+                  "2.4 GHz ceiling; the long launches give the clock); fraction of peak: the counted MFMA flops "
+                  f"over the duration against the nominal {PEAK_TFLOPS['bf16']:.0f} TFLOP/s (counters slow a launch "
+                  "by a few per cent). Stages whose launches ran no bf16 MFMA are left out.", "",
+                  "| stage | launches | MFMA flops per launch (counter) | avg us (under counters) | MfmaUtil % "
+                  "| effective clock GHz | fraction of nominal bf16 peak |",
+                  "|---|---|---|---|---|---|---|"]
+        for st in sorted(mf):
+            m = mf[st]
+            lines.append(f"| {st} | {m['launches']} | {m['flops_per_launch']:.4g} | {m['avg_us']:.1f} "
+                         f"| {m['mfma_util_pct']:.1f} | {m['clock_ghz']:.2f} | {m['frac_of_peak']:.3f} |")
     lines += ["", "Per launch means the mean over that stage's kernel launches in the profiled steps; "
               "the dispatch, noisy_router and expert_backward stages are several kernels, each counted as "
               "one launch (the expert backward's launches are those from an expert-backward call's first "
