@@ -275,22 +275,37 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
             for (int ab = 0; ab < AB; ++ab)
                 a[ab] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + arow + ab * 16 * ROWB + po));
-#pragma unroll
-            for (int g = 0; g < NBW; ++g) {
-                const int o = brow + g * 16 * ROWB + po;
-                bf16x8 bp[3];
+            // the weight parts of group g + 1 are read (and split) while the
+            // MFMAs of group g run
+            auto wfrag = [&](int g, bf16x8 (&bp)[3]) {
                 if constexpr (WF32) {
                     wf_frag(sb, g, KSPLIT ? wave : sub, bp);
                 } else {
+                    const int o = brow + g * 16 * ROWB + po;
 #pragma unroll
                     for (int p = 0; p < 3; ++p)
                         bp[p] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + p * EP * ROWB + o));
                 }
+            };
+            bf16x8 bp[2][3];
+            wfrag(0, bp[0]);
+#pragma unroll
+            for (int g = 0; g < NBW; ++g) {
+                if (g + 1 < NBW) wfrag(g + 1, bp[(g + 1) & 1]);
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
 #pragma unroll
                     for (int ab = 0; ab < AB; ++ab)
-                        acc[ab][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab], bp[p], acc[ab][g], 0, 0, 0);
+                        acc[ab][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab], bp[g & 1][p], acc[ab][g], 0, 0, 0);
+                }
+                if (g + 1 < NBW) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // the next group's reads
+#pragma unroll
+                    for (int r = 0; r < 3 * AB; ++r) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // the next split, a few VALU at a time
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
