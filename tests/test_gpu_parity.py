@@ -36,6 +36,10 @@ SMALL = {
     # experts of at least 512 rows: the 256-row GEMM tiles, with K and N tails
     "big_tiles": (3000, 200, 328, 4, 2, 1.0, "bf16", "relu", True, False, 1.0),
     "big_swiglu": (2048, 136, 200, 2, 1, 1.0, "bf16", "swiglu", False, False, 1.0),
+    # at least 256 tiles of 256 x 256 in the second GEMM: the split ring
+    # over the whole LDS, with a K tail (f = 264), an N tail (d = 4104) and
+    # partly filled row tiles
+    "wide_256": (2048, 4104, 264, 8, 2, 1.0, "bf16", "relu", True, False, 1.0),
     # capacity 300 and 170: one 320- or 192-row tile per expert, in the wide
     # column tiles (first GEMM) and the narrow ones (second), with K and N tails
     "tiles_320": (19200, 72, 776, 64, 1, 1.0, "bf16", "relu", True, False, 1.0),
@@ -287,7 +291,7 @@ def _ffn_rows(cfg, per_block=None, seed=7):
     return np.concatenate(got), np.concatenate(ref), np.concatenate(bnd), n
 
 
-@pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "tiles_320",
+@pytest.mark.parametrize("name", ["tiles", "top2_swiglu", "big_tiles", "big_swiglu", "wide_256", "tiles_320",
                                   "tiles_192", "tiles_128", "ragged_f32", "switch_base", "zipf_skew",
                                   "mixtral", "many_expert"] + SPLIT)
 def test_expert_ffn_elementwise(name):
