@@ -200,6 +200,97 @@ __global__ __launch_bounds__(256) void act_backward_kernel(
     }
 }
 
+// The bf16 activation backward with 16-byte accesses (the scheme of
+// transpose16_kernel): a thread takes 8 consecutive columns of one row for
+// the loads, the arithmetic and the row-major stores, then 8 consecutive
+// rows of one column for the transposed stores (gathered from the LDS tiles
+// one element at a time).  The same arithmetic element for element as
+// act_backward_kernel.  Needs f % 8 == 0; Cp is a multiple of 64.
+template <bool SW>
+__global__ __launch_bounds__(256) void act_backward16_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ G, const uint16_t *__restrict__ dH,
+    const int32_t *__restrict__ count, int64_t C, int f, int Cp, uint16_t *__restrict__ dAG,
+    uint16_t *__restrict__ Ht, uint16_t *__restrict__ dAt, uint16_t *__restrict__ dGt) {
+    __shared__ __attribute__((aligned(16))) uint16_t sH[TT][TT + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sA[TT][TT + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sG[SW ? TT : 1][TT + 8];
+    const int e = blockIdx.z;
+    const int j0 = blockIdx.x * TT;
+    const int m0 = blockIdx.y * TT;
+    int cnt = count[e];
+    cnt = cnt < 0 ? 0 : (cnt > C ? (int)C : cnt);
+    const int nf = SW ? 2 * f : f;
+    const int64_t rbase = (int64_t)e * C * f;
+    const int t = threadIdx.x;
+    // 64 rows x 8 pieces of 8 columns, two per thread
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int q = t + 256 * hh;
+        const int i = q >> 3, pc = (q & 7) * 8;
+        const int m = m0 + i, j = j0 + pc;
+        u32x4 hv = {0u, 0u, 0u, 0u}, av = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+        if (m < cnt && j < f) {
+            const int64_t o = rbase + (int64_t)m * f + j;
+            const u32x4 a8 = ld16(A + o);
+            const u32x4 d8 = ld16(dH + o);
+            u32x4 g8 = {0u, 0u, 0u, 0u};
+            if (SW) g8 = ld16(G + o);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float h2[2], da2[2], dg2[2];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const float a = bf2f((uint16_t)(a8[u] >> (16 * w)));
+                    const float dh = bf2f((uint16_t)(d8[u] >> (16 * w)));
+                    if (SW) {
+                        const float g = bf2f((uint16_t)(g8[u] >> (16 * w)));
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.44269504088896341f));
+                        const float sa = a * sg;
+                        h2[w] = sa * g;
+                        da2[w] = dh * g * (sg * (1.0f + a * (1.0f - sg)));
+                        dg2[w] = dh * sa;
+                    } else {
+                        h2[w] = fmaxf(a, 0.f);
+                        da2[w] = a > 0.f ? dh : 0.f;
+                        dg2[w] = 0.f;
+                    }
+                }
+                hv[u] = pack_bf16x2(h2[0], h2[1]);
+                av[u] = pack_bf16x2(da2[0], da2[1]);
+                gv[u] = pack_bf16x2(dg2[0], dg2[1]);
+            }
+            uint16_t *row = dAG + ((int64_t)e * C + m) * nf;
+            st16(row + j, av);
+            if (SW) st16(row + f + j, gv);
+        }
+        *reinterpret_cast<u32x4 *>(&sH[i][pc]) = hv;
+        *reinterpret_cast<u32x4 *>(&sA[i][pc]) = av;
+        if (SW) *reinterpret_cast<u32x4 *>(&sG[SW ? i : 0][pc]) = gv;
+    }
+    __syncthreads();
+    // 64 destination rows (columns j) x 8 pieces of 8 rows m
+    const int64_t tbase = (int64_t)e * f * Cp;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int q = t + 256 * hh;
+        const int jj = q >> 3, pr = (q & 7) * 8;
+        const int j = j0 + jj, m = m0 + pr;
+        if (j < f && m < Cp) {
+            const int64_t o = tbase + (int64_t)j * Cp + m;
+            u32x4 vh, va, vg;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                vh[u] = (uint32_t)sH[pr + 2 * u][jj] | ((uint32_t)sH[pr + 2 * u + 1][jj] << 16);
+                va[u] = (uint32_t)sA[pr + 2 * u][jj] | ((uint32_t)sA[pr + 2 * u + 1][jj] << 16);
+                if (SW) vg[u] = (uint32_t)sG[SW ? pr + 2 * u : 0][jj] | ((uint32_t)sG[SW ? pr + 2 * u + 1 : 0][jj] << 16);
+            }
+            st16(Ht + o, vh);
+            st16(dAt + o, va);
+            if (SW) st16(dGt + o, vg);
+        }
+    }
+}
+
 // dst[r] = sum over c < Cp of src[r][c] (fp32, lane-strided then a butterfly:
 // a fixed order), one wave per row, rounded to the storage dtype.
 template <bool BF16>
@@ -412,7 +503,16 @@ hipError_t launch_expert_backward(const void *xbuf, int dtype_bf16, const int32_
     hipLaunchKernelGGL((act_backward_kernel<BF, SWV>), grid, dim3(256), 0, s, (const T_ *)Aa, (const T_ *)Ga,   \
                        (const T_ *)dH, expert_count, C, f, Cp, (T_ *)dAG, (T_ *)Ht, (T_ *)dAt, (T_ *)dGt)
         if (C > 0) {
-            if (dtype_bf16) {
+            if (dtype_bf16 && f % 8 == 0) {
+                if (sw)
+                    hipLaunchKernelGGL((act_backward16_kernel<true>), grid, dim3(256), 0, s, (const uint16_t *)Aa,
+                                       (const uint16_t *)Ga, (const uint16_t *)dH, expert_count, C, f, Cp,
+                                       (uint16_t *)dAG, (uint16_t *)Ht, (uint16_t *)dAt, (uint16_t *)dGt);
+                else
+                    hipLaunchKernelGGL((act_backward16_kernel<false>), grid, dim3(256), 0, s, (const uint16_t *)Aa,
+                                       (const uint16_t *)Ga, (const uint16_t *)dH, expert_count, C, f, Cp,
+                                       (uint16_t *)dAG, (uint16_t *)Ht, (uint16_t *)dAt, (uint16_t *)dGt);
+            } else if (dtype_bf16) {
                 if (sw) MOE_ACTB(true, true, uint16_t); else MOE_ACTB(true, false, uint16_t);
             } else {
                 if (sw) MOE_ACTB(false, true, float); else MOE_ACTB(false, false, float);
