@@ -39,3 +39,34 @@ def bench():
 ])
 def test_kernel_stage(bench, name, stage):
     assert bench.kernel_stage(name) == stage
+
+
+def test_mfma_by_stage_from_counter_rows(bench, tmp_path):
+    """The MFMA pass summary on two made-up launches of the first GEMM: counted
+    flops, duration-weighted MfmaUtil, clock per XCD and the fraction of peak."""
+    import csv
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    name = "gemm_bf16_kernel<Tile<256, 128, 2, 64, 1, 2, 3, 2>, 2, false, false, false, false>"
+    rows = []
+    # launch 1: 1 ms, 2.0 GHz on 8 XCDs, 60 % busy, 1.25 TFLOP; launch 2: 3 ms, 1.5 GHz, 70 %
+    for did, dur_ns, ghz, util, flops in [(1, 1_000_000, 2.0, 60.0, 1.25e12), (2, 3_000_000, 1.5, 70.0, 3.75e12)]:
+        for cname, val in [("GRBM_GUI_ACTIVE", ghz * dur_ns * 8), ("MfmaUtil", util),
+                           ("SQ_INSTS_VALU_MFMA_MOPS_BF16", flops / 512)]:
+            rows.append(dict(Dispatch_Id=did, Kernel_Name=name, Counter_Name=cname, Counter_Value=val,
+                             Start_Timestamp=10, End_Timestamp=10 + dur_ns))
+    with open(tmp_path / "m_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=cols)
+        w.writeheader()
+        w.writerows(rows)
+    with open(tmp_path / "m_agent_info.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Agent_Type", "Num_Xcc"])
+        w.writeheader()
+        w.writerow(dict(Agent_Type="CPU", Num_Xcc=0))
+        w.writerow(dict(Agent_Type="GPU", Num_Xcc=8))
+    m = bench.mfma_by_stage(str(tmp_path))["expert_gemm1"]
+    assert m["launches"] == 2
+    assert m["flops_per_launch"] == pytest.approx(2.5e12)
+    assert m["avg_us"] == pytest.approx(2000.0)
+    assert m["mfma_util_pct"] == pytest.approx((60.0 * 1 + 70.0 * 3) / 4)
+    assert m["clock_ghz"] == pytest.approx((2.0 * 1 + 1.5 * 3) / 4)
+    assert m["frac_of_peak"] == pytest.approx(5.0e12 / 4e-3 / 2.5e15)
